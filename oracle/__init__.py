@@ -1,0 +1,133 @@
+"""fp64 CPU oracle of the mLSTM matrix-memory cell -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (``mlstm_matrix_memory_amd``)
+never imports, links or calls it, and it shares no code with the HIP library.
+
+The arithmetic lives in ``mlstm_oracle.c`` (plain C, fp64, OpenMP over the
+independent heads): the stabilized mLSTM recurrence of "xLSTM: Extended Long
+Short-Term Memory", section 2.3 (eq. (18), the normalizer paragraph and the
+multi-head paragraph) with the stabilizer of section 2.2 (eq. (17)).  This module
+only compiles it with gcc and marshals numpy arrays through ctypes.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "mlstm_oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, IEEE semantics, no fast-math)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+           "-o", output + ".tmp", source, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(output + ".tmp", output)
+    return output
+
+
+def _bind(lib):
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.oracle_fwd_f64.restype = ctypes.c_int
+    lib.oracle_fwd_f64.argtypes = [dp] * 6 + [ctypes.c_int] * 5 + [dp] * 3 + [dp] * 4
+    lib.oracle_step_f64.restype = ctypes.c_int
+    lib.oracle_step_f64.argtypes = [dp] * 6 + [ctypes.c_int] * 4 + [dp] * 4
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_num_threads.argtypes = []
+    return lib
+
+
+def load(path: str | None = None):
+    """Load (building first if absent) the oracle shared library."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(LIBRARY) or os.path.getmtime(LIBRARY) < os.path.getmtime(SOURCE):
+            build()
+        _lib = _bind(ctypes.CDLL(LIBRARY))
+    return _lib
+
+
+def _f64(x):
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+class Oracle:
+    """Thin numpy front end over one loaded oracle library."""
+
+    def __init__(self, lib=None):
+        self.lib = lib if lib is not None else load()
+
+    def fwd(self, q, k, v, i_pre, f_pre, o_pre, C0=None, n0=None, m0=None):
+        """Recurrent forward.  q,k [B,NH,S,dqk], v,o_pre [B,NH,S,dv], i_pre,f_pre [B,NH,S].
+
+        Returns (h [B,NH,S,dv], C [B,NH,dv,dqk], n [B,NH,dqk], m [B,NH]) in fp64, the
+        state in stabilized form (C' = C e^{-m}, n' = n e^{-m}).
+        """
+        q, k, v, i_pre, f_pre, o_pre = map(_f64, (q, k, v, i_pre, f_pre, o_pre))
+        B, NH, S, dqk = q.shape
+        dv = v.shape[-1]
+        assert k.shape == q.shape and v.shape == (B, NH, S, dv)
+        assert i_pre.shape == (B, NH, S) and f_pre.shape == (B, NH, S)
+        assert o_pre.shape == (B, NH, S, dv)
+        have_state = C0 is not None
+        if have_state:
+            C0, n0, m0 = _f64(C0), _f64(n0), _f64(m0)
+            assert C0.shape == (B, NH, dv, dqk) and n0.shape == (B, NH, dqk) and m0.shape == (B, NH)
+        h = np.empty((B, NH, S, dv))
+        C = np.empty((B, NH, dv, dqk))
+        n = np.empty((B, NH, dqk))
+        m = np.empty((B, NH))
+        rc = self.lib.oracle_fwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(o_pre),
+                                     B, NH, S, dqk, dv,
+                                     _ptr(C0) if have_state else None,
+                                     _ptr(n0) if have_state else None,
+                                     _ptr(m0) if have_state else None,
+                                     _ptr(h), _ptr(C), _ptr(n), _ptr(m))
+        if rc != 0:
+            raise ValueError("oracle_fwd_f64 rejected its arguments")
+        return h, C, n, m
+
+    def step(self, q, k, v, i_pre, f_pre, o_pre, C, n, m):
+        """One recurrent step.  q,k [B,NH,dqk], v,o_pre [B,NH,dv], i_pre,f_pre [B,NH].
+
+        The state (C [B,NH,dv,dqk], n [B,NH,dqk], m [B,NH]) is copied, not modified.
+        Returns (h [B,NH,dv], C, n, m) after the step.
+        """
+        q, k, v, i_pre, f_pre, o_pre = map(_f64, (q, k, v, i_pre, f_pre, o_pre))
+        C, n, m = np.array(C, dtype=np.float64), np.array(n, dtype=np.float64), np.array(m, dtype=np.float64)
+        B, NH, dqk = q.shape
+        dv = v.shape[-1]
+        assert C.shape == (B, NH, dv, dqk) and n.shape == (B, NH, dqk) and m.shape == (B, NH)
+        h = np.empty((B, NH, dv))
+        rc = self.lib.oracle_step_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(o_pre),
+                                      B, NH, dqk, dv, _ptr(C), _ptr(n), _ptr(m), _ptr(h))
+        if rc != 0:
+            raise ValueError("oracle_step_f64 rejected its arguments")
+        return h, C, n, m
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+
+def fwd(*args, **kwargs):
+    return Oracle().fwd(*args, **kwargs)
+
+
+def step(*args, **kwargs):
+    return Oracle().step(*args, **kwargs)

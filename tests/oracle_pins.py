@@ -1,0 +1,348 @@
+"""Pins of the fp64 oracle against facts fixed by the pages and by mathematics.
+
+Source: "xLSTM: Extended Long Short-Term Memory" (arXiv 2405.04517).
+Every pin is a function ``pin_*(orc)`` taking an ``oracle.Oracle``; it raises
+AssertionError when the oracle disagrees.  None of them retypes the oracle's
+stabilized recurrence: each compares it with a different formulation whose
+equality the pages or plain algebra guarantee:
+
+* the unstabilized recurrence (section 2.2: replacing f, i by the stabilized
+  f', i' changes no output; section 2.3: threshold 1.0 on |n^T q|);
+* the quadratic parallel form (section 2.3: without memory mixing the
+  recurrence can be rewritten in parallel form), written with numpy's own
+  log-sigmoid (``-logaddexp(0, -x)``) and masked matrix products;
+* eq. (18) itself (no decay, unit learning rate): C_S = V^T K by library GEMM;
+* causal linear attention (eq. (18) with unit gates, the fast-weight reading of
+  section 2.3) by masked matrix products;
+* closed forms of a single step, of the memoryless case and of one-pair
+  associative retrieval (section 2.3, the bidirectional associative memory
+  setting: a stored value is retrieved by a later query along its key);
+* head independence (section 2.3: no memory mixing across heads).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+RTOL = 1e-10
+
+
+def _sig(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def _log_sig(x):
+    # numpy's own stable evaluation, independent of the oracle's formula
+    return -np.logaddexp(0.0, -np.asarray(x, dtype=np.float64))
+
+
+def _close(a, b, rtol=RTOL, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: oracle produced non-finite values"
+    scale = max(float(np.max(np.abs(b))), 1e-300)
+    err = float(np.max(np.abs(a - b))) / scale
+    assert err <= rtol, f"{what}: max abs diff / max|ref| = {err:.3e} > {rtol:.1e}"
+
+
+def _inputs(rng, B, NH, S, dqk, dv, i_mu=0.0, i_sd=1.0, f_mu=1.0, f_sd=1.5):
+    q = rng.standard_normal((B, NH, S, dqk))
+    k = rng.standard_normal((B, NH, S, dqk)) / np.sqrt(dqk)
+    v = rng.standard_normal((B, NH, S, dv))
+    i = i_mu + i_sd * rng.standard_normal((B, NH, S))
+    f = f_mu + f_sd * rng.standard_normal((B, NH, S))
+    o = rng.standard_normal((B, NH, S, dv))
+    return q, k, v, i, f, o
+
+
+# --------------------------------------------------------------------------
+# independent formulations
+# --------------------------------------------------------------------------
+def unstabilized(q, k, v, i, f, o, C0=None, n0=None):
+    """Unstabilized recurrence: f = sigmoid, i = exp, threshold 1.0 on |n.q|."""
+    B, NH, S, dqk = q.shape
+    dv = v.shape[-1]
+    h = np.zeros((B, NH, S, dv))
+    Cs = np.zeros((B, NH, dv, dqk))
+    ns = np.zeros((B, NH, dqk))
+    nqs = np.zeros((B, NH, S))
+    for b in range(B):
+        for hd in range(NH):
+            C = np.zeros((dv, dqk)) if C0 is None else C0[b, hd].copy()
+            n = np.zeros(dqk) if n0 is None else n0[b, hd].copy()
+            for t in range(S):
+                fg = _sig(f[b, hd, t])
+                ig = np.exp(i[b, hd, t])
+                C = fg * C + ig * np.outer(v[b, hd, t], k[b, hd, t])
+                n = fg * n + ig * k[b, hd, t]
+                nq = n @ q[b, hd, t]
+                nqs[b, hd, t] = nq
+                h[b, hd, t] = _sig(o[b, hd, t]) * (C @ q[b, hd, t]) / max(abs(nq), 1.0)
+            Cs[b, hd], ns[b, hd] = C, n
+    return h, Cs, ns, nqs
+
+
+def stabilizer_closed_form(i, f, m0=None):
+    """m_t = max(m_0 + F_t, max_{s<=t} (i_s + F_t - F_s)), F = cumsum(log sigmoid(f))."""
+    B, NH, S = i.shape
+    F = np.cumsum(_log_sig(f), axis=-1)
+    m = np.empty((B, NH, S))
+    base = np.zeros((B, NH)) if m0 is None else np.asarray(m0, dtype=np.float64)
+    for t in range(S):
+        cand = i[..., : t + 1] + F[..., t : t + 1] - F[..., : t + 1]
+        m[..., t] = np.maximum(base + F[..., t], cand.max(axis=-1))
+    return m
+
+
+def parallel_form(q, k, v, i, f, o, C0=None, n0=None, m0=None):
+    """Quadratic (attention-like) parallel form of the whole sequence, per head.
+
+    With F_t the cumulative log forget gate and m_t the stabilizer, the decay
+    matrix is D_ts = exp(i_s + F_t - F_s - m_t) for s <= t (0 above the
+    diagonal) and the initial state enters with weight g_t = exp(m_0 + F_t - m_t).
+    """
+    B, NH, S, dqk = q.shape
+    dv = v.shape[-1]
+    if C0 is None:
+        C0 = np.zeros((B, NH, dv, dqk))
+        n0 = np.zeros((B, NH, dqk))
+        m0 = np.zeros((B, NH))
+    m = stabilizer_closed_form(i, f, m0)
+    F = np.cumsum(_log_sig(f), axis=-1)
+    h = np.empty((B, NH, S, dv))
+    Cf = np.empty((B, NH, dv, dqk))
+    nf = np.empty((B, NH, dqk))
+    for b in range(B):
+        for hd in range(NH):
+            Fb, ib, mb = F[b, hd], i[b, hd], m[b, hd]
+            logD = ib[None, :] + Fb[:, None] - Fb[None, :] - mb[:, None]
+            mask = np.tril(np.ones((S, S), dtype=bool))
+            D = np.where(mask, np.exp(np.where(mask, logD, 0.0)), 0.0)
+            g = np.exp(m0[b, hd] + Fb - mb)
+            Q, K, V = q[b, hd], k[b, hd], v[b, hd]
+            P = (Q @ K.T) * D
+            num = P @ V + g[:, None] * (Q @ C0[b, hd].T)
+            den = P.sum(axis=1) + g * (Q @ n0[b, hd])
+            h[b, hd] = _sig(o[b, hd]) * num / np.maximum(np.abs(den), np.exp(-mb))[:, None]
+            w = np.exp(ib + Fb[-1] - Fb - mb[-1])
+            a = np.exp(m0[b, hd] + Fb[-1] - mb[-1])
+            Cf[b, hd] = (V * w[:, None]).T @ K + a * C0[b, hd]
+            nf[b, hd] = K.T @ w + a * n0[b, hd]
+    return h, Cf, nf, m[..., -1].copy()
+
+
+# --------------------------------------------------------------------------
+# pins
+# --------------------------------------------------------------------------
+def pin_stabilizer_invariance(orc):
+    """Stabilized outputs equal the unstabilized ones; C' e^m = C, n' e^m = n."""
+    rng = np.random.default_rng(11)
+    q, k, v, i, f, o = _inputs(rng, 1, 2, 12, 3, 5)
+    h, C, n, m = orc.fwd(q, k, v, i, f, o)
+    hu, Cu, nu, nq = unstabilized(q, k, v, i, f, o)
+    # both branches of the normalizer floor must be exercised
+    assert np.any(np.abs(nq) < 1.0) and np.any(np.abs(nq) > 1.0)
+    _close(h, hu, what="h vs unstabilized")
+    _close(C * np.exp(m)[..., None, None], Cu, what="C' e^m vs C")
+    _close(n * np.exp(m)[..., None], nu, what="n' e^m vs n")
+
+
+def pin_parallel_form(orc):
+    """Recurrent form equals the quadratic parallel form (zero initial state)."""
+    rng = np.random.default_rng(12)
+    q, k, v, i, f, o = _inputs(rng, 2, 2, 40, 6, 5, i_sd=2.0, f_mu=2.0, f_sd=2.0)
+    h, C, n, m = orc.fwd(q, k, v, i, f, o)
+    hp, Cp, np_, mp = parallel_form(q, k, v, i, f, o)
+    _close(h, hp, what="h")
+    _close(C, Cp, what="C'")
+    _close(n, np_, what="n'")
+    _close(m, mp, what="m")
+
+
+def pin_parallel_form_initial_state(orc):
+    """Recurrent form from a given stabilized state equals the parallel form."""
+    rng = np.random.default_rng(13)
+    q, k, v, i, f, o = _inputs(rng, 1, 3, 24, 5, 4, i_sd=1.5)
+    C0 = rng.standard_normal((1, 3, 4, 5)) * 0.3
+    n0 = rng.standard_normal((1, 3, 5))
+    m0 = rng.uniform(-2.0, 5.0, (1, 3))
+    h, C, n, m = orc.fwd(q, k, v, i, f, o, C0, n0, m0)
+    hp, Cp, np_, mp = parallel_form(q, k, v, i, f, o, C0, n0, m0)
+    _close(h, hp, what="h")
+    _close(C, Cp, what="C'")
+    _close(n, np_, what="n'")
+    _close(m, mp, what="m")
+
+
+def pin_extreme_gates(orc):
+    """Huge gate pre-activations stay finite and still match the parallel form."""
+    rng = np.random.default_rng(14)
+    q, k, v, i, f, o = _inputs(rng, 1, 2, 32, 4, 4, i_sd=8.0, f_mu=1.0, f_sd=2.0)
+    f[0, 0, 5] = -800.0
+    f[0, 1, 9] = 800.0
+    f[0, 0, 20] = -60.0
+    i[0, 0, 3] = 40.0
+    i[0, 1, 17] = 40.0
+    i[0, 1, 2] = -300.0
+    h, C, n, m = orc.fwd(q, k, v, i, f, o)
+    hp, Cp, np_, mp = parallel_form(q, k, v, i, f, o)
+    _close(h, hp, what="h")
+    _close(C, Cp, what="C'")
+    _close(n, np_, what="n'")
+    _close(m, mp, what="m")
+
+
+def pin_deep_forget_after_spike(orc):
+    """A forget pre-activation far below the fp64 range of sigmoid still decays
+    a memory written with a larger input gate (log-domain gating keeps it)."""
+    rng = np.random.default_rng(23)
+    q, k, v, i, f, o = _inputs(rng, 1, 2, 6, 3, 4)
+    i[0, 0, 0] = 800.0
+    f[0, 0, 1] = -750.0      # sigmoid underflows, log sigmoid is -750 exactly
+    i[0, 1, 1] = 720.0
+    f[0, 1, 2] = -715.0
+    h, C, n, m = orc.fwd(q, k, v, i, f, o)
+    hp, Cp, np_, mp = parallel_form(q, k, v, i, f, o)
+    _close(h, hp, what="h")
+    _close(C, Cp, what="C'")
+    _close(n, np_, what="n'")
+    _close(m, mp, what="m")
+
+
+def pin_stabilizer_every_step(orc):
+    """The returned m after every prefix equals the unrolled closed form."""
+    rng = np.random.default_rng(15)
+    q, k, v, i, f, o = _inputs(rng, 1, 2, 16, 3, 3, i_sd=3.0, f_mu=0.0, f_sd=3.0)
+    mc = stabilizer_closed_form(i, f)
+    for t in range(1, 17):
+        _, _, _, m = orc.fwd(q[:, :, :t], k[:, :, :t], v[:, :, :t], i[:, :, :t], f[:, :, :t], o[:, :, :t])
+        _close(m, mc[..., t - 1], what=f"m after {t} steps")
+
+
+def pin_eq18_accumulation(orc):
+    """eq. (18): no decay (f~ = +inf) and i~ = 0 give C_S = V^T K, n_S = sum k, m = 0."""
+    rng = np.random.default_rng(16)
+    q, k, v, _, _, o = _inputs(rng, 2, 1, 9, 4, 6)
+    i = np.zeros((2, 1, 9))
+    f = np.full((2, 1, 9), np.inf)
+    h, C, n, m = orc.fwd(q, k, v, i, f, o)
+    for b in range(2):
+        _close(C[b, 0], v[b, 0].T @ k[b, 0], what="C vs V^T K")
+        _close(n[b, 0], k[b, 0].sum(axis=0), what="n vs sum k")
+    assert np.all(m == 0.0)
+
+
+def pin_causal_linear_attention(orc):
+    """Unit gates reduce retrieval to causal linear attention with |.| floor 1."""
+    rng = np.random.default_rng(17)
+    q, k, v, _, _, o = _inputs(rng, 1, 2, 20, 5, 3)
+    i = np.zeros((1, 2, 20))
+    f = np.full((1, 2, 20), np.inf)
+    h, _, _, _ = orc.fwd(q, k, v, i, f, o)
+    for hd in range(2):
+        A = np.tril(q[0, hd] @ k[0, hd].T)
+        num = A @ v[0, hd]
+        den = np.maximum(np.abs(A.sum(axis=1)), 1.0)
+        _close(h[0, hd], _sig(o[0, hd]) * num / den[:, None], what="h vs linear attention")
+
+
+def pin_single_step(orc):
+    """One step from the zero state has a closed form independent of f~."""
+    rng = np.random.default_rng(18)
+    q, k, v, i, f, o = _inputs(rng, 1, 6, 1, 4, 3, i_sd=2.0)
+    f[0, :, 0] = [-50.0, -2.0, 0.0, 1.5, 7.0, 60.0]
+    h, C, n, m = orc.fwd(q, k, v, i, f, o)
+    for hd in range(6):
+        kq = k[0, hd, 0] @ q[0, hd, 0]
+        ei = np.exp(i[0, hd, 0])
+        ref = _sig(o[0, hd, 0]) * v[0, hd, 0] * kq * ei / max(ei * abs(kq), 1.0)
+        _close(h[0, hd, 0], ref, what="h_1")
+        m1 = max(_log_sig(f[0, hd, 0]), i[0, hd, 0])
+        _close(m[0, hd], m1, what="m_1")
+        _close(C[0, hd], np.exp(i[0, hd, 0] - m1) * np.outer(v[0, hd, 0], k[0, hd, 0]), what="C'_1")
+        _close(n[0, hd], np.exp(i[0, hd, 0] - m1) * k[0, hd, 0], what="n'_1")
+
+
+def pin_memoryless(orc):
+    """A closed forget gate (f~ = -inf) forgets everything before the current token."""
+    rng = np.random.default_rng(19)
+    q, k, v, i, _, o = _inputs(rng, 1, 2, 10, 4, 5, i_sd=2.0)
+    f = np.full((1, 2, 10), -np.inf)
+    h, _, _, m = orc.fwd(q, k, v, i, f, o)
+    kq = np.einsum("bhtd,bhtd->bht", k, q)
+    ei = np.exp(i)
+    ref = _sig(o) * v * (kq * ei / np.maximum(ei * np.abs(kq), 1.0))[..., None]
+    _close(h, ref, what="memoryless h")
+    _close(m, i[..., -1], what="memoryless m")
+
+
+def pin_associative_retrieval(orc):
+    """One stored (k, v) pair is retrieved by later queries along +-k."""
+    rng = np.random.default_rng(20)
+    dqk, dv, S = 4, 5, 6
+    key = rng.standard_normal(dqk)
+    key /= np.linalg.norm(key)
+    val = rng.standard_normal(dv)
+    q = np.zeros((1, 2, S, dqk))
+    k = np.zeros((1, 2, S, dqk))
+    v = np.zeros((1, 2, S, dv))
+    k[0, :, 0] = key
+    v[0, :, 0] = val
+    i = np.full((1, 2, S), -np.inf)
+    i[0, 0, 0] = 2.0      # e^2 |k.q| >= 1: retrieval is normalized to +-v
+    i[0, 1, 0] = -3.0     # e^-3 |k.q| < 1: the floor binds, output scales with k.q
+    f = np.full((1, 2, S), np.inf)
+    o = rng.standard_normal((1, 2, S, dv))
+    signs = np.array([1.0, -1.0, 2.0, -0.5, 1.0, 3.0])
+    q[0, :, :] = signs[:, None] * key[None, :]
+    h, _, _, _ = orc.fwd(q, k, v, i, f, o)
+    for t in range(S):
+        _close(h[0, 0, t], _sig(o[0, 0, t]) * val * np.sign(signs[t]), what=f"retrieval head0 t={t}")
+        kq = signs[t]
+        ref = _sig(o[0, 1, t]) * val * kq * np.exp(-3.0) / max(np.exp(-3.0) * abs(kq), 1.0)
+        _close(h[0, 1, t], ref, what=f"retrieval head1 t={t}")
+
+
+def pin_head_independence(orc):
+    """Heads and batch entries are independent recurrences (no memory mixing)."""
+    rng = np.random.default_rng(21)
+    q, k, v, i, f, o = _inputs(rng, 2, 3, 7, 3, 4)
+    h, C, n, m = orc.fwd(q, k, v, i, f, o)
+    for b in range(2):
+        for hd in range(3):
+            sl = (slice(b, b + 1), slice(hd, hd + 1))
+            hs, Cs, ns, ms = orc.fwd(q[sl], k[sl], v[sl], i[sl], f[sl], o[sl])
+            assert np.array_equal(hs[0, 0], h[b, hd]) and np.array_equal(Cs[0, 0], C[b, hd])
+            assert np.array_equal(ns[0, 0], n[b, hd]) and np.array_equal(ms[0, 0], m[b, hd])
+
+
+def pin_step_continues_fwd(orc):
+    """fwd over S tokens equals fwd over a prefix followed by one-token steps."""
+    rng = np.random.default_rng(22)
+    q, k, v, i, f, o = _inputs(rng, 1, 2, 10, 4, 3, i_sd=2.0)
+    h, C, n, m = orc.fwd(q, k, v, i, f, o)
+    hp, Cs, ns, ms = orc.fwd(q[:, :, :6], k[:, :, :6], v[:, :, :6], i[:, :, :6], f[:, :, :6], o[:, :, :6])
+    _close(hp, h[:, :, :6], rtol=0.0, what="prefix h")
+    for t in range(6, 10):
+        ht, Cs, ns, ms = orc.step(q[:, :, t], k[:, :, t], v[:, :, t], i[:, :, t], f[:, :, t], o[:, :, t], Cs, ns, ms)
+        _close(ht, h[:, :, t], rtol=1e-13, what=f"step h t={t}")
+    _close(Cs, C, rtol=1e-13, what="C after steps")
+    _close(ns, n, rtol=1e-13, what="n after steps")
+    _close(ms, m, rtol=1e-13, what="m after steps")
+
+
+ALL_PINS = [
+    pin_stabilizer_invariance,
+    pin_parallel_form,
+    pin_parallel_form_initial_state,
+    pin_extreme_gates,
+    pin_deep_forget_after_spike,
+    pin_stabilizer_every_step,
+    pin_eq18_accumulation,
+    pin_causal_linear_attention,
+    pin_single_step,
+    pin_memoryless,
+    pin_associative_retrieval,
+    pin_head_independence,
+    pin_step_continues_fwd,
+]

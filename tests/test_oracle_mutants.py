@@ -1,0 +1,77 @@
+"""Planted mistakes in a copy of the oracle must each fail at least one pin (CPU only).
+
+Every mutant is a plausible slip in the oracle's arithmetic -- a dropped term, a
+wrong sign, a transposed operand, a wrong index -- applied to a temporary copy
+of ``oracle/mlstm_oracle.c`` and compiled with gcc.  The real oracle is never
+modified.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+MUTANTS = {
+    "forget_gate_dropped_on_C": (
+        "row[j] = f_s * row[j] + i_s * v[r] * k[j];",
+        "row[j] = row[j] + i_s * v[r] * k[j];"),
+    "outer_product_transposed": (
+        "row[j] = f_s * row[j] + i_s * v[r] * k[j];",
+        "row[j] = f_s * row[j] + i_s * v[j % dv] * k[r % dqk];"),
+    "stabilizer_sign": (
+        "const double f_s = exp(log_f + m_prev - m_t);",
+        "const double f_s = exp(log_f - m_prev - m_t);"),
+    "stabilizer_max_dropped": (
+        "const double m_t = fmax(log_f + m_prev, log_i);",
+        "const double m_t = log_f + m_prev;"),
+    "input_gate_not_exponential": (
+        "const double i_s = exp(log_i - m_t);",
+        "const double i_s = (log_i - m_t);"),
+    "forget_gate_not_log": (
+        "const double log_f = log_sigmoid(f_pre);",
+        "const double log_f = sigmoid(f_pre);"),
+    "naive_log_sigmoid": (
+        "return fmin(x, 0.0) - log1p(exp(-fabs(x)));",
+        "return log(1.0 / (1.0 + exp(-x)));"),
+    "normalizer_abs_dropped": (
+        "fmax(fabs(nq), exp(-m_t))",
+        "fmax(nq, exp(-m_t))"),
+    "normalizer_floor_sign": (
+        "fmax(fabs(nq), exp(-m_t))",
+        "fmax(fabs(nq), exp(m_t))"),
+    "normalizer_floor_unstabilized": (
+        "fmax(fabs(nq), exp(-m_t))",
+        "fmax(fabs(nq), 1.0)"),
+    "normalizer_no_decay": (
+        "n[j] = f_s * n[j] + i_s * k[j];",
+        "n[j] = n[j] + i_s * k[j];"),
+    "retrieval_with_key": (
+        "cq += row[j] * q[j];",
+        "cq += row[j] * k[j];"),
+    "output_gate_dropped": (
+        "h[r] = sigmoid(o_pre[r]) * cq / denom;",
+        "h[r] = cq / denom;"),
+    "head_stride": (
+        "double *Cb = C + (size_t)bh * dv * dqk;",
+        "double *Cb = C + (size_t)bh * dqk;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    before, after = MUTANTS[name]
+    src = open(oracle.SOURCE).read()
+    assert src.count(before) == 1, f"mutation site for {name} not found exactly once"
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(before, after))
+    lib_path = str(tmp_path / "libmutant.so")
+    oracle.build(str(mutated), lib_path)
+    orc = oracle.Oracle(oracle.load(lib_path))
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, FloatingPointError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
