@@ -1,0 +1,139 @@
+/*
+ * mlstm.h -- C ABI of libmlstm: the mLSTM matrix-memory cell on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Method: "xLSTM: Extended Long Short-Term Memory" (arXiv 2405.04517).
+ *   - section 2.3 "mLSTM", eq. (18): the memory of each head is a matrix C that
+ *     stores a key/value pair by the covariance update C_t = C_{t-1} + v_t k_t^T;
+ *     the forget gate is the decay rate applied to C_{t-1}, the input gate the
+ *     learning rate applied to v_t k_t^T, the output gate scales the retrieved
+ *     vector;
+ *   - section 2.3, normalizer paragraph: n_t is the input-gate and forget-gate
+ *     weighted sum of keys; retrieval divides C_t q_t by max(|n_t^T q_t|, 1.0);
+ *   - section 2.2, stabilizer paragraph and eq. (17): a log-domain state m_t keeps
+ *     the exponential input gate from overflowing, and using the stabilized gates
+ *     f'_t, i'_t changes no output;
+ *   - section 2.3, multi-head paragraph: heads do not mix, and the recurrence has an
+ *     equivalent parallel (chunkwise) form.
+ * Per (batch b, head h), token t:
+ *   log f_t = log sigmoid(f~_t)            (sigmoid forget gate)
+ *   log i_t = i~_t                         (exponential input gate)
+ *   m_t     = max(log f_t + m_{t-1}, log i_t)
+ *   C'_t    = exp(log f_t + m_{t-1} - m_t) C'_{t-1} + exp(i~_t - m_t) v_t k_t^T
+ *   n'_t    = exp(log f_t + m_{t-1} - m_t) n'_{t-1} + exp(i~_t - m_t) k_t
+ *   h_t     = sigmoid(o~_t) (.) (C'_t q_t) / max(|n'_t . q_t|, exp(-m_t))
+ * The state is kept and returned stabilized: C' = C e^{-m}, n' = n e^{-m}.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are dense, contiguous, row-major, in device memory, and owned by
+ *     the caller.  The library allocates no device memory and keeps no mutable
+ *     global state; calls on different streams are independent.
+ *   - Layouts: q,k [B,NH,S,d_qk]; v [B,NH,S,d_v]; i_pre,f_pre [B,NH,S] fp32;
+ *     o_pre [B,NH,S,d_v] fp32 (the output gate is applied component-wise);
+ *     h_out [B,NH,S,d_v]; C [B,NH,d_v,d_qk] fp32 (row r of a head's C holds value
+ *     dimension r); n [B,NH,d_qk] fp32; m [B,NH] fp32.
+ *   - dtype gives the element type of q, k, v and h_out (fp32 or bf16); the gate
+ *     pre-activations and the state are always fp32.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).  Calls
+ *     enqueue work and return without synchronizing.
+ *   - Errors: every argument is validated before anything is enqueued; on a bad
+ *     argument nothing is launched and a status other than MLSTM_OK is returned.
+ *     A failed launch returns MLSTM_ERR_HIP.  mlstm_error_detail() gives a
+ *     human-readable reason for the last failure on the calling thread.  NaN or
+ *     Inf in the inputs are propagated, not checked.
+ *   - Outputs must not alias inputs (except where an entry point says "in place").
+ *   - Alignment: tensors the kernels access with vector loads or stores must be
+ *     16-byte aligned (fwd: q, k, v, o_pre, h_out, C_final, n_final; step: q, k,
+ *     C, n); every other pointer needs the alignment of its element type.
+ */
+#ifndef MLSTM_H
+#define MLSTM_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mlstm_status {
+    MLSTM_OK = 0,
+    MLSTM_ERR_INVALID_ARG = 1,   /* null pointer, non-positive size, bad chunk, ...  */
+    MLSTM_ERR_UNSUPPORTED = 2,   /* valid but outside what the kernels implement     */
+    MLSTM_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required       */
+    MLSTM_ERR_HIP = 4            /* the HIP runtime reported an error                */
+} mlstm_status;
+
+typedef enum mlstm_dtype {
+    MLSTM_F32 = 0,
+    MLSTM_BF16 = 1
+} mlstm_dtype;
+
+/*
+ * Bytes of device workspace mlstm_fwd_parallel needs for these sizes (0 if none).
+ * Returns 0 as well for arguments mlstm_fwd_parallel would reject.
+ */
+size_t mlstm_fwd_workspace_bytes(int B, int NH, int S, int d_qk, int d_v, int chunk,
+                                 mlstm_dtype dtype);
+
+/*
+ * Chunkwise parallel forward over whole sequences (section 2.3, parallel form),
+ * from the zero state C' = 0, n' = 0, m = 0.
+ *
+ * Tokens are processed in chunks of `chunk` tokens: inside a chunk the cell is
+ * evaluated in its quadratic form with the log-forget cumulative-sum decay
+ * matrix and a per-row stabilizer; the stabilized state (C', n', m) is carried
+ * from chunk to chunk.  Results agree with the token-by-token recurrence up to
+ * rounding for every chunk size.
+ *
+ * Arguments
+ *   q, k, v         inputs, dtype, layouts above (read only)
+ *   i_pre, f_pre    input / forget gate pre-activations [B,NH,S] fp32
+ *   o_pre           output gate pre-activations [B,NH,S,d_v] fp32
+ *   B, NH, S        batch, heads, tokens per sequence: all >= 1
+ *   d_qk, d_v       key/query and value dimensions: multiples of 16, <= 4096
+ *   chunk           16, 32, 64 or 128; S must be a multiple of chunk
+ *   dtype           MLSTM_F32 or MLSTM_BF16
+ *   h_out           [B,NH,S,d_v] dtype, written
+ *   C_final, n_final, m_final
+ *                   final stabilized state [B,NH,d_v,d_qk], [B,NH,d_qk], [B,NH]
+ *                   fp32, written; the exact recurrent m_S is returned, so the
+ *                   triple can be handed to mlstm_step to continue decoding
+ *   workspace       device buffer of at least mlstm_fwd_workspace_bytes(...)
+ *                   bytes (may be NULL when that is 0); its contents on entry
+ *                   do not matter and are clobbered
+ *   stream          hipStream_t or NULL
+ */
+mlstm_status mlstm_fwd_parallel(const void *q, const void *k, const void *v,
+                                const float *i_pre, const float *f_pre, const float *o_pre,
+                                int B, int NH, int S, int d_qk, int d_v, int chunk,
+                                mlstm_dtype dtype,
+                                void *h_out, float *C_final, float *n_final, float *m_final,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One-token recurrent decode step (section 2.3, the recurrence applied once).
+ *
+ * The stabilized state (C, n, m) is read and updated IN PLACE; each element is
+ * read and rewritten by the same thread, so no separate output state exists.
+ *   q, k            [B,NH,d_qk] dtype;  v [B,NH,d_v] dtype
+ *   i_pre, f_pre    [B,NH] fp32;        o_pre [B,NH,d_v] fp32
+ *   B, NH           >= 1;  d_qk, d_v multiples of 16, <= 4096
+ *   C, n, m         [B,NH,d_v,d_qk], [B,NH,d_qk], [B,NH] fp32, in place
+ *   h_out           [B,NH,d_v] dtype, written
+ */
+mlstm_status mlstm_step(const void *q, const void *k, const void *v,
+                        const float *i_pre, const float *f_pre, const float *o_pre,
+                        int B, int NH, int d_qk, int d_v, mlstm_dtype dtype,
+                        float *C, float *n, float *m, void *h_out, void *stream);
+
+/* Static description of a status code. */
+const char *mlstm_status_string(mlstm_status status);
+
+/* Reason for the most recent failed call on this thread ("" if none). */
+const char *mlstm_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLSTM_H */

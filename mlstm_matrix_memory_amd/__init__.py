@@ -1,0 +1,18 @@
+"""MI355X-native mLSTM matrix-memory cell: HIP kernels behind a C ABI (libmlstm.so).
+
+Entry points (same names as include/mlstm.h):
+  mlstm_fwd_parallel  chunkwise parallel forward over whole sequences
+  mlstm_step          one-token recurrent decode step, state updated in place
+  mlstm_fwd_workspace_bytes, mlstm_status_string, mlstm_error_detail
+"""
+from .binding import (  # noqa: F401
+    MLSTM_BF16,
+    MLSTM_F32,
+    MlstmError,
+    load_library,
+    mlstm_error_detail,
+    mlstm_fwd_parallel,
+    mlstm_fwd_workspace_bytes,
+    mlstm_status_string,
+    mlstm_step,
+)

@@ -1,0 +1,197 @@
+"""ctypes binding of libmlstm (include/mlstm.h), same names as the C entry points.
+
+Argument marshalling only: this module checks tensor dtypes, shapes, devices and
+contiguity, allocates outputs and workspace with torch (device memory and the
+current stream are the only things torch provides), and passes raw pointers to
+the C ABI.  Every step of the mLSTM cell runs in the HIP kernels of
+``libmlstm.so``; there is no other implementation behind these functions, and
+they raise if the library is not built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(HERE, "libmlstm.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "mlstm.h")
+
+MLSTM_OK = 0
+MLSTM_ERR_INVALID_ARG = 1
+MLSTM_ERR_UNSUPPORTED = 2
+MLSTM_ERR_WORKSPACE = 3
+MLSTM_ERR_HIP = 4
+
+MLSTM_F32 = 0
+MLSTM_BF16 = 1
+
+_lib = None
+
+
+class MlstmError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{fn}: {mlstm_status_string(status)} ({status}): {detail}")
+
+
+def load_library(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load libmlstm.so; raises if it has not been built (no fallback exists)."""
+    global _lib
+    if _lib is not None and path == LIBRARY:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+                           "or `python mlstm_matrix_memory_amd/build.py`")
+    lib = ctypes.CDLL(path)
+    vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.mlstm_fwd_workspace_bytes.restype = sz
+    lib.mlstm_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.mlstm_fwd_parallel.restype = i
+    lib.mlstm_fwd_parallel.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, i,
+                                       vp, fp, fp, fp, vp, sz, vp]
+    lib.mlstm_step.restype = i
+    lib.mlstm_step.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, fp, fp, fp, vp, vp]
+    lib.mlstm_status_string.restype = ctypes.c_char_p
+    lib.mlstm_status_string.argtypes = [i]
+    lib.mlstm_error_detail.restype = ctypes.c_char_p
+    lib.mlstm_error_detail.argtypes = []
+    if path == LIBRARY:
+        _lib = lib
+    return lib
+
+
+def header_symbols(path: str = HEADER) -> list[str]:
+    """Names of the functions include/mlstm.h declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mlstm_[a-z_0-9]+)\s*\(", text)))
+
+
+def mlstm_status_string(status: int) -> str:
+    return load_library().mlstm_status_string(int(status)).decode()
+
+
+def mlstm_error_detail() -> str:
+    return load_library().mlstm_error_detail().decode()
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return MLSTM_F32
+    if t.dtype == torch.bfloat16:
+        return MLSTM_BF16
+    raise TypeError(f"q/k/v must be float32 or bfloat16, got {t.dtype}")
+
+
+def mlstm_fwd_workspace_bytes(B: int, NH: int, S: int, d_qk: int, d_v: int, chunk: int, dtype: int) -> int:
+    return int(load_library().mlstm_fwd_workspace_bytes(B, NH, S, d_qk, d_v, chunk, int(dtype)))
+
+
+def _check(t, name, shape, dtype, device):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(stream, device):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def mlstm_fwd_parallel(q, k, v, i_pre, f_pre, o_pre, chunk: int,
+                       h_out=None, C_final=None, n_final=None, m_final=None,
+                       workspace=None, stream=None):
+    """Chunkwise parallel forward from the zero state; returns (h, C, n, m).
+
+    q,k [B,NH,S,d_qk] and v [B,NH,S,d_v] float32 or bfloat16 on one GPU;
+    i_pre,f_pre [B,NH,S] and o_pre [B,NH,S,d_v] float32.  Outputs are allocated
+    when not given: h like v, C [B,NH,d_v,d_qk], n [B,NH,d_qk], m [B,NH] float32.
+    """
+    import torch
+    lib = load_library()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, NH, S, d]")
+    B, NH, S, dqk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    dt = _dtype_code(q)
+    _check(q, "q", (B, NH, S, dqk), q.dtype, dev)
+    _check(k, "k", (B, NH, S, dqk), q.dtype, dev)
+    _check(v, "v", (B, NH, S, dv), q.dtype, dev)
+    _check(i_pre, "i_pre", (B, NH, S), torch.float32, dev)
+    _check(f_pre, "f_pre", (B, NH, S), torch.float32, dev)
+    _check(o_pre, "o_pre", (B, NH, S, dv), torch.float32, dev)
+    if h_out is None:
+        h_out = torch.empty((B, NH, S, dv), dtype=q.dtype, device=dev)
+    if C_final is None:
+        C_final = torch.empty((B, NH, dv, dqk), dtype=torch.float32, device=dev)
+    if n_final is None:
+        n_final = torch.empty((B, NH, dqk), dtype=torch.float32, device=dev)
+    if m_final is None:
+        m_final = torch.empty((B, NH), dtype=torch.float32, device=dev)
+    _check(h_out, "h_out", (B, NH, S, dv), q.dtype, dev)
+    _check(C_final, "C_final", (B, NH, dv, dqk), torch.float32, dev)
+    _check(n_final, "n_final", (B, NH, dqk), torch.float32, dev)
+    _check(m_final, "m_final", (B, NH), torch.float32, dev)
+    need = int(lib.mlstm_fwd_workspace_bytes(B, NH, S, dqk, dv, chunk, dt))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.mlstm_fwd_parallel(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                i_pre.data_ptr(), f_pre.data_ptr(), o_pre.data_ptr(),
+                                B, NH, S, dqk, dv, int(chunk), dt,
+                                h_out.data_ptr(), C_final.data_ptr(), n_final.data_ptr(), m_final.data_ptr(),
+                                ws_ptr, ws_bytes, _stream_handle(stream, dev))
+    if st != MLSTM_OK:
+        raise MlstmError("mlstm_fwd_parallel", st, mlstm_error_detail())
+    return h_out, C_final, n_final, m_final
+
+
+def mlstm_step(q, k, v, i_pre, f_pre, o_pre, C, n, m, h_out=None, stream=None):
+    """One recurrent step; (C, n, m) are updated in place.  Returns h [B,NH,d_v].
+
+    q,k [B,NH,d_qk], v [B,NH,d_v] float32 or bfloat16; i_pre,f_pre [B,NH] and
+    o_pre [B,NH,d_v] float32; C [B,NH,d_v,d_qk], n [B,NH,d_qk], m [B,NH] float32.
+    """
+    import torch
+    lib = load_library()
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D [B, NH, d]")
+    B, NH, dqk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    dt = _dtype_code(q)
+    _check(q, "q", (B, NH, dqk), q.dtype, dev)
+    _check(k, "k", (B, NH, dqk), q.dtype, dev)
+    _check(v, "v", (B, NH, dv), q.dtype, dev)
+    _check(i_pre, "i_pre", (B, NH), torch.float32, dev)
+    _check(f_pre, "f_pre", (B, NH), torch.float32, dev)
+    _check(o_pre, "o_pre", (B, NH, dv), torch.float32, dev)
+    _check(C, "C", (B, NH, dv, dqk), torch.float32, dev)
+    _check(n, "n", (B, NH, dqk), torch.float32, dev)
+    _check(m, "m", (B, NH), torch.float32, dev)
+    if h_out is None:
+        h_out = torch.empty((B, NH, dv), dtype=q.dtype, device=dev)
+    _check(h_out, "h_out", (B, NH, dv), q.dtype, dev)
+    st = lib.mlstm_step(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                        i_pre.data_ptr(), f_pre.data_ptr(), o_pre.data_ptr(),
+                        B, NH, dqk, dv, dt,
+                        C.data_ptr(), n.data_ptr(), m.data_ptr(), h_out.data_ptr(),
+                        _stream_handle(stream, dev))
+    if st != MLSTM_OK:
+        raise MlstmError("mlstm_step", st, mlstm_error_detail())
+    return h_out

@@ -1,0 +1,83 @@
+// Internal declarations and device helpers of libmlstm (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/mlstm.h"
+
+namespace mlstm {
+
+typedef __bf16 bf16;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// ---- element conversions -------------------------------------------------
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+// four consecutive elements starting at p (p 8- or 16-byte aligned)
+__device__ __forceinline__ f32x4 load4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 load4(const bf16* p) {
+    bf16x4 b = *reinterpret_cast<const bf16x4*>(p);
+    return f32x4{(float)b[0], (float)b[1], (float)b[2], (float)b[3]};
+}
+
+// ---- gate math (fp32) ----------------------------------------------------
+// log sigmoid(x) = min(x,0) - log(1 + exp(-|x|)), finite for every finite x
+__device__ __forceinline__ float log_sigmoid(float x) {
+    return fminf(x, 0.0f) - log1pf(expf(-fabsf(x)));
+}
+__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// ---- wavefront helpers (64 lanes) ------------------------------------------
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
+    return x;
+}
+
+// ---- launchers (return hipSuccess or the launch error) --------------------
+struct FwdArgs {
+    const void* q; const void* k; const void* v;
+    const float* i_pre; const float* f_pre; const float* o_pre;
+    int B, NH, S, dqk, dv, chunk;
+    mlstm_dtype dtype;
+    void* h; float* C; float* n; float* m;
+    const float* C0; const float* n0; const float* m0;   // initial state, all null = zero
+    void* ws; size_t ws_bytes;
+    hipStream_t stream;
+};
+
+struct StepArgs {
+    const void* q; const void* k; const void* v;
+    const float* i_pre; const float* f_pre; const float* o_pre;
+    int B, NH, dqk, dv;
+    mlstm_dtype dtype;
+    float* C; float* n; float* m; void* h;
+    hipStream_t stream;
+};
+
+hipError_t launch_step(const StepArgs& a);
+
+// generic chunkwise forward on the vector ALUs (any supported shape, fp32 or bf16)
+size_t valu_fwd_workspace_bytes(const FwdArgs& a);
+hipError_t launch_fwd_valu(const FwdArgs& a);
+
+// chunkwise forward on bf16 MFMA (bf16 inputs, shapes it supports)
+bool mfma_fwd_supported(const FwdArgs& a);
+size_t mfma_fwd_workspace_bytes(const FwdArgs& a);
+hipError_t launch_fwd_mfma(const FwdArgs& a);
+
+}  // namespace mlstm

@@ -1,0 +1,131 @@
+"""C ABI of libmlstm on the CPU: the library loads, exports what include/mlstm.h
+declares, and rejects bad arguments before touching the GPU.
+
+Only validation paths are called here (they return before any HIP call); no
+compute runs without a GPU.
+"""
+import ctypes
+
+import pytest
+
+from mlstm_matrix_memory_amd import binding as b
+
+FAKE = 0x10000  # aligned, never dereferenced: every call below fails validation first
+FAKE_MIS = 0x10008
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return b.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = b.header_symbols()
+    assert {"mlstm_fwd_parallel", "mlstm_step", "mlstm_fwd_workspace_bytes",
+            "mlstm_status_string", "mlstm_error_detail"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in include/mlstm.h but not exported"
+
+
+def test_status_strings(lib):
+    for code in range(5):
+        assert b.mlstm_status_string(code)
+    assert b.mlstm_status_string(0) == "ok"
+    assert b.mlstm_status_string(99) == "unknown status"
+
+
+def _fwd(lib, B=1, NH=1, S=64, dqk=32, dv=32, chunk=16, dt=b.MLSTM_BF16, ptrs=None, ws=None, ws_bytes=0):
+    p = [FAKE] * 10 if ptrs is None else ptrs
+    return lib.mlstm_fwd_parallel(p[0], p[1], p[2], p[3], p[4], p[5], B, NH, S, dqk, dv, chunk, dt,
+                                  p[6], p[7], p[8], p[9], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,detail", [
+    (dict(B=0), "B=0"),
+    (dict(NH=-1), "NH=-1"),
+    (dict(S=0), "S=0"),
+    (dict(dqk=24), "d_qk=24"),
+    (dict(dv=8), "d_v=8"),
+    (dict(dqk=8192), "d_qk=8192"),
+    (dict(chunk=48), "chunk=48"),
+    (dict(S=100, chunk=64), "not a multiple"),
+    (dict(dt=7), "dtype=7"),
+])
+def test_fwd_rejects_bad_sizes(lib, kw, detail):
+    st = _fwd(lib, **kw)
+    assert st == b.MLSTM_ERR_INVALID_ARG
+    assert detail in b.mlstm_error_detail()
+
+
+@pytest.mark.parametrize("which", range(10))
+def test_fwd_rejects_null_pointer(lib, which):
+    ptrs = [FAKE] * 10
+    ptrs[which] = None
+    assert _fwd(lib, ptrs=ptrs) == b.MLSTM_ERR_INVALID_ARG
+    assert "NULL" in b.mlstm_error_detail()
+
+
+def test_fwd_rejects_misaligned_pointer(lib):
+    ptrs = [FAKE] * 10
+    ptrs[2] = FAKE_MIS
+    assert _fwd(lib, ptrs=ptrs) == b.MLSTM_ERR_INVALID_ARG
+    assert "aligned" in b.mlstm_error_detail()
+
+
+def test_fwd_rejects_small_workspace(lib):
+    need = b.mlstm_fwd_workspace_bytes(8, 4, 2048, 384, 384, 64, b.MLSTM_BF16)
+    if need == 0:
+        pytest.skip("this configuration needs no workspace")
+    assert _fwd(lib, B=8, NH=4, S=2048, dqk=384, dv=384, chunk=64, ws=None, ws_bytes=0) == b.MLSTM_ERR_WORKSPACE
+    assert _fwd(lib, B=8, NH=4, S=2048, dqk=384, dv=384, chunk=64, ws=FAKE, ws_bytes=need - 1) == b.MLSTM_ERR_WORKSPACE
+
+
+def test_workspace_bytes_is_zero_for_rejected_args():
+    assert b.mlstm_fwd_workspace_bytes(0, 1, 64, 32, 32, 16, b.MLSTM_BF16) == 0
+    assert b.mlstm_fwd_workspace_bytes(1, 1, 60, 32, 32, 16, b.MLSTM_BF16) == 0
+
+
+@pytest.mark.parametrize("kw,detail", [
+    (dict(B=0), "B=0"),
+    (dict(dqk=20), "d_qk=20"),
+    (dict(dv=4112), "d_v=4112"),
+    (dict(dt=3), "dtype=3"),
+])
+def test_step_rejects_bad_sizes(lib, kw, detail):
+    a = dict(B=2, NH=2, dqk=64, dv=64, dt=b.MLSTM_BF16)
+    a.update(kw)
+    st = lib.mlstm_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["NH"], a["dqk"], a["dv"], a["dt"],
+                        FAKE, FAKE, FAKE, FAKE, None)
+    assert st == b.MLSTM_ERR_INVALID_ARG
+    assert detail in b.mlstm_error_detail()
+
+
+def test_step_rejects_null_state(lib):
+    st = lib.mlstm_step(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 2, 64, 64, b.MLSTM_BF16,
+                        None, FAKE, FAKE, FAKE, None)
+    assert st == b.MLSTM_ERR_INVALID_ARG
+    assert "C is NULL" in b.mlstm_error_detail()
+
+
+def test_binding_has_same_names_as_abi():
+    import mlstm_matrix_memory_amd as pkg
+    for name in ("mlstm_fwd_parallel", "mlstm_step", "mlstm_fwd_workspace_bytes",
+                 "mlstm_status_string", "mlstm_error_detail"):
+        assert callable(getattr(pkg, name))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        b.load_library(str(tmp_path / "libmlstm.so"))
+
+
+def test_product_does_not_use_oracle():
+    """The product package never imports, loads or calls the oracle."""
+    import os
+    import re
+    pat = re.compile(r"(import\s+oracle|from\s+oracle|liboracle|oracle_fwd|oracle_step|mlstm_oracle)")
+    for dirpath, _, files in os.walk(b.HERE):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not pat.search(text), f"{f} references the oracle"
