@@ -38,7 +38,8 @@ __global__ __launch_bounds__(VALU_THREADS) void fwd_valu_kernel(
     T* __restrict__ h, float* __restrict__ C, float* __restrict__ n, float* __restrict__ m)
 {
     __shared__ float P[L][L + 1];
-    __shared__ float sb[L], si[L], sm[L], sa[L], sw[L], sden[L];
+    __shared__ double sb[L], smd[L];              // cumulative log forget gate, stabilizer (fp64)
+    __shared__ float si[L], sa[L], sw[L], sden[L], sfl[L];
     extern __shared__ float nq[];  // n' of this head, dqk floats
 
     const int vt = blockIdx.x;
@@ -61,19 +62,19 @@ __global__ __launch_bounds__(VALU_THREADS) void fwd_valu_kernel(
         Ch[idx] = C0 ? C0[(size_t)bh * dv * dqk + (size_t)r_begin * dqk + idx] : 0.0f;
     for (int j = tid; j < dqk; j += VALU_THREADS)
         nq[j] = n0 ? n0[(size_t)bh * dqk + j] : 0.0f;
-    float m_prev = m0 ? m0[bh] : 0.0f;
+    double m_prev = m0 ? (double)m0[bh] : 0.0;
     __syncthreads();
 
     for (int t0 = 0; t0 < S; t0 += L) {
         const int Lc = min(L, S - t0);
         // gates: log forget gate and its in-chunk cumulative sum
         if (tid < Lc) {
-            sb[tid] = log_sigmoid(fh[t0 + tid]);
+            sb[tid] = log_sigmoid_f64((double)fh[t0 + tid]);
             si[tid] = ih[t0 + tid];
         }
         __syncthreads();
         if (tid == 0) {
-            float acc = 0.0f;
+            double acc = 0.0;
             for (int s = 0; s < Lc; ++s) { acc += sb[s]; sb[s] = acc; }
         }
         // raw scores q_tau . k_s on and below the diagonal
@@ -91,15 +92,16 @@ __global__ __launch_bounds__(VALU_THREADS) void fwd_valu_kernel(
         // per-row stabilizer and inter-chunk weight
         if (tid < Lc) {
             const int tau = tid;
-            float mx = sb[tau] + m_prev;
-            for (int s = 0; s <= tau; ++s) mx = fmaxf(mx, sb[tau] - sb[s] + si[s]);
-            sm[tau] = mx;
-            sa[tau] = expf(sb[tau] + m_prev - mx);
+            double mx = sb[tau] + m_prev;
+            for (int s = 0; s <= tau; ++s) mx = fmax(mx, sb[tau] - sb[s] + (double)si[s]);
+            smd[tau] = mx;
+            sa[tau] = exp_arg(sb[tau] + m_prev - mx);
+            sfl[tau] = exp_arg(-mx);
         }
         __syncthreads();
         for (int idx = tid; idx < Lc * Lc; idx += VALU_THREADS) {
             const int tau = idx / Lc, s = idx % Lc;
-            if (s <= tau) P[tau][s] *= expf(sb[tau] - sb[s] + si[s] - sm[tau]);
+            if (s <= tau) P[tau][s] *= exp_arg(sb[tau] - sb[s] + (double)si[s] - smd[tau]);
         }
         __syncthreads();
         // normalizer: intra-chunk row sum + inter-chunk q . n'
@@ -123,16 +125,16 @@ __global__ __launch_bounds__(VALU_THREADS) void fwd_valu_kernel(
             float inter = 0.0f;
             for (int j = 0; j < dqk; ++j) inter += to_f32(qr[j]) * cr[j];
             const float num = intra + sa[tau] * inter;
-            const float denom = fmaxf(fabsf(sden[tau]), expf(-sm[tau]));
+            const float denom = fmaxf(fabsf(sden[tau]), sfl[tau]);
             const size_t o = (size_t)(t0 + tau) * dv + r;
             hh[o] = from_f32<T>(sigmoid(oh[o]) * num / denom);
         }
         __syncthreads();
         // state update
-        const float m_last = sm[Lc - 1];
-        const float b_last = sb[Lc - 1];
-        const float alpha = expf(b_last + m_prev - m_last);
-        if (tid < Lc) sw[tid] = expf(b_last - sb[tid] + si[tid] - m_last);
+        const double m_last = smd[Lc - 1];
+        const double b_last = sb[Lc - 1];
+        const float alpha = exp_arg(b_last + m_prev - m_last);
+        if (tid < Lc) sw[tid] = exp_arg(b_last - sb[tid] + (double)si[tid] - m_last);
         __syncthreads();
         for (int idx = tid; idx < rows * dqk; idx += VALU_THREADS) {
             const int rr = idx / dqk, j = idx % dqk, r = r_begin + rr;
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(VALU_THREADS) void fwd_valu_kernel(
     }
     if (vt == 0) {
         for (int j = tid; j < dqk; j += VALU_THREADS) n[(size_t)bh * dqk + j] = nq[j];
-        if (tid == 0) m[bh] = m_prev;
+        if (tid == 0) m[bh] = (float)m_prev;
     }
 }
 

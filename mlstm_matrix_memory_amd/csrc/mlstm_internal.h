@@ -36,6 +36,17 @@ __device__ __forceinline__ float log_sigmoid(float x) {
 }
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// The stabilizer and the exponent arguments of the gate weights are differences of
+// running sums that reach O(100) in magnitude.  The normalized retrieval can cancel
+// to a few parts in 1e4 in its denominator, so an absolute exponent error of 1e-6
+// (fp32 rounding at that magnitude) already shows up at the percent level.  All
+// scalar gate arithmetic is therefore done in fp64; only the final exp, applied to
+// an accurate argument, is taken in fp32.
+__device__ __forceinline__ double log_sigmoid_f64(double x) {
+    return fmin(x, 0.0) - log1p(exp(-fabs(x)));
+}
+__device__ __forceinline__ float exp_arg(double x) { return expf((float)x); }
+
 // ---- wavefront helpers (64 lanes) ------------------------------------------
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll

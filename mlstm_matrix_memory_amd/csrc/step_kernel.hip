@@ -35,13 +35,13 @@ __global__ __launch_bounds__(STEP_THREADS) void step_kernel(
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    // s1: stabilized gates (every thread, redundantly)
-    const float log_f = log_sigmoid(f_pre[bh]);
-    const float log_i = i_pre[bh];
-    const float m_prev = m[bh];
-    const float m_t = fmaxf(log_f + m_prev, log_i);
-    const float fs = expf(log_f + m_prev - m_t);
-    const float is = expf(log_i - m_t);
+    // s1: stabilized gates (every thread, redundantly; scalar gate math in fp64)
+    const double log_f = log_sigmoid_f64((double)f_pre[bh]);
+    const double log_i = (double)i_pre[bh];
+    const double m_prev = (double)m[bh];
+    const double m_t = fmax(log_f + m_prev, log_i);
+    const float fs = exp_arg(log_f + m_prev - m_t);
+    const float is = exp_arg(log_i - m_t);
 
     const T* qb = q + (size_t)bh * dqk;
     const T* kb = k + (size_t)bh * dqk;
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(STEP_THREADS) void step_kernel(
     float den = 0.0f;
 #pragma unroll
     for (int w = 0; w < STEP_WAVES; ++w) den += red[w];
-    const float inv_denom = 1.0f / fmaxf(fabsf(den), expf(-m_t));
+    const float inv_denom = 1.0f / fmaxf(fabsf(den), exp_arg(-m_t));
 
     // this lane's key and query columns, kept in registers for all rows
     f32x4 kr[NJ], qr[NJ];
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(STEP_THREADS) void step_kernel(
             if (r < dv) hb[r] = from_f32<T>(sigmoid(ob[r]) * mine * inv_denom);
         }
     }
-    if (tid == 0) m[bh] = m_t;
+    if (tid == 0) m[bh] = (float)m_t;
 }
 
 template <typename T, int NJ>
