@@ -1,0 +1,274 @@
+"""Benchmark of the mLSTM matrix-memory hot path on one MI355X.
+
+A timed step is one chunkwise parallel forward (mlstm_fwd_prepare + mlstm_fwd_scan,
+i.e. mlstm_fwd_parallel) over the lm_125m workload: B=8, NH=4, S=2048,
+d_qk=d_v=384, chunk 64, bf16 q/k/v, fp32 gate pre-activations, inputs resident in
+HBM.  `value` is forward tokens/s (B*S tokens per step) from the wall clock around
+exactly --steps steps.  The same run also times the one-token decode step
+(mlstm_step on the decode workload: batch 256, NH=4, d=512, fp32 state, 128
+consecutive steps) and reports it under "decode".
+
+Roofline: the dominant kernel of the forward is the scan; its duration is taken
+with HIP events recorded on the stream the kernels run on, and its algorithmic
+bytes per launch are
+    B*NH*S*(2*(2*d_qk + d_v) + 4*d_v + 2*d_v) + B*NH*(4*d_qk*d_v + 4*d_qk + 4)
+(q, k, v and h in bf16, o~ in fp32, final state in fp32; the workspace the two
+stages exchange is not algorithmic).  Algorithmic FLOPs of the forward are
+B*NH*S*((chunk+1)*(d_qk+d_v) + 4*d_qk*d_v).  "traffic" is filled from the
+measured HBM counters in profiles/ only while the kernel source they were taken
+on is unchanged.
+
+cpu_baseline: the fp64 oracle (oracle/, plain C + OpenMP over heads) timed on the
+host on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+METRIC = "mLSTM fwd tokens/s + TFLOP/s (% bf16 MFMA peak); step tokens/s (% HBM BW)"
+SCAN_SOURCE = os.path.join(ROOT, "mlstm_matrix_memory_amd", "csrc", "fwd_mfma_kernel.hip")
+STEP_SOURCE = os.path.join(ROOT, "mlstm_matrix_memory_amd", "csrc", "step_kernel.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def fwd_alg_flops(w) -> float:
+    return float(w.B * w.NH * w.S) * ((w.chunk + 1) * (w.dqk + w.dv) + 4.0 * w.dqk * w.dv)
+
+
+def scan_alg_bytes(w) -> float:
+    e = 2
+    per_tok = e * (2 * w.dqk + w.dv) + 4 * w.dv + e * w.dv
+    return float(w.B * w.NH * w.S) * per_tok + float(w.B * w.NH) * (4 * w.dqk * w.dv + 4 * w.dqk + 4)
+
+
+def fwd_alg_bytes(w) -> float:
+    return scan_alg_bytes(w) + float(w.B * w.NH * w.S) * 8  # + i~, f~ (fp32)
+
+
+def step_alg_bytes(w) -> float:
+    e = 2
+    per_head = 8 * w.dqk * w.dv + 8 * w.dqk + 8 + e * (2 * w.dqk + w.dv) + 8 + 4 * w.dv + e * w.dv
+    return float(w.B * w.NH) * per_head
+
+
+def source_hash(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, source: str, launches_per_call: int = 1):
+    """HBM bytes per launch from committed counter runs, if taken on this exact source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    try:
+        rec = json.load(open(TRAFFIC_FILE)).get(kernel)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_sha") != source_hash(source):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, x, budget_s: float = 12.0):
+    """Time the fp64 oracle on whole sequences of the workload (all heads of each)."""
+    import numpy as np
+    import oracle
+    orc = oracle.Oracle()
+    cores = orc.num_threads()
+
+    def run(nb):
+        sl = slice(0, nb)
+        args = [x[k][sl] for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")]
+        args = [np.ascontiguousarray(a, dtype=np.float64) for a in args]
+        t = time.perf_counter()
+        orc.fwd(*args)
+        return time.perf_counter() - t
+
+    t1 = run(1)
+    nb = 1
+    if t1 < budget_s:
+        nb = max(1, min(w.B, int(budget_s / max(t1, 1e-3))))
+        if nb > 1:
+            t1 = run(nb)
+    tok_s = nb * w.S / t1
+    return {"value": tok_s, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{nb} of {w.B} sequences (all {w.NH} heads, S={w.S}, d={w.dqk}) in {t1:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="lm_125m")
+    ap.add_argument("--decode-steps", type=int, default=128)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build runs on a single MI355X and has no "
+              "multi-GPU path (heads shard across GPUs with no communication; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    from mlstm_matrix_memory_amd import (MLSTM_BF16, inputs, mlstm_fwd_prepare, mlstm_fwd_scan,
+                                         mlstm_fwd_workspace_bytes, mlstm_step)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def gpu(a, dt):
+        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+        return t.to(torch.bfloat16) if dt == "bf16" else t
+
+    # ---------------- forward ------------------------------------------------
+    w = inputs.WORKLOADS[args.workload]
+    x = inputs.fwd_inputs(w)
+    d = {k: gpu(v, w.dtype if k in ("q", "k", "v") else "f32") for k, v in x.items()}
+    ws = torch.empty(max(1, mlstm_fwd_workspace_bytes(w.B, w.NH, w.S, w.dqk, w.dv, w.chunk, MLSTM_BF16)),
+                     dtype=torch.uint8, device=dev)
+    h = torch.empty((w.B, w.NH, w.S, w.dv), dtype=torch.bfloat16, device=dev)
+    C = torch.empty((w.B, w.NH, w.dv, w.dqk), dtype=torch.float32, device=dev)
+    n = torch.empty((w.B, w.NH, w.dqk), dtype=torch.float32, device=dev)
+    m = torch.empty((w.B, w.NH), dtype=torch.float32, device=dev)
+    fa = (d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"], w.chunk)
+
+    def prepare():
+        mlstm_fwd_prepare(*fa, workspace=ws)
+
+    def scan():
+        mlstm_fwd_scan(*fa, h, C, n, m, workspace=ws)
+
+    for _ in range(args.warmup):
+        prepare()
+        scan()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        evs[s][0].record()
+        prepare()
+        evs[s][1].record()
+        scan()
+        evs[s][2].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms_per_step = wall * 1e3 / args.steps
+    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    scan_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
+    fwd_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
+    tokens = w.B * w.S
+    value = tokens / (ms_per_step / 1e3)
+    flops = fwd_alg_flops(w)
+    tflops = flops / (ms_per_step / 1e3) / 1e12
+    fwd_gbs = fwd_alg_bytes(w) / (ms_per_step / 1e3) / 1e9
+    scan_bytes = scan_alg_bytes(w)
+    scan_gbs = scan_bytes / (scan_ms / 1e3) / 1e9
+    traffic = measured_traffic("chunk_scan", SCAN_SOURCE)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: mLSTM fwd B={w.B} NH={w.NH} S={w.S} d_qk={w.dqk} d_v={w.dv} "
+                               f"chunk={w.chunk} bf16 q/k/v, fp32 gates",
+                   "B": w.B, "NH": w.NH, "S": w.S, "d_qk": w.dqk, "d_v": w.dv, "chunk": w.chunk},
+        "fwd": {"tflops_alg": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
+                "hbm_gbs_alg": fwd_gbs, "hbm_frac": fwd_gbs / HBM_PEAK_GBS,
+                "event_ms": fwd_ms, "prepare_ms": prep_ms, "scan_ms": scan_ms},
+        "roofline": {"kernel": "chunk_scan", "bound": "hbm", "achieved": scan_gbs, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": scan_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "alg_bytes_per_launch": scan_bytes},
+    }
+
+    # ---------------- decode step ---------------------------------------------
+    if not args.no_decode:
+        del d, ws, h, C, n, m
+        torch.cuda.empty_cache()
+        wd = inputs.WORKLOADS["decode"]
+        T = args.decode_steps
+        st = inputs.step_state(wd)
+        xs = inputs.step_inputs(wd, steps=T)
+        C0 = gpu(st["C"], "f32")
+        n0 = gpu(st["n"], "f32")
+        m0 = gpu(st["m"], "f32")
+        dx = {k: gpu(v, "bf16" if k in ("q", "k", "v") else "f32") for k, v in xs.items()}
+        del xs, st
+        Cw, nw, mw = C0.clone(), n0.clone(), m0.clone()
+        hd = torch.empty((wd.B, wd.NH, wd.dv), dtype=torch.bfloat16, device=dev)
+
+        def one(t):
+            mlstm_step(dx["q"][t], dx["k"][t], dx["v"][t], dx["i_pre"][t], dx["f_pre"][t], dx["o_pre"][t],
+                       Cw, nw, mw, hd)
+        for t in range(min(8, T)):
+            one(t)
+        Cw.copy_(C0); nw.copy_(n0); mw.copy_(m0)   # pristine state, outside the timed region
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_start = time.perf_counter()
+        e0.record()
+        for t in range(T):
+            one(t)
+        e1.record()
+        torch.cuda.synchronize()
+        dwall = time.perf_counter() - t_start
+        dev_ms = e0.elapsed_time(e1)
+        step_bytes = step_alg_bytes(wd)
+        step_gbs = step_bytes * T / (dev_ms / 1e3) / 1e9
+        out["decode"] = {
+            "workload": f"decode: mlstm_step batch={wd.B} NH={wd.NH} d_qk=d_v={wd.dqk} fp32 state, "
+                        f"bf16 q/k/v, {T} consecutive steps",
+            "tokens_per_s": wd.B * T / (dwall), "us_per_step": dev_ms * 1e3 / T,
+            "roofline": {"kernel": "step_kernel", "bound": "hbm", "achieved": step_gbs, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": step_gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("step_kernel", STEP_SOURCE),
+                         "alg_bytes_per_launch": step_bytes},
+        }
+        del C0, n0, m0, Cw, nw, mw, dx
+        torch.cuda.empty_cache()
+
+    if args.copy_calibration_mib > 0:
+        nbytes = args.copy_calibration_mib * (1 << 20)
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = nbytes
+
+    # ---------------- CPU baseline (oracle) ------------------------------------
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, x)
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -111,6 +111,31 @@ mlstm_status mlstm_fwd_parallel(const void *q, const void *k, const void *v,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * The two stages of mlstm_fwd_parallel, for callers that schedule them apart
+ * (e.g. to time or overlap them).  Same arguments and rules as
+ * mlstm_fwd_parallel; on one stream and with one workspace,
+ *   mlstm_fwd_prepare(...) followed by mlstm_fwd_scan(...)
+ * computes exactly what mlstm_fwd_parallel(...) computes.
+ *   prepare: per chunk, in parallel over all chunks, the in-chunk cumulative log
+ *            forget gate, the chunk-local stabilizer and the decayed intra-chunk
+ *            scores, written to the workspace (a no-op for shapes whose
+ *            forward runs as a single kernel)
+ *   scan:    the sequential pass over chunks that carries (C', n', m) and writes
+ *            h_out and the final state; reads what prepare left in the workspace
+ */
+mlstm_status mlstm_fwd_prepare(const void *q, const void *k,
+                               const float *i_pre, const float *f_pre,
+                               int B, int NH, int S, int d_qk, int d_v, int chunk,
+                               mlstm_dtype dtype,
+                               void *workspace, size_t workspace_bytes, void *stream);
+mlstm_status mlstm_fwd_scan(const void *q, const void *k, const void *v,
+                            const float *i_pre, const float *f_pre, const float *o_pre,
+                            int B, int NH, int S, int d_qk, int d_v, int chunk,
+                            mlstm_dtype dtype,
+                            void *h_out, float *C_final, float *n_final, float *m_final,
+                            void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One-token recurrent decode step (section 2.3, the recurrence applied once).
  *
  * The stabilized state (C, n, m) is read and updated IN PLACE; each element is

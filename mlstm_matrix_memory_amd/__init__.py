@@ -2,6 +2,8 @@
 
 Entry points (same names as include/mlstm.h):
   mlstm_fwd_parallel  chunkwise parallel forward over whole sequences
+  mlstm_fwd_prepare, mlstm_fwd_scan
+                      the two stages of mlstm_fwd_parallel, for callers that schedule them apart
   mlstm_step          one-token recurrent decode step, state updated in place
   mlstm_fwd_workspace_bytes, mlstm_status_string, mlstm_error_detail
 """
@@ -12,6 +14,8 @@ from .binding import (  # noqa: F401
     load_library,
     mlstm_error_detail,
     mlstm_fwd_parallel,
+    mlstm_fwd_prepare,
+    mlstm_fwd_scan,
     mlstm_fwd_workspace_bytes,
     mlstm_status_string,
     mlstm_step,

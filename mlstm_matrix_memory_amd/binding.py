@@ -51,6 +51,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mlstm_fwd_parallel.restype = i
     lib.mlstm_fwd_parallel.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, i,
                                        vp, fp, fp, fp, vp, sz, vp]
+    lib.mlstm_fwd_prepare.restype = i
+    lib.mlstm_fwd_prepare.argtypes = [vp, vp, fp, fp, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.mlstm_fwd_scan.restype = i
+    lib.mlstm_fwd_scan.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, i,
+                                   vp, fp, fp, fp, vp, sz, vp]
     lib.mlstm_step.restype = i
     lib.mlstm_step.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, fp, fp, fp, vp, vp]
     lib.mlstm_status_string.restype = ctypes.c_char_p
@@ -107,15 +112,8 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def mlstm_fwd_parallel(q, k, v, i_pre, f_pre, o_pre, chunk: int,
-                       h_out=None, C_final=None, n_final=None, m_final=None,
-                       workspace=None, stream=None):
-    """Chunkwise parallel forward from the zero state; returns (h, C, n, m).
-
-    q,k [B,NH,S,d_qk] and v [B,NH,S,d_v] float32 or bfloat16 on one GPU;
-    i_pre,f_pre [B,NH,S] and o_pre [B,NH,S,d_v] float32.  Outputs are allocated
-    when not given: h like v, C [B,NH,d_v,d_qk], n [B,NH,d_qk], m [B,NH] float32.
-    """
+def _fwd_args(q, k, v, i_pre, f_pre, o_pre, chunk, h_out, C_final, n_final, m_final, workspace, need_outputs):
+    """Checks the forward's tensors, allocates what is missing; returns the argument tuple."""
     import torch
     lib = load_library()
     if q.dim() != 4 or v.dim() != 4:
@@ -132,23 +130,39 @@ def mlstm_fwd_parallel(q, k, v, i_pre, f_pre, o_pre, chunk: int,
     _check(i_pre, "i_pre", (B, NH, S), torch.float32, dev)
     _check(f_pre, "f_pre", (B, NH, S), torch.float32, dev)
     _check(o_pre, "o_pre", (B, NH, S, dv), torch.float32, dev)
-    if h_out is None:
-        h_out = torch.empty((B, NH, S, dv), dtype=q.dtype, device=dev)
-    if C_final is None:
-        C_final = torch.empty((B, NH, dv, dqk), dtype=torch.float32, device=dev)
-    if n_final is None:
-        n_final = torch.empty((B, NH, dqk), dtype=torch.float32, device=dev)
-    if m_final is None:
-        m_final = torch.empty((B, NH), dtype=torch.float32, device=dev)
-    _check(h_out, "h_out", (B, NH, S, dv), q.dtype, dev)
-    _check(C_final, "C_final", (B, NH, dv, dqk), torch.float32, dev)
-    _check(n_final, "n_final", (B, NH, dqk), torch.float32, dev)
-    _check(m_final, "m_final", (B, NH), torch.float32, dev)
+    if need_outputs:
+        if h_out is None:
+            h_out = torch.empty((B, NH, S, dv), dtype=q.dtype, device=dev)
+        if C_final is None:
+            C_final = torch.empty((B, NH, dv, dqk), dtype=torch.float32, device=dev)
+        if n_final is None:
+            n_final = torch.empty((B, NH, dqk), dtype=torch.float32, device=dev)
+        if m_final is None:
+            m_final = torch.empty((B, NH), dtype=torch.float32, device=dev)
+        _check(h_out, "h_out", (B, NH, S, dv), q.dtype, dev)
+        _check(C_final, "C_final", (B, NH, dv, dqk), torch.float32, dev)
+        _check(n_final, "n_final", (B, NH, dqk), torch.float32, dev)
+        _check(m_final, "m_final", (B, NH), torch.float32, dev)
     need = int(lib.mlstm_fwd_workspace_bytes(B, NH, S, dqk, dv, chunk, dt))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return (B, NH, S, dqk, dv, dt, h_out, C_final, n_final, m_final, workspace, ws_ptr, ws_bytes, dev)
+
+
+def mlstm_fwd_parallel(q, k, v, i_pre, f_pre, o_pre, chunk: int,
+                       h_out=None, C_final=None, n_final=None, m_final=None,
+                       workspace=None, stream=None):
+    """Chunkwise parallel forward from the zero state; returns (h, C, n, m).
+
+    q,k [B,NH,S,d_qk] and v [B,NH,S,d_v] float32 or bfloat16 on one GPU;
+    i_pre,f_pre [B,NH,S] and o_pre [B,NH,S,d_v] float32.  Outputs are allocated
+    when not given: h like v, C [B,NH,d_v,d_qk], n [B,NH,d_qk], m [B,NH] float32.
+    """
+    lib = load_library()
+    (B, NH, S, dqk, dv, dt, h_out, C_final, n_final, m_final, workspace, ws_ptr, ws_bytes, dev) = _fwd_args(
+        q, k, v, i_pre, f_pre, o_pre, chunk, h_out, C_final, n_final, m_final, workspace, True)
     st = lib.mlstm_fwd_parallel(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                 i_pre.data_ptr(), f_pre.data_ptr(), o_pre.data_ptr(),
                                 B, NH, S, dqk, dv, int(chunk), dt,
@@ -156,6 +170,33 @@ def mlstm_fwd_parallel(q, k, v, i_pre, f_pre, o_pre, chunk: int,
                                 ws_ptr, ws_bytes, _stream_handle(stream, dev))
     if st != MLSTM_OK:
         raise MlstmError("mlstm_fwd_parallel", st, mlstm_error_detail())
+    return h_out, C_final, n_final, m_final
+
+
+def mlstm_fwd_prepare(q, k, v, i_pre, f_pre, o_pre, chunk: int, workspace, stream=None):
+    """First stage of mlstm_fwd_parallel (per-chunk gates and decayed scores into workspace)."""
+    lib = load_library()
+    (B, NH, S, dqk, dv, dt, _, _, _, _, workspace, ws_ptr, ws_bytes, dev) = _fwd_args(
+        q, k, v, i_pre, f_pre, o_pre, chunk, None, None, None, None, workspace, False)
+    st = lib.mlstm_fwd_prepare(q.data_ptr(), k.data_ptr(), i_pre.data_ptr(), f_pre.data_ptr(),
+                               B, NH, S, dqk, dv, int(chunk), dt, ws_ptr, ws_bytes, _stream_handle(stream, dev))
+    if st != MLSTM_OK:
+        raise MlstmError("mlstm_fwd_prepare", st, mlstm_error_detail())
+
+
+def mlstm_fwd_scan(q, k, v, i_pre, f_pre, o_pre, chunk: int, h_out, C_final, n_final, m_final,
+                   workspace, stream=None):
+    """Second stage of mlstm_fwd_parallel (sequential pass over chunks); outputs given."""
+    lib = load_library()
+    (B, NH, S, dqk, dv, dt, h_out, C_final, n_final, m_final, workspace, ws_ptr, ws_bytes, dev) = _fwd_args(
+        q, k, v, i_pre, f_pre, o_pre, chunk, h_out, C_final, n_final, m_final, workspace, True)
+    st = lib.mlstm_fwd_scan(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                            i_pre.data_ptr(), f_pre.data_ptr(), o_pre.data_ptr(),
+                            B, NH, S, dqk, dv, int(chunk), dt,
+                            h_out.data_ptr(), C_final.data_ptr(), n_final.data_ptr(), m_final.data_ptr(),
+                            ws_ptr, ws_bytes, _stream_handle(stream, dev))
+    if st != MLSTM_OK:
+        raise MlstmError("mlstm_fwd_scan", st, mlstm_error_detail())
     return h_out, C_final, n_final, m_final
 
 

@@ -60,12 +60,31 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
     s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
     return __builtin_bit_cast(bf16x4, v);
 }
+// Workgroup barrier that orders LDS traffic only: this wave's LDS operations are
+// complete (lgkmcnt 0) before it signals, but global loads still in flight stay in
+// flight, so register prefetches issued before the barrier keep overlapping with
+// the work after it.  (The full __syncthreads fence would wait for them.)  The
+// memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 __device__ __forceinline__ bf16x8 cvt8(f32x4 a, f32x4 b) {
     return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
                   (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
+}
+
+// Sum over the 16 lanes of each row of a wave with DPP lane permutes (VALU only,
+// no LDS round trips): swap neighbours, swap pairs, mirror within 8, mirror within 16.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xF, 0xF, false)); // row_half_mirror
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x140, 0xF, 0xF, false)); // row_mirror
+    return x;
 }
 
 // inclusive scans over the lanes of one wave (64 lanes), fp64
@@ -87,27 +106,62 @@ __device__ __forceinline__ double wave_scan_max(double x, int lane) {
 }
 
 // ---------------------------------------------------------------------------
-// workspace layout: P_loc as bf16 hi/lo pairs [heads][chunk][2][L][L]; the
-// in-chunk cumulative log forget gate and chunk-local stabilizer as fp64
-// [heads][S]; den_loc and w_loc as fp32 [heads][S]
+// workspace layout (one allocation, 256-byte aligned pieces)
 // ---------------------------------------------------------------------------
 struct Ws {
-    bf16* P; double* b; double* mloc; float* den; float* wloc;
+    bf16* P;        // [heads][chunk][2][L][L]  decayed intra-chunk scores, bf16 hi then lo
+    double* b;      // [heads][S]  in-chunk cumulative log forget gate
+    double* mloc;   // [heads][S]  chunk-local stabilizer
+    float* den;     // [heads][S]  row sums of the decayed scores (fp32, before rounding)
+    float* wloc;    // [heads][S]  chunk-local update weights
+    float* dn;      // [heads][chunk][DQ]  K^T w_loc of each chunk
+    // six per-token arrays in one allocation [6][heads][S], in this order:
+    float* a;       // weight of the carried state in each row
+    float* r;       // rescale of the chunk-local scores to the carried stabilizer
+    float* fl;      // floor exp(-m_t) of the normalizer
+    float* w;       // update weights with the carried stabilizer
+    float* den2;    // copy of den (row sums of the decayed scores)
+    float* alt;     // alpha of the token's chunk, repeated over its tokens
+    size_t hs;      // heads * S: stride between the six arrays
+    float* alpha;   // [heads][chunk]  decay of the carried state across the chunk
+    float* nent;    // [heads][chunk][DQ]  normalizer n' entering each chunk
+    float* nfin;    // [heads][DQ]  final normalizer
+    float* mfin;    // [heads]      final stabilizer
 };
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline Ws ws_layout(void* base, size_t heads, size_t S, int L) {
+inline size_t ws_walk(void* base, size_t heads, size_t S, int L, int DQ, Ws* out) {
+    const size_t nC = S / L;
     char* p = (char*)base;
+    size_t off = 0;
+    auto take = [&](size_t bytes) { char* q = p + off; off += align256(bytes); return q; };
     Ws w;
-    w.P = (bf16*)p;                       p += align256(2 * heads * S * L * sizeof(bf16));
-    w.b = (double*)p;                     p += align256(heads * S * sizeof(double));
-    w.mloc = (double*)p;                  p += align256(heads * S * sizeof(double));
-    w.den = (float*)p;                    p += align256(heads * S * sizeof(float));
-    w.wloc = (float*)p;
+    w.P = (bf16*)take(2 * heads * S * L * sizeof(bf16));
+    w.b = (double*)take(heads * S * sizeof(double));
+    w.mloc = (double*)take(heads * S * sizeof(double));
+    w.den = (float*)take(heads * S * sizeof(float));
+    w.wloc = (float*)take(heads * S * sizeof(float));
+    w.dn = (float*)take(heads * nC * DQ * sizeof(float));
+    w.hs = heads * S;
+    w.a = (float*)take(6 * heads * S * sizeof(float));
+    w.r = w.a + w.hs;
+    w.fl = w.a + 2 * w.hs;
+    w.w = w.a + 3 * w.hs;
+    w.den2 = w.a + 4 * w.hs;
+    w.alt = w.a + 5 * w.hs;
+    w.alpha = (float*)take(heads * nC * sizeof(float));
+    w.nent = (float*)take(heads * nC * DQ * sizeof(float));
+    w.nfin = (float*)take(heads * DQ * sizeof(float));
+    w.mfin = (float*)take(heads * sizeof(float));
+    if (out) *out = w;
+    return off;
+}
+inline Ws ws_layout(void* base, size_t heads, size_t S, int L, int DQ) {
+    Ws w;
+    ws_walk(base, heads, S, L, DQ, &w);
     return w;
 }
-inline size_t ws_bytes(size_t heads, size_t S, int L) {
-    return align256(2 * heads * S * L * sizeof(bf16)) + 2 * align256(heads * S * sizeof(double)) +
-           2 * align256(heads * S * sizeof(float));
+inline size_t ws_bytes(size_t heads, size_t S, int L, int DQ) {
+    return ws_walk(nullptr, heads, S, L, DQ, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -124,7 +178,7 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     constexpr int LB = L / 16;
     constexpr int PPITCH = L + 8;
     __shared__ double sb[L], sml[L];
-    __shared__ float si[L];
+    __shared__ float si[L], swl[L];
     __shared__ double wsum[2], wmax[2];  // per-wave totals of the two scans (separate: no reuse race)
     __shared__ __attribute__((aligned(16))) bf16 sP[2][L * PPITCH];   // hi, lo
 
@@ -163,7 +217,9 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
         const double bL = sb[L - 1], mL = sml[L - 1];
         ws.b[tok0 + tid] = sb[tid];
         ws.mloc[tok0 + tid] = sml[tid];
-        ws.wloc[tok0 + tid] = exp_arg(bL - sb[tid] + (double)si[tid] - mL);
+        const float wl = exp_arg(bL - sb[tid] + (double)si[tid] - mL);
+        ws.wloc[tok0 + tid] = wl;
+        swl[tid] = wl;
     }
 
     // decayed scores, one 16-row block per wave pass
@@ -214,6 +270,138 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
         const bf16* src = sP[half] + row * PPITCH + col;
         bf16x8 v = bf16x8{src[0], src[1], src[2], src[3], src[4], src[5], src[6], src[7]};
         *reinterpret_cast<bf16x8*>(Pout + (size_t)half * L * L + (size_t)row * L + col) = v;
+    }
+    // chunk contribution to the normalizer: K^T w_loc (fp32; k exact bf16)
+    float* dn = ws.dn + ((size_t)bh * (S / L) + c) * dqk;
+    for (int j = tid; j < dqk; j += PREP_THREADS) {
+        float acc = 0.0f;
+#pragma unroll 8
+        for (int t = 0; t < L; ++t) acc += swl[t] * (float)kh[(size_t)t * dqk + j];
+        dn[j] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// kernel 1b: per head, the stabilizer and normalizer carried across chunks
+// ---------------------------------------------------------------------------
+// m entering chunk c follows the max-plus recurrence m <- max(b_L + m, m_loc_L);
+// with it every per-token weight of the scan is fixed:
+//   a_t = exp(b_t + m_p - m_t), r_t = exp(m_loc_t - m_t), fl_t = exp(-m_t),
+//   w_t = exp(m_loc_L - m_L) w_loc_t, alpha_c = exp(b_L + m_p - m_L),
+// and the normalizer entering each chunk follows n' <- alpha n' + exp(m_loc_L - m_L) K^T w_loc.
+constexpr int GS_THREADS = 256;
+constexpr int GS_TILE = 512;     // chunks per pass over LDS
+constexpr int GS_NJ = 4096 / GS_THREADS;
+
+template <int L>
+__global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int dqk,
+                                                               const float* __restrict__ n0,
+                                                               const float* __restrict__ m0)
+{
+    __shared__ double sbl[GS_TILE], sml[GS_TILE], smp[GS_TILE + 1];
+    __shared__ float salpha[GS_TILE], srl[GS_TILE];
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int nC = S / L;
+    const size_t tokh = (size_t)bh * S;
+    double m_run = m0 ? (double)m0[bh] : 0.0;
+    float nreg[GS_NJ];
+#pragma unroll
+    for (int u = 0; u < GS_NJ; ++u) {
+        const int j = tid + GS_THREADS * u;
+        nreg[u] = (j < dqk && n0) ? n0[(size_t)bh * dqk + j] : 0.0f;
+    }
+    for (int c0 = 0; c0 < nC; c0 += GS_TILE) {
+        const int nt = min(GS_TILE, nC - c0);
+        for (int i = tid; i < nt; i += GS_THREADS) {
+            const size_t t = tokh + (size_t)(c0 + i) * L + L - 1;
+            sbl[i] = ws.b[t];
+            sml[i] = ws.mloc[t];
+        }
+        __syncthreads();
+        if (tid == 0) {
+            double mp = m_run;
+            for (int i = 0; i < nt; ++i) {
+                smp[i] = mp;
+                const double mL = fmax(sbl[i] + mp, sml[i]);
+                salpha[i] = exp_arg(sbl[i] + mp - mL);
+                srl[i] = exp_arg(sml[i] - mL);
+                mp = mL;
+            }
+            smp[nt] = mp;
+        }
+        __syncthreads();
+        m_run = smp[nt];
+        for (int t = tid; t < nt * L; t += GS_THREADS) {
+            const int ci = t / L;
+            const size_t g = tokh + (size_t)c0 * L + t;
+            const double mp = smp[ci];
+            const double bt = ws.b[g], ml = ws.mloc[g];
+            const double mt = fmax(bt + mp, ml);
+            ws.a[g] = exp_arg(bt + mp - mt);
+            ws.r[g] = exp_arg(ml - mt);
+            ws.fl[g] = exp_arg(-mt);
+            ws.w[g] = srl[ci] * ws.wloc[g];
+            ws.alt[g] = salpha[ci];
+        }
+        for (int i = tid; i < nt; i += GS_THREADS) ws.alpha[(size_t)bh * nC + c0 + i] = salpha[i];
+#pragma unroll
+        for (int u = 0; u < GS_NJ; ++u) {
+            const int j = tid + GS_THREADS * u;
+            if (j < dqk) {
+                float nv = nreg[u];
+#pragma unroll 8
+                for (int i = 0; i < nt; ++i) {
+                    const size_t cc = (size_t)bh * nC + c0 + i;
+                    ws.nent[cc * dqk + j] = nv;
+                    nv = salpha[i] * nv + srl[i] * ws.dn[cc * dqk + j];
+                }
+                nreg[u] = nv;
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int u = 0; u < GS_NJ; ++u) {
+        const int j = tid + GS_THREADS * u;
+        if (j < dqk) ws.nfin[(size_t)bh * dqk + j] = nreg[u];
+    }
+    if (tid == 0) ws.mfin[bh] = (float)m_run;
+}
+
+// ---------------------------------------------------------------------------
+// kernel 1c: the normalizer of every token
+// ---------------------------------------------------------------------------
+// den_t = r_t den_loc_t + a_t (q_t . n'_entering), in fp32: this is the quantity the
+// retrieval divides by, and the one that cancels, so it is formed from exact bf16
+// q and the fp32 normalizer state (no bf16 rounding of computed values).
+constexpr int DEN_THREADS = 256;
+
+template <int L>
+__global__ __launch_bounds__(DEN_THREADS) void den_kernel(const bf16* __restrict__ q, Ws ws, int S, int dqk)
+{
+    __shared__ __attribute__((aligned(16))) float sn[4096];
+    const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+    const int nC = S / L;
+    const float* ne = ws.nent + ((size_t)bh * nC + c) * dqk;
+    for (int j = tid; j < dqk; j += DEN_THREADS) sn[j] = ne[j];
+    __syncthreads();
+    const size_t tok0 = (size_t)bh * S + (size_t)c * L;
+    const int lp = tid & 15;
+    for (int row = tid >> 4; row < L; row += DEN_THREADS / 16) {
+        const bf16* qr = q + (tok0 + row) * dqk;
+        float acc = 0.0f;
+        for (int j0 = lp * 8; j0 < dqk; j0 += 128) {
+            const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(qr + j0);
+            const f32x4 n0 = *reinterpret_cast<const f32x4*>(sn + j0);
+            const f32x4 n1 = *reinterpret_cast<const f32x4*>(sn + j0 + 4);
+            acc += (float)q8[0] * n0[0] + (float)q8[1] * n0[1] + (float)q8[2] * n0[2] + (float)q8[3] * n0[3]
+                 + (float)q8[4] * n1[0] + (float)q8[5] * n1[1] + (float)q8[6] * n1[2] + (float)q8[7] * n1[3];
+        }
+        acc = row16_sum(acc);
+        if (lp == 0) {
+            const size_t g = tok0 + row;
+            ws.den2[g] = ws.r[g] * ws.den[g] + ws.a[g] * acc;
+        }
     }
 }
 
@@ -503,13 +691,366 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// kernel 2, pipelined form (chunks of 32 or 64 tokens)
+// ---------------------------------------------------------------------------
+// Same mathematics as chunk_scan, with every per-token weight and the entering
+// normalizer precomputed by gate_scan, so the only sequential dependence left is
+// the state itself.  Global loads run one step ahead of the MFMAs: while slab s
+// is multiplied, slab s+1 (or slab 0 of the next chunk) is in flight into
+// registers, and while chunk c is processed, chunk c+1's V tile, decayed scores,
+// output-gate pre-activations and weights are in flight.  Q/K slabs are double
+// buffered in LDS, so a slab costs one barrier; a chunk adds two (partial sums of
+// Q C'^T over the key parts, and release of the chunk-level tiles).
+template <int L_, int DQ_, int NC_, int NK_, int SB_, int MINB_>
+struct Scan2Cfg {
+    static constexpr int L = L_, DQ = DQ_, NC = NC_, NK = NK_, SB = SB_, MINB = MINB_;
+    static constexpr int W = NC * NK, THREADS = 64 * W, TV = 16 * NC;
+    static constexpr int DP = DQ / NK, NS = DP / SB, SW = NK * SB;
+    static constexpr int QP = SW + 4;      // Q pitch: row stride = 2 (mod 32) dwords
+    static constexpr int KP = SW + 16;     // K pitch: row stride = 8 (mod 32) dwords
+    static constexpr int VP = ((TV + 63) / 64) * 64 + 16;
+    static constexpr int PP = L + 8, OP = TV + 4;
+    static constexpr int LB = L / 16, SBB = SB / 16, NSB = DP / 16;
+    static constexpr int RED = LB * (NK - 1) * NC * 256;   // floats
+    // staged 16-byte units
+    static constexpr int U_Q = L * SW / 8, U_SLAB = 2 * U_Q;
+    static constexpr int U_V = L * TV / 8, U_P = 2 * L * L / 8, U_O = L * TV / 4;
+    static constexpr int U_SC = 6 * L / 4;
+    static constexpr int U_CH = U_V + U_P + U_O + U_SC;
+    static constexpr int NPS = (U_SLAB + THREADS - 1) / THREADS;
+    static constexpr int NPC = (U_CH + THREADS - 1) / THREADS;
+    static_assert(SW % 64 == 0 && SB % 32 == 0 && DP % SB == 0, "slab tiling");
+    static_assert(LB % NK == 0 && L % 32 == 0 && L <= 64, "row blocks");
+    static_assert(THREADS <= 1024, "workgroup too large");
+};
+
+template <class C>
+struct alignas(16) Scan2Smem {
+    alignas(16) bf16 q[2][C::L * C::QP];
+    alignas(16) bf16 k[2][C::L * C::KP];
+    alignas(16) bf16 v[C::L * C::VP];
+    alignas(16) bf16 p[2][C::L * C::PP];
+    alignas(16) float o[C::L * C::OP];
+    alignas(16) float sc[6][C::L];       // a, r, fl, w, den (full normalizer), alpha (per chunk, repeated)
+    alignas(16) float red[C::RED > 0 ? C::RED : 4];
+};
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Per-thread loop over n 16-byte units of one staged region; `body(idx, u)` is
+// called for idx = tid + u*THREADS < n with a compile-time u.
+template <int THREADS, int N, int BASE, class F>
+__device__ __forceinline__ void for_units(int tid, F&& body) {
+#pragma unroll
+    for (int u = 0; u < cdiv(N, THREADS); ++u) {
+        const int idx = tid + u * THREADS;
+        if ((N % THREADS == 0) || idx < N) body(idx, BASE + u);
+    }
+}
+
+template <class C>
+struct Pref {
+    static constexpr int NQ = cdiv(C::U_Q, C::THREADS);      // Q units per thread
+    static constexpr int NSL = 2 * NQ;                         // Q + K
+    static constexpr int NV = cdiv(C::U_V, C::THREADS);
+    static constexpr int NP = cdiv(C::U_P, C::THREADS);
+    static constexpr int NO = cdiv(C::U_O, C::THREADS);
+    static constexpr int NSC = cdiv(C::U_SC, C::THREADS);
+    static constexpr int NCH = NV + NP + NO + NSC;
+};
+
+template <class C>
+__device__ __forceinline__ void slab_load(f32x4 (&reg)[Pref<C>::NSL], int tid, const bf16* qh, const bf16* kh,
+                                          size_t t0, int s) {
+    constexpr int NQ = Pref<C>::NQ;
+    auto src_off = [&](int idx) {
+        const int row = idx / (C::SW / 8), c8 = 8 * (idx % (C::SW / 8));
+        return (t0 + row) * C::DQ + (c8 / C::SB) * C::DP + s * C::SB + (c8 % C::SB);
+    };
+    for_units<C::THREADS, C::U_Q, 0>(tid, [&](int idx, int u) {
+        reg[u] = *reinterpret_cast<const f32x4*>(qh + src_off(idx));
+    });
+    for_units<C::THREADS, C::U_Q, NQ>(tid, [&](int idx, int u) {
+        reg[u] = *reinterpret_cast<const f32x4*>(kh + src_off(idx));
+    });
+}
+
+template <class C>
+__device__ __forceinline__ void slab_store(const f32x4 (&reg)[Pref<C>::NSL], Scan2Smem<C>& sm, int buf, int tid) {
+    constexpr int NQ = Pref<C>::NQ;
+    for_units<C::THREADS, C::U_Q, 0>(tid, [&](int idx, int u) {
+        const int row = idx / (C::SW / 8), c8 = 8 * (idx % (C::SW / 8));
+        f32x2* d = reinterpret_cast<f32x2*>(sm.q[buf] + row * C::QP + c8);   // 8-byte aligned rows
+        d[0] = f32x2{reg[u][0], reg[u][1]};
+        d[1] = f32x2{reg[u][2], reg[u][3]};
+    });
+    for_units<C::THREADS, C::U_Q, NQ>(tid, [&](int idx, int u) {
+        const int row = idx / (C::SW / 8), c8 = 8 * (idx % (C::SW / 8));
+        *reinterpret_cast<f32x4*>(sm.k[buf] + row * C::KP + c8) = reg[u];
+    });
+}
+
+struct ChunkSrc {
+    const bf16* v; const bf16* P; const float* o;
+    const float* sc;     // a of the chunk's first token; the other five arrays follow at stride hs
+    size_t hs;
+    int vcols;           // valid value columns of the tile
+};
+
+template <class C>
+__device__ __forceinline__ void chunk_load(f32x4 (&reg)[Pref<C>::NCH], int tid, const ChunkSrc& cs, int dv) {
+    using PF = Pref<C>;
+    for_units<C::THREADS, C::U_V, 0>(tid, [&](int idx, int u) {
+        const int row = idx / (C::TV / 8), col = 8 * (idx % (C::TV / 8));
+        reg[u] = (col < cs.vcols) ? *reinterpret_cast<const f32x4*>(cs.v + (size_t)row * dv + col) : f32x4{0, 0, 0, 0};
+    });
+    for_units<C::THREADS, C::U_P, PF::NV>(tid, [&](int idx, int u) {
+        reg[u] = *reinterpret_cast<const f32x4*>(cs.P + 8 * idx);
+    });
+    for_units<C::THREADS, C::U_O, PF::NV + PF::NP>(tid, [&](int idx, int u) {
+        const int row = idx / (C::TV / 4), col = 4 * (idx % (C::TV / 4));
+        reg[u] = (col < cs.vcols) ? *reinterpret_cast<const f32x4*>(cs.o + (size_t)row * dv + col) : f32x4{0, 0, 0, 0};
+    });
+    for_units<C::THREADS, C::U_SC, PF::NV + PF::NP + PF::NO>(tid, [&](int idx, int u) {
+        const int arr = idx / (C::L / 4), i4 = idx % (C::L / 4);
+        reg[u] = *reinterpret_cast<const f32x4*>(cs.sc + arr * cs.hs + 4 * i4);
+    });
+}
+
+template <class C>
+__device__ __forceinline__ void chunk_store(const f32x4 (&reg)[Pref<C>::NCH], Scan2Smem<C>& sm, int tid) {
+    using PF = Pref<C>;
+    for_units<C::THREADS, C::U_V, 0>(tid, [&](int idx, int u) {
+        const int row = idx / (C::TV / 8), col = 8 * (idx % (C::TV / 8));
+        *reinterpret_cast<f32x4*>(sm.v + row * C::VP + col) = reg[u];
+    });
+    for_units<C::THREADS, C::U_P, PF::NV>(tid, [&](int idx, int u) {
+        const int half = idx / (C::L * C::L / 8), rem = idx % (C::L * C::L / 8);
+        const int row = rem / (C::L / 8), col = 8 * (rem % (C::L / 8));
+        *reinterpret_cast<f32x4*>(sm.p[half] + row * C::PP + col) = reg[u];
+    });
+    for_units<C::THREADS, C::U_O, PF::NV + PF::NP>(tid, [&](int idx, int u) {
+        const int row = idx / (C::TV / 4), col = 4 * (idx % (C::TV / 4));
+        *reinterpret_cast<f32x4*>(sm.o + row * C::OP + col) = reg[u];
+    });
+    for_units<C::THREADS, C::U_SC, PF::NV + PF::NP + PF::NO>(tid, [&](int idx, int u) {
+        const int arr = idx / (C::L / 4), i4 = idx % (C::L / 4);
+        *reinterpret_cast<f32x4*>(&sm.sc[arr][4 * i4]) = reg[u];
+    });
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
+    const float* __restrict__ o_pre, Ws ws, int S, int dv, int n_vt, int remap,
+    const float* __restrict__ C0,
+    bf16* __restrict__ h, float* __restrict__ Cout, float* __restrict__ nout, float* __restrict__ mout)
+{
+    constexpr int L = C::L, DQ = C::DQ, NC = C::NC, NK = C::NK, SB = C::SB;
+    constexpr int THREADS = C::THREADS, TV = C::TV, DP = C::DP, NS = C::NS;
+    constexpr int QP = C::QP, KP = C::KP, VP = C::VP, PP = C::PP, OP = C::OP;
+    constexpr int LB = C::LB, SBB = C::SBB, NSB = C::NSB;
+    // Lazy decay: the registers hold C^ = C' / sigma; each chunk's decay alpha is
+    // folded into sigma and into the weights of the update (w / sigma) and of the
+    // retrieval (a sigma), and the registers are rescaled only when sigma would
+    // leave the range where 1/sigma is comfortably finite.
+    constexpr float SIGMA_MIN = 0x1p-60f;
+    __shared__ Scan2Smem<C> sm;
+
+    int wg = blockIdx.x;
+    if (remap) {
+        const int G = gridDim.x;
+        wg = (wg % 8) * (G / 8) + wg / 8;
+    }
+    const int bh = wg / n_vt, vt = wg % n_vt;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int cb = wave % NC, kq = wave / NC;
+    const int ln = lane & 15, lg = lane >> 4;
+    const int vcol = vt * TV + 16 * cb;
+    const bool active = vcol < dv;
+    const int nC = S / L;
+
+    const size_t tokh = (size_t)bh * S;
+    const bf16* qh = q + tokh * DQ;
+    const bf16* kh = k + tokh * DQ;
+    bf16* hh = h + tokh * dv;
+
+    auto chunk_src = [&](int c) {
+        ChunkSrc cs;
+        const size_t t0 = (size_t)c * L;
+        cs.v = v + (tokh + t0) * dv + vt * TV;
+        cs.P = ws.P + 2 * (tokh + t0) * L;
+        cs.o = o_pre + (tokh + t0) * dv + vt * TV;
+        cs.sc = ws.a + tokh + t0;
+        cs.hs = ws.hs;
+        cs.vcols = min(TV, dv - vt * TV);
+        return cs;
+    };
+
+    // state: block jb holds key rows j = kq*DP + 16*jb + 4*lg + i, value column vcol + ln
+    f32x4 st[NSB];
+#pragma unroll
+    for (int jb = 0; jb < NSB; ++jb) {
+        st[jb] = f32x4{0, 0, 0, 0};
+        if (C0 && active)
+            st[jb] = *reinterpret_cast<const f32x4*>(
+                C0 + ((size_t)bh * dv + vcol + ln) * DQ + kq * DP + 16 * jb + 4 * lg);
+    }
+
+    f32x4 rs[Pref<C>::NSL], rc[Pref<C>::NCH];
+    chunk_load<C>(rc, tid, chunk_src(0), dv);
+    slab_load<C>(rs, tid, qh, kh, 0, 0);
+    float sigma = 1.0f;
+
+    for (int c = 0; c < nC; ++c) {
+        const size_t t0 = (size_t)c * L;
+        chunk_store<C>(rc, sm, tid);
+        f32x4 acc_inter[LB];
+#pragma unroll
+        for (int tb = 0; tb < LB; ++tb) acc_inter[tb] = f32x4{0, 0, 0, 0};
+        bf16x8 vwh[L / 32], vwl[L / 32];
+        float sig_new = 1.0f, st_scale = 1.0f;   // set after the first barrier (alpha is in LDS)
+
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            const int buf = (c * NS + s) & 1;
+            slab_store<C>(rs, sm, buf, tid);
+            lds_barrier();
+            // next loads in flight while this slab is multiplied
+            if (s + 1 < NS) slab_load<C>(rs, tid, qh, kh, t0, s + 1);
+            else if (c + 1 < nC) slab_load<C>(rs, tid, qh, kh, t0 + L, 0);
+            if (s == NS - 1 && c + 1 < nC) chunk_load<C>(rc, tid, chunk_src(c + 1), dv);
+            if (s == 0) {
+                const float cand = sigma * sm.sc[5][0];
+                const bool rescale = cand < SIGMA_MIN;
+                st_scale = rescale ? cand : 1.0f;
+                sig_new = rescale ? 1.0f : cand;
+            }
+            if (active) {
+                if (s == 0) {
+                    // (w / sigma') (.) V for this wave's 16 columns, split into bf16 hi + lo
+                    const float inv_sig = 1.0f / sig_new;
+#pragma unroll
+                    for (int kk = 0; kk < L / 32; ++kk) {
+                        const int vrow = (32 * kk + 8 * lg + (ln >> 2)) * VP + 16 * cb + 4 * (ln & 3);
+                        const bf16x8 vb = cat(lds_read_tr(sm.v + vrow), lds_read_tr(sm.v + vrow + 4 * VP));
+                        const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sm.sc[3][32 * kk + 8 * lg]) * inv_sig;
+                        const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sm.sc[3][32 * kk + 8 * lg + 4]) * inv_sig;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float x = (e < 4 ? w0[e & 3] : w1[e & 3]) * (float)vb[e];
+                            const bf16 hi = (bf16)x;
+                            vwh[kk][e] = hi;
+                            vwl[kk][e] = (bf16)(x - (float)hi);
+                        }
+                    }
+                }
+                // inter-chunk retrieval: acc_inter += Q[:, slab] (C'_hi + C'_lo)^T[slab, cols]
+#pragma unroll
+                for (int kk = 0; kk < SB / 32; ++kk) {
+                    bf16x8 bhi, blo;
+                    split8(st[s * SBB + 2 * kk], st[s * SBB + 2 * kk + 1], bhi, blo);
+#pragma unroll
+                    for (int tb = 0; tb < LB; ++tb) {
+                        const bf16* qa = sm.q[buf] + (16 * tb + ln) * QP + kq * SB + 32 * kk + 4 * lg;
+                        const bf16x8 aop = cat(*reinterpret_cast<const bf16x4*>(qa),
+                                               *reinterpret_cast<const bf16x4*>(qa + 16));
+                        acc_inter[tb] = mfma(aop, bhi, acc_inter[tb]);
+                        acc_inter[tb] = mfma(aop, blo, acc_inter[tb]);
+                    }
+                }
+                // state update: C^[slab] += K[:, slab]^T ((w / sigma') V)_{hi+lo}
+                if (st_scale != 1.0f) {
+#pragma unroll
+                    for (int jb = 0; jb < SBB; ++jb) st[s * SBB + jb] *= st_scale;
+                }
+#pragma unroll
+                for (int kk = 0; kk < L / 32; ++kk) {
+#pragma unroll
+                    for (int jb = 0; jb < SBB; ++jb) {
+                        const bf16* ka = sm.k[buf] + (32 * kk + 8 * lg + (ln >> 2)) * KP + kq * SB + 16 * jb + 4 * (ln & 3);
+                        const bf16x8 aop = cat(lds_read_tr(ka), lds_read_tr(ka + 4 * KP));
+                        st[s * SBB + jb] = mfma(aop, vwh[kk], st[s * SBB + jb]);
+                        st[s * SBB + jb] = mfma(aop, vwl[kk], st[s * SBB + jb]);
+                    }
+                }
+            }
+        }
+
+        // --- partial sums over key parts, then the rows each part owns --------
+        if (NK > 1 && active) {
+#pragma unroll
+            for (int tb = 0; tb < LB; ++tb) {
+                const int owner = tb % NK;
+                if (owner == kq) continue;
+                const int slot = kq < owner ? kq : kq - 1;
+                *reinterpret_cast<f32x4*>(sm.red + (((tb * (NK - 1) + slot) * NC + cb) * 256 + lane * 4)) = acc_inter[tb];
+            }
+        }
+        lds_barrier();
+        if (active) {
+#pragma unroll
+            for (int tb = 0; tb < LB; ++tb) {
+                if (tb % NK != kq) continue;
+                f32x4 inter = acc_inter[tb];
+#pragma unroll
+                for (int sl = 0; sl < NK - 1; ++sl)
+                    inter += *reinterpret_cast<const f32x4*>(sm.red + (((tb * (NK - 1) + sl) * NC + cb) * 256 + lane * 4));
+                f32x4 intra = {0, 0, 0, 0};
+#pragma unroll
+                for (int kk = 0; kk <= (16 * tb + 15) / 32; ++kk) {
+                    const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(sm.p[0] + (16 * tb + ln) * PP + 32 * kk + 8 * lg);
+                    const bf16x8 alo = *reinterpret_cast<const bf16x8*>(sm.p[1] + (16 * tb + ln) * PP + 32 * kk + 8 * lg);
+                    const bf16* vb = sm.v + (32 * kk + 8 * lg + (ln >> 2)) * VP + 16 * cb + 4 * (ln & 3);
+                    const bf16x8 bop = cat(lds_read_tr(vb), lds_read_tr(vb + 4 * VP));
+                    intra = mfma(ahi, bop, intra);
+                    intra = mfma(alo, bop, intra);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tau = 16 * tb + 4 * lg + i;
+                    const float aa = sm.sc[0][tau] * sigma, ra = sm.sc[1][tau], fl = sm.sc[2][tau];
+                    const float num = ra * intra[i] + aa * inter[i];
+                    const float den = sm.sc[4][tau];
+                    const float og = __builtin_amdgcn_rcpf(1.0f + __expf(-sm.o[tau * OP + 16 * cb + ln]));
+                    const float hv = og * num * __builtin_amdgcn_rcpf(fmaxf(fabsf(den), fl));
+                    hh[(t0 + tau) * dv + vcol + ln] = (bf16)hv;
+                }
+            }
+        }
+        sigma = sig_new;
+        lds_barrier();
+    }
+
+    if (active) {
+#pragma unroll
+        for (int jb = 0; jb < NSB; ++jb)
+            *reinterpret_cast<f32x4*>(Cout + ((size_t)bh * dv + vcol + ln) * DQ + kq * DP + 16 * jb + 4 * lg) = st[jb] * sigma;
+    }
+    if (vt == 0) {
+        for (int j = tid; j < DQ; j += THREADS) nout[(size_t)bh * DQ + j] = ws.nfin[(size_t)bh * DQ + j];
+        if (tid == 0) mout[bh] = ws.mfin[bh];
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 template <int L>
-hipError_t launch_prep(const FwdArgs& a, const Ws& w) {
+hipError_t launch_prep(const FwdArgs& a, const Ws& w, bool gates) {
     dim3 grid(a.S / L, a.B * a.NH);
     hipLaunchKernelGGL((chunk_prep_kernel<L>), grid, dim3(PREP_THREADS), 0, a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, a.i_pre, a.f_pre, a.S, a.dqk, w);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !gates) return e;
+    hipLaunchKernelGGL((gate_scan_kernel<L>), dim3(a.B * a.NH), dim3(GS_THREADS), 0, a.stream,
+                       w, a.S, a.dqk, a.n0, a.m0);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((den_kernel<L>), dim3(a.S / L, a.B * a.NH), dim3(DEN_THREADS), 0, a.stream,
+                       (const bf16*)a.q, w, a.S, a.dqk);
     return hipGetLastError();
 }
 
@@ -524,31 +1065,54 @@ hipError_t launch_scan(const FwdArgs& a, const Ws& w) {
     return hipGetLastError();
 }
 
+template <class C>
+hipError_t launch_scan2(const FwdArgs& a, const Ws& w) {
+    const int n_vt = (a.dv + C::TV - 1) / C::TV;
+    const int G = a.B * a.NH * n_vt;
+    const int remap = (G % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((chunk_scan2_kernel<C>), dim3(G), dim3(C::THREADS), 0, a.stream,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.o_pre, w, a.S, a.dv, n_vt, remap,
+                       a.C0, (bf16*)a.h, a.C, a.n, a.m);
+    return hipGetLastError();
+}
+
+// stage 0 = prepare (chunk_prep [+ gate_scan]), stage 1 = scan
 template <int L, int DQ, int NC, int NK, int SB, int MINB>
-hipError_t run(const FwdArgs& a) {
-    Ws w = ws_layout(a.ws, (size_t)a.B * a.NH, a.S, L);
-    hipError_t e = launch_prep<L>(a, w);
-    if (e != hipSuccess) return e;
+hipError_t run1(const FwdArgs& a, int stage) {
+    Ws w = ws_layout(a.ws, (size_t)a.B * a.NH, a.S, L, a.dqk);
+    if (stage == 0) return launch_prep<L>(a, w, false);
     return launch_scan<ScanCfg<L, DQ, NC, NK, SB, MINB>>(a, w);
 }
 
-typedef hipError_t (*RunFn)(const FwdArgs&);
+template <int L, int DQ, int NC, int NK, int SB, int MINB>
+hipError_t run2(const FwdArgs& a, int stage) {
+    Ws w = ws_layout(a.ws, (size_t)a.B * a.NH, a.S, L, a.dqk);
+    if (stage == 0) return launch_prep<L>(a, w, true);
+    return launch_scan2<Scan2Cfg<L, DQ, NC, NK, SB, MINB>>(a, w);
+}
 
-// supported (chunk, d_qk) pairs and the tiling used for each
+typedef hipError_t (*RunFn)(const FwdArgs&, int);
+
+// supported (chunk, d_qk) pairs and the tiling used for each:
+// (chunk, d_qk, column blocks, key parts, slab, workgroups per CU)
 RunFn pick(int L, int dqk) {
-#define MLSTM_CASE(L_, DQ_, NC_, NK_, SB_, MINB_) \
-    if (L == L_ && dqk == DQ_) return &run<L_, DQ_, NC_, NK_, SB_, MINB_>;
-    // (chunk, d_qk, column blocks, key parts, slab, workgroups per CU)
-    MLSTM_CASE(32, 128, 4, 1, 128, 1)
-    MLSTM_CASE(32, 384, 3, 2, 64, 1)
-    MLSTM_CASE(64, 128, 4, 1, 128, 1)
-    MLSTM_CASE(64, 256, 4, 2, 64, 1)
-    MLSTM_CASE(64, 384, 3, 4, 32, 1)
-    MLSTM_CASE(64, 512, 4, 2, 64, 1)
-    MLSTM_CASE(64, 1024, 2, 2, 64, 2)
-    MLSTM_CASE(128, 128, 4, 2, 32, 1)
-    MLSTM_CASE(128, 256, 4, 2, 32, 1)
-#undef MLSTM_CASE
+#define MLSTM_V2(L_, DQ_, NC_, NK_, SB_, MINB_) \
+    if (L == L_ && dqk == DQ_) return &run2<L_, DQ_, NC_, NK_, SB_, MINB_>;
+#define MLSTM_V1(L_, DQ_, NC_, NK_, SB_, MINB_) \
+    if (L == L_ && dqk == DQ_) return &run1<L_, DQ_, NC_, NK_, SB_, MINB_>;
+    // one wave per SIMD: the compiler may use the whole register file (arch + acc
+    // VGPRs) and nothing spills, so no scratch reload ever waits on the prefetches
+    MLSTM_V2(32, 128, 4, 1, 128, 1)
+    MLSTM_V2(32, 384, 3, 1, 128, 1)
+    MLSTM_V2(64, 128, 4, 1, 128, 1)
+    MLSTM_V2(64, 256, 4, 1, 128, 1)
+    MLSTM_V2(64, 384, 4, 1, 128, 1)
+    MLSTM_V2(64, 512, 4, 1, 128, 1)
+    MLSTM_V2(64, 1024, 2, 2, 64, 1)
+    MLSTM_V1(128, 128, 4, 2, 32, 1)
+    MLSTM_V1(128, 256, 4, 2, 32, 1)
+#undef MLSTM_V2
+#undef MLSTM_V1
     return nullptr;
 }
 
@@ -559,13 +1123,19 @@ bool mfma_fwd_supported(const FwdArgs& a) {
 }
 
 size_t mfma_fwd_workspace_bytes(const FwdArgs& a) {
-    return ws_bytes((size_t)a.B * a.NH, a.S, a.chunk);
+    return ws_bytes((size_t)a.B * a.NH, a.S, a.chunk, a.dqk);
 }
 
-hipError_t launch_fwd_mfma(const FwdArgs& a) {
+hipError_t launch_fwd_mfma_prepare(const FwdArgs& a) {
     RunFn f = pick(a.chunk, a.dqk);
     if (!f) return hipErrorNotSupported;
-    return f(a);
+    return f(a, 0);
+}
+
+hipError_t launch_fwd_mfma_scan(const FwdArgs& a) {
+    RunFn f = pick(a.chunk, a.dqk);
+    if (!f) return hipErrorNotSupported;
+    return f(a, 1);
 }
 
 }  // namespace mlstm

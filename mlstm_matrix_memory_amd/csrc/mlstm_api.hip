@@ -83,12 +83,12 @@ size_t mlstm_fwd_workspace_bytes(int B, int NH, int S, int d_qk, int d_v, int ch
     return fwd_ws_bytes(make_fwd_args(B, NH, S, d_qk, d_v, chunk, dtype));
 }
 
-mlstm_status mlstm_fwd_parallel(const void* q, const void* k, const void* v,
-                                const float* i_pre, const float* f_pre, const float* o_pre,
-                                int B, int NH, int S, int d_qk, int d_v, int chunk,
-                                mlstm_dtype dtype,
-                                void* h_out, float* C_final, float* n_final, float* m_final,
-                                void* workspace, size_t workspace_bytes, void* stream) {
+// Validates the forward's arguments and fills a; stage bits: 1 = prepare, 2 = scan.
+static mlstm_status fwd_common(const void* q, const void* k, const void* v,
+                               const float* i_pre, const float* f_pre, const float* o_pre,
+                               int B, int NH, int S, int d_qk, int d_v, int chunk, mlstm_dtype dtype,
+                               void* h_out, float* C_final, float* n_final, float* m_final,
+                               void* workspace, size_t workspace_bytes, void* stream, int stages) {
     mlstm_status s = check_fwd_sizes(B, NH, S, d_qk, d_v, chunk, dtype);
     if (s != MLSTM_OK) return s;
     // tensors read or written with vector accesses need 16-byte alignment, the others their element size
@@ -96,6 +96,9 @@ mlstm_status mlstm_fwd_parallel(const void* q, const void* k, const void* v,
     const char* names[] = {"q", "k", "v", "i_pre", "f_pre", "o_pre", "h_out", "C_final", "n_final", "m_final"};
     const unsigned align[] = {16, 16, 16, 4, 4, 16, 16, 16, 16, 4};
     for (int p = 0; p < 10; ++p) {
+        // prepare alone reads only q, k and the two scalar gates
+        const bool needed = (stages & 2) || p == 0 || p == 1 || p == 3 || p == 4;
+        if (!needed) continue;
         if (!ptrs[p]) return fail(MLSTM_ERR_INVALID_ARG, "%s is NULL", names[p]);
         if (!aligned(ptrs[p], align[p]))
             return fail(MLSTM_ERR_INVALID_ARG, "%s is not %u-byte aligned", names[p], align[p]);
@@ -112,10 +115,42 @@ mlstm_status mlstm_fwd_parallel(const void* q, const void* k, const void* v,
     }
     a.ws = workspace; a.ws_bytes = workspace_bytes;
     a.stream = reinterpret_cast<hipStream_t>(stream);
-    hipError_t e = (dtype == MLSTM_BF16 && mlstm::mfma_fwd_supported(a)) ? mlstm::launch_fwd_mfma(a)
-                                                                          : mlstm::launch_fwd_valu(a);
+    const bool two_stage = dtype == MLSTM_BF16 && mlstm::mfma_fwd_supported(a);
+    hipError_t e = hipSuccess;
+    if (two_stage) {
+        if (stages & 1) e = mlstm::launch_fwd_mfma_prepare(a);
+        if (e == hipSuccess && (stages & 2)) e = mlstm::launch_fwd_mfma_scan(a);
+    } else if (stages & 2) {
+        e = mlstm::launch_fwd_valu(a);
+    }
     if (e != hipSuccess) return fail(MLSTM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();
+}
+
+mlstm_status mlstm_fwd_parallel(const void* q, const void* k, const void* v,
+                                const float* i_pre, const float* f_pre, const float* o_pre,
+                                int B, int NH, int S, int d_qk, int d_v, int chunk,
+                                mlstm_dtype dtype,
+                                void* h_out, float* C_final, float* n_final, float* m_final,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    return fwd_common(q, k, v, i_pre, f_pre, o_pre, B, NH, S, d_qk, d_v, chunk, dtype,
+                      h_out, C_final, n_final, m_final, workspace, workspace_bytes, stream, 3);
+}
+
+mlstm_status mlstm_fwd_prepare(const void* q, const void* k, const float* i_pre, const float* f_pre,
+                               int B, int NH, int S, int d_qk, int d_v, int chunk, mlstm_dtype dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    return fwd_common(q, k, nullptr, i_pre, f_pre, nullptr, B, NH, S, d_qk, d_v, chunk, dtype,
+                      nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream, 1);
+}
+
+mlstm_status mlstm_fwd_scan(const void* q, const void* k, const void* v,
+                            const float* i_pre, const float* f_pre, const float* o_pre,
+                            int B, int NH, int S, int d_qk, int d_v, int chunk, mlstm_dtype dtype,
+                            void* h_out, float* C_final, float* n_final, float* m_final,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+    return fwd_common(q, k, v, i_pre, f_pre, o_pre, B, NH, S, d_qk, d_v, chunk, dtype,
+                      h_out, C_final, n_final, m_final, workspace, workspace_bytes, stream, 2);
 }
 
 mlstm_status mlstm_step(const void* q, const void* k, const void* v,

@@ -89,6 +89,7 @@ hipError_t launch_fwd_valu(const FwdArgs& a);
 // chunkwise forward on bf16 MFMA (bf16 inputs, shapes it supports)
 bool mfma_fwd_supported(const FwdArgs& a);
 size_t mfma_fwd_workspace_bytes(const FwdArgs& a);
-hipError_t launch_fwd_mfma(const FwdArgs& a);
+hipError_t launch_fwd_mfma_prepare(const FwdArgs& a);
+hipError_t launch_fwd_mfma_scan(const FwdArgs& a);
 
 }  // namespace mlstm

@@ -21,8 +21,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = b.header_symbols()
-    assert {"mlstm_fwd_parallel", "mlstm_step", "mlstm_fwd_workspace_bytes",
-            "mlstm_status_string", "mlstm_error_detail"} <= set(names)
+    assert {"mlstm_fwd_parallel", "mlstm_fwd_prepare", "mlstm_fwd_scan", "mlstm_step",
+            "mlstm_fwd_workspace_bytes", "mlstm_status_string", "mlstm_error_detail"} <= set(names)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in include/mlstm.h but not exported"
 
@@ -109,8 +109,8 @@ def test_step_rejects_null_state(lib):
 
 def test_binding_has_same_names_as_abi():
     import mlstm_matrix_memory_amd as pkg
-    for name in ("mlstm_fwd_parallel", "mlstm_step", "mlstm_fwd_workspace_bytes",
-                 "mlstm_status_string", "mlstm_error_detail"):
+    for name in ("mlstm_fwd_parallel", "mlstm_fwd_prepare", "mlstm_fwd_scan", "mlstm_step",
+                 "mlstm_fwd_workspace_bytes", "mlstm_status_string", "mlstm_error_detail"):
         assert callable(getattr(pkg, name))
 
 
@@ -129,3 +129,13 @@ def test_product_does_not_use_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not pat.search(text), f"{f} references the oracle"
+
+
+def test_prepare_checks_only_what_it_reads(lib):
+    # v, o_pre and the outputs are not read by the prepare stage, so NULL is fine there,
+    # but q, k and the gates are required
+    st = lib.mlstm_fwd_prepare(FAKE, None, FAKE, FAKE, 1, 1, 64, 32, 32, 16, b.MLSTM_BF16, None, 0, None)
+    assert st == b.MLSTM_ERR_INVALID_ARG and "k is NULL" in b.mlstm_error_detail()
+    st = lib.mlstm_fwd_scan(FAKE, FAKE, None, FAKE, FAKE, FAKE, 1, 1, 64, 32, 32, 16, b.MLSTM_BF16,
+                            FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    assert st == b.MLSTM_ERR_INVALID_ARG and "v is NULL" in b.mlstm_error_detail()
