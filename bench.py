@@ -66,12 +66,12 @@ def source_hash(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, source: str, launches_per_call: int = 1):
-    """HBM bytes per launch from committed counter runs, if taken on this exact source."""
+def measured_traffic(kernel: str, source: str, workload: str):
+    """HBM bytes per launch from committed counter runs, if taken on this exact source and workload."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
     try:
-        rec = json.load(open(TRAFFIC_FILE)).get(kernel)
+        rec = json.load(open(TRAFFIC_FILE)).get(f"{kernel}:{workload}")
     except (ValueError, OSError):
         return None
     if not rec or rec.get("source_sha") != source_hash(source):
@@ -181,7 +181,7 @@ def main() -> int:
     fwd_gbs = fwd_alg_bytes(w) / (ms_per_step / 1e3) / 1e9
     scan_bytes = scan_alg_bytes(w)
     scan_gbs = scan_bytes / (scan_ms / 1e3) / 1e9
-    traffic = measured_traffic("chunk_scan", SCAN_SOURCE)
+    traffic = measured_traffic("chunk_scan", SCAN_SOURCE, w.name)
 
     out = {
         "metric": METRIC,
@@ -247,7 +247,7 @@ def main() -> int:
             "tokens_per_s": wd.B * T / (dwall), "us_per_step": dev_ms * 1e3 / T,
             "roofline": {"kernel": "step_kernel", "bound": "hbm", "achieved": step_gbs, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": step_gbs / HBM_PEAK_GBS,
-                         "traffic": measured_traffic("step_kernel", STEP_SOURCE),
+                         "traffic": measured_traffic("step_kernel", STEP_SOURCE, wd.name),
                          "alg_bytes_per_launch": step_bytes},
         }
         del C0, n0, m0, Cw, nw, mw, dx
@@ -258,7 +258,7 @@ def main() -> int:
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
-        dst.copy_(src)
+        torch.neg(src, out=dst)   # one elementwise kernel: reads and writes nbytes each
         torch.cuda.synchronize()
         out["copy_calibration_bytes"] = nbytes
 
