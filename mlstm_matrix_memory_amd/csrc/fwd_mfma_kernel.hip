@@ -168,7 +168,24 @@ inline size_t ws_bytes(size_t heads, size_t S, int L, int DQ) {
 // kernel 1: per-chunk gates and intra-chunk decayed scores
 // ---------------------------------------------------------------------------
 constexpr int PREP_THREADS = 256;
+constexpr int PREP_SB = 64;                 // key columns per staged slab of Q and K
+constexpr int PREP_KP = PREP_SB + 8;        // LDS row pitch (bf16): 36 dwords, b128 operand reads conflict free
 
+template <int L>
+struct alignas(16) PrepSmem {
+    alignas(16) bf16 q[L * PREP_KP];
+    alignas(16) bf16 k[L * PREP_KP];
+    double sb[L], sml[L];
+    float si[L], swl[L];
+    float red[4][PREP_SB];
+    double wsum[2], wmax[2];  // per-wave totals of the two scans (separate: no reuse race)
+};
+
+// Q and K of the chunk are staged through LDS one slab of key columns at a time
+// (each element is read from HBM once); the next slab is already in flight in
+// registers while the current one is multiplied.  Wave w owns the 16-row blocks
+// tb = w, w + 4, ... of the score matrix with all their causal column blocks, so
+// every row sum is formed inside one wave in a fixed order.
 template <int L>
 __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k,
@@ -176,16 +193,32 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     int S, int dqk, Ws ws)
 {
     constexpr int LB = L / 16;
-    constexpr int PPITCH = L + 8;
-    __shared__ double sb[L], sml[L];
-    __shared__ float si[L], swl[L];
-    __shared__ double wsum[2], wmax[2];  // per-wave totals of the two scans (separate: no reuse race)
-    __shared__ __attribute__((aligned(16))) bf16 sP[2][L * PPITCH];   // hi, lo
+    constexpr int NW = PREP_THREADS / 64;
+    constexpr int TBW = (LB + NW - 1) / NW;          // row blocks per wave
+    constexpr int UNITS = L * PREP_SB / 8;           // 16-byte units of one slab of Q (or K)
+    constexpr int UPT = (2 * UNITS + PREP_THREADS - 1) / PREP_THREADS;
+    __shared__ PrepSmem<L> sm;
 
     const int c = blockIdx.x, bh = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, lg = lane >> 4;
     const size_t tok0 = (size_t)bh * S + (size_t)c * L;
+    const bf16* qh = q + tok0 * dqk;
+    const bf16* kh = k + tok0 * dqk;
+
+    auto slab_load = [&](f32x4 (&reg)[UPT], int j0) {
+#pragma unroll
+        for (int u = 0; u < UPT; ++u) {
+            const int idx = tid + u * PREP_THREADS;
+            if (idx < 2 * UNITS) {
+                const int which = idx / UNITS, rem = idx % UNITS;
+                const int row = rem / (PREP_SB / 8), c8 = 8 * (rem % (PREP_SB / 8));
+                reg[u] = *reinterpret_cast<const f32x4*>((which ? kh : qh) + (size_t)row * dqk + j0 + c8);
+            }
+        }
+    };
+    f32x4 reg[UPT];
+    slab_load(reg, 0);
 
     // gates: cumulative log forget gate and chunk-local stabilizer, by wave scans (fp64)
     double lf = 0.0, ii = 0.0;
@@ -196,88 +229,113 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     double bcum = 0.0;
     if (wave < 2) {
         bcum = wave_scan_add(lf, lane);
-        if (lane == 63) wsum[wave] = bcum;
+        if (lane == 63) sm.wsum[wave] = bcum;
     }
     __syncthreads();
-    if (wave == 1) bcum += wsum[0];
+    if (wave == 1) bcum += sm.wsum[0];
     double umax = 0.0;
     if (wave < 2) {
         umax = wave_scan_max(tid < L ? ii - bcum : -INFINITY, lane);
-        if (lane == 63) wmax[wave] = umax;
+        if (lane == 63) sm.wmax[wave] = umax;
     }
     __syncthreads();
-    if (wave == 1) umax = fmax(umax, wmax[0]);
+    if (wave == 1) umax = fmax(umax, sm.wmax[0]);
     if (tid < L) {
-        sb[tid] = bcum;
-        si[tid] = (float)ii;
-        sml[tid] = bcum + umax;
+        sm.sb[tid] = bcum;
+        sm.si[tid] = (float)ii;
+        sm.sml[tid] = bcum + umax;
     }
     __syncthreads();
     if (tid < L) {
-        const double bL = sb[L - 1], mL = sml[L - 1];
-        ws.b[tok0 + tid] = sb[tid];
-        ws.mloc[tok0 + tid] = sml[tid];
-        const float wl = exp_arg(bL - sb[tid] + (double)si[tid] - mL);
+        const double bL = sm.sb[L - 1], mL = sm.sml[L - 1];
+        ws.b[tok0 + tid] = sm.sb[tid];
+        ws.mloc[tok0 + tid] = sm.sml[tid];
+        const float wl = exp_arg(bL - sm.sb[tid] + (double)sm.si[tid] - mL);
         ws.wloc[tok0 + tid] = wl;
-        swl[tid] = wl;
+        sm.swl[tid] = wl;
     }
 
-    // decayed scores, one 16-row block per wave pass
-    const bf16* qh = q + tok0 * dqk;
-    const bf16* kh = k + tok0 * dqk;
-    for (int tb = wave; tb < LB; tb += PREP_THREADS / 64) {
-        const int rows_tb = tb;
-        f32x4 den4 = {0, 0, 0, 0};
-        for (int sbk = 0; sbk < LB; ++sbk) {
-            f32x4 acc = {0, 0, 0, 0};
-            if (sbk <= rows_tb) {
-                const bf16* qa = qh + (size_t)(16 * rows_tb + ln) * dqk + 8 * lg;
-                const bf16* kb = kh + (size_t)(16 * sbk + ln) * dqk + 8 * lg;
-                for (int kk = 0; kk < dqk; kk += 32) {
-                    bf16x8 a = *reinterpret_cast<const bf16x8*>(qa + kk);
-                    bf16x8 bb = *reinterpret_cast<const bf16x8*>(kb + kk);
-                    acc = mfma(a, bb, acc);
+    f32x4 acc[TBW][LB];
+#pragma unroll
+    for (int r = 0; r < TBW; ++r)
+#pragma unroll
+        for (int sbk = 0; sbk < LB; ++sbk) acc[r][sbk] = f32x4{0, 0, 0, 0};
+    float* dn = ws.dn + ((size_t)bh * (S / L) + c) * dqk;
+
+    for (int j0 = 0; j0 < dqk; j0 += PREP_SB) {
+        __syncthreads();   // previous slab fully consumed
+#pragma unroll
+        for (int u = 0; u < UPT; ++u) {
+            const int idx = tid + u * PREP_THREADS;
+            if (idx < 2 * UNITS) {
+                const int which = idx / UNITS, rem = idx % UNITS;
+                const int row = rem / (PREP_SB / 8), c8 = 8 * (rem % (PREP_SB / 8));
+                *reinterpret_cast<f32x4*>((which ? sm.k : sm.q) + row * PREP_KP + c8) = reg[u];
+            }
+        }
+        __syncthreads();
+        if (j0 + PREP_SB < dqk) slab_load(reg, j0 + PREP_SB);
+        // raw scores of this wave's causal blocks, contracted over the slab
+#pragma unroll
+        for (int r = 0; r < TBW; ++r) {
+            const int tb = wave + NW * r;
+            if (tb >= LB) continue;
+#pragma unroll
+            for (int kk = 0; kk < PREP_SB / 32; ++kk) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(sm.q + (16 * tb + ln) * PREP_KP + 32 * kk + 8 * lg);
+#pragma unroll
+                for (int sbk = 0; sbk < LB; ++sbk) {
+                    if (sbk > tb) continue;
+                    const bf16x8 bb = *reinterpret_cast<const bf16x8*>(sm.k + (16 * sbk + ln) * PREP_KP + 32 * kk + 8 * lg);
+                    acc[r][sbk] = mfma(a, bb, acc[r][sbk]);
                 }
             }
+        }
+        // chunk contribution to the normalizer, K^T w_loc, for this slab's columns (fp32)
+        {
+            const int col = tid % PREP_SB, part = tid / PREP_SB;
+            constexpr int RP = L / (PREP_THREADS / PREP_SB);
+            float acc_n = 0.0f;
+#pragma unroll 8
+            for (int t = part * RP; t < (part + 1) * RP; ++t) acc_n += sm.swl[t] * (float)sm.k[t * PREP_KP + col];
+            sm.red[part][col] = acc_n;
+        }
+        __syncthreads();
+        if (tid < PREP_SB) {
+            float v = 0.0f;
+#pragma unroll
+            for (int part = 0; part < PREP_THREADS / PREP_SB; ++part) v += sm.red[part][tid];
+            dn[j0 + tid] = v;
+        }
+    }
+
+    // decay, row sums (fp32, before rounding), and P_loc out as bf16 hi then lo
+    bf16* Pout = ws.P + 2 * tok0 * L;
+#pragma unroll
+    for (int r = 0; r < TBW; ++r) {
+        const int tb = wave + NW * r;
+        if (tb >= LB) continue;
+        f32x4 den4 = {0, 0, 0, 0};
+#pragma unroll
+        for (int sbk = 0; sbk < LB; ++sbk) {
             const int s = 16 * sbk + ln;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int tau = 16 * rows_tb + 4 * lg + i;
+                const int tau = 16 * tb + 4 * lg + i;
                 float p = 0.0f;
-                if (s <= tau) p = acc[i] * exp_arg(sb[tau] - sb[s] + (double)si[s] - sml[tau]);
+                if (sbk <= tb && s <= tau)
+                    p = acc[r][sbk][i] * exp_arg(sm.sb[tau] - sm.sb[s] + (double)sm.si[s] - sm.sml[tau]);
                 den4[i] += p;
                 const bf16 hi = (bf16)p;
-                sP[0][tau * PPITCH + s] = hi;
-                sP[1][tau * PPITCH + s] = (bf16)(p - (float)hi);
+                Pout[(size_t)tau * L + s] = hi;
+                Pout[(size_t)L * L + (size_t)tau * L + s] = (bf16)(p - (float)hi);
             }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            float d = den4[i];
-            d += __shfl_xor(d, 1, 64);
-            d += __shfl_xor(d, 2, 64);
-            d += __shfl_xor(d, 4, 64);
-            d += __shfl_xor(d, 8, 64);
-            if (ln == 0) ws.den[tok0 + 16 * rows_tb + 4 * lg + i] = d;
+            const float d = row16_sum(den4[i]);
+            if (ln == 0) ws.den[tok0 + 16 * tb + 4 * lg + i] = d;
         }
-    }
-    __syncthreads();
-    // rows of P_loc (hi block, then lo block) out, 16 bytes per lane
-    bf16* Pout = ws.P + 2 * tok0 * L;
-    for (int idx = tid; idx < 2 * L * L / 8; idx += PREP_THREADS) {
-        const int half = idx / (L * L / 8), rem = idx % (L * L / 8);
-        const int row = rem / (L / 8), col = 8 * (rem % (L / 8));
-        const bf16* src = sP[half] + row * PPITCH + col;
-        bf16x8 v = bf16x8{src[0], src[1], src[2], src[3], src[4], src[5], src[6], src[7]};
-        *reinterpret_cast<bf16x8*>(Pout + (size_t)half * L * L + (size_t)row * L + col) = v;
-    }
-    // chunk contribution to the normalizer: K^T w_loc (fp32; k exact bf16)
-    float* dn = ws.dn + ((size_t)bh * (S / L) + c) * dqk;
-    for (int j = tid; j < dqk; j += PREP_THREADS) {
-        float acc = 0.0f;
-#pragma unroll 8
-        for (int t = 0; t < L; ++t) acc += swl[t] * (float)kh[(size_t)t * dqk + j];
-        dn[j] = acc;
     }
 }
 
@@ -292,7 +350,12 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
 constexpr int GS_THREADS = 256;
 constexpr int GS_TILE = 512;     // chunks per pass over LDS
 constexpr int GS_NJ = 4096 / GS_THREADS;
+constexpr int GS_BATCH = 8;      // loads issued together before their results are used
 
+// The stabilizer recurrence m <- max(b_L + m, m_loc_L) is a max-plus affine map
+// m -> max(A + m, B); maps compose as (A1, B1) then (A2, B2) = (A1 + A2, max(B1 + A2, B2)),
+// so one wave scans a tile of chunks in parallel (each lane first composes a run
+// of consecutive chunks, then the lanes combine by an inclusive shuffle scan).
 template <int L>
 __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int dqk,
                                                                const float* __restrict__ n0,
@@ -300,7 +363,7 @@ __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int
 {
     __shared__ double sbl[GS_TILE], sml[GS_TILE], smp[GS_TILE + 1];
     __shared__ float salpha[GS_TILE], srl[GS_TILE];
-    const int bh = blockIdx.x, tid = threadIdx.x;
+    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
     const int nC = S / L;
     const size_t tokh = (size_t)bh * S;
     double m_run = m0 ? (double)m0[bh] : 0.0;
@@ -318,42 +381,86 @@ __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int
             sml[i] = ws.mloc[t];
         }
         __syncthreads();
-        if (tid == 0) {
-            double mp = m_run;
-            for (int i = 0; i < nt; ++i) {
+        if (tid < 64) {
+            const int run = (nt + 63) / 64;
+            const int i0 = min(nt, lane * run), i1 = min(nt, i0 + run);
+            double A = 0.0, B = -INFINITY;            // identity map
+            for (int i = i0; i < i1; ++i) {
+                A += sbl[i];
+                B = fmax(B + sbl[i], sml[i]);
+            }
+            // inclusive scan of the lanes' maps, then shift to an exclusive one
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const double Ap = __shfl_up(A, off, 64), Bp = __shfl_up(B, off, 64);
+                if (lane >= off) {
+                    B = fmax(Bp + A, B);
+                    A = Ap + A;
+                }
+            }
+            double Ae = __shfl_up(A, 1, 64), Be = __shfl_up(B, 1, 64);
+            if (lane == 0) { Ae = 0.0; Be = -INFINITY; }
+            double mp = fmax(Ae + m_run, Be);
+            for (int i = i0; i < i1; ++i) {
                 smp[i] = mp;
                 const double mL = fmax(sbl[i] + mp, sml[i]);
                 salpha[i] = exp_arg(sbl[i] + mp - mL);
                 srl[i] = exp_arg(sml[i] - mL);
                 mp = mL;
             }
-            smp[nt] = mp;
+            if (lane == 63) smp[nt] = fmax(A + m_run, B);
         }
         __syncthreads();
         m_run = smp[nt];
-        for (int t = tid; t < nt * L; t += GS_THREADS) {
-            const int ci = t / L;
-            const size_t g = tokh + (size_t)c0 * L + t;
-            const double mp = smp[ci];
-            const double bt = ws.b[g], ml = ws.mloc[g];
-            const double mt = fmax(bt + mp, ml);
-            ws.a[g] = exp_arg(bt + mp - mt);
-            ws.r[g] = exp_arg(ml - mt);
-            ws.fl[g] = exp_arg(-mt);
-            ws.w[g] = srl[ci] * ws.wloc[g];
-            ws.alt[g] = salpha[ci];
+        // per-token weights
+        for (int tb0 = 0; tb0 < nt * L; tb0 += GS_THREADS * GS_BATCH) {
+            double bt[GS_BATCH], ml[GS_BATCH];
+            float wl[GS_BATCH];
+#pragma unroll
+            for (int u = 0; u < GS_BATCH; ++u) {
+                const int t = tb0 + tid + GS_THREADS * u;
+                if (t < nt * L) {
+                    const size_t g = tokh + (size_t)c0 * L + t;
+                    bt[u] = ws.b[g];
+                    ml[u] = ws.mloc[g];
+                    wl[u] = ws.wloc[g];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < GS_BATCH; ++u) {
+                const int t = tb0 + tid + GS_THREADS * u;
+                if (t < nt * L) {
+                    const int ci = t / L;
+                    const size_t g = tokh + (size_t)c0 * L + t;
+                    const double mp = smp[ci];
+                    const double mt = fmax(bt[u] + mp, ml[u]);
+                    ws.a[g] = exp_arg(bt[u] + mp - mt);
+                    ws.r[g] = exp_arg(ml[u] - mt);
+                    ws.fl[g] = exp_arg(-mt);
+                    ws.w[g] = srl[ci] * wl[u];
+                    ws.alt[g] = salpha[ci];
+                }
+            }
         }
         for (int i = tid; i < nt; i += GS_THREADS) ws.alpha[(size_t)bh * nC + c0 + i] = salpha[i];
+        // normalizer entering each chunk: n' <- alpha n' + rl K^T w_loc, one column per thread
 #pragma unroll
         for (int u = 0; u < GS_NJ; ++u) {
             const int j = tid + GS_THREADS * u;
             if (j < dqk) {
                 float nv = nreg[u];
-#pragma unroll 8
-                for (int i = 0; i < nt; ++i) {
-                    const size_t cc = (size_t)bh * nC + c0 + i;
-                    ws.nent[cc * dqk + j] = nv;
-                    nv = salpha[i] * nv + srl[i] * ws.dn[cc * dqk + j];
+                for (int i0 = 0; i0 < nt; i0 += 2 * GS_BATCH) {
+                    float d[2 * GS_BATCH];
+#pragma unroll
+                    for (int e = 0; e < 2 * GS_BATCH; ++e)
+                        if (i0 + e < nt) d[e] = ws.dn[((size_t)bh * nC + c0 + i0 + e) * dqk + j];
+#pragma unroll
+                    for (int e = 0; e < 2 * GS_BATCH; ++e) {
+                        if (i0 + e < nt) {
+                            ws.nent[((size_t)bh * nC + c0 + i0 + e) * dqk + j] = nv;
+                            nv = salpha[i0 + e] * nv + srl[i0 + e] * d[e];
+                        }
+                    }
                 }
                 nreg[u] = nv;
             }
@@ -1100,15 +1207,19 @@ RunFn pick(int L, int dqk) {
     if (L == L_ && dqk == DQ_) return &run2<L_, DQ_, NC_, NK_, SB_, MINB_>;
 #define MLSTM_V1(L_, DQ_, NC_, NK_, SB_, MINB_) \
     if (L == L_ && dqk == DQ_) return &run1<L_, DQ_, NC_, NK_, SB_, MINB_>;
-    // one wave per SIMD: the compiler may use the whole register file (arch + acc
-    // VGPRs) and nothing spills, so no scratch reload ever waits on the prefetches
+    // Four waves per workgroup (one per SIMD) let the compiler use the whole
+    // register file and nothing spills, so no scratch reload waits on the
+    // prefetches.  Eight waves (two per SIMD, key dimension split in two or four
+    // parts) hide more LDS latency behind the other wave's MFMAs; where they fit
+    // the register budget they measured faster (d_qk 384: 204 vs 254 us,
+    // d_qk 1024: 597 vs 677 us on the 125M- and 1.3B-class layer shapes).
     MLSTM_V2(32, 128, 4, 1, 128, 1)
     MLSTM_V2(32, 384, 3, 1, 128, 1)
     MLSTM_V2(64, 128, 4, 1, 128, 1)
     MLSTM_V2(64, 256, 4, 1, 128, 1)
-    MLSTM_V2(64, 384, 4, 1, 128, 1)
+    MLSTM_V2(64, 384, 4, 2, 64, 1)
     MLSTM_V2(64, 512, 4, 1, 128, 1)
-    MLSTM_V2(64, 1024, 2, 2, 64, 1)
+    MLSTM_V2(64, 1024, 2, 4, 32, 1)
     MLSTM_V1(128, 128, 4, 2, 32, 1)
     MLSTM_V1(128, 256, 4, 2, 32, 1)
 #undef MLSTM_V2
