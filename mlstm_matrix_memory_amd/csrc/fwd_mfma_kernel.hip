@@ -808,17 +808,18 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan_kernel(
 // output-gate pre-activations and weights are in flight.  Q/K slabs are double
 // buffered in LDS, so a slab costs one barrier; a chunk adds two (partial sums of
 // Q C'^T over the key parts, and release of the chunk-level tiles).
-template <int L_, int DQ_, int NC_, int NK_, int SB_, int MINB_>
+template <int L_, int DQ_, int NC_, int NK_, int SB_, int MINB_, int CW_>
 struct Scan2Cfg {
     static constexpr int L = L_, DQ = DQ_, NC = NC_, NK = NK_, SB = SB_, MINB = MINB_;
-    static constexpr int W = NC * NK, THREADS = 64 * W, TV = 16 * NC;
+    static constexpr int CW = CW_;         // 16-column blocks per wave
+    static constexpr int W = NC * NK, THREADS = 64 * W, TV = 16 * NC * CW;
     static constexpr int DP = DQ / NK, NS = DP / SB, SW = NK * SB;
     static constexpr int QP = SW + 4;      // Q pitch: row stride = 2 (mod 32) dwords
     static constexpr int KP = SW + 16;     // K pitch: row stride = 8 (mod 32) dwords
     static constexpr int VP = ((TV + 63) / 64) * 64 + 16;
     static constexpr int PP = L + 8, OP = TV + 4;
     static constexpr int LB = L / 16, SBB = SB / 16, NSB = DP / 16;
-    static constexpr int RED = LB * (NK - 1) * NC * 256;   // floats
+    static constexpr int RED = LB * (NK - 1) * NC * CW * 256;   // floats
     // staged 16-byte units
     static constexpr int U_Q = L * SW / 8, U_SLAB = 2 * U_Q;
     static constexpr int U_V = L * TV / 8, U_P = 2 * L * L / 8, U_O = L * TV / 4;
@@ -839,7 +840,12 @@ struct alignas(16) Scan2Smem {
     alignas(16) bf16 p[2][C::L * C::PP];
     alignas(16) float o[C::L * C::OP];
     alignas(16) float sc[6][C::L];       // a, r, fl, w, den (full normalizer), alpha (per chunk, repeated)
-    alignas(16) float red[C::RED > 0 ? C::RED : 4];
+    // The partial retrievals of the key parts are exchanged through the K slab
+    // buffer the chunk's last slab did not use when they fit there: every wave is
+    // past the barrier of that slab, and the next chunk's first slab is stored
+    // after the barrier that ends the chunk.  Otherwise they get their own array.
+    static constexpr bool RED_IN_K = C::RED * sizeof(float) <= C::L * C::KP * sizeof(bf16);
+    alignas(16) float red[RED_IN_K ? 4 : C::RED];
 };
 
 typedef __attribute__((ext_vector_type(2))) float f32x2;
@@ -955,7 +961,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
     const float* __restrict__ C0,
     bf16* __restrict__ h, float* __restrict__ Cout, float* __restrict__ nout, float* __restrict__ mout)
 {
-    constexpr int L = C::L, DQ = C::DQ, NC = C::NC, NK = C::NK, SB = C::SB;
+    constexpr int L = C::L, DQ = C::DQ, NC = C::NC, NK = C::NK, SB = C::SB, CW = C::CW;
     constexpr int THREADS = C::THREADS, TV = C::TV, DP = C::DP, NS = C::NS;
     constexpr int QP = C::QP, KP = C::KP, VP = C::VP, PP = C::PP, OP = C::OP;
     constexpr int LB = C::LB, SBB = C::SBB, NSB = C::NSB;
@@ -975,8 +981,13 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cb = wave % NC, kq = wave / NC;
     const int ln = lane & 15, lg = lane >> 4;
-    const int vcol = vt * TV + 16 * cb;
-    const bool active = vcol < dv;
+    // this wave's CW column blocks: tile columns 16 * (CW * cb + x), x < CW
+    const int tcol = 16 * CW * cb;
+    const int vcol = vt * TV + tcol;
+    bool act[CW];
+#pragma unroll
+    for (int x = 0; x < CW; ++x) act[x] = vcol + 16 * x < dv;
+    const bool active = act[0];
     const int nC = S / L;
 
     const size_t tokh = (size_t)bh * S;
@@ -996,15 +1007,17 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
         return cs;
     };
 
-    // state: block jb holds key rows j = kq*DP + 16*jb + 4*lg + i, value column vcol + ln
-    f32x4 st[NSB];
+    // state: st[x][jb] holds key rows j = kq*DP + 16*jb + 4*lg + i, value column vcol + 16x + ln
+    f32x4 st[CW][NSB];
 #pragma unroll
-    for (int jb = 0; jb < NSB; ++jb) {
-        st[jb] = f32x4{0, 0, 0, 0};
-        if (C0 && active)
-            st[jb] = *reinterpret_cast<const f32x4*>(
-                C0 + ((size_t)bh * dv + vcol + ln) * DQ + kq * DP + 16 * jb + 4 * lg);
-    }
+    for (int x = 0; x < CW; ++x)
+#pragma unroll
+        for (int jb = 0; jb < NSB; ++jb) {
+            st[x][jb] = f32x4{0, 0, 0, 0};
+            if (C0 && act[x])
+                st[x][jb] = *reinterpret_cast<const f32x4*>(
+                    C0 + ((size_t)bh * dv + vcol + 16 * x + ln) * DQ + kq * DP + 16 * jb + 4 * lg);
+        }
 
     f32x4 rs[Pref<C>::NSL], rc[Pref<C>::NCH];
     chunk_load<C>(rc, tid, chunk_src(0), dv);
@@ -1014,10 +1027,12 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
     for (int c = 0; c < nC; ++c) {
         const size_t t0 = (size_t)c * L;
         chunk_store<C>(rc, sm, tid);
-        f32x4 acc_inter[LB];
+        f32x4 acc_inter[LB][CW];
 #pragma unroll
-        for (int tb = 0; tb < LB; ++tb) acc_inter[tb] = f32x4{0, 0, 0, 0};
-        bf16x8 vwh[L / 32], vwl[L / 32];
+        for (int tb = 0; tb < LB; ++tb)
+#pragma unroll
+            for (int x = 0; x < CW; ++x) acc_inter[tb][x] = f32x4{0, 0, 0, 0};
+        bf16x8 vwh[CW][L / 32], vwl[CW][L / 32];
         float sig_new = 1.0f, st_scale = 1.0f;   // set after the first barrier (alpha is in LDS)
 
 #pragma unroll
@@ -1037,63 +1052,104 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
             }
             if (active) {
                 if (s == 0) {
-                    // (w / sigma') (.) V for this wave's 16 columns, split into bf16 hi + lo
+                    // (w / sigma') (.) V for this wave's columns, split into bf16 hi + lo
                     const float inv_sig = 1.0f / sig_new;
 #pragma unroll
                     for (int kk = 0; kk < L / 32; ++kk) {
-                        const int vrow = (32 * kk + 8 * lg + (ln >> 2)) * VP + 16 * cb + 4 * (ln & 3);
-                        const bf16x8 vb = cat(lds_read_tr(sm.v + vrow), lds_read_tr(sm.v + vrow + 4 * VP));
                         const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sm.sc[3][32 * kk + 8 * lg]) * inv_sig;
                         const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sm.sc[3][32 * kk + 8 * lg + 4]) * inv_sig;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float x = (e < 4 ? w0[e & 3] : w1[e & 3]) * (float)vb[e];
-                            const bf16 hi = (bf16)x;
-                            vwh[kk][e] = hi;
-                            vwl[kk][e] = (bf16)(x - (float)hi);
+                        for (int x = 0; x < CW; ++x) {
+                            const int vrow = (32 * kk + 8 * lg + (ln >> 2)) * VP + tcol + 16 * x + 4 * (ln & 3);
+                            const bf16x8 vb = cat(lds_read_tr(sm.v + vrow), lds_read_tr(sm.v + vrow + 4 * VP));
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const float xv = (e < 4 ? w0[e & 3] : w1[e & 3]) * (float)vb[e];
+                                const bf16 hi = (bf16)xv;
+                                vwh[x][kk][e] = hi;
+                                vwl[x][kk][e] = (bf16)(xv - (float)hi);
+                            }
                         }
                     }
                 }
-                // inter-chunk retrieval: acc_inter += Q[:, slab] (C'_hi + C'_lo)^T[slab, cols]
+                __builtin_amdgcn_sched_barrier(0);
+                // The slab's operands are read from LDS before the products that use
+                // them, and the K operands of the update stream in while the
+                // retrieval multiplies, so the matrix pipe does not wait on LDS
+                // latency operand by operand.
+                constexpr int KQ = SB / 32, KU = L / 32;
+                bf16x8 qa[KQ][LB], ka[KU][SBB];
 #pragma unroll
-                for (int kk = 0; kk < SB / 32; ++kk) {
-                    bf16x8 bhi, blo;
-                    split8(st[s * SBB + 2 * kk], st[s * SBB + 2 * kk + 1], bhi, blo);
+                for (int kk = 0; kk < KQ; ++kk)
 #pragma unroll
                     for (int tb = 0; tb < LB; ++tb) {
-                        const bf16* qa = sm.q[buf] + (16 * tb + ln) * QP + kq * SB + 32 * kk + 4 * lg;
-                        const bf16x8 aop = cat(*reinterpret_cast<const bf16x4*>(qa),
-                                               *reinterpret_cast<const bf16x4*>(qa + 16));
-                        acc_inter[tb] = mfma(aop, bhi, acc_inter[tb]);
-                        acc_inter[tb] = mfma(aop, blo, acc_inter[tb]);
+                        const bf16* qp = sm.q[buf] + (16 * tb + ln) * QP + kq * SB + 32 * kk + 4 * lg;
+                        qa[kk][tb] = cat(*reinterpret_cast<const bf16x4*>(qp), *reinterpret_cast<const bf16x4*>(qp + 16));
                     }
-                }
-                // state update: C^[slab] += K[:, slab]^T ((w / sigma') V)_{hi+lo}
-                if (st_scale != 1.0f) {
 #pragma unroll
-                    for (int jb = 0; jb < SBB; ++jb) st[s * SBB + jb] *= st_scale;
-                }
-#pragma unroll
-                for (int kk = 0; kk < L / 32; ++kk) {
+                for (int kk = 0; kk < KU; ++kk)
 #pragma unroll
                     for (int jb = 0; jb < SBB; ++jb) {
-                        const bf16* ka = sm.k[buf] + (32 * kk + 8 * lg + (ln >> 2)) * KP + kq * SB + 16 * jb + 4 * (ln & 3);
-                        const bf16x8 aop = cat(lds_read_tr(ka), lds_read_tr(ka + 4 * KP));
-                        st[s * SBB + jb] = mfma(aop, vwh[kk], st[s * SBB + jb]);
-                        st[s * SBB + jb] = mfma(aop, vwl[kk], st[s * SBB + jb]);
+                        const bf16* kp = sm.k[buf] + (32 * kk + 8 * lg + (ln >> 2)) * KP + kq * SB + 16 * jb + 4 * (ln & 3);
+                        ka[kk][jb] = cat(lds_read_tr(kp), lds_read_tr(kp + 4 * KP));
                     }
+                // inter-chunk retrieval: acc_inter += Q[:, slab] (C^_hi + C^_lo)^T[slab, cols];
+                // each Q operand serves all CW column blocks
+#pragma unroll
+                for (int kk = 0; kk < KQ; ++kk) {
+                    bf16x8 bhi[CW], blo[CW];
+#pragma unroll
+                    for (int x = 0; x < CW; ++x)
+                        split8(st[x][s * SBB + 2 * kk], st[x][s * SBB + 2 * kk + 1], bhi[x], blo[x]);
+#pragma unroll
+                    for (int tb = 0; tb < LB; ++tb)
+#pragma unroll
+                        for (int x = 0; x < CW; ++x) {
+                            acc_inter[tb][x] = mfma(qa[kk][tb], bhi[x], acc_inter[tb][x]);
+                            acc_inter[tb][x] = mfma(qa[kk][tb], blo[x], acc_inter[tb][x]);
+                        }
                 }
+                // state update: C^[slab] += K[:, slab]^T ((w / sigma') V)_{hi+lo}
+#pragma unroll
+                for (int x = 0; x < CW; ++x)
+#pragma unroll
+                    for (int jb = 0; jb < SBB; ++jb) st[x][s * SBB + jb] *= st_scale;
+#pragma unroll
+                for (int kk = 0; kk < KU; ++kk)
+#pragma unroll
+                    for (int jb = 0; jb < SBB; ++jb)
+#pragma unroll
+                        for (int x = 0; x < CW; ++x) {
+                            st[x][s * SBB + jb] = mfma(ka[kk][jb], vwh[x][kk], st[x][s * SBB + jb]);
+                            st[x][s * SBB + jb] = mfma(ka[kk][jb], vwl[x][kk], st[x][s * SBB + jb]);
+                        }
+                // instruction order: all Q reads, then the K reads one by one between
+                // the retrieval products, then the remaining products
+                constexpr int NQR = KQ * LB, NKR = 2 * KU * SBB;
+                constexpr int NMI = 2 * KQ * LB * CW, NMU = 2 * KU * SBB * CW;
+                static_assert(NMI >= NKR, "enough retrieval products to cover the K reads");
+                __builtin_amdgcn_sched_group_barrier(0x100, NQR, 0);
+#pragma unroll
+                for (int i = 0; i < NKR; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, NMI + NMU - NKR, 0);
             }
         }
 
         // --- partial sums over key parts, then the rows each part owns --------
+        float* red = Scan2Smem<C>::RED_IN_K ? reinterpret_cast<float*>(sm.k[1 - ((c * NS + NS - 1) & 1)]) : sm.red;
         if (NK > 1 && active) {
 #pragma unroll
             for (int tb = 0; tb < LB; ++tb) {
                 const int owner = tb % NK;
                 if (owner == kq) continue;
                 const int slot = kq < owner ? kq : kq - 1;
-                *reinterpret_cast<f32x4*>(sm.red + (((tb * (NK - 1) + slot) * NC + cb) * 256 + lane * 4)) = acc_inter[tb];
+#pragma unroll
+                for (int x = 0; x < CW; ++x)
+                    *reinterpret_cast<f32x4*>(red + ((((tb * (NK - 1) + slot) * NC + cb) * CW + x) * 256 + lane * 4)) =
+                        acc_inter[tb][x];
             }
         }
         lds_barrier();
@@ -1101,29 +1157,40 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
 #pragma unroll
             for (int tb = 0; tb < LB; ++tb) {
                 if (tb % NK != kq) continue;
-                f32x4 inter = acc_inter[tb];
+                f32x4 inter[CW], intra[CW];
 #pragma unroll
-                for (int sl = 0; sl < NK - 1; ++sl)
-                    inter += *reinterpret_cast<const f32x4*>(sm.red + (((tb * (NK - 1) + sl) * NC + cb) * 256 + lane * 4));
-                f32x4 intra = {0, 0, 0, 0};
+                for (int x = 0; x < CW; ++x) {
+                    inter[x] = acc_inter[tb][x];
+#pragma unroll
+                    for (int sl = 0; sl < NK - 1; ++sl)
+                        inter[x] += *reinterpret_cast<const f32x4*>(
+                            red + ((((tb * (NK - 1) + sl) * NC + cb) * CW + x) * 256 + lane * 4));
+                    intra[x] = f32x4{0, 0, 0, 0};
+                }
 #pragma unroll
                 for (int kk = 0; kk <= (16 * tb + 15) / 32; ++kk) {
                     const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(sm.p[0] + (16 * tb + ln) * PP + 32 * kk + 8 * lg);
                     const bf16x8 alo = *reinterpret_cast<const bf16x8*>(sm.p[1] + (16 * tb + ln) * PP + 32 * kk + 8 * lg);
-                    const bf16* vb = sm.v + (32 * kk + 8 * lg + (ln >> 2)) * VP + 16 * cb + 4 * (ln & 3);
-                    const bf16x8 bop = cat(lds_read_tr(vb), lds_read_tr(vb + 4 * VP));
-                    intra = mfma(ahi, bop, intra);
-                    intra = mfma(alo, bop, intra);
+#pragma unroll
+                    for (int x = 0; x < CW; ++x) {
+                        const bf16* vb = sm.v + (32 * kk + 8 * lg + (ln >> 2)) * VP + tcol + 16 * x + 4 * (ln & 3);
+                        const bf16x8 bop = cat(lds_read_tr(vb), lds_read_tr(vb + 4 * VP));
+                        intra[x] = mfma(ahi, bop, intra[x]);
+                        intra[x] = mfma(alo, bop, intra[x]);
+                    }
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tau = 16 * tb + 4 * lg + i;
                     const float aa = sm.sc[0][tau] * sigma, ra = sm.sc[1][tau], fl = sm.sc[2][tau];
-                    const float num = ra * intra[i] + aa * inter[i];
-                    const float den = sm.sc[4][tau];
-                    const float og = __builtin_amdgcn_rcpf(1.0f + __expf(-sm.o[tau * OP + 16 * cb + ln]));
-                    const float hv = og * num * __builtin_amdgcn_rcpf(fmaxf(fabsf(den), fl));
-                    hh[(t0 + tau) * dv + vcol + ln] = (bf16)hv;
+                    const float rden = __builtin_amdgcn_rcpf(fmaxf(fabsf(sm.sc[4][tau]), fl));
+#pragma unroll
+                    for (int x = 0; x < CW; ++x) {
+                        if (!act[x]) continue;
+                        const float num = ra * intra[x][i] + aa * inter[x][i];
+                        const float og = __builtin_amdgcn_rcpf(1.0f + __expf(-sm.o[tau * OP + tcol + 16 * x + ln]));
+                        hh[(t0 + tau) * dv + vcol + 16 * x + ln] = (bf16)(og * num * rden);
+                    }
                 }
             }
         }
@@ -1131,10 +1198,13 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
         lds_barrier();
     }
 
-    if (active) {
+#pragma unroll
+    for (int x = 0; x < CW; ++x) {
+        if (!act[x]) continue;
 #pragma unroll
         for (int jb = 0; jb < NSB; ++jb)
-            *reinterpret_cast<f32x4*>(Cout + ((size_t)bh * dv + vcol + ln) * DQ + kq * DP + 16 * jb + 4 * lg) = st[jb] * sigma;
+            *reinterpret_cast<f32x4*>(Cout + ((size_t)bh * dv + vcol + 16 * x + ln) * DQ + kq * DP + 16 * jb + 4 * lg) =
+                st[x][jb] * sigma;
     }
     if (vt == 0) {
         for (int j = tid; j < DQ; j += THREADS) nout[(size_t)bh * DQ + j] = ws.nfin[(size_t)bh * DQ + j];
@@ -1191,11 +1261,11 @@ hipError_t run1(const FwdArgs& a, int stage) {
     return launch_scan<ScanCfg<L, DQ, NC, NK, SB, MINB>>(a, w);
 }
 
-template <int L, int DQ, int NC, int NK, int SB, int MINB>
+template <int L, int DQ, int NC, int NK, int SB, int MINB, int CW>
 hipError_t run2(const FwdArgs& a, int stage) {
     Ws w = ws_layout(a.ws, (size_t)a.B * a.NH, a.S, L, a.dqk);
     if (stage == 0) return launch_prep<L>(a, w, true);
-    return launch_scan2<Scan2Cfg<L, DQ, NC, NK, SB, MINB>>(a, w);
+    return launch_scan2<Scan2Cfg<L, DQ, NC, NK, SB, MINB, CW>>(a, w);
 }
 
 typedef hipError_t (*RunFn)(const FwdArgs&, int);
@@ -1203,23 +1273,23 @@ typedef hipError_t (*RunFn)(const FwdArgs&, int);
 // supported (chunk, d_qk) pairs and the tiling used for each:
 // (chunk, d_qk, column blocks, key parts, slab, workgroups per CU)
 RunFn pick(int L, int dqk) {
-#define MLSTM_V2(L_, DQ_, NC_, NK_, SB_, MINB_) \
-    if (L == L_ && dqk == DQ_) return &run2<L_, DQ_, NC_, NK_, SB_, MINB_>;
+#define MLSTM_V2(L_, DQ_, NC_, NK_, SB_, MINB_, CW_) \
+    if (L == L_ && dqk == DQ_) return &run2<L_, DQ_, NC_, NK_, SB_, MINB_, CW_>;
 #define MLSTM_V1(L_, DQ_, NC_, NK_, SB_, MINB_) \
     if (L == L_ && dqk == DQ_) return &run1<L_, DQ_, NC_, NK_, SB_, MINB_>;
     // Four waves per workgroup (one per SIMD) let the compiler use the whole
-    // register file and nothing spills, so no scratch reload waits on the
-    // prefetches.  Eight waves (two per SIMD, key dimension split in two or four
-    // parts) hide more LDS latency behind the other wave's MFMAs; where they fit
-    // the register budget they measured faster (d_qk 384: 204 vs 254 us,
-    // d_qk 1024: 597 vs 677 us on the 125M- and 1.3B-class layer shapes).
-    MLSTM_V2(32, 128, 4, 1, 128, 1)
-    MLSTM_V2(32, 384, 3, 1, 128, 1)
-    MLSTM_V2(64, 128, 4, 1, 128, 1)
-    MLSTM_V2(64, 256, 4, 1, 128, 1)
-    MLSTM_V2(64, 384, 4, 2, 64, 1)
-    MLSTM_V2(64, 512, 4, 1, 128, 1)
-    MLSTM_V2(64, 1024, 2, 4, 32, 1)
+    // register file; eight waves (two per SIMD, key dimension split in two or
+    // four parts) hide more latency behind the other wave's MFMAs.  Every entry
+    // is chosen by measurement among the tilings that do not spill, except
+    // d_qk 1024, whose eight-wave tiling spills a little and still measured
+    // fastest (lm 1.3B-class layer shape: 618 us against 660 us for four waves).
+    MLSTM_V2(32, 128, 4, 1, 128, 1, 1)
+    MLSTM_V2(32, 384, 3, 1, 128, 1, 1)
+    MLSTM_V2(64, 128, 4, 1, 128, 1, 1)
+    MLSTM_V2(64, 256, 4, 2, 32, 1, 1)
+    MLSTM_V2(64, 384, 4, 2, 32, 1, 1)
+    MLSTM_V2(64, 512, 4, 2, 32, 1, 1)
+    MLSTM_V2(64, 1024, 2, 4, 32, 1, 1)
     MLSTM_V1(128, 128, 4, 2, 32, 1)
     MLSTM_V1(128, 256, 4, 2, 32, 1)
 #undef MLSTM_V2
