@@ -347,15 +347,18 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
 //   a_t = exp(b_t + m_p - m_t), r_t = exp(m_loc_t - m_t), fl_t = exp(-m_t),
 //   w_t = exp(m_loc_L - m_L) w_loc_t, alpha_c = exp(b_L + m_p - m_L),
 // and the normalizer entering each chunk follows n' <- alpha n' + exp(m_loc_L - m_L) K^T w_loc.
-constexpr int GS_THREADS = 256;
+constexpr int GS_THREADS = 64;   // one wave per workgroup
+constexpr int GS_COLS = 64;      // key columns of the normalizer per workgroup
 constexpr int GS_TILE = 512;     // chunks per pass over LDS
-constexpr int GS_NJ = 4096 / GS_THREADS;
-constexpr int GS_BATCH = 8;      // loads issued together before their results are used
+constexpr int GS_BATCH = 16;     // loads issued together before their results are used
 
 // The stabilizer recurrence m <- max(b_L + m, m_loc_L) is a max-plus affine map
 // m -> max(A + m, B); maps compose as (A1, B1) then (A2, B2) = (A1 + A2, max(B1 + A2, B2)),
-// so one wave scans a tile of chunks in parallel (each lane first composes a run
+// so the wave scans a tile of chunks in parallel (each lane first composes a run
 // of consecutive chunks, then the lanes combine by an inclusive shuffle scan).
+// Grid (key-column groups, heads): every workgroup of a head repeats that short
+// scan, then carries the normalizer for its 64 key columns and writes the
+// per-token weights of its share of the tokens.
 template <int L>
 __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int dqk,
                                                                const float* __restrict__ n0,
@@ -363,25 +366,21 @@ __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int
 {
     __shared__ double sbl[GS_TILE], sml[GS_TILE], smp[GS_TILE + 1];
     __shared__ float salpha[GS_TILE], srl[GS_TILE];
-    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int part = blockIdx.x, nparts = gridDim.x, bh = blockIdx.y, lane = threadIdx.x;
     const int nC = S / L;
     const size_t tokh = (size_t)bh * S;
+    const int j = part * GS_COLS + lane;
     double m_run = m0 ? (double)m0[bh] : 0.0;
-    float nreg[GS_NJ];
-#pragma unroll
-    for (int u = 0; u < GS_NJ; ++u) {
-        const int j = tid + GS_THREADS * u;
-        nreg[u] = (j < dqk && n0) ? n0[(size_t)bh * dqk + j] : 0.0f;
-    }
+    float nv = (j < dqk && n0) ? n0[(size_t)bh * dqk + j] : 0.0f;
     for (int c0 = 0; c0 < nC; c0 += GS_TILE) {
         const int nt = min(GS_TILE, nC - c0);
-        for (int i = tid; i < nt; i += GS_THREADS) {
+        for (int i = lane; i < nt; i += GS_THREADS) {
             const size_t t = tokh + (size_t)(c0 + i) * L + L - 1;
             sbl[i] = ws.b[t];
             sml[i] = ws.mloc[t];
         }
         __syncthreads();
-        if (tid < 64) {
+        {
             const int run = (nt + 63) / 64;
             const int i0 = min(nt, lane * run), i1 = min(nt, i0 + run);
             double A = 0.0, B = -INFINITY;            // identity map
@@ -412,14 +411,16 @@ __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int
         }
         __syncthreads();
         m_run = smp[nt];
-        // per-token weights
-        for (int tb0 = 0; tb0 < nt * L; tb0 += GS_THREADS * GS_BATCH) {
+        // per-token weights of this workgroup's share of the tile's tokens
+        const int ntok = nt * L, per = (ntok + nparts - 1) / nparts;
+        const int tlo = part * per, thi = min(ntok, tlo + per);
+        for (int tb0 = tlo; tb0 < thi; tb0 += GS_THREADS * GS_BATCH) {
             double bt[GS_BATCH], ml[GS_BATCH];
             float wl[GS_BATCH];
 #pragma unroll
             for (int u = 0; u < GS_BATCH; ++u) {
-                const int t = tb0 + tid + GS_THREADS * u;
-                if (t < nt * L) {
+                const int t = tb0 + lane + GS_THREADS * u;
+                if (t < thi) {
                     const size_t g = tokh + (size_t)c0 * L + t;
                     bt[u] = ws.b[g];
                     ml[u] = ws.mloc[g];
@@ -428,8 +429,8 @@ __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int
             }
 #pragma unroll
             for (int u = 0; u < GS_BATCH; ++u) {
-                const int t = tb0 + tid + GS_THREADS * u;
-                if (t < nt * L) {
+                const int t = tb0 + lane + GS_THREADS * u;
+                if (t < thi) {
                     const int ci = t / L;
                     const size_t g = tokh + (size_t)c0 * L + t;
                     const double mp = smp[ci];
@@ -442,37 +443,28 @@ __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int
                 }
             }
         }
-        for (int i = tid; i < nt; i += GS_THREADS) ws.alpha[(size_t)bh * nC + c0 + i] = salpha[i];
-        // normalizer entering each chunk: n' <- alpha n' + rl K^T w_loc, one column per thread
+        if (part == 0)
+            for (int i = lane; i < nt; i += GS_THREADS) ws.alpha[(size_t)bh * nC + c0 + i] = salpha[i];
+        // normalizer entering each chunk: n' <- alpha n' + rl K^T w_loc, one key column per lane
+        if (j < dqk) {
+            for (int i0 = 0; i0 < nt; i0 += GS_BATCH) {
+                float d[GS_BATCH];
 #pragma unroll
-        for (int u = 0; u < GS_NJ; ++u) {
-            const int j = tid + GS_THREADS * u;
-            if (j < dqk) {
-                float nv = nreg[u];
-                for (int i0 = 0; i0 < nt; i0 += 2 * GS_BATCH) {
-                    float d[2 * GS_BATCH];
+                for (int e = 0; e < GS_BATCH; ++e)
+                    if (i0 + e < nt) d[e] = ws.dn[((size_t)bh * nC + c0 + i0 + e) * dqk + j];
 #pragma unroll
-                    for (int e = 0; e < 2 * GS_BATCH; ++e)
-                        if (i0 + e < nt) d[e] = ws.dn[((size_t)bh * nC + c0 + i0 + e) * dqk + j];
-#pragma unroll
-                    for (int e = 0; e < 2 * GS_BATCH; ++e) {
-                        if (i0 + e < nt) {
-                            ws.nent[((size_t)bh * nC + c0 + i0 + e) * dqk + j] = nv;
-                            nv = salpha[i0 + e] * nv + srl[i0 + e] * d[e];
-                        }
+                for (int e = 0; e < GS_BATCH; ++e) {
+                    if (i0 + e < nt) {
+                        ws.nent[((size_t)bh * nC + c0 + i0 + e) * dqk + j] = nv;
+                        nv = salpha[i0 + e] * nv + srl[i0 + e] * d[e];
                     }
                 }
-                nreg[u] = nv;
             }
         }
         __syncthreads();
     }
-#pragma unroll
-    for (int u = 0; u < GS_NJ; ++u) {
-        const int j = tid + GS_THREADS * u;
-        if (j < dqk) ws.nfin[(size_t)bh * dqk + j] = nreg[u];
-    }
-    if (tid == 0) ws.mfin[bh] = (float)m_run;
+    if (j < dqk) ws.nfin[(size_t)bh * dqk + j] = nv;
+    if (part == 0 && lane == 0) ws.mfin[bh] = (float)m_run;
 }
 
 // ---------------------------------------------------------------------------
@@ -1222,7 +1214,7 @@ hipError_t launch_prep(const FwdArgs& a, const Ws& w, bool gates) {
                        (const bf16*)a.q, (const bf16*)a.k, a.i_pre, a.f_pre, a.S, a.dqk, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !gates) return e;
-    hipLaunchKernelGGL((gate_scan_kernel<L>), dim3(a.B * a.NH), dim3(GS_THREADS), 0, a.stream,
+    hipLaunchKernelGGL((gate_scan_kernel<L>), dim3((a.dqk + GS_COLS - 1) / GS_COLS, a.B * a.NH), dim3(GS_THREADS), 0, a.stream,
                        w, a.S, a.dqk, a.n0, a.m0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

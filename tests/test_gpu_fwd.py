@@ -76,6 +76,23 @@ def test_bf16_chunk_sweep(orc, chunk):
     _compare(orc, x, chunk, "bf16")
 
 
+# every (chunk, d_qk) the bf16 MFMA path has a tiling for, each with a d_v that
+# leaves a partial value tile (d_v not a multiple of the tile width)
+MFMA_SHAPES = [(32, 128, 80), (32, 384, 112), (64, 128, 96), (64, 256, 272), (64, 384, 400),
+               (64, 512, 80), (64, 1024, 48), (128, 128, 96), (128, 256, 144)]
+
+
+@pytest.mark.parametrize("chunk,dqk,dv", MFMA_SHAPES, ids=lambda v: str(v))
+def test_bf16_mfma_tilings(orc, chunk, dqk, dv):
+    w = inputs.WORKLOADS["lm_125m"]
+    announce(f"fwd bf16 tiling B=1 NH=2 S=256 dqk={dqk} dv={dv} chunk={chunk}")
+    from mlstm_matrix_memory_amd import MLSTM_BF16, mlstm_fwd_workspace_bytes
+    # a workspace is needed only by the MFMA path: this shape must not fall back to the VALU kernel
+    assert mlstm_fwd_workspace_bytes(1, 2, 256, dqk, dv, chunk, MLSTM_BF16) > 0
+    x = inputs.fwd_inputs(w, seed=300 + dqk + dv, B=1, NH=2, S=256, dqk=dqk, dv=dv)
+    _compare(orc, x, chunk, "bf16")
+
+
 FULL = [
     # (batch indices, head indices) of the sampled heads, shaped [1, n] so the
     # selection keeps the [B, NH] leading axes
