@@ -127,9 +127,10 @@ struct Ws {
     float* nent;    // [heads][chunk][DQ]  normalizer n' entering each chunk
     float* nfin;    // [heads][DQ]  final normalizer
     float* mfin;    // [heads]      final stabilizer
+    float* cst;     // [heads][G][DV][DQ]  state entering each sequence segment (slot 0 unused)
 };
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline size_t ws_walk(void* base, size_t heads, size_t S, int L, int DQ, Ws* out) {
+inline size_t ws_walk(void* base, size_t heads, size_t S, int L, int DQ, int DV, int G, Ws* out) {
     const size_t nC = S / L;
     char* p = (char*)base;
     size_t off = 0;
@@ -152,16 +153,17 @@ inline size_t ws_walk(void* base, size_t heads, size_t S, int L, int DQ, Ws* out
     w.nent = (float*)take(heads * nC * DQ * sizeof(float));
     w.nfin = (float*)take(heads * DQ * sizeof(float));
     w.mfin = (float*)take(heads * sizeof(float));
+    w.cst = G > 1 ? (float*)take(heads * G * (size_t)DV * DQ * sizeof(float)) : nullptr;
     if (out) *out = w;
     return off;
 }
-inline Ws ws_layout(void* base, size_t heads, size_t S, int L, int DQ) {
+inline Ws ws_layout(void* base, size_t heads, size_t S, int L, int DQ, int DV, int G) {
     Ws w;
-    ws_walk(base, heads, S, L, DQ, &w);
+    ws_walk(base, heads, S, L, DQ, DV, G, &w);
     return w;
 }
-inline size_t ws_bytes(size_t heads, size_t S, int L, int DQ) {
-    return ws_walk(nullptr, heads, S, L, DQ, nullptr);
+inline size_t ws_bytes(size_t heads, size_t S, int L, int DQ, int DV, int G) {
+    return ws_walk(nullptr, heads, S, L, DQ, DV, G, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -505,288 +507,146 @@ __global__ __launch_bounds__(DEN_THREADS) void den_kernel(const bf16* __restrict
 }
 
 // ---------------------------------------------------------------------------
-// kernel 2: sequential scan over chunks, state in accumulators
+// kernels 2a/2b: sequence segments (few heads, long sequences)
 // ---------------------------------------------------------------------------
-// NC column blocks of 16 value columns x NK key parts = NC*NK waves per workgroup.
-template <int L_, int DQ_, int NC_, int NK_, int SB_, int MINB_>
-struct ScanCfg {
-    static constexpr int L = L_, DQ = DQ_, NC = NC_, NK = NK_, SB = SB_;
-    static constexpr int MINB = MINB_;     // workgroups per CU the register budget must allow
-    static constexpr int W = NC * NK, THREADS = 64 * W, TV = 16 * NC;
-    static constexpr int DP = DQ / NK;     // key rows owned by one wave
-    static constexpr int NS = DP / SB;     // slabs per chunk
-    static constexpr int SW = NK * SB;     // staged slab width (key columns)
-    static constexpr int QP = SW + 4;      // Q pitch: row stride = 2 (mod 32) dwords
-    static constexpr int KP = SW + 16;     // K pitch: row stride = 8 (mod 32) dwords
-    static constexpr int VP = ((TV + 63) / 64) * 64 + 16;  // V pitch: 8 (mod 32) dwords
-    static constexpr int LB = L / 16;      // 16-row blocks of a chunk
-    static constexpr int SBB = SB / 16;    // state blocks per slab
-    static constexpr int NSB = DP / 16;    // state blocks per wave
-    static_assert(SW % 64 == 0, "slab width must be a multiple of 64 columns");
-    static_assert(SB % 32 == 0 && DP % SB == 0, "slab must tile the key rows of a wave");
-    static_assert(LB % NK == 0, "row blocks must split evenly over the key parts");
-    static_assert(L % 32 == 0, "chunk must be a multiple of 32 tokens");
-    static_assert(THREADS <= 1024, "workgroup too large");
-};
+// Once gate_scan has put every per-token weight in the carried stabilization,
+// the state after a run of chunks is affine in the state before it:
+//   C'_end = A_g C'_start + dC_g,   A_g = prod_{c in g} alpha_c,
+//   dC_g   = sum_{t in g} omega_t v_t k_t^T,  omega_t = w_t prod_{c in g, c > chunk(t)} alpha_c.
+// seg_state_kernel forms dC_g of every segment but the last as one contraction
+// over the segment's tokens (MFMA with fp32 accumulation; omega V split in bf16
+// hi + lo as in the scan); seg_combine_kernel chains the segments.  The scan then
+// runs every segment in parallel from its own entering state.
+constexpr int SS_THREADS = 256;
+constexpr int SS_TILE = 64;            // key rows and value columns of a workgroup's tile
+constexpr int SS_P = SS_TILE + 16;     // LDS pitch (bf16) of the token-major tiles
 
-template <class C>
-struct alignas(16) ScanSmem {
-    union alignas(16) {
-        struct {
-            alignas(16) bf16 q[C::L * C::QP];
-            alignas(16) bf16 k[C::L * C::KP];
-        } slab;
-        float red[C::L * C::TV];     // Q C'^T summed over the key parts, in D layout
-    } u;
-    alignas(16) bf16 v[C::L * C::VP];     // V tile (for P V)
-    alignas(16) bf16 vwh[C::L * C::VP];   // hi(w (.) V)
-    alignas(16) bf16 vwl[C::L * C::VP];   // lo(w (.) V)
-    float n[C::DQ];
-    double b[C::L], mloc[C::L];          // fp64 gate arithmetic
-    float denloc[C::L], wloc[C::L];
-    float a[C::L], r[C::L], fl[C::L], w[C::L], den[C::L];
-};
+template <int L>
+__global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
+    const bf16* __restrict__ k, const bf16* __restrict__ v, Ws ws, int S, int dqk, int dv, int G)
+{
+    __shared__ __attribute__((aligned(16))) bf16 sk[L * SS_P];
+    __shared__ __attribute__((aligned(16))) bf16 svh[L * SS_P];
+    __shared__ __attribute__((aligned(16))) bf16 svl[L * SS_P];
+    __shared__ float somega[L];
+    constexpr int UNITS = L * SS_TILE / 8;                  // 16-byte units of one tile
+    constexpr int UPT = (UNITS + SS_THREADS - 1) / SS_THREADS;
 
+    const int n_kt = dqk / SS_TILE;
+    const int kt = blockIdx.x % n_kt, vt = blockIdx.x / n_kt;
+    const int g = blockIdx.y, bh = blockIdx.z;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int ln = lane & 15, lg = lane >> 4;
+    const int wr = wave >> 1, wc = wave & 1;                // 32 keys x 32 values per wave
+    const int nC = S / L, nCs = nC / G;
+    const int key0 = kt * SS_TILE, val0 = vt * SS_TILE;
+    const size_t tokh = (size_t)bh * S;
+
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
+
+    float A = 1.0f;          // product of alpha over the segment's chunks after the current one
+    for (int ci = nCs - 1; ci >= 0; --ci) {
+        const int c = g * nCs + ci;
+        const size_t t0 = tokh + (size_t)c * L;
+        __syncthreads();     // previous tiles consumed
+        if (tid < L) somega[tid] = ws.w[t0 + tid] * A;
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < UPT; ++u) {
+            const int idx = tid + u * SS_THREADS;
+            if (idx < UNITS) {
+                const int row = idx / (SS_TILE / 8), c8 = 8 * (idx % (SS_TILE / 8));
+                *reinterpret_cast<bf16x8*>(sk + row * SS_P + c8) =
+                    *reinterpret_cast<const bf16x8*>(k + (t0 + row) * dqk + key0 + c8);
+                bf16x8 xv = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                if (val0 + c8 < dv) xv = *reinterpret_cast<const bf16x8*>(v + (t0 + row) * dv + val0 + c8);
+                const float om = somega[row];
+                bf16x8 xh, xl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = om * (float)xv[e];
+                    xh[e] = (bf16)x;
+                    xl[e] = (bf16)(x - (float)xh[e]);
+                }
+                *reinterpret_cast<bf16x8*>(svh + row * SS_P + c8) = xh;
+                *reinterpret_cast<bf16x8*>(svl + row * SS_P + c8) = xl;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < L / 32; ++kk) {
+            const int trow = 32 * kk + 8 * lg + (ln >> 2);
+            bf16x8 ka[2], vh[2], vl[2];
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                const bf16* kp = sk + trow * SS_P + 32 * wr + 16 * a + 4 * (ln & 3);
+                ka[a] = cat(lds_read_tr(kp), lds_read_tr(kp + 4 * SS_P));
+                const bf16* vp = svh + trow * SS_P + 32 * wc + 16 * a + 4 * (ln & 3);
+                vh[a] = cat(lds_read_tr(vp), lds_read_tr(vp + 4 * SS_P));
+                const bf16* vq = svl + trow * SS_P + 32 * wc + 16 * a + 4 * (ln & 3);
+                vl[a] = cat(lds_read_tr(vq), lds_read_tr(vq + 4 * SS_P));
+            }
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                    acc[a][b] = mfma(ka[a], vh[b], acc[a][b]);
+                    acc[a][b] = mfma(ka[a], vl[b], acc[a][b]);
+                }
+        }
+        A *= ws.alpha[(size_t)bh * nC + c];
+    }
+    // dC_g into slot g + 1: rows of the D layout are keys, columns are values
+    float* dst = ws.cst + ((size_t)bh * G + g + 1) * (size_t)dv * dqk;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int col = val0 + 32 * wc + 16 * b + ln;
+            if (col < dv)
+                *reinterpret_cast<f32x4*>(dst + (size_t)col * dqk + key0 + 32 * wr + 16 * a + 4 * lg) = acc[a][b];
+        }
+}
+
+constexpr int SC_THREADS = 256;
+constexpr int SC_MAXG = 64;
+
+// C'_start(g + 1) = A_g C'_start(g) + dC_g, in place over slots 1 .. G-1; slot 0 is
+// the caller's initial state (or zero).
+__global__ __launch_bounds__(SC_THREADS) void seg_combine_kernel(Ws ws, int nC, int G, int dqk, int dv,
+                                                                 const float* __restrict__ C0)
+{
+    __shared__ float sA[SC_MAXG];
+    const int bh = blockIdx.y, tid = threadIdx.x;
+    const int nCs = nC / G;
+    if (tid < G - 1) {
+        float prod = 1.0f;
+        for (int ci = 0; ci < nCs; ++ci) prod *= ws.alpha[(size_t)bh * nC + tid * nCs + ci];
+        sA[tid] = prod;
+    }
+    __syncthreads();
+    const size_t per = (size_t)dv * dqk;
+    const size_t e = ((size_t)blockIdx.x * SC_THREADS + tid) * 4;
+    if (e >= per) return;
+    f32x4 c = C0 ? *reinterpret_cast<const f32x4*>(C0 + (size_t)bh * per + e) : f32x4{0, 0, 0, 0};
+    float* base = ws.cst + (size_t)bh * G * per + e;
+    for (int g = 0; g + 1 < G; ++g) {
+        f32x4* slot = reinterpret_cast<f32x4*>(base + (size_t)(g + 1) * per);
+        c = sA[g] * c + *slot;
+        *slot = c;
+    }
+}
+
+// bf16 hi + lo split of two f32x4 state blocks into one B operand (8 key rows)
 __device__ __forceinline__ void split8(f32x4 x0, f32x4 x1, bf16x8& hi, bf16x8& lo) {
     hi = cvt8(x0, x1);
     f32x4 r0 = x0 - f32x4{(float)hi[0], (float)hi[1], (float)hi[2], (float)hi[3]};
     f32x4 r1 = x1 - f32x4{(float)hi[4], (float)hi[5], (float)hi[6], (float)hi[7]};
     lo = cvt8(r0, r1);
-}
-
-template <class C>
-__global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ o_pre, Ws ws, int S, int dv, int n_vt, int remap,
-    const float* __restrict__ C0, const float* __restrict__ n0, const float* __restrict__ m0,
-    bf16* __restrict__ h, float* __restrict__ Cout, float* __restrict__ nout, float* __restrict__ mout)
-{
-    constexpr int L = C::L, DQ = C::DQ, NC = C::NC, NK = C::NK, SB = C::SB;
-    constexpr int THREADS = C::THREADS, TV = C::TV, DP = C::DP, NS = C::NS, SW = C::SW;
-    constexpr int QP = C::QP, KP = C::KP, VP = C::VP, LB = C::LB, SBB = C::SBB, NSB = C::NSB;
-    __shared__ ScanSmem<C> sm;
-
-    // workgroup -> (head, value tile); consecutive slots share an XCD when remapped
-    int wg = blockIdx.x;
-    if (remap) {
-        const int G = gridDim.x;
-        wg = (wg % 8) * (G / 8) + wg / 8;
-    }
-    const int bh = wg / n_vt, vt = wg % n_vt;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int cb = wave % NC, kq = wave / NC;
-    const int ln = lane & 15, lg = lane >> 4;
-    const int vcol = vt * TV + 16 * cb;          // first value column of this wave
-    const bool active = vcol < dv;
-    const int vtile_cols = min(TV, dv - vt * TV); // valid columns of the tile
-
-    const size_t tokh = (size_t)bh * S;
-    const bf16* qh = q + tokh * DQ;
-    const bf16* kh = k + tokh * DQ;
-    const bf16* vh = v + tokh * dv;
-    const float* oh = o_pre + tokh * dv;
-    bf16* hh = h + tokh * dv;
-
-    // state: block jb holds key rows j = kq*DP + 16*jb + 4*lg + i, value column vcol + ln
-    f32x4 st[NSB];
-#pragma unroll
-    for (int jb = 0; jb < NSB; ++jb) {
-        st[jb] = f32x4{0, 0, 0, 0};
-        if (C0 && active)
-            st[jb] = *reinterpret_cast<const f32x4*>(
-                C0 + ((size_t)bh * dv + vcol + ln) * DQ + kq * DP + 16 * jb + 4 * lg);
-    }
-    for (int j = tid; j < DQ; j += THREADS) sm.n[j] = n0 ? n0[(size_t)bh * DQ + j] : 0.0f;
-    double m_prev = m0 ? (double)m0[bh] : 0.0;
-
-    const int n_chunks = S / L;
-    for (int c = 0; c < n_chunks; ++c) {
-        const size_t t0 = (size_t)c * L;
-        // --- stage gates and the V tile -----------------------------------
-        for (int i = tid; i < L; i += THREADS) {
-            sm.b[i] = ws.b[tokh + t0 + i];
-            sm.mloc[i] = ws.mloc[tokh + t0 + i];
-            sm.denloc[i] = ws.den[tokh + t0 + i];
-            sm.wloc[i] = ws.wloc[tokh + t0 + i];
-        }
-        for (int idx = tid; idx < L * TV / 8; idx += THREADS) {
-            const int row = idx / (TV / 8), col = 8 * (idx % (TV / 8));
-            bf16x8 x = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            if (col < vtile_cols)
-                x = *reinterpret_cast<const bf16x8*>(vh + (t0 + row) * dv + vt * TV + col);
-            *reinterpret_cast<bf16x8*>(sm.v + row * VP + col) = x;
-        }
-        __syncthreads();
-        // --- per-token stabilizer terms -------------------------------------
-        const double bL = sm.b[L - 1], mlocL = sm.mloc[L - 1];
-        const double mL = fmax(bL + m_prev, mlocL);
-        const float alpha = exp_arg(bL + m_prev - mL);
-        const float rL = exp_arg(mlocL - mL);
-        for (int i = tid; i < L; i += THREADS) {
-            const double mt = fmax(sm.b[i] + m_prev, sm.mloc[i]);
-            sm.fl[i] = exp_arg(-mt);                  // floor of |den|: exp(-m_t)
-            sm.a[i] = exp_arg(sm.b[i] + m_prev - mt);
-            sm.r[i] = exp_arg(sm.mloc[i] - mt);
-            sm.w[i] = rL * sm.wloc[i];
-            sm.den[i] = 0.0f;
-        }
-        __syncthreads();
-        // w (.) V split into bf16 hi + lo
-        for (int idx = tid; idx < L * TV / 8; idx += THREADS) {
-            const int row = idx / (TV / 8), col = 8 * (idx % (TV / 8));
-            const float ws_ = sm.w[row];
-            const bf16* src = sm.v + row * VP + col;
-            bf16x8 xh, xl;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = ws_ * (float)src[e];
-                xh[e] = (bf16)x;
-                xl[e] = (bf16)(x - (float)xh[e]);
-            }
-            *reinterpret_cast<bf16x8*>(sm.vwh + row * VP + col) = xh;
-            *reinterpret_cast<bf16x8*>(sm.vwl + row * VP + col) = xl;
-        }
-        // (the first slab barrier below also publishes vwh / vwl)
-
-        f32x4 acc_inter[LB];
-#pragma unroll
-        for (int tb = 0; tb < LB; ++tb) acc_inter[tb] = f32x4{0, 0, 0, 0};
-
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-            // --- stage Q and K slab s (NK pieces of SB key columns) ----------
-            for (int idx = tid; idx < L * SW / 8; idx += THREADS) {
-                const int row = idx / (SW / 8), c8 = 8 * (idx % (SW / 8));
-                const int part = c8 / SB, jcol = part * DP + s * SB + (c8 % SB);
-                bf16x8 xq = *reinterpret_cast<const bf16x8*>(qh + (t0 + row) * DQ + jcol);
-                bf16x8 xk = *reinterpret_cast<const bf16x8*>(kh + (t0 + row) * DQ + jcol);
-                bf16* dq = sm.u.slab.q + row * QP + c8;   // 8-byte aligned rows
-                *reinterpret_cast<bf16x4*>(dq) = bf16x4{xq[0], xq[1], xq[2], xq[3]};
-                *reinterpret_cast<bf16x4*>(dq + 4) = bf16x4{xq[4], xq[5], xq[6], xq[7]};
-                *reinterpret_cast<bf16x8*>(sm.u.slab.k + row * KP + c8) = xk;
-            }
-            __syncthreads();
-            if (active) {
-                // inter-chunk retrieval: acc_inter += Q[:, slab] (C'_hi + C'_lo)^T[slab, cols]
-#pragma unroll
-                for (int kk = 0; kk < SB / 32; ++kk) {
-                    bf16x8 bhi, blo;
-                    split8(st[s * SBB + 2 * kk], st[s * SBB + 2 * kk + 1], bhi, blo);
-#pragma unroll
-                    for (int tb = 0; tb < LB; ++tb) {
-                        const bf16* qa = sm.u.slab.q + (16 * tb + ln) * QP + kq * SB + 32 * kk + 4 * lg;
-                        const bf16x8 aop = cat(*reinterpret_cast<const bf16x4*>(qa),
-                                               *reinterpret_cast<const bf16x4*>(qa + 16));
-                        acc_inter[tb] = mfma(aop, bhi, acc_inter[tb]);
-                        acc_inter[tb] = mfma(aop, blo, acc_inter[tb]);
-                    }
-                }
-                // state update: C'^T[slab] = alpha C'^T[slab] + K[:, slab]^T (w V)_{hi+lo}
-#pragma unroll
-                for (int jb = 0; jb < SBB; ++jb) st[s * SBB + jb] *= alpha;
-#pragma unroll
-                for (int kk = 0; kk < L / 32; ++kk) {
-                    // B operands: rows (tokens) 32kk + 8lg + 0..7 of w V, column vcol + ln
-                    const int vrow = (32 * kk + 8 * lg + (ln >> 2)) * VP + 16 * cb + 4 * (ln & 3);
-                    const bf16x8 bhi = cat(lds_read_tr(sm.vwh + vrow), lds_read_tr(sm.vwh + vrow + 4 * VP));
-                    const bf16x8 blo = cat(lds_read_tr(sm.vwl + vrow), lds_read_tr(sm.vwl + vrow + 4 * VP));
-#pragma unroll
-                    for (int jb = 0; jb < SBB; ++jb) {
-                        const bf16* ka = sm.u.slab.k + (32 * kk + 8 * lg + (ln >> 2)) * KP + kq * SB + 16 * jb + 4 * (ln & 3);
-                        const bf16x8 aop = cat(lds_read_tr(ka), lds_read_tr(ka + 4 * KP));
-                        st[s * SBB + jb] = mfma(aop, bhi, st[s * SBB + jb]);
-                        st[s * SBB + jb] = mfma(aop, blo, st[s * SBB + jb]);
-                    }
-                }
-            }
-            // normalizer, inter part: den[tau] += Q[tau, slab] . n'[slab]  (16 lanes per row)
-            for (int idx = tid; idx < L * 16; idx += THREADS) {
-                const int tau = idx >> 4, lp = idx & 15;
-                constexpr int CPL = SW / 16;  // columns per lane
-                float acc = 0.0f;
-#pragma unroll
-                for (int e = 0; e < CPL; ++e) {
-                    const int cc = lp * CPL + e;
-                    const int j = (cc / SB) * DP + s * SB + (cc % SB);
-                    acc += (float)sm.u.slab.q[tau * QP + cc] * sm.n[j];
-                }
-                acc += __shfl_xor(acc, 1, 64);
-                acc += __shfl_xor(acc, 2, 64);
-                acc += __shfl_xor(acc, 4, 64);
-                acc += __shfl_xor(acc, 8, 64);
-                if (lp == 0) sm.den[tau] += acc;
-            }
-            __syncthreads();
-            // normalizer state: n'[slab] = alpha n' + K[:, slab]^T w
-            for (int cc = tid; cc < SW; cc += THREADS) {
-                const int j = (cc / SB) * DP + s * SB + (cc % SB);
-                float acc = 0.0f;
-                for (int t = 0; t < L; ++t) acc += sm.w[t] * (float)sm.u.slab.k[t * KP + cc];
-                sm.n[j] = alpha * sm.n[j] + acc;
-            }
-            __syncthreads();
-        }
-
-        // --- sum Q C'^T over the key parts in a fixed order (deterministic) ----
-        if (NK > 1) {
-#pragma unroll
-            for (int kp = 0; kp < NK; ++kp) {
-                if (kq == kp && active) {
-#pragma unroll
-                    for (int tb = 0; tb < LB; ++tb) {
-                        f32x4* dst = reinterpret_cast<f32x4*>(sm.u.red + (tb * NC + cb) * 256 + lane * 4);
-                        *dst = (kp == 0) ? acc_inter[tb] : (*dst + acc_inter[tb]);
-                    }
-                }
-                __syncthreads();
-            }
-        }
-        // --- intra-chunk product, normalize, gate, store (part kq owns tb % NK == kq) ---
-        if (active) {
-            const bf16* Pc = ws.P + 2 * (tokh + t0) * L;   // hi block, then lo block
-#pragma unroll
-            for (int tb = 0; tb < LB; ++tb) {
-                if (tb % NK != kq) continue;
-                const f32x4 inter = (NK > 1)
-                    ? *reinterpret_cast<const f32x4*>(sm.u.red + (tb * NC + cb) * 256 + lane * 4)
-                    : acc_inter[tb];
-                // intra: (P_hi + P_lo)[rows of tb, s <= last row of tb] V[:, cols]
-                f32x4 intra = {0, 0, 0, 0};
-                for (int kk = 0; kk <= (16 * tb + 15) / 32; ++kk) {
-                    const bf16* pa = Pc + (size_t)(16 * tb + ln) * L + 32 * kk + 8 * lg;
-                    const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(pa);
-                    const bf16x8 alo = *reinterpret_cast<const bf16x8*>(pa + L * L);
-                    const bf16* vb = sm.v + (32 * kk + 8 * lg + (ln >> 2)) * VP + 16 * cb + 4 * (ln & 3);
-                    const bf16x8 bop = cat(lds_read_tr(vb), lds_read_tr(vb + 4 * VP));
-                    intra = mfma(ahi, bop, intra);
-                    intra = mfma(alo, bop, intra);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int tau = 16 * tb + 4 * lg + i;
-                    const float ra = sm.r[tau], aa = sm.a[tau];
-                    const float num = ra * intra[i] + aa * inter[i];
-                    const float den = ra * sm.denloc[tau] + aa * sm.den[tau];
-                    const size_t o = (t0 + tau) * dv + vcol + ln;
-                    const float hv = sigmoid(oh[o]) * num / fmaxf(fabsf(den), sm.fl[tau]);
-                    hh[o] = (bf16)hv;
-                }
-            }
-        }
-        m_prev = mL;
-        __syncthreads();
-    }
-
-    // final stabilized state
-    if (active) {
-#pragma unroll
-        for (int jb = 0; jb < NSB; ++jb)
-            *reinterpret_cast<f32x4*>(Cout + ((size_t)bh * dv + vcol + ln) * DQ + kq * DP + 16 * jb + 4 * lg) = st[jb];
-    }
-    if (vt == 0) {
-        for (int j = tid; j < DQ; j += THREADS) nout[(size_t)bh * DQ + j] = sm.n[j];
-        if (tid == 0) mout[bh] = (float)m_prev;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -949,7 +809,7 @@ __device__ __forceinline__ void chunk_store(const f32x4 (&reg)[Pref<C>::NCH], Sc
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ o_pre, Ws ws, int S, int dv, int n_vt, int remap,
+    const float* __restrict__ o_pre, Ws ws, int S, int G, int dv, int n_vt, int remap,
     const float* __restrict__ C0,
     bf16* __restrict__ h, float* __restrict__ Cout, float* __restrict__ nout, float* __restrict__ mout)
 {
@@ -969,7 +829,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
         const int G = gridDim.x;
         wg = (wg % 8) * (G / 8) + wg / 8;
     }
-    const int bh = wg / n_vt, vt = wg % n_vt;
+    // workgroup -> (head, sequence segment, value tile)
+    const int bh = wg / (G * n_vt), seg = (wg / n_vt) % G, vt = wg % n_vt;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int cb = wave % NC, kq = wave / NC;
     const int ln = lane & 15, lg = lane >> 4;
@@ -980,9 +841,12 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
 #pragma unroll
     for (int x = 0; x < CW; ++x) act[x] = vcol + 16 * x < dv;
     const bool active = act[0];
-    const int nC = S / L;
+    const int nC = S / L / G;                      // chunks of this segment
 
-    const size_t tokh = (size_t)bh * S;
+    const size_t tokh = (size_t)bh * S + (size_t)seg * (S / G);
+    // state entering the segment: the caller's (or zero) for the first, else the chained one
+    const float* Cin = seg == 0 ? (C0 ? C0 + (size_t)bh * dv * DQ : nullptr)
+                                : ws.cst + ((size_t)bh * G + seg) * (size_t)dv * DQ;
     const bf16* qh = q + tokh * DQ;
     const bf16* kh = k + tokh * DQ;
     bf16* hh = h + tokh * dv;
@@ -1006,9 +870,9 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
 #pragma unroll
         for (int jb = 0; jb < NSB; ++jb) {
             st[x][jb] = f32x4{0, 0, 0, 0};
-            if (C0 && act[x])
+            if (Cin && act[x])
                 st[x][jb] = *reinterpret_cast<const f32x4*>(
-                    C0 + ((size_t)bh * dv + vcol + 16 * x + ln) * DQ + kq * DP + 16 * jb + 4 * lg);
+                    Cin + (size_t)(vcol + 16 * x + ln) * DQ + kq * DP + 16 * jb + 4 * lg);
         }
 
     f32x4 rs[Pref<C>::NSL], rc[Pref<C>::NCH];
@@ -1190,6 +1054,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
         lds_barrier();
     }
 
+    if (seg != G - 1) return;
 #pragma unroll
     for (int x = 0; x < CW; ++x) {
         if (!act[x]) continue;
@@ -1208,12 +1073,12 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
 // host side
 // ---------------------------------------------------------------------------
 template <int L>
-hipError_t launch_prep(const FwdArgs& a, const Ws& w, bool gates) {
+hipError_t launch_prep(const FwdArgs& a, const Ws& w) {
     dim3 grid(a.S / L, a.B * a.NH);
     hipLaunchKernelGGL((chunk_prep_kernel<L>), grid, dim3(PREP_THREADS), 0, a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, a.i_pre, a.f_pre, a.S, a.dqk, w);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !gates) return e;
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gate_scan_kernel<L>), dim3((a.dqk + GS_COLS - 1) / GS_COLS, a.B * a.NH), dim3(GS_THREADS), 0, a.stream,
                        w, a.S, a.dqk, a.n0, a.m0);
     e = hipGetLastError();
@@ -1223,52 +1088,65 @@ hipError_t launch_prep(const FwdArgs& a, const Ws& w, bool gates) {
     return hipGetLastError();
 }
 
+// Sequence segments per head: enough that (heads x value tiles x segments) covers
+// the chip, each segment at least 4 chunks long.  Long sequences over few heads
+// (the long-context shape) are otherwise a handful of sequential workgroups.
 template <class C>
-hipError_t launch_scan(const FwdArgs& a, const Ws& w) {
-    const int n_vt = (a.dv + C::TV - 1) / C::TV;
-    const int G = a.B * a.NH * n_vt;
-    const int remap = (G % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((chunk_scan_kernel<C>), dim3(G), dim3(C::THREADS), 0, a.stream,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.o_pre, w, a.S, a.dv, n_vt, remap,
-                       a.C0, a.n0, a.m0, (bf16*)a.h, a.C, a.n, a.m);
-    return hipGetLastError();
+int segments(const FwdArgs& a) {
+    const int units = a.B * a.NH * ((a.dv + C::TV - 1) / C::TV);
+    const int nC = a.S / C::L;
+    int G = 1;
+    while (2 * G <= SC_MAXG && units * 2 * G <= 256 && nC % (2 * G) == 0 && nC / (2 * G) >= 4) G *= 2;
+    return G;
 }
 
 template <class C>
-hipError_t launch_scan2(const FwdArgs& a, const Ws& w) {
+hipError_t launch_scan2(const FwdArgs& a, const Ws& w, int G) {
+    constexpr int L = C::L;
+    const int heads = a.B * a.NH;
+    if (G > 1) {
+        dim3 sgrid((a.dqk / SS_TILE) * ((a.dv + SS_TILE - 1) / SS_TILE), G - 1, heads);
+        hipLaunchKernelGGL((seg_state_kernel<L>), sgrid, dim3(SS_THREADS), 0, a.stream,
+                           (const bf16*)a.k, (const bf16*)a.v, w, a.S, a.dqk, a.dv, G);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const size_t quads = (size_t)a.dv * a.dqk / 4;
+        hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)((quads + SC_THREADS - 1) / SC_THREADS), heads),
+                           dim3(SC_THREADS), 0, a.stream, w, a.S / L, G, a.dqk, a.dv, a.C0);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int n_vt = (a.dv + C::TV - 1) / C::TV;
-    const int G = a.B * a.NH * n_vt;
-    const int remap = (G % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((chunk_scan2_kernel<C>), dim3(G), dim3(C::THREADS), 0, a.stream,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.o_pre, w, a.S, a.dv, n_vt, remap,
+    const int nwg = heads * G * n_vt;
+    const int remap = (nwg % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((chunk_scan2_kernel<C>), dim3(nwg), dim3(C::THREADS), 0, a.stream,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.o_pre, w, a.S, G, a.dv, n_vt, remap,
                        a.C0, (bf16*)a.h, a.C, a.n, a.m);
     return hipGetLastError();
 }
 
-// stage 0 = prepare (chunk_prep [+ gate_scan]), stage 1 = scan
-template <int L, int DQ, int NC, int NK, int SB, int MINB>
-hipError_t run1(const FwdArgs& a, int stage) {
-    Ws w = ws_layout(a.ws, (size_t)a.B * a.NH, a.S, L, a.dqk);
-    if (stage == 0) return launch_prep<L>(a, w, false);
-    return launch_scan<ScanCfg<L, DQ, NC, NK, SB, MINB>>(a, w);
-}
-
+// stage 0 = prepare (chunk_prep, gate_scan, den), stage 1 = scan (segments, chunk_scan2),
+// stage 2 = workspace size only
 template <int L, int DQ, int NC, int NK, int SB, int MINB, int CW>
-hipError_t run2(const FwdArgs& a, int stage) {
-    Ws w = ws_layout(a.ws, (size_t)a.B * a.NH, a.S, L, a.dqk);
-    if (stage == 0) return launch_prep<L>(a, w, true);
-    return launch_scan2<Scan2Cfg<L, DQ, NC, NK, SB, MINB, CW>>(a, w);
+hipError_t run2(const FwdArgs& a, int stage, size_t* bytes) {
+    using C = Scan2Cfg<L, DQ, NC, NK, SB, MINB, CW>;
+    const int G = segments<C>(a);
+    if (stage == 2) {
+        *bytes = ws_bytes((size_t)a.B * a.NH, a.S, L, a.dqk, a.dv, G);
+        return hipSuccess;
+    }
+    Ws w = ws_layout(a.ws, (size_t)a.B * a.NH, a.S, L, a.dqk, a.dv, G);
+    if (stage == 0) return launch_prep<L>(a, w);
+    return launch_scan2<C>(a, w, G);
 }
 
-typedef hipError_t (*RunFn)(const FwdArgs&, int);
+typedef hipError_t (*RunFn)(const FwdArgs&, int, size_t*);
 
 // supported (chunk, d_qk) pairs and the tiling used for each:
-// (chunk, d_qk, column blocks, key parts, slab, workgroups per CU)
+// (chunk, d_qk, column blocks, key parts, slab, workgroups per CU, column blocks per wave)
 RunFn pick(int L, int dqk) {
 #define MLSTM_V2(L_, DQ_, NC_, NK_, SB_, MINB_, CW_) \
     if (L == L_ && dqk == DQ_) return &run2<L_, DQ_, NC_, NK_, SB_, MINB_, CW_>;
-#define MLSTM_V1(L_, DQ_, NC_, NK_, SB_, MINB_) \
-    if (L == L_ && dqk == DQ_) return &run1<L_, DQ_, NC_, NK_, SB_, MINB_>;
     // Four waves per workgroup (one per SIMD) let the compiler use the whole
     // register file; eight waves (two per SIMD, key dimension split in two or
     // four parts) hide more latency behind the other wave's MFMAs.  Every entry
@@ -1282,33 +1160,38 @@ RunFn pick(int L, int dqk) {
     MLSTM_V2(64, 384, 4, 2, 32, 1, 1)
     MLSTM_V2(64, 512, 4, 2, 32, 1, 1)
     MLSTM_V2(64, 1024, 2, 4, 32, 1, 1)
-    MLSTM_V1(128, 128, 4, 2, 32, 1)
-    MLSTM_V1(128, 256, 4, 2, 32, 1)
 #undef MLSTM_V2
-#undef MLSTM_V1
     return nullptr;
 }
+
+// The chunk size only sets how the recurrence is re-associated: every chunk size
+// gives the same result up to rounding.  A 128-token chunk is computed as two
+// consecutive 64-token chunks, whose tiles fit the LDS and register budget.
+int mfma_chunk(const FwdArgs& a) { return a.chunk == 128 ? 64 : a.chunk; }
 
 }  // namespace
 
 bool mfma_fwd_supported(const FwdArgs& a) {
-    return a.dtype == MLSTM_BF16 && a.S % a.chunk == 0 && pick(a.chunk, a.dqk) != nullptr;
+    return a.dtype == MLSTM_BF16 && a.S % a.chunk == 0 && pick(mfma_chunk(a), a.dqk) != nullptr;
 }
 
 size_t mfma_fwd_workspace_bytes(const FwdArgs& a) {
-    return ws_bytes((size_t)a.B * a.NH, a.S, a.chunk, a.dqk);
+    RunFn f = pick(mfma_chunk(a), a.dqk);
+    size_t bytes = 0;
+    if (f) (void)f(a, 2, &bytes);
+    return bytes;
 }
 
 hipError_t launch_fwd_mfma_prepare(const FwdArgs& a) {
-    RunFn f = pick(a.chunk, a.dqk);
+    RunFn f = pick(mfma_chunk(a), a.dqk);
     if (!f) return hipErrorNotSupported;
-    return f(a, 0);
+    return f(a, 0, nullptr);
 }
 
 hipError_t launch_fwd_mfma_scan(const FwdArgs& a) {
-    RunFn f = pick(a.chunk, a.dqk);
+    RunFn f = pick(mfma_chunk(a), a.dqk);
     if (!f) return hipErrorNotSupported;
-    return f(a, 1);
+    return f(a, 1, nullptr);
 }
 
 }  // namespace mlstm

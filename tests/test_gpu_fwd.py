@@ -93,6 +93,20 @@ def test_bf16_mfma_tilings(orc, chunk, dqk, dv):
     _compare(orc, x, chunk, "bf16")
 
 
+# few heads over a long sequence: the scan splits each head's sequence into
+# segments chained through their entering states (long-context gate statistics)
+SEGMENTED = [(dict(B=1, NH=1, S=2048, dqk=128, dv=96), 64), (dict(B=1, NH=2, S=1024, dqk=384, dv=384), 32),
+             (dict(B=1, NH=1, S=4096, dqk=256, dv=256), 128)]
+
+
+@pytest.mark.parametrize("over,chunk", SEGMENTED, ids=lambda v: str(v))
+def test_bf16_segmented_sequence(orc, over, chunk):
+    w = inputs.WORKLOADS["long_ctx"]
+    announce(f"fwd bf16 segmented {over} chunk={chunk}")
+    x = inputs.fwd_inputs(w, seed=400 + over["dqk"], **over)
+    _compare(orc, x, chunk, "bf16")
+
+
 FULL = [
     # (batch indices, head indices) of the sampled heads, shaped [1, n] so the
     # selection keeps the [B, NH] leading axes
