@@ -349,17 +349,21 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
 //   a_t = exp(b_t + m_p - m_t), r_t = exp(m_loc_t - m_t), fl_t = exp(-m_t),
 //   w_t = exp(m_loc_L - m_L) w_loc_t, alpha_c = exp(b_L + m_p - m_L),
 // and the normalizer entering each chunk follows n' <- alpha n' + exp(m_loc_L - m_L) K^T w_loc.
-constexpr int GS_THREADS = 64;   // one wave per workgroup
-constexpr int GS_COLS = 64;      // key columns of the normalizer per workgroup
+constexpr int GS_WAVES = 8;
+constexpr int GS_THREADS = 64 * GS_WAVES;
+constexpr int GS_COLS = 64;      // key columns of the normalizer per workgroup (one per lane)
 constexpr int GS_TILE = 512;     // chunks per pass over LDS
 constexpr int GS_BATCH = 16;     // loads issued together before their results are used
 
 // The stabilizer recurrence m <- max(b_L + m, m_loc_L) is a max-plus affine map
 // m -> max(A + m, B); maps compose as (A1, B1) then (A2, B2) = (A1 + A2, max(B1 + A2, B2)),
-// so the wave scans a tile of chunks in parallel (each lane first composes a run
+// so one wave scans a tile of chunks in parallel (each lane first composes a run
 // of consecutive chunks, then the lanes combine by an inclusive shuffle scan).
-// Grid (key-column groups, heads): every workgroup of a head repeats that short
-// scan, then carries the normalizer for its 64 key columns and writes the
+// The normalizer recurrence n' <- alpha n' + rl dn is affine too: each wave
+// carries it over its own range of chunks from zero, the ranges are chained
+// through LDS, and each wave then walks its range again from the true value.
+// Grid (key-column groups, heads): every workgroup of a head repeats the short
+// stabilizer scan, carries the normalizer for its 64 key columns and writes the
 // per-token weights of its share of the tokens.
 template <int L>
 __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int dqk,
@@ -368,21 +372,23 @@ __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int
 {
     __shared__ double sbl[GS_TILE], sml[GS_TILE], smp[GS_TILE + 1];
     __shared__ float salpha[GS_TILE], srl[GS_TILE];
-    const int part = blockIdx.x, nparts = gridDim.x, bh = blockIdx.y, lane = threadIdx.x;
+    __shared__ float spart[GS_WAVES][GS_COLS], sprod[GS_WAVES], sfin[GS_COLS];
+    const int part = blockIdx.x, nparts = gridDim.x, bh = blockIdx.y;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nC = S / L;
     const size_t tokh = (size_t)bh * S;
     const int j = part * GS_COLS + lane;
     double m_run = m0 ? (double)m0[bh] : 0.0;
-    float nv = (j < dqk && n0) ? n0[(size_t)bh * dqk + j] : 0.0f;
+    float n_in = (j < dqk && n0) ? n0[(size_t)bh * dqk + j] : 0.0f;   // normalizer entering the tile
     for (int c0 = 0; c0 < nC; c0 += GS_TILE) {
         const int nt = min(GS_TILE, nC - c0);
-        for (int i = lane; i < nt; i += GS_THREADS) {
+        for (int i = tid; i < nt; i += GS_THREADS) {
             const size_t t = tokh + (size_t)(c0 + i) * L + L - 1;
             sbl[i] = ws.b[t];
             sml[i] = ws.mloc[t];
         }
         __syncthreads();
-        {
+        if (wave == 0) {
             const int run = (nt + 63) / 64;
             const int i0 = min(nt, lane * run), i1 = min(nt, i0 + run);
             double A = 0.0, B = -INFINITY;            // identity map
@@ -421,7 +427,7 @@ __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int
             float wl[GS_BATCH];
 #pragma unroll
             for (int u = 0; u < GS_BATCH; ++u) {
-                const int t = tb0 + lane + GS_THREADS * u;
+                const int t = tb0 + tid + GS_THREADS * u;
                 if (t < thi) {
                     const size_t g = tokh + (size_t)c0 * L + t;
                     bt[u] = ws.b[g];
@@ -431,7 +437,7 @@ __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int
             }
 #pragma unroll
             for (int u = 0; u < GS_BATCH; ++u) {
-                const int t = tb0 + lane + GS_THREADS * u;
+                const int t = tb0 + tid + GS_THREADS * u;
                 if (t < thi) {
                     const int ci = t / L;
                     const size_t g = tokh + (size_t)c0 * L + t;
@@ -446,27 +452,50 @@ __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int
             }
         }
         if (part == 0)
-            for (int i = lane; i < nt; i += GS_THREADS) ws.alpha[(size_t)bh * nC + c0 + i] = salpha[i];
-        // normalizer entering each chunk: n' <- alpha n' + rl K^T w_loc, one key column per lane
-        if (j < dqk) {
-            for (int i0 = 0; i0 < nt; i0 += GS_BATCH) {
-                float d[GS_BATCH];
+            for (int i = tid; i < nt; i += GS_THREADS) ws.alpha[(size_t)bh * nC + c0 + i] = salpha[i];
+        // normalizer entering each chunk: n' <- alpha n' + rl K^T w_loc, one key column per lane,
+        // wave q over chunks [q0, q1) of the tile
+        const int qrun = (nt + GS_WAVES - 1) / GS_WAVES;
+        const int q0 = min(nt, wave * qrun), q1 = min(nt, q0 + qrun);
+        const float* dnp = ws.dn + ((size_t)bh * nC + c0) * dqk + j;
+        float* nep = ws.nent + ((size_t)bh * nC + c0) * dqk + j;
+        float v = 0.0f, prod = 1.0f;
+        for (int i0 = q0; i0 < q1; i0 += GS_BATCH) {
+            float d[GS_BATCH];
 #pragma unroll
-                for (int e = 0; e < GS_BATCH; ++e)
-                    if (i0 + e < nt) d[e] = ws.dn[((size_t)bh * nC + c0 + i0 + e) * dqk + j];
+            for (int e = 0; e < GS_BATCH; ++e)
+                if (i0 + e < q1 && j < dqk) d[e] = dnp[(size_t)(i0 + e) * dqk];
 #pragma unroll
-                for (int e = 0; e < GS_BATCH; ++e) {
-                    if (i0 + e < nt) {
-                        ws.nent[((size_t)bh * nC + c0 + i0 + e) * dqk + j] = nv;
-                        nv = salpha[i0 + e] * nv + srl[i0 + e] * d[e];
-                    }
+            for (int e = 0; e < GS_BATCH; ++e)
+                if (i0 + e < q1) {
+                    v = salpha[i0 + e] * v + srl[i0 + e] * (j < dqk ? d[e] : 0.0f);
+                    prod *= salpha[i0 + e];
                 }
-            }
         }
+        spart[wave][lane] = v;
+        if (lane == 0) sprod[wave] = prod;
+        __syncthreads();
+        float nv = n_in;
+        for (int w2 = 0; w2 < wave; ++w2) nv = sprod[w2] * nv + spart[w2][lane];
+        for (int i0 = q0; i0 < q1; i0 += GS_BATCH) {
+            float d[GS_BATCH];
+#pragma unroll
+            for (int e = 0; e < GS_BATCH; ++e)
+                if (i0 + e < q1 && j < dqk) d[e] = dnp[(size_t)(i0 + e) * dqk];
+#pragma unroll
+            for (int e = 0; e < GS_BATCH; ++e)
+                if (i0 + e < q1 && j < dqk) {
+                    nep[(size_t)(i0 + e) * dqk] = nv;
+                    nv = salpha[i0 + e] * nv + srl[i0 + e] * d[e];
+                }
+        }
+        if (wave == GS_WAVES - 1) sfin[lane] = nv;
+        __syncthreads();
+        n_in = sfin[lane];
         __syncthreads();
     }
-    if (j < dqk) ws.nfin[(size_t)bh * dqk + j] = nv;
-    if (part == 0 && lane == 0) ws.mfin[bh] = (float)m_run;
+    if (wave == 0 && j < dqk) ws.nfin[(size_t)bh * dqk + j] = n_in;
+    if (part == 0 && tid == 0) ws.mfin[bh] = (float)m_run;
 }
 
 // ---------------------------------------------------------------------------
@@ -528,7 +557,6 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
     __shared__ __attribute__((aligned(16))) bf16 sk[L * SS_P];
     __shared__ __attribute__((aligned(16))) bf16 svh[L * SS_P];
     __shared__ __attribute__((aligned(16))) bf16 svl[L * SS_P];
-    __shared__ float somega[L];
     constexpr int UNITS = L * SS_TILE / 8;                  // 16-byte units of one tile
     constexpr int UPT = (UNITS + SS_THREADS - 1) / SS_THREADS;
 
@@ -542,6 +570,27 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
     const int key0 = kt * SS_TILE, val0 = vt * SS_TILE;
     const size_t tokh = (size_t)bh * S;
 
+    // next chunk's K and V units, update weights of their rows and its alpha, in flight
+    // while the current chunk is multiplied (chunks are walked last to first)
+    bf16x8 rk[UPT], rv[UPT];
+    float rw[UPT], ralpha = 1.0f;
+    auto load = [&](int ci) {
+        const int c = g * nCs + ci;
+        const size_t t0 = tokh + (size_t)c * L;
+#pragma unroll
+        for (int u = 0; u < UPT; ++u) {
+            const int idx = tid + u * SS_THREADS;
+            if (idx < UNITS) {
+                const int row = idx / (SS_TILE / 8), c8 = 8 * (idx % (SS_TILE / 8));
+                rk[u] = *reinterpret_cast<const bf16x8*>(k + (t0 + row) * dqk + key0 + c8);
+                rv[u] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                if (val0 + c8 < dv) rv[u] = *reinterpret_cast<const bf16x8*>(v + (t0 + row) * dv + val0 + c8);
+                rw[u] = ws.w[t0 + row];
+            }
+        }
+        ralpha = ws.alpha[(size_t)bh * nC + c];
+    };
+
     f32x4 acc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; ++a)
@@ -549,26 +598,20 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
         for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
 
     float A = 1.0f;          // product of alpha over the segment's chunks after the current one
+    load(nCs - 1);
     for (int ci = nCs - 1; ci >= 0; --ci) {
-        const int c = g * nCs + ci;
-        const size_t t0 = tokh + (size_t)c * L;
         __syncthreads();     // previous tiles consumed
-        if (tid < L) somega[tid] = ws.w[t0 + tid] * A;
-        __syncthreads();
 #pragma unroll
         for (int u = 0; u < UPT; ++u) {
             const int idx = tid + u * SS_THREADS;
             if (idx < UNITS) {
                 const int row = idx / (SS_TILE / 8), c8 = 8 * (idx % (SS_TILE / 8));
-                *reinterpret_cast<bf16x8*>(sk + row * SS_P + c8) =
-                    *reinterpret_cast<const bf16x8*>(k + (t0 + row) * dqk + key0 + c8);
-                bf16x8 xv = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-                if (val0 + c8 < dv) xv = *reinterpret_cast<const bf16x8*>(v + (t0 + row) * dv + val0 + c8);
-                const float om = somega[row];
+                *reinterpret_cast<bf16x8*>(sk + row * SS_P + c8) = rk[u];
+                const float om = rw[u] * A;
                 bf16x8 xh, xl;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float x = om * (float)xv[e];
+                    const float x = om * (float)rv[u][e];
                     xh[e] = (bf16)x;
                     xl[e] = (bf16)(x - (float)xh[e]);
                 }
@@ -576,7 +619,9 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
                 *reinterpret_cast<bf16x8*>(svl + row * SS_P + c8) = xl;
             }
         }
+        A *= ralpha;
         __syncthreads();
+        if (ci > 0) load(ci - 1);
 #pragma unroll
         for (int kk = 0; kk < L / 32; ++kk) {
             const int trow = 32 * kk + 8 * lg + (ln >> 2);
@@ -598,7 +643,6 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
                     acc[a][b] = mfma(ka[a], vl[b], acc[a][b]);
                 }
         }
-        A *= ws.alpha[(size_t)bh * nC + c];
     }
     // dC_g into slot g + 1: rows of the D layout are keys, columns are values
     float* dst = ws.cst + ((size_t)bh * G + g + 1) * (size_t)dv * dqk;
