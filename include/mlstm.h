@@ -69,8 +69,10 @@ typedef enum mlstm_dtype {
 } mlstm_dtype;
 
 /*
- * Bytes of device workspace mlstm_fwd_parallel needs for these sizes (0 if none).
- * Returns 0 as well for arguments mlstm_fwd_parallel would reject.
+ * Bytes of device workspace a forward over these sizes needs (0 if none): what
+ * mlstm_fwd_parallel (and its two stages) need when S is a multiple of chunk,
+ * and what mlstm_fwd_parallel_state needs for any S >= 1.  Returns 0 as well for
+ * arguments both would reject.
  */
 size_t mlstm_fwd_workspace_bytes(int B, int NH, int S, int d_qk, int d_v, int chunk,
                                  mlstm_dtype dtype);
@@ -109,6 +111,36 @@ mlstm_status mlstm_fwd_parallel(const void *q, const void *k, const void *v,
                                 mlstm_dtype dtype,
                                 void *h_out, float *C_final, float *n_final, float *m_final,
                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Chunkwise parallel forward that continues from a given stabilized state and
+ * accepts any sequence length (section 2.3: the recurrence carried across the
+ * chunks of the parallel form; a sequence split anywhere and run piece by piece,
+ * each piece from the state the previous one returned, gives the result of one
+ * run over the whole sequence, up to rounding).
+ *
+ * Same arguments, layouts and rules as mlstm_fwd_parallel, except:
+ *   S               any length >= 1; when S is not a multiple of chunk, the
+ *                   last S % chunk tokens form a shorter final chunk
+ *   C_init, n_init, m_init
+ *                   stabilized state entering token 0: [B,NH,d_v,d_qk],
+ *                   [B,NH,d_qk], [B,NH] fp32, read only (C_init 16-byte aligned)
+ *                   -- e.g. the final state of an earlier call, or of
+ *                   mlstm_step.  All three NULL = the zero state.  Giving only
+ *                   some of them is MLSTM_ERR_INVALID_ARG, and so is any
+ *                   overlap between them and C_final, n_final, m_final (pass a
+ *                   second buffer to continue a state).
+ *   workspace       at least mlstm_fwd_workspace_bytes(B, NH, S, ...) bytes
+ * With S a multiple of chunk and the zero state it computes exactly what
+ * mlstm_fwd_parallel computes.
+ */
+mlstm_status mlstm_fwd_parallel_state(const void *q, const void *k, const void *v,
+                                      const float *i_pre, const float *f_pre, const float *o_pre,
+                                      int B, int NH, int S, int d_qk, int d_v, int chunk,
+                                      mlstm_dtype dtype,
+                                      const float *C_init, const float *n_init, const float *m_init,
+                                      void *h_out, float *C_final, float *n_final, float *m_final,
+                                      void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * The two stages of mlstm_fwd_parallel, for callers that schedule them apart

@@ -2,6 +2,8 @@
 
 Entry points (same names as include/mlstm.h):
   mlstm_fwd_parallel  chunkwise parallel forward over whole sequences
+  mlstm_fwd_parallel_state
+                      the same from a given state, for any sequence length
   mlstm_fwd_prepare, mlstm_fwd_scan
                       the two stages of mlstm_fwd_parallel, for callers that schedule them apart
   mlstm_step          one-token recurrent decode step, state updated in place
@@ -14,6 +16,7 @@ from .binding import (  # noqa: F401
     load_library,
     mlstm_error_detail,
     mlstm_fwd_parallel,
+    mlstm_fwd_parallel_state,
     mlstm_fwd_prepare,
     mlstm_fwd_scan,
     mlstm_fwd_workspace_bytes,

@@ -51,6 +51,9 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mlstm_fwd_parallel.restype = i
     lib.mlstm_fwd_parallel.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, i,
                                        vp, fp, fp, fp, vp, sz, vp]
+    lib.mlstm_fwd_parallel_state.restype = i
+    lib.mlstm_fwd_parallel_state.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, i,
+                                             fp, fp, fp, vp, fp, fp, fp, vp, sz, vp]
     lib.mlstm_fwd_prepare.restype = i
     lib.mlstm_fwd_prepare.argtypes = [vp, vp, fp, fp, i, i, i, i, i, i, i, vp, sz, vp]
     lib.mlstm_fwd_scan.restype = i
@@ -170,6 +173,38 @@ def mlstm_fwd_parallel(q, k, v, i_pre, f_pre, o_pre, chunk: int,
                                 ws_ptr, ws_bytes, _stream_handle(stream, dev))
     if st != MLSTM_OK:
         raise MlstmError("mlstm_fwd_parallel", st, mlstm_error_detail())
+    return h_out, C_final, n_final, m_final
+
+
+def mlstm_fwd_parallel_state(q, k, v, i_pre, f_pre, o_pre, chunk: int, C_init=None, n_init=None, m_init=None,
+                             h_out=None, C_final=None, n_final=None, m_final=None,
+                             workspace=None, stream=None):
+    """Chunkwise parallel forward from a given stabilized state, any S >= 1; returns (h, C, n, m).
+
+    Like mlstm_fwd_parallel; C_init [B,NH,d_v,d_qk], n_init [B,NH,d_qk], m_init [B,NH]
+    float32 give the state entering the first token (all None = zero state) and
+    must not share memory with the final state.
+    """
+    import torch
+    lib = load_library()
+    (B, NH, S, dqk, dv, dt, h_out, C_final, n_final, m_final, workspace, ws_ptr, ws_bytes, dev) = _fwd_args(
+        q, k, v, i_pre, f_pre, o_pre, chunk, h_out, C_final, n_final, m_final, workspace, True)
+    given = [t is not None for t in (C_init, n_init, m_init)]
+    if any(given):
+        if not all(given):
+            raise ValueError("C_init, n_init and m_init must be given together")
+        _check(C_init, "C_init", (B, NH, dv, dqk), torch.float32, dev)
+        _check(n_init, "n_init", (B, NH, dqk), torch.float32, dev)
+        _check(m_init, "m_init", (B, NH), torch.float32, dev)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    st = lib.mlstm_fwd_parallel_state(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      i_pre.data_ptr(), f_pre.data_ptr(), o_pre.data_ptr(),
+                                      B, NH, S, dqk, dv, int(chunk), dt,
+                                      ptr(C_init), ptr(n_init), ptr(m_init),
+                                      h_out.data_ptr(), C_final.data_ptr(), n_final.data_ptr(), m_final.data_ptr(),
+                                      ws_ptr, ws_bytes, _stream_handle(stream, dev))
+    if st != MLSTM_OK:
+        raise MlstmError("mlstm_fwd_parallel_state", st, mlstm_error_detail())
     return h_out, C_final, n_final, m_final
 
 

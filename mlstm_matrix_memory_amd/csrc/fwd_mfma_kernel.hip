@@ -192,7 +192,7 @@ template <int L>
 __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k,
     const float* __restrict__ i_pre, const float* __restrict__ f_pre,
-    int S, int dqk, Ws ws)
+    int S, int Sx, int dqk, Ws ws)
 {
     constexpr int LB = L / 16;
     constexpr int NW = PREP_THREADS / 64;
@@ -204,9 +204,10 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     const int c = blockIdx.x, bh = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, lg = lane >> 4;
-    const size_t tok0 = (size_t)bh * S + (size_t)c * L;
-    const bf16* qh = q + tok0 * dqk;
-    const bf16* kh = k + tok0 * dqk;
+    const size_t tok0 = (size_t)bh * S + (size_t)c * L;     // workspace token index
+    const size_t tin0 = (size_t)bh * Sx + (size_t)c * L;    // input token index
+    const bf16* qh = q + tin0 * dqk;
+    const bf16* kh = k + tin0 * dqk;
 
     auto slab_load = [&](f32x4 (&reg)[UPT], int j0) {
 #pragma unroll
@@ -225,8 +226,8 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     // gates: cumulative log forget gate and chunk-local stabilizer, by wave scans (fp64)
     double lf = 0.0, ii = 0.0;
     if (tid < L) {
-        lf = log_sigmoid_f64((double)f_pre[tok0 + tid]);
-        ii = (double)i_pre[tok0 + tid];
+        lf = log_sigmoid_f64((double)f_pre[tin0 + tid]);
+        ii = (double)i_pre[tin0 + tid];
     }
     double bcum = 0.0;
     if (wave < 2) {
@@ -507,7 +508,7 @@ __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int
 constexpr int DEN_THREADS = 256;
 
 template <int L>
-__global__ __launch_bounds__(DEN_THREADS) void den_kernel(const bf16* __restrict__ q, Ws ws, int S, int dqk)
+__global__ __launch_bounds__(DEN_THREADS) void den_kernel(const bf16* __restrict__ q, Ws ws, int S, int Sx, int dqk)
 {
     __shared__ __attribute__((aligned(16))) float sn[4096];
     const int c = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
@@ -518,7 +519,7 @@ __global__ __launch_bounds__(DEN_THREADS) void den_kernel(const bf16* __restrict
     const size_t tok0 = (size_t)bh * S + (size_t)c * L;
     const int lp = tid & 15;
     for (int row = tid >> 4; row < L; row += DEN_THREADS / 16) {
-        const bf16* qr = q + (tok0 + row) * dqk;
+        const bf16* qr = q + ((size_t)bh * Sx + (size_t)c * L + row) * dqk;
         float acc = 0.0f;
         for (int j0 = lp * 8; j0 < dqk; j0 += 128) {
             const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(qr + j0);
@@ -547,12 +548,12 @@ __global__ __launch_bounds__(DEN_THREADS) void den_kernel(const bf16* __restrict
 // hi + lo as in the scan); seg_combine_kernel chains the segments.  The scan then
 // runs every segment in parallel from its own entering state.
 constexpr int SS_THREADS = 256;
-constexpr int SS_TILE = 64;            // key rows and value columns of a workgroup's tile
+constexpr int SS_TILE = 128;           // key rows and value columns of a workgroup's tile
 constexpr int SS_P = SS_TILE + 16;     // LDS pitch (bf16) of the token-major tiles
 
 template <int L>
 __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
-    const bf16* __restrict__ k, const bf16* __restrict__ v, Ws ws, int S, int dqk, int dv, int G)
+    const bf16* __restrict__ k, const bf16* __restrict__ v, Ws ws, int S, int Sx, int dqk, int dv, int G)
 {
     __shared__ __attribute__((aligned(16))) bf16 sk[L * SS_P];
     __shared__ __attribute__((aligned(16))) bf16 svh[L * SS_P];
@@ -565,10 +566,10 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
     const int g = blockIdx.y, bh = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, lg = lane >> 4;
-    const int wr = wave >> 1, wc = wave & 1;                // 32 keys x 32 values per wave
+    const int wr = wave >> 1, wc = wave & 1;                // 64 keys x 64 values per wave
     const int nC = S / L, nCs = nC / G;
     const int key0 = kt * SS_TILE, val0 = vt * SS_TILE;
-    const size_t tokh = (size_t)bh * S;
+    const size_t tokh = (size_t)bh * S, tinh = (size_t)bh * Sx;
 
     // next chunk's K and V units, update weights of their rows and its alpha, in flight
     // while the current chunk is multiplied (chunks are walked last to first)
@@ -576,26 +577,26 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
     float rw[UPT], ralpha = 1.0f;
     auto load = [&](int ci) {
         const int c = g * nCs + ci;
-        const size_t t0 = tokh + (size_t)c * L;
+        const size_t t0 = tokh + (size_t)c * L, ti0 = tinh + (size_t)c * L;
 #pragma unroll
         for (int u = 0; u < UPT; ++u) {
             const int idx = tid + u * SS_THREADS;
             if (idx < UNITS) {
                 const int row = idx / (SS_TILE / 8), c8 = 8 * (idx % (SS_TILE / 8));
-                rk[u] = *reinterpret_cast<const bf16x8*>(k + (t0 + row) * dqk + key0 + c8);
+                rk[u] = *reinterpret_cast<const bf16x8*>(k + (ti0 + row) * dqk + key0 + c8);
                 rv[u] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-                if (val0 + c8 < dv) rv[u] = *reinterpret_cast<const bf16x8*>(v + (t0 + row) * dv + val0 + c8);
+                if (val0 + c8 < dv) rv[u] = *reinterpret_cast<const bf16x8*>(v + (ti0 + row) * dv + val0 + c8);
                 rw[u] = ws.w[t0 + row];
             }
         }
         ralpha = ws.alpha[(size_t)bh * nC + c];
     };
 
-    f32x4 acc[2][2];
+    f32x4 acc[4][4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
+        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
 
     float A = 1.0f;          // product of alpha over the segment's chunks after the current one
     load(nCs - 1);
@@ -625,20 +626,20 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
 #pragma unroll
         for (int kk = 0; kk < L / 32; ++kk) {
             const int trow = 32 * kk + 8 * lg + (ln >> 2);
-            bf16x8 ka[2], vh[2], vl[2];
+            bf16x8 ka[4], vh[4], vl[4];
 #pragma unroll
-            for (int a = 0; a < 2; ++a) {
-                const bf16* kp = sk + trow * SS_P + 32 * wr + 16 * a + 4 * (ln & 3);
+            for (int a = 0; a < 4; ++a) {
+                const bf16* kp = sk + trow * SS_P + 64 * wr + 16 * a + 4 * (ln & 3);
                 ka[a] = cat(lds_read_tr(kp), lds_read_tr(kp + 4 * SS_P));
-                const bf16* vp = svh + trow * SS_P + 32 * wc + 16 * a + 4 * (ln & 3);
+                const bf16* vp = svh + trow * SS_P + 64 * wc + 16 * a + 4 * (ln & 3);
                 vh[a] = cat(lds_read_tr(vp), lds_read_tr(vp + 4 * SS_P));
-                const bf16* vq = svl + trow * SS_P + 32 * wc + 16 * a + 4 * (ln & 3);
+                const bf16* vq = svl + trow * SS_P + 64 * wc + 16 * a + 4 * (ln & 3);
                 vl[a] = cat(lds_read_tr(vq), lds_read_tr(vq + 4 * SS_P));
             }
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int b = 0; b < 2; ++b) {
+                for (int b = 0; b < 4; ++b) {
                     acc[a][b] = mfma(ka[a], vh[b], acc[a][b]);
                     acc[a][b] = mfma(ka[a], vl[b], acc[a][b]);
                 }
@@ -647,20 +648,21 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
     // dC_g into slot g + 1: rows of the D layout are keys, columns are values
     float* dst = ws.cst + ((size_t)bh * G + g + 1) * (size_t)dv * dqk;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int col = val0 + 32 * wc + 16 * b + ln;
+        for (int b = 0; b < 4; ++b) {
+            const int col = val0 + 64 * wc + 16 * b + ln;
             if (col < dv)
-                *reinterpret_cast<f32x4*>(dst + (size_t)col * dqk + key0 + 32 * wr + 16 * a + 4 * lg) = acc[a][b];
+                *reinterpret_cast<f32x4*>(dst + (size_t)col * dqk + key0 + 64 * wr + 16 * a + 4 * lg) = acc[a][b];
         }
 }
 
 constexpr int SC_THREADS = 256;
 constexpr int SC_MAXG = 64;
 
-// C'_start(g + 1) = A_g C'_start(g) + dC_g, in place over slots 1 .. G-1; slot 0 is
-// the caller's initial state (or zero).
+// C'_start(g + 1) = A_g C'_start(g) + dC_g, in place over slots 1 .. G-1; slot 0
+// receives a copy of the initial state (or zero), so no segment reads the
+// caller's buffer while another writes the final state.
 __global__ __launch_bounds__(SC_THREADS) void seg_combine_kernel(Ws ws, int nC, int G, int dqk, int dv,
                                                                  const float* __restrict__ C0)
 {
@@ -678,6 +680,7 @@ __global__ __launch_bounds__(SC_THREADS) void seg_combine_kernel(Ws ws, int nC, 
     if (e >= per) return;
     f32x4 c = C0 ? *reinterpret_cast<const f32x4*>(C0 + (size_t)bh * per + e) : f32x4{0, 0, 0, 0};
     float* base = ws.cst + (size_t)bh * G * per + e;
+    *reinterpret_cast<f32x4*>(base) = c;      // the first segment starts from slot 0
     for (int g = 0; g + 1 < G; ++g) {
         f32x4* slot = reinterpret_cast<f32x4*>(base + (size_t)(g + 1) * per);
         c = sA[g] * c + *slot;
@@ -853,7 +856,7 @@ __device__ __forceinline__ void chunk_store(const f32x4 (&reg)[Pref<C>::NCH], Sc
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
-    const float* __restrict__ o_pre, Ws ws, int S, int G, int dv, int n_vt, int remap,
+    const float* __restrict__ o_pre, Ws ws, int S, int Sx, int G, int dv, int n_vt, int remap,
     const float* __restrict__ C0,
     bf16* __restrict__ h, float* __restrict__ Cout, float* __restrict__ nout, float* __restrict__ mout)
 {
@@ -887,20 +890,21 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
     const bool active = act[0];
     const int nC = S / L / G;                      // chunks of this segment
 
-    const size_t tokh = (size_t)bh * S + (size_t)seg * (S / G);
+    const size_t tokh = (size_t)bh * S + (size_t)seg * (S / G);    // workspace token index
+    const size_t tinh = (size_t)bh * Sx + (size_t)seg * (S / G);   // input / output token index
     // state entering the segment: the caller's (or zero) for the first, else the chained one
-    const float* Cin = seg == 0 ? (C0 ? C0 + (size_t)bh * dv * DQ : nullptr)
-                                : ws.cst + ((size_t)bh * G + seg) * (size_t)dv * DQ;
-    const bf16* qh = q + tokh * DQ;
-    const bf16* kh = k + tokh * DQ;
-    bf16* hh = h + tokh * dv;
+    const float* Cin = G == 1 ? (C0 ? C0 + (size_t)bh * dv * DQ : nullptr)
+                              : ws.cst + ((size_t)bh * G + seg) * (size_t)dv * DQ;
+    const bf16* qh = q + tinh * DQ;
+    const bf16* kh = k + tinh * DQ;
+    bf16* hh = h + tinh * dv;
 
     auto chunk_src = [&](int c) {
         ChunkSrc cs;
         const size_t t0 = (size_t)c * L;
-        cs.v = v + (tokh + t0) * dv + vt * TV;
+        cs.v = v + (tinh + t0) * dv + vt * TV;
         cs.P = ws.P + 2 * (tokh + t0) * L;
-        cs.o = o_pre + (tokh + t0) * dv + vt * TV;
+        cs.o = o_pre + (tinh + t0) * dv + vt * TV;
         cs.sc = ws.a + tokh + t0;
         cs.hs = ws.hs;
         cs.vcols = min(TV, dv - vt * TV);
@@ -1120,7 +1124,7 @@ template <int L>
 hipError_t launch_prep(const FwdArgs& a, const Ws& w) {
     dim3 grid(a.S / L, a.B * a.NH);
     hipLaunchKernelGGL((chunk_prep_kernel<L>), grid, dim3(PREP_THREADS), 0, a.stream,
-                       (const bf16*)a.q, (const bf16*)a.k, a.i_pre, a.f_pre, a.S, a.dqk, w);
+                       (const bf16*)a.q, (const bf16*)a.k, a.i_pre, a.f_pre, a.S, a.Sx, a.dqk, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((gate_scan_kernel<L>), dim3((a.dqk + GS_COLS - 1) / GS_COLS, a.B * a.NH), dim3(GS_THREADS), 0, a.stream,
@@ -1128,7 +1132,7 @@ hipError_t launch_prep(const FwdArgs& a, const Ws& w) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((den_kernel<L>), dim3(a.S / L, a.B * a.NH), dim3(DEN_THREADS), 0, a.stream,
-                       (const bf16*)a.q, w, a.S, a.dqk);
+                       (const bf16*)a.q, w, a.S, a.Sx, a.dqk);
     return hipGetLastError();
 }
 
@@ -1140,6 +1144,7 @@ int segments(const FwdArgs& a) {
     const int units = a.B * a.NH * ((a.dv + C::TV - 1) / C::TV);
     const int nC = a.S / C::L;
     int G = 1;
+    if (a.dqk % SS_TILE != 0) return G;       // the segment-state tiles cover whole key blocks
     while (2 * G <= SC_MAXG && units * 2 * G <= 256 && nC % (2 * G) == 0 && nC / (2 * G) >= 4) G *= 2;
     return G;
 }
@@ -1151,7 +1156,7 @@ hipError_t launch_scan2(const FwdArgs& a, const Ws& w, int G) {
     if (G > 1) {
         dim3 sgrid((a.dqk / SS_TILE) * ((a.dv + SS_TILE - 1) / SS_TILE), G - 1, heads);
         hipLaunchKernelGGL((seg_state_kernel<L>), sgrid, dim3(SS_THREADS), 0, a.stream,
-                           (const bf16*)a.k, (const bf16*)a.v, w, a.S, a.dqk, a.dv, G);
+                           (const bf16*)a.k, (const bf16*)a.v, w, a.S, a.Sx, a.dqk, a.dv, G);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const size_t quads = (size_t)a.dv * a.dqk / 4;
@@ -1164,7 +1169,7 @@ hipError_t launch_scan2(const FwdArgs& a, const Ws& w, int G) {
     const int nwg = heads * G * n_vt;
     const int remap = (nwg % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL((chunk_scan2_kernel<C>), dim3(nwg), dim3(C::THREADS), 0, a.stream,
-                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.o_pre, w, a.S, G, a.dv, n_vt, remap,
+                       (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.o_pre, w, a.S, a.Sx, G, a.dv, n_vt, remap,
                        a.C0, (bf16*)a.h, a.C, a.n, a.m);
     return hipGetLastError();
 }

@@ -1,4 +1,6 @@
 // Chunkwise parallel forward of the mLSTM cell on the vector ALUs (fp32 math).
+// Also the tail kernel of a sequence whose length is not a multiple of the
+// chunk: the last chunk simply has fewer tokens.
 //
 // "xLSTM: Extended Long Short-Term Memory": section 2.3 (covariance update
 // eq. (18), normalizer with floor, parallel form of the recurrence), section 2.2
@@ -33,7 +35,7 @@ template <typename T, int L>
 __global__ __launch_bounds__(VALU_THREADS) void fwd_valu_kernel(
     const T* __restrict__ q, const T* __restrict__ k, const T* __restrict__ v,
     const float* __restrict__ i_pre, const float* __restrict__ f_pre,
-    const float* __restrict__ o_pre, int S, int dqk, int dv,
+    const float* __restrict__ o_pre, int S, int Sx, int t_begin, int dqk, int dv,
     const float* __restrict__ C0, const float* __restrict__ n0, const float* __restrict__ m0,
     T* __restrict__ h, float* __restrict__ C, float* __restrict__ n, float* __restrict__ m)
 {
@@ -48,13 +50,14 @@ __global__ __launch_bounds__(VALU_THREADS) void fwd_valu_kernel(
     const int r_begin = vt * VALU_TV;
     const int rows = min(VALU_TV, dv - r_begin);
 
-    const T* qh = q + (size_t)bh * S * dqk;
-    const T* kh = k + (size_t)bh * S * dqk;
-    const T* vh = v + (size_t)bh * S * dv;
-    const float* ih = i_pre + (size_t)bh * S;
-    const float* fh = f_pre + (size_t)bh * S;
-    const float* oh = o_pre + (size_t)bh * S * dv;
-    T* hh = h + (size_t)bh * S * dv;
+    // per-token tensors have Sx tokens per head; tokens [t_begin, S) are processed
+    const T* qh = q + (size_t)bh * Sx * dqk;
+    const T* kh = k + (size_t)bh * Sx * dqk;
+    const T* vh = v + (size_t)bh * Sx * dv;
+    const float* ih = i_pre + (size_t)bh * Sx;
+    const float* fh = f_pre + (size_t)bh * Sx;
+    const float* oh = o_pre + (size_t)bh * Sx * dv;
+    T* hh = h + (size_t)bh * Sx * dv;
     float* Ch = C + (size_t)bh * dv * dqk + (size_t)r_begin * dqk;
 
     // initial state
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(VALU_THREADS) void fwd_valu_kernel(
     double m_prev = m0 ? (double)m0[bh] : 0.0;
     __syncthreads();
 
-    for (int t0 = 0; t0 < S; t0 += L) {
+    for (int t0 = t_begin; t0 < S; t0 += L) {
         const int Lc = min(L, S - t0);
         // gates: log forget gate and its in-chunk cumulative sum
         if (tid < Lc) {
@@ -162,7 +165,7 @@ hipError_t launch_tl(const FwdArgs& a) {
     dim3 grid((a.dv + VALU_TV - 1) / VALU_TV, a.B * a.NH);
     hipLaunchKernelGGL((fwd_valu_kernel<T, L>), grid, dim3(VALU_THREADS), a.dqk * sizeof(float), a.stream,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, a.i_pre, a.f_pre, a.o_pre,
-                       a.S, a.dqk, a.dv, a.C0, a.n0, a.m0, (T*)a.h, a.C, a.n, a.m);
+                       a.S, a.Sx, a.t_begin, a.dqk, a.dv, a.C0, a.n0, a.m0, (T*)a.h, a.C, a.n, a.m);
     return hipGetLastError();
 }
 

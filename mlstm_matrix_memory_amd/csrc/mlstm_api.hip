@@ -43,8 +43,8 @@ mlstm_status check_dtype(mlstm_dtype dt) {
     return MLSTM_OK;
 }
 
-// validates everything except pointers and workspace; fills a (sizes only)
-mlstm_status check_fwd_sizes(int B, int NH, int S, int dqk, int dv, int chunk, mlstm_dtype dt) {
+// validates everything except pointers and workspace
+mlstm_status check_fwd_sizes(int B, int NH, int S, int dqk, int dv, int chunk, mlstm_dtype dt, bool ragged_ok) {
     if (B < 1 || NH < 1 || S < 1)
         return fail(MLSTM_ERR_INVALID_ARG, "B=%d, NH=%d, S=%d must all be >= 1", B, NH, S);
     mlstm_status s = check_dims(dqk, dv);
@@ -52,7 +52,7 @@ mlstm_status check_fwd_sizes(int B, int NH, int S, int dqk, int dv, int chunk, m
     if ((s = check_dtype(dt)) != MLSTM_OK) return s;
     if (chunk != 16 && chunk != 32 && chunk != 64 && chunk != 128)
         return fail(MLSTM_ERR_INVALID_ARG, "chunk=%d must be 16, 32, 64 or 128", chunk);
-    if (S % chunk != 0)
+    if (!ragged_ok && S % chunk != 0)
         return fail(MLSTM_ERR_INVALID_ARG, "S=%d is not a multiple of chunk=%d", S, chunk);
     const long long heads = (long long)B * NH;
     if (heads > 65535LL * 64)
@@ -65,13 +65,43 @@ mlstm_status check_fwd_sizes(int B, int NH, int S, int dqk, int dv, int chunk, m
 
 mlstm::FwdArgs make_fwd_args(int B, int NH, int S, int dqk, int dv, int chunk, mlstm_dtype dt) {
     mlstm::FwdArgs a = {};
-    a.B = B; a.NH = NH; a.S = S; a.dqk = dqk; a.dv = dv; a.chunk = chunk; a.dtype = dt;
+    a.B = B; a.NH = NH; a.S = S; a.Sx = S; a.t_begin = 0; a.dqk = dqk; a.dv = dv; a.chunk = chunk; a.dtype = dt;
     return a;
 }
 
-size_t fwd_ws_bytes(const mlstm::FwdArgs& a) {
-    if (a.dtype == MLSTM_BF16 && mlstm::mfma_fwd_supported(a)) return mlstm::mfma_fwd_workspace_bytes(a);
-    return mlstm::valu_fwd_workspace_bytes(a);
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// How a forward over S tokens runs: the longest multiple of the chunk on the bf16
+// MFMA path when it covers the shape, the rest (a ragged tail, or everything on
+// the fp32 path and on shapes the MFMA path does not cover) on the VALU kernel.
+// Between the two, the state passes through the workspace.
+struct FwdPlan {
+    int S_main;             // tokens on the MFMA path (0 = none)
+    bool tail;              // the VALU kernel runs over [S_main, S)
+    size_t main_bytes;      // workspace of the MFMA path
+    size_t mid_bytes;       // state handed from the MFMA path to the tail
+    size_t total() const { return align256(main_bytes) + mid_bytes; }
+};
+
+FwdPlan plan_fwd(int B, int NH, int S, int dqk, int dv, int chunk, mlstm_dtype dt) {
+    FwdPlan pl = {};
+    const int S_main = S - S % chunk;
+    mlstm::FwdArgs a = make_fwd_args(B, NH, S_main, dqk, dv, chunk, dt);
+    if (S_main > 0 && dt == MLSTM_BF16 && mlstm::mfma_fwd_supported(a)) {
+        pl.S_main = S_main;
+        pl.main_bytes = mlstm::mfma_fwd_workspace_bytes(a);
+    }
+    pl.tail = pl.S_main < S;
+    if (pl.tail && pl.S_main > 0) {
+        const size_t heads = (size_t)B * NH;
+        pl.mid_bytes = align256(heads * dv * dqk * 4) + align256(heads * dqk * 4) + align256(heads * 4);
+    }
+    return pl;
+}
+
+bool overlaps(const void* p, size_t pb, const void* q, size_t qb) {
+    const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+    return a < b + qb && b < a + pb;
 }
 
 }  // namespace
@@ -79,17 +109,20 @@ size_t fwd_ws_bytes(const mlstm::FwdArgs& a) {
 extern "C" {
 
 size_t mlstm_fwd_workspace_bytes(int B, int NH, int S, int d_qk, int d_v, int chunk, mlstm_dtype dtype) {
-    if (check_fwd_sizes(B, NH, S, d_qk, d_v, chunk, dtype) != MLSTM_OK) return 0;
-    return fwd_ws_bytes(make_fwd_args(B, NH, S, d_qk, d_v, chunk, dtype));
+    if (check_fwd_sizes(B, NH, S, d_qk, d_v, chunk, dtype, true) != MLSTM_OK) return 0;
+    return plan_fwd(B, NH, S, d_qk, d_v, chunk, dtype).total();
 }
 
-// Validates the forward's arguments and fills a; stage bits: 1 = prepare, 2 = scan.
+// Validates the forward's arguments and launches it; stage bits: 1 = prepare, 2 = scan
+// (the staged entry points require S to be a multiple of chunk and the zero initial state).
 static mlstm_status fwd_common(const void* q, const void* k, const void* v,
                                const float* i_pre, const float* f_pre, const float* o_pre,
                                int B, int NH, int S, int d_qk, int d_v, int chunk, mlstm_dtype dtype,
+                               const float* C_init, const float* n_init, const float* m_init,
                                void* h_out, float* C_final, float* n_final, float* m_final,
-                               void* workspace, size_t workspace_bytes, void* stream, int stages) {
-    mlstm_status s = check_fwd_sizes(B, NH, S, d_qk, d_v, chunk, dtype);
+                               void* workspace, size_t workspace_bytes, void* stream, int stages,
+                               bool ragged_ok) {
+    mlstm_status s = check_fwd_sizes(B, NH, S, d_qk, d_v, chunk, dtype, ragged_ok);
     if (s != MLSTM_OK) return s;
     // tensors read or written with vector accesses need 16-byte alignment, the others their element size
     const void* ptrs[] = {q, k, v, i_pre, f_pre, o_pre, h_out, C_final, n_final, m_final};
@@ -103,24 +136,57 @@ static mlstm_status fwd_common(const void* q, const void* k, const void* v,
         if (!aligned(ptrs[p], align[p]))
             return fail(MLSTM_ERR_INVALID_ARG, "%s is not %u-byte aligned", names[p], align[p]);
     }
-    mlstm::FwdArgs a = make_fwd_args(B, NH, S, d_qk, d_v, chunk, dtype);
-    a.q = q; a.k = k; a.v = v; a.i_pre = i_pre; a.f_pre = f_pre; a.o_pre = o_pre;
-    a.h = h_out; a.C = C_final; a.n = n_final; a.m = m_final;
-    a.C0 = nullptr; a.n0 = nullptr; a.m0 = nullptr;
-    const size_t need = fwd_ws_bytes(a);
+    const size_t heads = (size_t)B * NH;
+    const int given = (C_init != nullptr) + (n_init != nullptr) + (m_init != nullptr);
+    if (given != 0 && given != 3)
+        return fail(MLSTM_ERR_INVALID_ARG, "C_init, n_init and m_init must be given together (or all NULL)");
+    if (given == 3) {
+        if (!aligned16(C_init)) return fail(MLSTM_ERR_INVALID_ARG, "C_init is not 16-byte aligned");
+        if (!aligned(n_init, 4) || !aligned(m_init, 4))
+            return fail(MLSTM_ERR_INVALID_ARG, "n_init / m_init are not 4-byte aligned");
+        const void* in[] = {C_init, n_init, m_init};
+        const size_t inb[] = {heads * d_v * d_qk * 4, heads * d_qk * 4, heads * 4};
+        const void* out[] = {C_final, n_final, m_final};
+        for (int i = 0; i < 3; ++i)
+            for (int o = 0; o < 3; ++o)
+                if (overlaps(in[i], inb[i], out[o], inb[o]))
+                    return fail(MLSTM_ERR_INVALID_ARG, "the initial state overlaps the final state");
+    }
+    const FwdPlan pl = plan_fwd(B, NH, S, d_qk, d_v, chunk, dtype);
+    const size_t need = pl.total();
     if (need > 0) {
         if (!workspace || workspace_bytes < need)
             return fail(MLSTM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
         if (!aligned16(workspace)) return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
     }
-    a.ws = workspace; a.ws_bytes = workspace_bytes;
-    a.stream = reinterpret_cast<hipStream_t>(stream);
-    const bool two_stage = dtype == MLSTM_BF16 && mlstm::mfma_fwd_supported(a);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    if (two_stage) {
+    // state handed from the MFMA part to the tail, in the workspace after the MFMA part's own
+    float* C_mid = nullptr; float* n_mid = nullptr; float* m_mid = nullptr;
+    if (pl.mid_bytes > 0) {
+        char* base = (char*)workspace + align256(pl.main_bytes);
+        C_mid = (float*)base;
+        n_mid = (float*)(base + align256(heads * d_v * d_qk * 4));
+        m_mid = (float*)(base + align256(heads * d_v * d_qk * 4) + align256(heads * d_qk * 4));
+    }
+    if (pl.S_main > 0) {
+        mlstm::FwdArgs a = make_fwd_args(B, NH, pl.S_main, d_qk, d_v, chunk, dtype);
+        a.Sx = S;
+        a.q = q; a.k = k; a.v = v; a.i_pre = i_pre; a.f_pre = f_pre; a.o_pre = o_pre; a.h = h_out;
+        a.C = pl.tail ? C_mid : C_final; a.n = pl.tail ? n_mid : n_final; a.m = pl.tail ? m_mid : m_final;
+        a.C0 = C_init; a.n0 = n_init; a.m0 = m_init;
+        a.ws = workspace; a.ws_bytes = pl.main_bytes; a.stream = st;
         if (stages & 1) e = mlstm::launch_fwd_mfma_prepare(a);
         if (e == hipSuccess && (stages & 2)) e = mlstm::launch_fwd_mfma_scan(a);
-    } else if (stages & 2) {
+    }
+    if (e == hipSuccess && pl.tail && (stages & 2)) {
+        mlstm::FwdArgs a = make_fwd_args(B, NH, S, d_qk, d_v, chunk, dtype);
+        a.t_begin = pl.S_main;
+        a.q = q; a.k = k; a.v = v; a.i_pre = i_pre; a.f_pre = f_pre; a.o_pre = o_pre; a.h = h_out;
+        a.C = C_final; a.n = n_final; a.m = m_final;
+        if (pl.S_main > 0) { a.C0 = C_mid; a.n0 = n_mid; a.m0 = m_mid; }
+        else { a.C0 = C_init; a.n0 = n_init; a.m0 = m_init; }
+        a.stream = st;
         e = mlstm::launch_fwd_valu(a);
     }
     if (e != hipSuccess) return fail(MLSTM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -133,15 +199,26 @@ mlstm_status mlstm_fwd_parallel(const void* q, const void* k, const void* v,
                                 mlstm_dtype dtype,
                                 void* h_out, float* C_final, float* n_final, float* m_final,
                                 void* workspace, size_t workspace_bytes, void* stream) {
-    return fwd_common(q, k, v, i_pre, f_pre, o_pre, B, NH, S, d_qk, d_v, chunk, dtype,
-                      h_out, C_final, n_final, m_final, workspace, workspace_bytes, stream, 3);
+    return fwd_common(q, k, v, i_pre, f_pre, o_pre, B, NH, S, d_qk, d_v, chunk, dtype, nullptr, nullptr, nullptr,
+                      h_out, C_final, n_final, m_final, workspace, workspace_bytes, stream, 3, false);
+}
+
+mlstm_status mlstm_fwd_parallel_state(const void* q, const void* k, const void* v,
+                                      const float* i_pre, const float* f_pre, const float* o_pre,
+                                      int B, int NH, int S, int d_qk, int d_v, int chunk,
+                                      mlstm_dtype dtype,
+                                      const float* C_init, const float* n_init, const float* m_init,
+                                      void* h_out, float* C_final, float* n_final, float* m_final,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    return fwd_common(q, k, v, i_pre, f_pre, o_pre, B, NH, S, d_qk, d_v, chunk, dtype, C_init, n_init, m_init,
+                      h_out, C_final, n_final, m_final, workspace, workspace_bytes, stream, 3, true);
 }
 
 mlstm_status mlstm_fwd_prepare(const void* q, const void* k, const float* i_pre, const float* f_pre,
                                int B, int NH, int S, int d_qk, int d_v, int chunk, mlstm_dtype dtype,
                                void* workspace, size_t workspace_bytes, void* stream) {
-    return fwd_common(q, k, nullptr, i_pre, f_pre, nullptr, B, NH, S, d_qk, d_v, chunk, dtype,
-                      nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream, 1);
+    return fwd_common(q, k, nullptr, i_pre, f_pre, nullptr, B, NH, S, d_qk, d_v, chunk, dtype, nullptr, nullptr,
+                      nullptr, nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream, 1, false);
 }
 
 mlstm_status mlstm_fwd_scan(const void* q, const void* k, const void* v,
@@ -149,8 +226,8 @@ mlstm_status mlstm_fwd_scan(const void* q, const void* k, const void* v,
                             int B, int NH, int S, int d_qk, int d_v, int chunk, mlstm_dtype dtype,
                             void* h_out, float* C_final, float* n_final, float* m_final,
                             void* workspace, size_t workspace_bytes, void* stream) {
-    return fwd_common(q, k, v, i_pre, f_pre, o_pre, B, NH, S, d_qk, d_v, chunk, dtype,
-                      h_out, C_final, n_final, m_final, workspace, workspace_bytes, stream, 2);
+    return fwd_common(q, k, v, i_pre, f_pre, o_pre, B, NH, S, d_qk, d_v, chunk, dtype, nullptr, nullptr, nullptr,
+                      h_out, C_final, n_final, m_final, workspace, workspace_bytes, stream, 2, false);
 }
 
 mlstm_status mlstm_step(const void* q, const void* k, const void* v,

@@ -64,6 +64,8 @@ struct FwdArgs {
     const void* q; const void* k; const void* v;
     const float* i_pre; const float* f_pre; const float* o_pre;
     int B, NH, S, dqk, dv, chunk;
+    int Sx;                 // token stride of the caller's per-token tensors (>= S)
+    int t_begin;            // first token processed (fp32 / tail kernel); tokens [t_begin, S)
     mlstm_dtype dtype;
     void* h; float* C; float* n; float* m;
     const float* C0; const float* n0; const float* m0;   // initial state, all null = zero

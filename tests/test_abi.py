@@ -21,8 +21,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = b.header_symbols()
-    assert {"mlstm_fwd_parallel", "mlstm_fwd_prepare", "mlstm_fwd_scan", "mlstm_step",
-            "mlstm_fwd_workspace_bytes", "mlstm_status_string", "mlstm_error_detail"} <= set(names)
+    assert {"mlstm_fwd_parallel", "mlstm_fwd_parallel_state", "mlstm_fwd_prepare", "mlstm_fwd_scan",
+            "mlstm_step", "mlstm_fwd_workspace_bytes", "mlstm_status_string", "mlstm_error_detail"} <= set(names)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in include/mlstm.h but not exported"
 
@@ -82,7 +82,43 @@ def test_fwd_rejects_small_workspace(lib):
 
 def test_workspace_bytes_is_zero_for_rejected_args():
     assert b.mlstm_fwd_workspace_bytes(0, 1, 64, 32, 32, 16, b.MLSTM_BF16) == 0
-    assert b.mlstm_fwd_workspace_bytes(1, 1, 60, 32, 32, 16, b.MLSTM_BF16) == 0
+    assert b.mlstm_fwd_workspace_bytes(1, 1, 64, 32, 32, 48, b.MLSTM_BF16) == 0
+    assert b.mlstm_fwd_workspace_bytes(1, 1, 64, 24, 32, 16, b.MLSTM_BF16) == 0
+
+
+def test_workspace_of_a_ragged_sequence_holds_the_handover_state():
+    # a sequence that is not a multiple of the chunk runs its last tokens after the
+    # MFMA part; the state between the two lives in the workspace
+    whole = b.mlstm_fwd_workspace_bytes(8, 4, 1984, 384, 384, 64, b.MLSTM_BF16)
+    ragged = b.mlstm_fwd_workspace_bytes(8, 4, 2000, 384, 384, 64, b.MLSTM_BF16)
+    assert whole > 0
+    assert ragged >= whole + 8 * 4 * 384 * 384 * 4
+
+
+def _fwd_state(lib, init, S=64, chunk=16, dt=b.MLSTM_F32, outs=(FAKE, FAKE, FAKE)):
+    p = [FAKE] * 7
+    return lib.mlstm_fwd_parallel_state(p[0], p[1], p[2], p[3], p[4], p[5], 1, 1, S, 32, 32, chunk, dt,
+                                        init[0], init[1], init[2], p[6], outs[0], outs[1], outs[2], None, 0, None)
+
+
+def test_state_forward_needs_all_or_none_of_the_initial_state(lib):
+    for init in ((FAKE, None, None), (None, FAKE, FAKE), (FAKE, FAKE, None)):
+        assert _fwd_state(lib, init) == b.MLSTM_ERR_INVALID_ARG
+        assert "together" in b.mlstm_error_detail()
+
+
+def test_state_forward_rejects_overlapping_state(lib):
+    init = (0x100000, 0x200000, 0x300000)
+    outs = (0x400000, 0x200000 + 64, 0x500000)      # n_final inside n_init
+    assert _fwd_state(lib, init, outs=outs) == b.MLSTM_ERR_INVALID_ARG
+    assert "overlaps" in b.mlstm_error_detail()
+
+
+def test_only_the_state_forward_accepts_a_ragged_sequence(lib):
+    assert _fwd(lib, S=100, chunk=64) == b.MLSTM_ERR_INVALID_ARG
+    # the state forward passes size validation for S=100 and stops at the next check
+    assert _fwd_state(lib, (FAKE, None, None), S=100, chunk=64) == b.MLSTM_ERR_INVALID_ARG
+    assert "together" in b.mlstm_error_detail()
 
 
 @pytest.mark.parametrize("kw,detail", [
@@ -109,8 +145,8 @@ def test_step_rejects_null_state(lib):
 
 def test_binding_has_same_names_as_abi():
     import mlstm_matrix_memory_amd as pkg
-    for name in ("mlstm_fwd_parallel", "mlstm_fwd_prepare", "mlstm_fwd_scan", "mlstm_step",
-                 "mlstm_fwd_workspace_bytes", "mlstm_status_string", "mlstm_error_detail"):
+    for name in ("mlstm_fwd_parallel", "mlstm_fwd_parallel_state", "mlstm_fwd_prepare", "mlstm_fwd_scan",
+                 "mlstm_step", "mlstm_fwd_workspace_bytes", "mlstm_status_string", "mlstm_error_detail"):
         assert callable(getattr(pkg, name))
 
 
