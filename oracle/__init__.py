@@ -40,6 +40,8 @@ def _bind(lib):
     lib.oracle_fwd_f64.argtypes = [dp] * 6 + [ctypes.c_int] * 5 + [dp] * 3 + [dp] * 4
     lib.oracle_step_f64.restype = ctypes.c_int
     lib.oracle_step_f64.argtypes = [dp] * 6 + [ctypes.c_int] * 4 + [dp] * 4
+    lib.oracle_bwd_f64.restype = ctypes.c_int
+    lib.oracle_bwd_f64.argtypes = [dp] * 7 + [ctypes.c_int] * 5 + [dp] * 6
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     return lib
@@ -120,6 +122,24 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_step_f64 rejected its arguments")
         return h, C, n, m
+
+    def bwd(self, q, k, v, i_pre, f_pre, o_pre, dh):
+        """Gradients of the zero-state forward w.r.t. (q, k, v, i_pre, f_pre, o_pre) given dh.
+
+        Shapes as fwd; dh like h.  Returns (dq, dk, dv, di, df, do) in fp64.
+        """
+        q, k, v, i_pre, f_pre, o_pre, dh = map(_f64, (q, k, v, i_pre, f_pre, o_pre, dh))
+        B, NH, S, dqk = q.shape
+        dv = v.shape[-1]
+        assert k.shape == q.shape and v.shape == (B, NH, S, dv) and dh.shape == (B, NH, S, dv)
+        assert i_pre.shape == (B, NH, S) and f_pre.shape == (B, NH, S) and o_pre.shape == (B, NH, S, dv)
+        out = [np.empty_like(q), np.empty_like(k), np.empty_like(v), np.empty_like(i_pre),
+               np.empty_like(f_pre), np.empty_like(o_pre)]
+        rc = self.lib.oracle_bwd_f64(_ptr(q), _ptr(k), _ptr(v), _ptr(i_pre), _ptr(f_pre), _ptr(o_pre), _ptr(dh),
+                                     B, NH, S, dqk, dv, *[_ptr(a) for a in out])
+        if rc != 0:
+            raise ValueError("oracle_bwd_f64 rejected its arguments")
+        return tuple(out)
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())

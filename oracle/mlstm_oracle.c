@@ -164,6 +164,119 @@ int oracle_step_f64(const double *q, const double *k, const double *v,
     return 0;
 }
 
+/*
+ * Gradients of the forward from the zero state with respect to every input,
+ * given the gradient dh of a loss that depends on h only (the final state is
+ * not differentiated).
+ *
+ * Derivative of the quadratic parallel form of the recurrence (section 2.3:
+ * the recurrence and its parallel form; section 2.2: the stabilizer leaves h
+ * unchanged, so no gradient flows through it).  Per head, with
+ *   F_t    = sum_{j<=t} log sigmoid(f~_j)
+ *   D_ts   = exp(F_t - F_s + i~_s)          (s <= t; 0 otherwise)
+ *   S_ts   = q_t . k_s
+ *   num_t  = sum_s D_ts S_ts v_s,   den_t = sum_s D_ts S_ts
+ *   N_t    = max(|den_t|, 1),       g_t = sigmoid(o~_t),   u_t = num_t / N_t
+ *   h_t    = g_t (.) u_t
+ * the chain rule gives
+ *   do~_t  = dh_t (.) u_t (.) g_t (.) (1 - g_t)
+ *   dnum_t = dh_t (.) g_t / N_t
+ *   dden_t = -sign(den_t) (dh_t (.) g_t) . num_t / N_t^2   if |den_t| > 1, else 0
+ *   dA_ts  = dnum_t . v_s + dden_t                  (A_ts = D_ts S_ts)
+ *   dv_s   = sum_{t>=s} D_ts S_ts dnum_t
+ *   dq_t   = sum_{s<=t} dA_ts D_ts k_s,   dk_s = sum_{t>=s} dA_ts D_ts q_t
+ *   dlogD_ts = dA_ts D_ts S_ts:  di~_s = sum_t dlogD_ts,  dF_t += sum_s dlogD_ts,
+ *                                dF_s -= sum_t dlogD_ts
+ *   dlf_j  = sum_{t>=j} dF_t,    df~_j = dlf_j sigmoid(-f~_j)
+ * in fp64, unstabilized (the test inputs keep every exponent far from overflow).
+ * Layouts as oracle_fwd_f64; dh like h; outputs like their inputs.
+ * Returns 0, or -1 on a bad argument.
+ */
+int oracle_bwd_f64(const double *q, const double *k, const double *v,
+                   const double *i_pre, const double *f_pre, const double *o_pre, const double *dh,
+                   int B, int NH, int S, int dqk, int dv,
+                   double *dq, double *dk, double *dvv, double *di, double *df, double *dout)
+{
+    if (B < 0 || NH < 0 || S < 0 || dqk <= 0 || dv <= 0)
+        return -1;
+    if (!q || !k || !v || !i_pre || !f_pre || !o_pre || !dh || !dq || !dk || !dvv || !di || !df || !dout)
+        return -1;
+    const int heads = B * NH;
+
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < heads; ++bh) {
+        const size_t t0 = (size_t)bh * S;
+        const double *qh = q + t0 * dqk, *kh = k + t0 * dqk, *vh = v + t0 * dv;
+        const double *ih = i_pre + t0, *fh = f_pre + t0, *oh = o_pre + t0 * dv, *dhh = dh + t0 * dv;
+        double *dqh = dq + t0 * dqk, *dkh = dk + t0 * dqk, *dvh = dvv + t0 * dv;
+        double *dih = di + t0, *dfh = df + t0, *doh = dout + t0 * dv;
+        double *F = malloc(sizeof(double) * S), *dF = calloc(S, sizeof(double));
+        double *Smat = malloc(sizeof(double) * (size_t)S * S), *Dmat = malloc(sizeof(double) * (size_t)S * S);
+        double *num = calloc((size_t)S * dv, sizeof(double)), *den = calloc(S, sizeof(double));
+        double *dnum = malloc(sizeof(double) * (size_t)S * dv), *dden = malloc(sizeof(double) * S);
+        double acc = 0.0;
+        for (int t = 0; t < S; ++t) {
+            acc += log_sigmoid(fh[t]);
+            F[t] = acc;
+        }
+        /* forward: scores, decay, numerator and denominator */
+        for (int t = 0; t < S; ++t)
+            for (int s = 0; s <= t; ++s) {
+                double dot = 0.0;
+                for (int j = 0; j < dqk; ++j) dot += qh[(size_t)t * dqk + j] * kh[(size_t)s * dqk + j];
+                const double d = exp(F[t] - F[s] + ih[s]);
+                Smat[(size_t)t * S + s] = dot;
+                Dmat[(size_t)t * S + s] = d;
+                for (int r = 0; r < dv; ++r) num[(size_t)t * dv + r] += d * dot * vh[(size_t)s * dv + r];
+                den[t] += d * dot;
+            }
+        /* output gate and normalizer */
+        for (int t = 0; t < S; ++t) {
+            const double N = fmax(fabs(den[t]), 1.0);
+            double dun = 0.0;
+            for (int r = 0; r < dv; ++r) {
+                const size_t e = (size_t)t * dv + r;
+                const double g = sigmoid(oh[e]);
+                const double u = num[e] / N;
+                doh[e] = dhh[e] * u * g * (1.0 - g);
+                dnum[e] = dhh[e] * g / N;
+                dun += dhh[e] * g * num[e];
+            }
+            dden[t] = fabs(den[t]) > 1.0 ? -(den[t] > 0 ? 1.0 : -1.0) * dun / (N * N) : 0.0;
+        }
+        /* scores, keys, values and the log-decay */
+        memset(dqh, 0, sizeof(double) * (size_t)S * dqk);
+        memset(dkh, 0, sizeof(double) * (size_t)S * dqk);
+        memset(dvh, 0, sizeof(double) * (size_t)S * dv);
+        memset(dih, 0, sizeof(double) * S);
+        for (int t = 0; t < S; ++t)
+            for (int s = 0; s <= t; ++s) {
+                const double d = Dmat[(size_t)t * S + s], sc = Smat[(size_t)t * S + s];
+                double dA = dden[t];
+                for (int r = 0; r < dv; ++r) {
+                    dA += dnum[(size_t)t * dv + r] * vh[(size_t)s * dv + r];
+                    dvh[(size_t)s * dv + r] += d * sc * dnum[(size_t)t * dv + r];
+                }
+                for (int j = 0; j < dqk; ++j) {
+                    dqh[(size_t)t * dqk + j] += dA * d * kh[(size_t)s * dqk + j];
+                    dkh[(size_t)s * dqk + j] += dA * d * qh[(size_t)t * dqk + j];
+                }
+                const double dl = dA * d * sc;
+                dih[s] += dl;
+                dF[t] += dl;
+                dF[s] -= dl;
+            }
+        /* forget gate: reverse cumulative sum, then through log sigmoid */
+        double rev = 0.0;
+        for (int j = S - 1; j >= 0; --j) {
+            rev += dF[j];
+            dfh[j] = rev * sigmoid(-fh[j]);
+        }
+        free(F); free(dF); free(Smat); free(Dmat); free(num); free(den); free(dnum); free(dden);
+    }
+    return 0;
+}
+
 /* Number of OpenMP threads a parallel region of the oracle would use. */
 int oracle_num_threads(void)
 {

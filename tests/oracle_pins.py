@@ -18,6 +18,11 @@ equality the pages or plain algebra guarantee:
   associative retrieval (section 2.3, the bidirectional associative memory
   setting: a stored value is retrieved by a later query along its key);
 * head independence (section 2.3: no memory mixing across heads).
+
+The backward (``Oracle.bwd``, the derivative of the quadratic form written out)
+is pinned against central finite differences of the *recurrent* forward -- a
+different formulation -- in both regimes of the normalizer floor, and by its
+linearity in the incoming gradient.
 """
 from __future__ import annotations
 
@@ -330,6 +335,71 @@ def pin_step_continues_fwd(orc):
     _close(ns, n, rtol=1e-13, what="n after steps")
     _close(ms, m, rtol=1e-13, what="m after steps")
 
+
+def _fd_case(seed, i_shift, S=7, dqk=4, dv=3, B=1, NH=2):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, NH, S, dqk))
+    k = rng.standard_normal((B, NH, S, dqk)) / 2
+    v = rng.standard_normal((B, NH, S, dv))
+    i = rng.standard_normal((B, NH, S)) + i_shift
+    f = 2.0 * rng.standard_normal((B, NH, S)) + 1.0
+    o = rng.standard_normal((B, NH, S, dv))
+    dh = rng.standard_normal((B, NH, S, dv))
+    return [q, k, v, i, f, o], dh
+
+
+def _finite_differences(orc, args, dh, eps=1e-6):
+    """Central differences of sum(dh * h) through the recurrent forward, every input element."""
+    def loss(a):
+        return float(np.sum(orc.fwd(*a)[0] * dh))
+    grads = []
+    for ai in range(len(args)):
+        g = np.zeros_like(args[ai])
+        for idx in np.ndindex(*args[ai].shape):
+            a = [x.copy() for x in args]
+            a[ai][idx] += eps
+            up = loss(a)
+            a[ai][idx] -= 2 * eps
+            g[idx] = (up - loss(a)) / (2 * eps)
+        grads.append(g)
+    return grads
+
+
+def _check_bwd_fd(orc, i_shift, seed):
+    args, dh = _fd_case(seed, i_shift)
+    got = orc.bwd(*args, dh)
+    want = _finite_differences(orc, args, dh)
+    for name, g, w in zip(("dq", "dk", "dv", "di", "df", "do"), got, want):
+        scale = max(float(np.max(np.abs(w))), 1e-12)
+        err = float(np.max(np.abs(g - w))) / scale
+        assert err < 1e-5, f"{name}: backward differs from finite differences by {err:.2e}"
+
+
+def pin_bwd_finite_differences_floor_inactive(orc):
+    # large input gates: |n . q| far above the floor, so the normalizer's derivative is live
+    _check_bwd_fd(orc, i_shift=4.0, seed=71)
+
+
+def pin_bwd_finite_differences_floor_active(orc):
+    # very negative input gates: the floor max(|n . q|, 1) is active everywhere
+    _check_bwd_fd(orc, i_shift=-6.0, seed=72)
+
+
+def pin_bwd_linear_in_dh(orc):
+    args, dh = _fd_case(73, 1.0, S=9)
+    rng = np.random.default_rng(74)
+    dh2 = rng.standard_normal(dh.shape)
+    g1, g2 = orc.bwd(*args, dh), orc.bwd(*args, dh2)
+    g12 = orc.bwd(*args, 2.0 * dh - 3.0 * dh2)
+    for a, b, c in zip(g1, g2, g12):
+        _close(c, 2.0 * a - 3.0 * b, rtol=1e-11, what="linearity in dh")
+
+
+BWD_PINS = [
+    pin_bwd_finite_differences_floor_inactive,
+    pin_bwd_finite_differences_floor_active,
+    pin_bwd_linear_in_dh,
+]
 
 ALL_PINS = [
     pin_stabilizer_invariance,

@@ -10,7 +10,7 @@ import os
 import pytest
 
 import oracle
-from oracle_pins import ALL_PINS
+from oracle_pins import ALL_PINS, BWD_PINS
 
 MUTANTS = {
     "forget_gate_dropped_on_C": (
@@ -55,6 +55,28 @@ MUTANTS = {
     "head_stride": (
         "double *Cb = C + (size_t)bh * dv * dqk;",
         "double *Cb = C + (size_t)bh * dqk;"),
+    # backward
+    "bwd_normalizer_sign": (
+        "dden[t] = fabs(den[t]) > 1.0 ? -(den[t] > 0 ? 1.0 : -1.0) * dun / (N * N) : 0.0;",
+        "dden[t] = fabs(den[t]) > 1.0 ? (den[t] > 0 ? 1.0 : -1.0) * dun / (N * N) : 0.0;"),
+    "bwd_floor_ignored": (
+        "dden[t] = fabs(den[t]) > 1.0 ? -(den[t] > 0 ? 1.0 : -1.0) * dun / (N * N) : 0.0;",
+        "dden[t] = -(den[t] > 0 ? 1.0 : -1.0) * dun / (N * N);"),
+    "bwd_output_gate_derivative": (
+        "doh[e] = dhh[e] * u * g * (1.0 - g);",
+        "doh[e] = dhh[e] * u * g;"),
+    "bwd_value_grad_without_score": (
+        "dvh[(size_t)s * dv + r] += d * sc * dnum[(size_t)t * dv + r];",
+        "dvh[(size_t)s * dv + r] += d * dnum[(size_t)t * dv + r];"),
+    "bwd_key_side_decay_dropped": (
+        "                dF[s] -= dl;\n",
+        ""),
+    "bwd_forget_cumsum_forward": (
+        "for (int j = S - 1; j >= 0; --j) {",
+        "for (int j = 0; j < S; ++j) {"),
+    "bwd_log_sigmoid_derivative": (
+        "dfh[j] = rev * sigmoid(-fh[j]);",
+        "dfh[j] = rev * sigmoid(fh[j]);"),
 }
 
 
@@ -69,7 +91,7 @@ def test_mutant_is_caught(name, tmp_path):
     oracle.build(str(mutated), lib_path)
     orc = oracle.Oracle(oracle.load(lib_path))
     failed = []
-    for pin in ALL_PINS:
+    for pin in ALL_PINS + BWD_PINS:
         try:
             pin(orc)
         except (AssertionError, FloatingPointError, ValueError):
