@@ -183,6 +183,51 @@ mlstm_status mlstm_step(const void *q, const void *k, const void *v,
                         int B, int NH, int d_qk, int d_v, mlstm_dtype dtype,
                         float *C, float *n, float *m, void *h_out, void *stream);
 
+/*
+ * Bytes of device workspace mlstm_bwd_parallel needs for these sizes (0 for
+ * arguments it would reject).
+ */
+size_t mlstm_bwd_workspace_bytes(int B, int NH, int S, int d_qk, int d_v, mlstm_dtype dtype);
+
+/*
+ * Gradients of the forward from the zero state (what mlstm_fwd_parallel computes
+ * for h_out) with respect to all six inputs, given the gradient dh of a loss with
+ * respect to h_out.  Section 2.3 (the parallel form of the cell, which is what is
+ * differentiated) and section 2.2 (the stabilizer m_t changes no output, so no
+ * gradient flows through it; the gradients are computed in the stabilized
+ * quantities and are those of the unstabilized cell).
+ *
+ * With F_t the cumulative log forget gate and D_ts = exp(F_t - F_s + i~_s) for
+ * s <= t, the forward is h_t = sigmoid(o~_t) (.) num_t / max(|den_t|, 1) with
+ * num_t = sum_s D_ts (q_t . k_s) v_s and den_t = sum_s D_ts (q_t . k_s).  Where
+ * the floor is active (|den_t| <= 1) den_t receives no gradient.
+ *
+ * Arguments
+ *   q, k, v, i_pre, f_pre, o_pre
+ *                   the forward's inputs, layouts and dtype as for the forward
+ *                   (read only)
+ *   dh              [B,NH,S,d_v] dtype, gradient with respect to h_out (read only)
+ *   B, NH, S        >= 1; S need not be a multiple of anything
+ *   d_qk, d_v       multiples of 16, <= 4096
+ *   dtype           MLSTM_F32 or MLSTM_BF16 (of q, k, v and dh)
+ *   grad_q, grad_k  [B,NH,S,d_qk] fp32, written
+ *   grad_v          [B,NH,S,d_v] fp32, written
+ *   grad_i, grad_f  [B,NH,S] fp32, written (gradients w.r.t. i_pre and f_pre)
+ *   grad_o          [B,NH,S,d_v] fp32, written (gradient w.r.t. o_pre)
+ *   workspace       device buffer of at least mlstm_bwd_workspace_bytes(...)
+ *                   bytes, 16-byte aligned; contents on entry do not matter
+ *   stream          hipStream_t or NULL
+ * Every pointer must be 16-byte aligned except i_pre, f_pre, grad_i, grad_f
+ * (4 bytes).  Outputs must not alias inputs, the workspace or each other.
+ */
+mlstm_status mlstm_bwd_parallel(const void *q, const void *k, const void *v,
+                                const float *i_pre, const float *f_pre, const float *o_pre,
+                                const void *dh,
+                                int B, int NH, int S, int d_qk, int d_v, mlstm_dtype dtype,
+                                float *grad_q, float *grad_k, float *grad_v,
+                                float *grad_i, float *grad_f, float *grad_o,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static description of a status code. */
 const char *mlstm_status_string(mlstm_status status);
 

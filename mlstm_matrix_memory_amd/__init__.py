@@ -7,6 +7,8 @@ Entry points (same names as include/mlstm.h):
   mlstm_fwd_prepare, mlstm_fwd_scan
                       the two stages of mlstm_fwd_parallel, for callers that schedule them apart
   mlstm_step          one-token recurrent decode step, state updated in place
+  mlstm_bwd_parallel  gradients of the zero-state forward with respect to all inputs
+  mlstm_bwd_workspace_bytes
   mlstm_fwd_workspace_bytes, mlstm_status_string, mlstm_error_detail
 """
 from .binding import (  # noqa: F401
@@ -14,6 +16,8 @@ from .binding import (  # noqa: F401
     MLSTM_F32,
     MlstmError,
     load_library,
+    mlstm_bwd_parallel,
+    mlstm_bwd_workspace_bytes,
     mlstm_error_detail,
     mlstm_fwd_parallel,
     mlstm_fwd_parallel_state,

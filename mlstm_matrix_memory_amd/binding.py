@@ -59,6 +59,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mlstm_fwd_scan.restype = i
     lib.mlstm_fwd_scan.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, i,
                                    vp, fp, fp, fp, vp, sz, vp]
+    lib.mlstm_bwd_workspace_bytes.restype = sz
+    lib.mlstm_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.mlstm_bwd_parallel.restype = i
+    lib.mlstm_bwd_parallel.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, i,
+                                       fp, fp, fp, fp, fp, fp, vp, sz, vp]
     lib.mlstm_step.restype = i
     lib.mlstm_step.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, fp, fp, fp, vp, vp]
     lib.mlstm_status_string.restype = ctypes.c_char_p
@@ -233,6 +238,47 @@ def mlstm_fwd_scan(q, k, v, i_pre, f_pre, o_pre, chunk: int, h_out, C_final, n_f
     if st != MLSTM_OK:
         raise MlstmError("mlstm_fwd_scan", st, mlstm_error_detail())
     return h_out, C_final, n_final, m_final
+
+
+def mlstm_bwd_workspace_bytes(B: int, NH: int, S: int, d_qk: int, d_v: int, dtype: int) -> int:
+    return int(load_library().mlstm_bwd_workspace_bytes(B, NH, S, d_qk, d_v, int(dtype)))
+
+
+def mlstm_bwd_parallel(q, k, v, i_pre, f_pre, o_pre, dh, grads=None, workspace=None, stream=None):
+    """Gradients of the zero-state forward given dh; returns (dq, dk, dv, di, df, do), float32.
+
+    Inputs as for mlstm_fwd_parallel; dh [B,NH,S,d_v] in the dtype of q.  `grads`
+    may hold the six output tensors (float32, shapes of q, k, v, i_pre, f_pre, o_pre).
+    """
+    import torch
+    lib = load_library()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, NH, S, d]")
+    B, NH, S, dqk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    dt = _dtype_code(q)
+    shapes = [(B, NH, S, dqk), (B, NH, S, dqk), (B, NH, S, dv), (B, NH, S), (B, NH, S), (B, NH, S, dv)]
+    for t, name, shp, tdt in zip((q, k, v, i_pre, f_pre, o_pre, dh), ("q", "k", "v", "i_pre", "f_pre", "o_pre", "dh"),
+                                 shapes + [(B, NH, S, dv)], [q.dtype] * 3 + [torch.float32] * 3 + [q.dtype]):
+        _check(t, name, shp, tdt, dev)
+    if grads is None:
+        grads = tuple(torch.empty(shp, dtype=torch.float32, device=dev) for shp in shapes)
+    for t, name, shp in zip(grads, ("grad_q", "grad_k", "grad_v", "grad_i", "grad_f", "grad_o"), shapes):
+        _check(t, name, shp, torch.float32, dev)
+    need = int(lib.mlstm_bwd_workspace_bytes(B, NH, S, dqk, dv, dt))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    st = lib.mlstm_bwd_parallel(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                i_pre.data_ptr(), f_pre.data_ptr(), o_pre.data_ptr(), dh.data_ptr(),
+                                B, NH, S, dqk, dv, dt, *[g.data_ptr() for g in grads],
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                _stream_handle(stream, dev))
+    if st != MLSTM_OK:
+        raise MlstmError("mlstm_bwd_parallel", st, mlstm_error_detail())
+    return tuple(grads)
 
 
 def mlstm_step(q, k, v, i_pre, f_pre, o_pre, C, n, m, h_out=None, stream=None):

@@ -259,6 +259,57 @@ mlstm_status mlstm_step(const void* q, const void* k, const void* v,
     return ok();
 }
 
+// sizes the backward accepts: those of the forward without the chunk
+static mlstm_status check_bwd_sizes(int B, int NH, int S, int dqk, int dv, mlstm_dtype dt) {
+    mlstm_status s = check_fwd_sizes(B, NH, S, dqk, dv, 16, dt, true);
+    if (s != MLSTM_OK) return s;
+    if (S > 65535 * 64) return fail(MLSTM_ERR_UNSUPPORTED, "S=%d exceeds the backward's %d tokens", S, 65535 * 64);
+    return MLSTM_OK;
+}
+
+static mlstm::BwdArgs make_bwd_args(int B, int NH, int S, int dqk, int dv, mlstm_dtype dt) {
+    mlstm::BwdArgs a = {};
+    a.B = B; a.NH = NH; a.S = S; a.dqk = dqk; a.dv = dv; a.dtype = dt;
+    return a;
+}
+
+size_t mlstm_bwd_workspace_bytes(int B, int NH, int S, int d_qk, int d_v, mlstm_dtype dtype) {
+    if (check_bwd_sizes(B, NH, S, d_qk, d_v, dtype) != MLSTM_OK) return 0;
+    return mlstm::bwd_workspace_bytes(make_bwd_args(B, NH, S, d_qk, d_v, dtype));
+}
+
+mlstm_status mlstm_bwd_parallel(const void* q, const void* k, const void* v,
+                                const float* i_pre, const float* f_pre, const float* o_pre,
+                                const void* dh,
+                                int B, int NH, int S, int d_qk, int d_v, mlstm_dtype dtype,
+                                float* grad_q, float* grad_k, float* grad_v,
+                                float* grad_i, float* grad_f, float* grad_o,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    mlstm_status s = check_bwd_sizes(B, NH, S, d_qk, d_v, dtype);
+    if (s != MLSTM_OK) return s;
+    const void* ptrs[] = {q, k, v, i_pre, f_pre, o_pre, dh, grad_q, grad_k, grad_v, grad_i, grad_f, grad_o};
+    const char* names[] = {"q", "k", "v", "i_pre", "f_pre", "o_pre", "dh",
+                           "grad_q", "grad_k", "grad_v", "grad_i", "grad_f", "grad_o"};
+    const unsigned align[] = {16, 16, 16, 4, 4, 16, 16, 16, 16, 16, 4, 4, 16};
+    for (int p = 0; p < 13; ++p) {
+        if (!ptrs[p]) return fail(MLSTM_ERR_INVALID_ARG, "%s is NULL", names[p]);
+        if (!aligned(ptrs[p], align[p]))
+            return fail(MLSTM_ERR_INVALID_ARG, "%s is not %u-byte aligned", names[p], align[p]);
+    }
+    mlstm::BwdArgs a = make_bwd_args(B, NH, S, d_qk, d_v, dtype);
+    const size_t need = mlstm::bwd_workspace_bytes(a);
+    if (!workspace || workspace_bytes < need)
+        return fail(MLSTM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+    if (!aligned16(workspace)) return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    a.q = q; a.k = k; a.v = v; a.dh = dh; a.i_pre = i_pre; a.f_pre = f_pre; a.o_pre = o_pre;
+    a.dq = grad_q; a.dk = grad_k; a.dvv = grad_v; a.di = grad_i; a.df = grad_f; a.dout = grad_o;
+    a.ws = workspace;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = mlstm::launch_bwd(a);
+    if (e != hipSuccess) return fail(MLSTM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 const char* mlstm_status_string(mlstm_status status) {
     switch (status) {
         case MLSTM_OK: return "ok";

@@ -82,6 +82,16 @@ struct StepArgs {
     hipStream_t stream;
 };
 
+struct BwdArgs {
+    const void* q; const void* k; const void* v; const void* dh;
+    const float* i_pre; const float* f_pre; const float* o_pre;
+    int B, NH, S, dqk, dv;
+    mlstm_dtype dtype;
+    float* dq; float* dk; float* dvv; float* di; float* df; float* dout;
+    void* ws;
+    hipStream_t stream;
+};
+
 hipError_t launch_step(const StepArgs& a);
 
 // generic chunkwise forward on the vector ALUs (any supported shape, fp32 or bf16)
@@ -93,5 +103,9 @@ bool mfma_fwd_supported(const FwdArgs& a);
 size_t mfma_fwd_workspace_bytes(const FwdArgs& a);
 hipError_t launch_fwd_mfma_prepare(const FwdArgs& a);
 hipError_t launch_fwd_mfma_scan(const FwdArgs& a);
+
+// backward of the zero-state forward (tiled quadratic form on the vector ALUs)
+size_t bwd_workspace_bytes(const BwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);
 
 }  // namespace mlstm

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the mLSTM forward and decode step.
+"""Seeded synthetic inputs for the mLSTM forward, its backward and the decode step.
 
 This module holds input recipes only -- shapes, distributions, seeds and the
 fp32 -> bf16 rounding of inputs -- and none of the mLSTM arithmetic.  It is the one
@@ -14,6 +14,7 @@ Workloads (xLSTM language-model layer shapes; gate pre-activations fp32):
 
 Recipe (per workload, generator ``numpy.random.default_rng(seed)``):
   draw order q, k, v, i~, f~, o~ (then the spike positions, then the decode state);
+  the backward's dh ~ N(0,1) comes from a generator of its own (seed + 2000);
   normals drawn directly in float32; k scaled by 1/sqrt(d_qk) in fp32 for the
   forward workloads (decode keys are unscaled N(0,1)); q, k, v of bf16 workloads
   rounded to bf16 with round-to-nearest-even, kept here as float32 arrays that
@@ -117,6 +118,19 @@ def fwd_inputs(w: Workload, seed: int | None = None, B: int | None = None, NH: i
     if w.dtype == "bf16":
         q, k, v = bf16_round(q), bf16_round(k), bf16_round(v)
     return dict(q=q, k=k, v=v, i_pre=i_pre, f_pre=f_pre, o_pre=o_pre)
+
+
+def bwd_dh(w: Workload, seed: int | None = None, B: int | None = None, NH: int | None = None,
+           S: int | None = None, dv: int | None = None) -> np.ndarray:
+    """Gradient with respect to h for a backward: N(0,1) [B,NH,S,dv] float32, bf16-rounded
+    for bf16 workloads (generator seeded with seed + 2000)."""
+    B = w.B if B is None else B
+    NH = w.NH if NH is None else NH
+    S = w.S if S is None else S
+    dv = w.dv if dv is None else dv
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 2000)
+    dh = _normal(rng, (B, NH, S, dv))
+    return bf16_round(dh) if w.dtype == "bf16" else dh
 
 
 def step_state(w: Workload, seed: int | None = None, B: int | None = None, NH: int | None = None,

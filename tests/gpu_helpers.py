@@ -56,3 +56,14 @@ def check(name: str, got, ref, tol: float, errs: dict) -> None:
     e = rel_err(got, ref)
     errs[name] = e
     assert e <= tol, f"{name}: relative error {e:.3e} > {tol:.1e}"
+
+
+def bwd_gpu(x: dict, dh: np.ndarray, dtype: str):
+    """mlstm_bwd_parallel on cuda:0; returns (dq, dk, dv, di, df, do) as float64 numpy."""
+    from mlstm_matrix_memory_amd import mlstm_bwd_parallel
+    import torch
+    q, k, v = (to_gpu(x[n], dtype) for n in ("q", "k", "v"))
+    i_pre, f_pre, o_pre = (to_gpu(x[n], "f32") for n in ("i_pre", "f_pre", "o_pre"))
+    g = mlstm_bwd_parallel(q, k, v, i_pre, f_pre, o_pre, to_gpu(dh, dtype))
+    torch.cuda.synchronize()
+    return tuple(to_np(t) for t in g)

@@ -22,7 +22,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = b.header_symbols()
     assert {"mlstm_fwd_parallel", "mlstm_fwd_parallel_state", "mlstm_fwd_prepare", "mlstm_fwd_scan",
-            "mlstm_step", "mlstm_fwd_workspace_bytes", "mlstm_status_string", "mlstm_error_detail"} <= set(names)
+            "mlstm_step", "mlstm_fwd_workspace_bytes", "mlstm_status_string", "mlstm_error_detail",
+            "mlstm_bwd_parallel", "mlstm_bwd_workspace_bytes"} <= set(names)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in include/mlstm.h but not exported"
 
@@ -146,7 +147,8 @@ def test_step_rejects_null_state(lib):
 def test_binding_has_same_names_as_abi():
     import mlstm_matrix_memory_amd as pkg
     for name in ("mlstm_fwd_parallel", "mlstm_fwd_parallel_state", "mlstm_fwd_prepare", "mlstm_fwd_scan",
-                 "mlstm_step", "mlstm_fwd_workspace_bytes", "mlstm_status_string", "mlstm_error_detail"):
+                 "mlstm_step", "mlstm_fwd_workspace_bytes", "mlstm_status_string", "mlstm_error_detail",
+                 "mlstm_bwd_parallel", "mlstm_bwd_workspace_bytes"):
         assert callable(getattr(pkg, name))
 
 
@@ -175,3 +177,49 @@ def test_prepare_checks_only_what_it_reads(lib):
     st = lib.mlstm_fwd_scan(FAKE, FAKE, None, FAKE, FAKE, FAKE, 1, 1, 64, 32, 32, 16, b.MLSTM_BF16,
                             FAKE, FAKE, FAKE, FAKE, None, 0, None)
     assert st == b.MLSTM_ERR_INVALID_ARG and "v is NULL" in b.mlstm_error_detail()
+
+
+def _bwd(lib, B=1, NH=1, S=100, dqk=32, dv=32, dt=b.MLSTM_BF16, ptrs=None, ws=FAKE, ws_bytes=1 << 30):
+    p = [FAKE] * 13 if ptrs is None else ptrs
+    return lib.mlstm_bwd_parallel(*p[:7], B, NH, S, dqk, dv, dt, *p[7:], ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,detail", [
+    (dict(B=0), "B=0"),
+    (dict(S=0), "S=0"),
+    (dict(dqk=24), "d_qk=24"),
+    (dict(dv=4112), "d_v=4112"),
+    (dict(dt=5), "dtype=5"),
+    (dict(S=65535 * 64 + 1), "exceeds"),
+])
+def test_bwd_rejects_bad_sizes(lib, kw, detail):
+    assert _bwd(lib, **kw) != b.MLSTM_OK
+    assert detail in b.mlstm_error_detail()
+
+
+@pytest.mark.parametrize("which", range(13))
+def test_bwd_rejects_null_pointer(lib, which):
+    ptrs = [FAKE] * 13
+    ptrs[which] = None
+    assert _bwd(lib, ptrs=ptrs) == b.MLSTM_ERR_INVALID_ARG
+    assert "NULL" in b.mlstm_error_detail()
+
+
+def test_bwd_rejects_misaligned_and_small_workspace(lib):
+    ptrs = [FAKE] * 13
+    ptrs[7] = FAKE_MIS                                    # grad_q
+    assert _bwd(lib, ptrs=ptrs) == b.MLSTM_ERR_INVALID_ARG
+    assert "grad_q" in b.mlstm_error_detail()
+    need = b.mlstm_bwd_workspace_bytes(1, 1, 100, 32, 32, b.MLSTM_BF16)
+    assert need > 0
+    assert _bwd(lib, ws_bytes=need - 1) == b.MLSTM_ERR_WORKSPACE
+    assert _bwd(lib, ws=None) == b.MLSTM_ERR_WORKSPACE
+    assert _bwd(lib, ws=FAKE_MIS, ws_bytes=need) == b.MLSTM_ERR_INVALID_ARG
+
+
+def test_bwd_workspace_grows_with_the_sequence():
+    small = b.mlstm_bwd_workspace_bytes(1, 2, 64, 32, 48, b.MLSTM_F32)
+    large = b.mlstm_bwd_workspace_bytes(1, 2, 640, 32, 48, b.MLSTM_F32)
+    # per token at least the fp64 cumulative gate and stabilizer and the fp32 dnum row
+    assert large - small >= 2 * (640 - 64) * (16 + 48 * 4)
+    assert b.mlstm_bwd_workspace_bytes(1, 1, 64, 24, 32, b.MLSTM_F32) == 0
