@@ -18,8 +18,9 @@
 //   df~_j = sigmoid(-f~_j) sum_{t>=j} dF_t
 // (the last line collects dlog D_ts = G_ts S_ts over the query and key positions).
 //
-// Three tiled passes over 64-token blocks, all VALU with fp32 accumulation and
-// fp64 exponent arguments:
+// Tiled passes over 64-token blocks with fp32 accumulation and fp64 exponent
+// arguments (on the vector ALUs here; bf16 inputs with d_qk, d_v <= 512 take the
+// MFMA form of the two middle passes further down):
 //   bwd_gate_kernel   per head: F and m (prefix sum, prefix max), fp64
 //   bwd_rows_kernel   per (query block, head): num', den' over key blocks <= it, then
 //                     dnum', dden', do~; then dq over the same key blocks
@@ -37,8 +38,10 @@ constexpr int BW_THREADS = 256;  // 16 x 16 threads, each a 4 x 4 piece of a 64 
 struct BwdWs {
     double* F;      // [heads][S] cumulative log forget gate
     double* m;      // [heads][S] stabilizer
-    float* dnum;    // [heads][S][dv] num' while it accumulates, then dnum'
+    float* dnum;    // [heads][S][dv] num' while it accumulates, then dnum' (vector-ALU path);
+                    // the MFMA path keeps dnum' there as bf16 hi [heads][S][dv], then lo
     float* dden;    // [heads][S] dden'
+    float* qdq;     // [heads][S] q_t . dq_t (MFMA path)
 };
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -50,6 +53,7 @@ inline size_t bwd_ws_walk(char* base, size_t heads, size_t S, int dv, BwdWs* out
     w.m = (double*)take(heads * S * sizeof(double));
     w.dnum = (float*)take(heads * S * dv * sizeof(float));
     w.dden = (float*)take(heads * S * sizeof(float));
+    w.qdq = (float*)take(heads * S * sizeof(float));
     if (out) *out = w;
     return off;
 }
@@ -413,9 +417,11 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_cols_kernel(BwdIn<T> in, BwdWs
 
 // ---- kernel 4: gate gradients per head ----------------------------------------
 // di~_j = k_j . dk_j ;  dF_j = q_j . dq_j - k_j . dk_j ;  df~_j = sigmoid(-f~_j) sum_{t>=j} dF_t
-template <typename T>
+// DOTS: q . dq comes from the workspace and k . dk is already in di (MFMA path)
+template <typename T, bool DOTS>
 __global__ __launch_bounds__(BW_THREADS) void bwd_gates_kernel(BwdIn<T> in, const float* __restrict__ dq,
                                                                const float* __restrict__ dk,
+                                                               const float* __restrict__ qdq_in,
                                                                float* __restrict__ di, float* __restrict__ df)
 {
     __shared__ double part[BW_THREADS / 64];
@@ -428,13 +434,17 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_gates_kernel(BwdIn<T> in, cons
         const int t = e0 - tid;
         double dF = 0.0;
         if (t >= 0) {
-            double qdq = 0.0, kdk = 0.0;
-            for (int j = 0; j < dqk; ++j) {
-                qdq += (double)to_f32(in.q[(tokh + t) * dqk + j]) * dq[(tokh + t) * dqk + j];
-                kdk += (double)to_f32(in.k[(tokh + t) * dqk + j]) * dk[(tokh + t) * dqk + j];
+            if (DOTS) {
+                dF = (double)qdq_in[tokh + t] - (double)di[tokh + t];
+            } else {
+                double qdq = 0.0, kdk = 0.0;
+                for (int j = 0; j < dqk; ++j) {
+                    qdq += (double)to_f32(in.q[(tokh + t) * dqk + j]) * dq[(tokh + t) * dqk + j];
+                    kdk += (double)to_f32(in.k[(tokh + t) * dqk + j]) * dk[(tokh + t) * dqk + j];
+                }
+                di[tokh + t] = (float)kdk;
+                dF = qdq - kdk;
             }
-            di[tokh + t] = (float)kdk;
-            dF = qdq - kdk;
         }
         double x = dF;
 #pragma unroll
@@ -457,6 +467,388 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_gates_kernel(BwdIn<T> in, cons
     }
 }
 
+// ===========================================================================
+// bf16 MFMA form of the two tiled passes (bf16 inputs, max(d_qk, d_v) <= 512)
+// ===========================================================================
+// Same mathematics as bwd_rows_kernel / bwd_cols_kernel.  A wave owns 16 tokens
+// of its block (queries in the row pass, keys in the column pass) and keeps every
+// tile with that token index as the MFMA column: score-shaped tiles are held as
+// S^T[s][t] (row pass) or S[t][s] (column pass), and per-token vectors as
+// X^T[n][t].  In that D layout lane l holds column l%16 and rows 4(l/16) + i, which
+// is also a valid B operand when the k-slots 8(l/16) + j are mapped to rows
+// {4(l/16) + j} of one 16-row block (j < 4) and of the next (j >= 4); the
+// matching A operands are read from LDS either straight (rows contiguous in the
+// contraction index) or with the transposing read.
+//
+// Precision: q, k, v and dh are exact bf16 inputs, but P = S (.) D', G = dA (.) D'
+// and dnum' are computed fp32 values.  A single bf16 rounding of them costs up to
+// ~1e-1 relative error on the gradients, so each is split into bf16 hi + lo and
+// its product taken as two MFMAs (three when both operands are computed: the
+// lo x lo term is below fp32 rounding).
+constexpr int MB_THREADS = 256;
+
+__device__ __forceinline__ void hilo(float x, bf16& hi, bf16& lo) {
+    hi = (bf16)x;
+    lo = (bf16)(x - (float)hi);
+}
+
+// 16 bytes of bf16 from global memory, or zeros
+__device__ __forceinline__ bf16x8 ld8(const bf16* p, bool ok) {
+    if (!ok) return bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// stage rows [row0, row0 + R) of a [.., d] bf16 tensor into LDS (pitch P), zero outside
+template <int R, int D, int P>
+__device__ __forceinline__ void stage_rows(bf16* dst, const bf16* src, size_t tok0, int row0, int S, int d, int tid) {
+    constexpr int U = R * D / 8;
+    for (int u = tid; u < U; u += MB_THREADS) {
+        const int r = u / (D / 8), c8 = 8 * (u % (D / 8));
+        const bool ok = row0 + r < S && c8 < d;
+        *reinterpret_cast<bf16x8*>(dst + r * P + c8) = ld8(src + (tok0 + row0 + r) * d + c8, ok);
+    }
+}
+
+template <int D>
+struct alignas(16) RowsSmem {
+    bf16 k[64 * (D + 8)];
+    bf16 v[64 * (D + 8)];
+    double gs[64];       // F_s - i~_s of the key block
+};
+
+// per (head, query block of 64): num', den' over key blocks <= it, then dnum', dden',
+// do~ (wave-local), then dq over the same key blocks, and q_t . dq_t
+template <int D>
+__global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdWs ws, float* __restrict__ dq,
+                                                          float* __restrict__ dout)
+{
+    constexpr int P = D + 8;
+    constexpr int NB = D / 16, KS = D / 32;
+    __shared__ RowsSmem<D> sm;
+    const int rb = gridDim.y - 1 - blockIdx.y, bh = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 15, g = lane >> 4;
+    const int S = in.S, dqk = in.dqk, dv = in.dv;
+    const size_t tokh = (size_t)bh * S;
+    const int r0 = rb * 64;
+    const int t = r0 + 16 * wave + ln;          // this lane's query
+    const bool tval = t < S;
+    const double Rt = tval ? ws.F[tokh + t] - ws.m[tokh + t] : 0.0;
+    const float fl = tval ? exp_arg(-ws.m[tokh + t]) : 1.0f;
+
+    // q_t as B operands: k-slot 8g + j <-> key dimension 32 kk + 8g + j
+    bf16x8 qb[KS];
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) qb[kk] = ld8(in.q + (tokh + t) * dqk + 32 * kk + 8 * g, tval && 32 * kk + 8 * g < dqk);
+
+    auto stage = [&](int c0) {
+        __syncthreads();
+        stage_rows<64, D, P>(sm.k, in.k, tokh, c0, S, dqk, tid);
+        stage_rows<64, D, P>(sm.v, in.v, tokh, c0, S, dv, tid);
+        if (tid < 64) {
+            const int s = min(c0 + tid, S - 1);
+            sm.gs[tid] = ws.F[tokh + s] - (double)in.i_pre[tokh + s];
+        }
+        __syncthreads();
+    };
+    // D'[s][t] for this lane's 16 entries of a tile pair (s = 16 sb + 4g + i)
+    auto decay4 = [&](float (&d)[4][4], int c0) {
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int sl = 16 * sb + 4 * g + i;
+                d[sb][i] = (tval && c0 + sl <= t) ? exp_arg(Rt - sm.gs[sl]) : 0.0f;
+            }
+    };
+
+    // ---- pass 1: num'^T[n][t] and den_t -------------------------------------
+    f32x4 num[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) num[nb] = f32x4{0, 0, 0, 0};
+    float den = 0.0f;
+    for (int cb = 0; cb <= rb; ++cb) {
+        const int c0 = 64 * cb;
+        stage(c0);
+        f32x4 st[4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) st[sb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(sm.k + (16 * sb + ln) * P + 32 * kk + 8 * g);
+                st[sb] = mfma(a, qb[kk], st[sb]);
+            }
+        float d[4][4];
+        decay4(d, c0);
+        bf16x8 ph[2], pl[2];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p = st[sb][i] * d[sb][i];
+                den += p;
+                bf16 hi, lo;
+                hilo(p, hi, lo);
+                ph[sb >> 1][4 * (sb & 1) + i] = hi;
+                pl[sb >> 1][4 * (sb & 1) + i] = lo;
+            }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                const bf16* vp = sm.v + (32 * pr + 4 * g + (ln >> 2)) * P + 16 * nb + 4 * (ln & 3);
+                const bf16x8 a = cat(lds_read_tr(vp), lds_read_tr(vp + 16 * P));
+                num[nb] = mfma(a, ph[pr], num[nb]);
+                num[nb] = mfma(a, pl[pr], num[nb]);
+            }
+    }
+
+    // ---- per query: u, do~, dnum', dden' ------------------------------------
+    den += __shfl_xor(den, 16, 64);
+    den += __shfl_xor(den, 32, 64);
+    const float rN = 1.0f / fmaxf(fabsf(den), fl);
+    float duu = 0.0f;
+    const bf16* dhp = in.dh + (tokh + t) * dv;
+    const float* op = in.o_pre + (tokh + t) * dv;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        const int n0 = 16 * nb + 4 * g;
+        if (tval && n0 < dv) {
+            const f32x4 o4 = load4(op + n0), dh4 = load4(dhp + n0);
+            f32x4 do4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float u = num[nb][i] * rN;
+                const float gg = sigmoid(o4[i]);
+                do4[i] = dh4[i] * u * gg * (1.0f - gg);
+                const float du = dh4[i] * gg;
+                duu += du * u;
+                num[nb][i] = du * rN;
+            }
+            *reinterpret_cast<f32x4*>(dout + (tokh + t) * dv + n0) = do4;
+        } else {
+            num[nb] = f32x4{0, 0, 0, 0};
+        }
+    }
+    duu += __shfl_xor(duu, 16, 64);
+    duu += __shfl_xor(duu, 32, 64);
+    const float dd = (tval && fabsf(den) > fl) ? -(den > 0.0f ? 1.0f : -1.0f) * duu * rN : 0.0f;
+    if (tval && g == 0) ws.dden[tokh + t] = dd;
+    // dnum' for the column pass (bf16 hi, then lo) and as B operands here
+    bf16* dnh_g = reinterpret_cast<bf16*>(ws.dnum);
+    bf16* dnl_g = dnh_g + (size_t)gridDim.x * S * dv;
+    bf16x8 dnh[NB / 2], dnl[NB / 2];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        bf16x4 h4, l4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            bf16 hi, lo;
+            hilo(num[nb][i], hi, lo);
+            h4[i] = hi;
+            l4[i] = lo;
+            dnh[nb >> 1][4 * (nb & 1) + i] = hi;
+            dnl[nb >> 1][4 * (nb & 1) + i] = lo;
+        }
+        const int n0 = 16 * nb + 4 * g;
+        if (tval && n0 < dv) {
+            *reinterpret_cast<bf16x4*>(dnh_g + (tokh + t) * dv + n0) = h4;
+            *reinterpret_cast<bf16x4*>(dnl_g + (tokh + t) * dv + n0) = l4;
+        }
+    }
+
+    // ---- pass 2: dq^T[j][t] += K^T G^T, G^T = (V dnum'^T + dden') (.) D' ------
+    f32x4 dqa[NB];
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) dqa[jb] = f32x4{0, 0, 0, 0};
+    for (int cb = 0; cb <= rb; ++cb) {
+        const int c0 = 64 * cb;
+        stage(c0);
+        f32x4 da[4];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb) da[sb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int pr = 0; pr < NB / 2; ++pr)
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) {
+                const bf16* vp = sm.v + (16 * sb + ln) * P + 32 * pr + 4 * g;
+                const bf16x8 a = cat(*reinterpret_cast<const bf16x4*>(vp), *reinterpret_cast<const bf16x4*>(vp + 16));
+                da[sb] = mfma(a, dnh[pr], da[sb]);
+                da[sb] = mfma(a, dnl[pr], da[sb]);
+            }
+        float d[4][4];
+        decay4(d, c0);
+        bf16x8 gh[2], gl[2];
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bf16 hi, lo;
+                hilo((da[sb][i] + dd) * d[sb][i], hi, lo);
+                gh[sb >> 1][4 * (sb & 1) + i] = hi;
+                gl[sb >> 1][4 * (sb & 1) + i] = lo;
+            }
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb)
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                const bf16* kp = sm.k + (32 * pr + 4 * g + (ln >> 2)) * P + 16 * jb + 4 * (ln & 3);
+                const bf16x8 a = cat(lds_read_tr(kp), lds_read_tr(kp + 16 * P));
+                dqa[jb] = mfma(a, gh[pr], dqa[jb]);
+                dqa[jb] = mfma(a, gl[pr], dqa[jb]);
+            }
+    }
+    float qdq = 0.0f;
+#pragma unroll
+    for (int jb = 0; jb < NB; ++jb) {
+        const int j0 = 16 * jb + 4 * g;
+        if (tval && j0 < dqk) {
+            *reinterpret_cast<f32x4*>(dq + (tokh + t) * dqk + j0) = dqa[jb];
+            const f32x4 q4 = load4(in.q + (tokh + t) * dqk + j0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qdq += q4[i] * dqa[jb][i];
+        }
+    }
+    qdq += __shfl_xor(qdq, 16, 64);
+    qdq += __shfl_xor(qdq, 32, 64);
+    if (tval && g == 0) ws.qdq[tokh + t] = qdq;
+}
+
+template <int D, int QB>
+struct alignas(16) ColsSmem {
+    bf16 q[QB * (D + 8)];
+    bf16 dh[QB * (D + 8)];      // dnum' hi
+    bf16 dl[QB * (D + 8)];      // dnum' lo
+    double rt[QB];              // F_t - m_t of the query block
+    float dd[QB];               // dden'_t
+};
+
+// per (head, key block of 64): dk, dv over query blocks >= it (QB queries at a
+// time), and k_s . dk_s (= di~_s)
+template <int D, int QB>
+__global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdWs ws, float* __restrict__ dk,
+                                                          float* __restrict__ dvv, float* __restrict__ di)
+{
+    constexpr int P = D + 8;
+    constexpr int NB = D / 16, KS = D / 32, TB = QB / 16;
+    __shared__ ColsSmem<D, QB> sm;
+    const int cb = blockIdx.y, bh = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 15, g = lane >> 4;
+    const int S = in.S, dqk = in.dqk, dv = in.dv;
+    const size_t tokh = (size_t)bh * S;
+    const int c0 = cb * 64;
+    const int s = c0 + 16 * wave + ln;           // this lane's key
+    const bool sval = s < S;
+    const double Qs = sval ? ws.F[tokh + s] - (double)in.i_pre[tokh + s] : 0.0;
+    const bf16* dnh_g = reinterpret_cast<const bf16*>(ws.dnum);
+    const bf16* dnl_g = dnh_g + (size_t)gridDim.x * S * dv;
+
+    f32x4 dka[NB], dva[NB];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) dka[b] = dva[b] = f32x4{0, 0, 0, 0};
+
+    for (int r0 = c0; r0 < S; r0 += QB) {
+        __syncthreads();
+        stage_rows<QB, D, P>(sm.q, in.q, tokh, r0, S, dqk, tid);
+        stage_rows<QB, D, P>(sm.dh, dnh_g, tokh, r0, S, dv, tid);
+        stage_rows<QB, D, P>(sm.dl, dnl_g, tokh, r0, S, dv, tid);
+        if (tid < QB) {
+            const int tt = min(r0 + tid, S - 1);
+            sm.rt[tid] = ws.F[tokh + tt] - ws.m[tokh + tt];
+            sm.dd[tid] = r0 + tid < S ? ws.dden[tokh + tt] : 0.0f;
+        }
+        __syncthreads();
+        // S[t][s] and dA[t][s] - dden'_t for the TB query blocks
+        f32x4 sc[TB], da[TB];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) sc[tb] = da[tb] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            // k_s and v_s as B operands: k-slot 8g + j <-> dimension 32 kk + 8g + j (cache-resident)
+            const bf16x8 kb = ld8(in.k + (tokh + s) * dqk + 32 * kk + 8 * g, sval && 32 * kk + 8 * g < dqk);
+            const bf16x8 vb = ld8(in.v + (tokh + s) * dv + 32 * kk + 8 * g, sval && 32 * kk + 8 * g < dv);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const int off = (16 * tb + ln) * P + 32 * kk + 8 * g;
+                sc[tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.q + off), kb, sc[tb]);
+                da[tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.dh + off), vb, da[tb]);
+                da[tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.dl + off), vb, da[tb]);
+            }
+        }
+        // P = S (.) D', G = (dA + dden') (.) D', as hi/lo B operands over query slots
+        bf16x8 ph[TB / 2], pl[TB / 2], gh[TB / 2], gl[TB / 2];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tl = 16 * tb + 4 * g + i;
+                const float d = (sval && s <= r0 + tl && r0 + tl < S) ? exp_arg(sm.rt[tl] - Qs) : 0.0f;
+                bf16 hi, lo;
+                hilo(sc[tb][i] * d, hi, lo);
+                ph[tb >> 1][4 * (tb & 1) + i] = hi;
+                pl[tb >> 1][4 * (tb & 1) + i] = lo;
+                hilo((da[tb][i] + sm.dd[tl]) * d, hi, lo);
+                gh[tb >> 1][4 * (tb & 1) + i] = hi;
+                gl[tb >> 1][4 * (tb & 1) + i] = lo;
+            }
+        // dk^T[j][s] += Q^T G ;  dv^T[n][s] += dnum'^T P
+#pragma unroll
+        for (int b = 0; b < NB; ++b)
+#pragma unroll
+            for (int pr = 0; pr < TB / 2; ++pr) {
+                const int off = (32 * pr + 4 * g + (ln >> 2)) * P + 16 * b + 4 * (ln & 3);
+                const bf16x8 aq = cat(lds_read_tr(sm.q + off), lds_read_tr(sm.q + off + 16 * P));
+                dka[b] = mfma(aq, gh[pr], dka[b]);
+                dka[b] = mfma(aq, gl[pr], dka[b]);
+                const bf16x8 ah = cat(lds_read_tr(sm.dh + off), lds_read_tr(sm.dh + off + 16 * P));
+                const bf16x8 al = cat(lds_read_tr(sm.dl + off), lds_read_tr(sm.dl + off + 16 * P));
+                dva[b] = mfma(ah, ph[pr], dva[b]);
+                dva[b] = mfma(ah, pl[pr], dva[b]);
+                dva[b] = mfma(al, ph[pr], dva[b]);
+            }
+    }
+    float kdk = 0.0f;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const int j0 = 16 * b + 4 * g;
+        if (sval && j0 < dqk) {
+            *reinterpret_cast<f32x4*>(dk + (tokh + s) * dqk + j0) = dka[b];
+            const f32x4 k4 = load4(in.k + (tokh + s) * dqk + j0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) kdk += k4[i] * dka[b][i];
+        }
+        if (sval && j0 < dv) *reinterpret_cast<f32x4*>(dvv + (tokh + s) * dv + j0) = dva[b];
+    }
+    kdk += __shfl_xor(kdk, 16, 64);
+    kdk += __shfl_xor(kdk, 32, 64);
+    if (sval && g == 0) di[tokh + s] = kdk;
+}
+
+// smallest tile width covering both dimensions (0 = not on the MFMA path)
+int mfma_bwd_width(const BwdArgs& a) {
+    if (a.dtype != MLSTM_BF16) return 0;
+    const int d = a.dqk > a.dv ? a.dqk : a.dv;
+    const int widths[5] = {64, 128, 256, 384, 512};
+    for (int i = 0; i < 5; ++i)
+        if (d <= widths[i]) return widths[i];
+    return 0;
+}
+
+template <int D, int QB>
+hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdIn<bf16>& in, const BwdWs& w) {
+    const int heads = a.B * a.NH, nb = (a.S + 63) / 64;
+    hipLaunchKernelGGL((bwd_rows_mfma<D>), dim3(heads, nb), dim3(MB_THREADS), 0, a.stream, in, w, a.dq, a.dout);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_cols_mfma<D, QB>), dim3(heads, nb), dim3(MB_THREADS), 0, a.stream, in, w, a.dk, a.dvv,
+                       a.di);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_gates_kernel<bf16, true>), dim3(heads), dim3(BW_THREADS), 0, a.stream, in, a.dq, a.dk,
+                       w.qdq, a.di, a.df);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_bwd_t(const BwdArgs& a) {
     const int heads = a.B * a.NH;
@@ -470,11 +862,22 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
     hipLaunchKernelGGL(bwd_gate_kernel, dim3(heads), dim3(BW_THREADS), 0, a.stream, a.i_pre, a.f_pre, a.S, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if constexpr (sizeof(T) == 2) {
+        switch (mfma_bwd_width(a)) {
+            case 64: return launch_bwd_mfma<64, 64>(a, in, w);
+            case 128: return launch_bwd_mfma<128, 64>(a, in, w);
+            case 256: return launch_bwd_mfma<256, 64>(a, in, w);
+            case 384: return launch_bwd_mfma<384, 64>(a, in, w);
+            case 512: return launch_bwd_mfma<512, 32>(a, in, w);
+            default: break;
+        }
+    }
     hipLaunchKernelGGL((bwd_rows_kernel<T>), dim3(heads, nb), dim3(BW_THREADS), 0, a.stream, in, w, a.dq, a.dout);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_cols_kernel<T>), dim3(heads, nb), dim3(BW_THREADS), 0, a.stream, in, w, a.dk, a.dvv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_gates_kernel<T>), dim3(heads), dim3(BW_THREADS), 0, a.stream, in, a.dq, a.dk, a.di, a.df);
+    hipLaunchKernelGGL((bwd_gates_kernel<T, false>), dim3(heads), dim3(BW_THREADS), 0, a.stream, in, a.dq, a.dk,
+                       nullptr, a.di, a.df);
     return hipGetLastError();
 }
 

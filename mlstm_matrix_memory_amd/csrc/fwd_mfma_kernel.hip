@@ -48,18 +48,6 @@
 namespace mlstm {
 namespace {
 
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// transposing LDS read: 4 bf16 from the rows the lanes of this lane's 16-group point at
-__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
-    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
-    return __builtin_bit_cast(bf16x4, v);
-}
 // Workgroup barrier that orders LDS traffic only: this wave's LDS operations are
 // complete (lgkmcnt 0) before it signals, but global loads still in flight stay in
 // flight, so register prefetches issued before the barrier keep overlapping with
@@ -69,9 +57,6 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
-    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
 __device__ __forceinline__ bf16x8 cvt8(f32x4 a, f32x4 b) {
     return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],
                   (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};

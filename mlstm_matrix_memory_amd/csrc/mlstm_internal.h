@@ -59,6 +59,30 @@ __device__ __forceinline__ float wave_max(float x) {
     return x;
 }
 
+// ---- MFMA helpers (v_mfma_f32_16x16x32_bf16) --------------------------------
+// D[m][n] += sum_k A[m][k] B[k][n] over a 16 x 16 x 32 block.  Lane l supplies
+// A[l%16][8(l/16) .. 8(l/16)+7] and B[8(l/16) .. +7][l%16] and holds
+// D[4(l/16) + i][l%16], i = 0..3.  Which contraction index sits in which of the
+// 32 k-slots is free, as long as A and B agree.
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// transposing LDS read (ds_read_b64_tr_b16): the 16 lanes of a group point at 4
+// rows (lanes 4r .. 4r+3 at row r, 4 consecutive columns each); lane j receives
+// column j of those 4 rows, in row order
+__device__ __forceinline__ bf16x4 lds_read_tr(const bf16* p) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    return __builtin_bit_cast(bf16x4, v);
+}
+
+__device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 // ---- launchers (return hipSuccess or the launch error) --------------------
 struct FwdArgs {
     const void* q; const void* k; const void* v;

@@ -93,6 +93,38 @@ def test_bf16_reduced(orc, name, over):
     _compare(orc, x, dh, "bf16")
 
 
+# every tile width of the bf16 MFMA form (the smallest of 64, 128, 256, 384, 512
+# covering max(d_qk, d_v)), with ragged sequence ends, unequal d_qk / d_v, d not a
+# multiple of 32, and the long-context gate distribution with input-gate spikes
+MFMA_CASES = [
+    ("lm_125m", dict(B=1, NH=2, S=130, dqk=64, dv=48)),
+    ("lm_125m", dict(B=2, NH=1, S=1, dqk=64, dv=64)),
+    ("lm_125m", dict(B=1, NH=1, S=200, dqk=128, dv=80)),
+    ("long_ctx", dict(B=1, NH=2, S=300, dqk=256, dv=256)),
+    ("lm_125m", dict(B=1, NH=1, S=257, dqk=384, dv=160)),
+    ("lm_125m", dict(B=1, NH=2, S=200, dqk=512, dv=512)),
+    ("long_ctx", dict(B=1, NH=1, S=190, dqk=112, dv=448)),
+]
+
+
+@pytest.mark.parametrize("name,over", MFMA_CASES, ids=lambda v: str(v))
+def test_bf16_mfma_widths(orc, name, over):
+    w = inputs.WORKLOADS[name]
+    announce(f"bwd bf16 mfma {name} {over}")
+    x = inputs.fwd_inputs(w, seed=400 + w.seed, **over)
+    dh = inputs.bwd_dh(w, seed=400 + w.seed, B=over["B"], NH=over["NH"], S=over["S"], dv=over["dv"])
+    _compare(orc, x, dh, "bf16")
+
+
+def test_bf16_mfma_normalizer_floor(orc):
+    # input gates lowered by 3: the floor is active on part of the rows
+    w = inputs.WORKLOADS["lm_125m"]
+    announce("bwd bf16 mfma floor B=1 NH=2 S=200 d=128")
+    x = inputs.fwd_inputs(w, seed=410, B=1, NH=2, S=200, dqk=128, dv=128)
+    x["i_pre"] = (x["i_pre"] - np.float32(3.0)).astype(np.float32)
+    _compare(orc, x, inputs.bwd_dh(w, seed=410, B=1, NH=2, S=200, dv=128), "bf16")
+
+
 @pytest.mark.parametrize("name,heads", [("lm_125m", [(0, 0), (7, 3)]), ("lm_1_3b", [(2, 1)])])
 def test_bf16_full_size_sampled_heads(orc, name, heads):
     w = inputs.WORKLOADS[name]
