@@ -6,7 +6,10 @@ d_qk=d_v=384, chunk 64, bf16 q/k/v, fp32 gate pre-activations, inputs resident i
 HBM.  `value` is forward tokens/s (B*S tokens per step) from the wall clock around
 exactly --steps steps.  The same run also times the one-token decode step
 (mlstm_step on the decode workload: batch 256, NH=4, d=512, fp32 state, 128
-consecutive steps) and reports it under "decode".
+consecutive steps) and reports it under "decode", and the backward
+(mlstm_bwd_parallel: gradients of the same forward with respect to q, k, v and
+the three gate pre-activations, given dh) on the forward's workload under
+"backward".
 
 Roofline: the dominant kernel of the forward is the scan; its duration is taken
 with HIP events recorded on the stream the kernels run on, and its algorithmic
@@ -20,6 +23,12 @@ on is unchanged.
 
 cpu_baseline: the fp64 oracle (oracle/, plain C + OpenMP over heads) timed on the
 host on a bounded sample of the same workload.
+
+Backward: algorithmic FLOPs of the tiled quadratic form are, per head, the
+S(S+1)/2 causal (t, s) pairs times 6 (d_qk + d_v): scores and numerator
+recomputed, then dA, dq, dk and dv, one multiply-add each per pair and dimension.
+The whole call is timed with HIP events on its stream; its roofline is against
+the bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -54,6 +63,10 @@ def scan_alg_bytes(w) -> float:
 
 def fwd_alg_bytes(w) -> float:
     return scan_alg_bytes(w) + float(w.B * w.NH * w.S) * 8  # + i~, f~ (fp32)
+
+
+def bwd_alg_flops(w) -> float:
+    return float(w.B * w.NH) * w.S * (w.S + 1) / 2 * 6.0 * (w.dqk + w.dv)
 
 
 def step_alg_bytes(w) -> float:
@@ -114,6 +127,8 @@ def main() -> int:
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
     args = ap.parse_args()
@@ -127,8 +142,8 @@ def main() -> int:
     import numpy as np
     import torch
 
-    from mlstm_matrix_memory_amd import (MLSTM_BF16, inputs, mlstm_fwd_prepare, mlstm_fwd_scan,
-                                         mlstm_fwd_workspace_bytes, mlstm_step)
+    from mlstm_matrix_memory_amd import (MLSTM_BF16, inputs, mlstm_bwd_parallel, mlstm_bwd_workspace_bytes,
+                                         mlstm_fwd_prepare, mlstm_fwd_scan, mlstm_fwd_workspace_bytes, mlstm_step)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -207,10 +222,40 @@ def main() -> int:
                      "alg_bytes_per_launch": scan_bytes},
     }
 
+    # ---------------- backward ------------------------------------------------
+    del ws, h, C, n, m
+    torch.cuda.empty_cache()
+    if not args.no_bwd:
+        dh = gpu(inputs.bwd_dh(w), w.dtype)
+        bws = torch.empty(max(1, mlstm_bwd_workspace_bytes(w.B, w.NH, w.S, w.dqk, w.dv, MLSTM_BF16)),
+                          dtype=torch.uint8, device=dev)
+        grads = mlstm_bwd_parallel(*fa[:6], dh, workspace=bws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_start = time.perf_counter()
+        e0.record()
+        for _ in range(args.bwd_steps):
+            mlstm_bwd_parallel(*fa[:6], dh, grads=grads, workspace=bws)
+        e1.record()
+        torch.cuda.synchronize()
+        bwall = time.perf_counter() - t_start
+        bwd_ms = e0.elapsed_time(e1) / args.bwd_steps
+        bflops = bwd_alg_flops(w)
+        btf = bflops / (bwd_ms / 1e3) / 1e12
+        out["backward"] = {
+            "workload": f"{w.name}: mlstm_bwd_parallel B={w.B} NH={w.NH} S={w.S} d_qk={w.dqk} d_v={w.dv} "
+                        "bf16 q/k/v/dh, fp32 gradients",
+            "tokens_per_s": tokens * args.bwd_steps / bwall, "ms_per_call": bwd_ms,
+            "roofline": {"kernel": "mlstm_bwd_parallel (whole call)", "bound": "mfma", "achieved": btf,
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": btf / BF16_PEAK_TFLOPS,
+                         "traffic": None, "alg_flops_per_call": bflops},
+        }
+        del dh, bws, grads
+        torch.cuda.empty_cache()
+    del d
+
     # ---------------- decode step ---------------------------------------------
     if not args.no_decode:
-        del d, ws, h, C, n, m
-        torch.cuda.empty_cache()
         wd = inputs.WORKLOADS["decode"]
         T = args.decode_steps
         st = inputs.step_state(wd)

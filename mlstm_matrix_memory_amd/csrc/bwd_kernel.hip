@@ -151,7 +151,16 @@ struct BwdIn {
     const T* q; const T* k; const T* v; const T* dh;
     const float* i_pre; const float* f_pre; const float* o_pre;
     int S, dqk, dv;
+    int heads, nb;          // heads and 64-token blocks per head
 };
+
+// (head, block) of a workgroup of the 1-D grid over blocks x heads: all heads' block
+// 0 first, then block 1, ...; block 0 is each kernel's heaviest, so the longest
+// workgroups start first and the short ones fill in at the end
+__device__ __forceinline__ void grid_block(int heads, int& bh, int& blk) {
+    bh = blockIdx.x % heads;
+    blk = blockIdx.x / heads;
+}
 
 // D'_ts for row t (query) and column s (key) of the current tile pair, 0 above the diagonal
 __device__ __forceinline__ float decay(const BwdSmem& sm, int tq, int sk, int r, int c) {
@@ -498,14 +507,29 @@ __device__ __forceinline__ bf16x8 ld8(const bf16* p, bool ok) {
     return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// stage rows [row0, row0 + R) of a [.., d] bf16 tensor into LDS (pitch P), zero outside
-template <int R, int D, int P>
+// stage rows [row0, row0 + R) of a [.., d] bf16 tensor into LDS (pitch P), zero
+// outside; loads are issued in batches of BATCH per thread before their stores, so
+// that many are in flight at once
+template <int R, int D, int P, int MAXB>
 __device__ __forceinline__ void stage_rows(bf16* dst, const bf16* src, size_t tok0, int row0, int S, int d, int tid) {
-    constexpr int U = R * D / 8;
-    for (int u = tid; u < U; u += MB_THREADS) {
-        const int r = u / (D / 8), c8 = 8 * (u % (D / 8));
-        const bool ok = row0 + r < S && c8 < d;
-        *reinterpret_cast<bf16x8*>(dst + r * P + c8) = ld8(src + (tok0 + row0 + r) * d + c8, ok);
+    constexpr int U = R * D / 8;                        // 16-byte units
+    constexpr int UPT = (U + MB_THREADS - 1) / MB_THREADS;
+    constexpr int BATCH = UPT < MAXB ? UPT : MAXB;
+#pragma unroll
+    for (int b0 = 0; b0 < UPT; b0 += BATCH) {
+        bf16x8 tmp[BATCH];
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            const int u = tid + (b0 + b) * MB_THREADS;
+            const int r = u / (D / 8), c8 = 8 * (u % (D / 8));
+            tmp[b] = ld8(src + (tok0 + row0 + r) * d + c8, b0 + b < UPT && u < U && row0 + r < S && c8 < d);
+        }
+#pragma unroll
+        for (int b = 0; b < BATCH; ++b) {
+            const int u = tid + (b0 + b) * MB_THREADS;
+            const int r = u / (D / 8), c8 = 8 * (u % (D / 8));
+            if (b0 + b < UPT && u < U) *reinterpret_cast<bf16x8*>(dst + r * P + c8) = tmp[b];
+        }
     }
 }
 
@@ -525,7 +549,9 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
     constexpr int P = D + 8;
     constexpr int NB = D / 16, KS = D / 32;
     __shared__ RowsSmem<D> sm;
-    const int rb = gridDim.y - 1 - blockIdx.y, bh = blockIdx.x;
+    int bh, rb;
+    grid_block(in.heads, bh, rb);
+    rb = in.nb - 1 - rb;                        // the last query blocks have the most key blocks
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 15, g = lane >> 4;
     const int S = in.S, dqk = in.dqk, dv = in.dv;
     const size_t tokh = (size_t)bh * S;
@@ -542,8 +568,8 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
 
     auto stage = [&](int c0) {
         __syncthreads();
-        stage_rows<64, D, P>(sm.k, in.k, tokh, c0, S, dqk, tid);
-        stage_rows<64, D, P>(sm.v, in.v, tokh, c0, S, dv, tid);
+        stage_rows<64, D, P, 8>(sm.k, in.k, tokh, c0, S, dqk, tid);
+        stage_rows<64, D, P, 8>(sm.v, in.v, tokh, c0, S, dv, tid);
         if (tid < 64) {
             const int s = min(c0 + tid, S - 1);
             sm.gs[tid] = ws.F[tokh + s] - (double)in.i_pre[tokh + s];
@@ -637,7 +663,7 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
     if (tval && g == 0) ws.dden[tokh + t] = dd;
     // dnum' for the column pass (bf16 hi, then lo) and as B operands here
     bf16* dnh_g = reinterpret_cast<bf16*>(ws.dnum);
-    bf16* dnl_g = dnh_g + (size_t)gridDim.x * S * dv;
+    bf16* dnl_g = dnh_g + (size_t)in.heads * S * dv;
     bf16x8 dnh[NB / 2], dnl[NB / 2];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -733,7 +759,8 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
     constexpr int P = D + 8;
     constexpr int NB = D / 16, KS = D / 32, TB = QB / 16;
     __shared__ ColsSmem<D, QB> sm;
-    const int cb = blockIdx.y, bh = blockIdx.x;
+    int bh, cb;
+    grid_block(in.heads, bh, cb);               // the first key blocks have the most query blocks
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 15, g = lane >> 4;
     const int S = in.S, dqk = in.dqk, dv = in.dv;
     const size_t tokh = (size_t)bh * S;
@@ -742,7 +769,7 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
     const bool sval = s < S;
     const double Qs = sval ? ws.F[tokh + s] - (double)in.i_pre[tokh + s] : 0.0;
     const bf16* dnh_g = reinterpret_cast<const bf16*>(ws.dnum);
-    const bf16* dnl_g = dnh_g + (size_t)gridDim.x * S * dv;
+    const bf16* dnl_g = dnh_g + (size_t)in.heads * S * dv;
 
     f32x4 dka[NB], dva[NB];
 #pragma unroll
@@ -750,9 +777,9 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
 
     for (int r0 = c0; r0 < S; r0 += QB) {
         __syncthreads();
-        stage_rows<QB, D, P>(sm.q, in.q, tokh, r0, S, dqk, tid);
-        stage_rows<QB, D, P>(sm.dh, dnh_g, tokh, r0, S, dv, tid);
-        stage_rows<QB, D, P>(sm.dl, dnl_g, tokh, r0, S, dv, tid);
+        stage_rows<QB, D, P, 4>(sm.q, in.q, tokh, r0, S, dqk, tid);
+        stage_rows<QB, D, P, 4>(sm.dh, dnh_g, tokh, r0, S, dv, tid);
+        stage_rows<QB, D, P, 4>(sm.dl, dnl_g, tokh, r0, S, dv, tid);
         if (tid < QB) {
             const int tt = min(r0 + tid, S - 1);
             sm.rt[tid] = ws.F[tokh + tt] - ws.m[tokh + tt];
@@ -838,10 +865,10 @@ int mfma_bwd_width(const BwdArgs& a) {
 template <int D, int QB>
 hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdIn<bf16>& in, const BwdWs& w) {
     const int heads = a.B * a.NH, nb = (a.S + 63) / 64;
-    hipLaunchKernelGGL((bwd_rows_mfma<D>), dim3(heads, nb), dim3(MB_THREADS), 0, a.stream, in, w, a.dq, a.dout);
+    hipLaunchKernelGGL((bwd_rows_mfma<D>), dim3(heads * nb), dim3(MB_THREADS), 0, a.stream, in, w, a.dq, a.dout);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_cols_mfma<D, QB>), dim3(heads, nb), dim3(MB_THREADS), 0, a.stream, in, w, a.dk, a.dvv,
+    hipLaunchKernelGGL((bwd_cols_mfma<D, QB>), dim3(heads * nb), dim3(MB_THREADS), 0, a.stream, in, w, a.dk, a.dvv,
                        a.di);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_gates_kernel<bf16, true>), dim3(heads), dim3(BW_THREADS), 0, a.stream, in, a.dq, a.dk,
@@ -859,6 +886,8 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
     in.i_pre = a.i_pre; in.f_pre = a.f_pre; in.o_pre = a.o_pre;
     in.S = a.S; in.dqk = a.dqk; in.dv = a.dv;
     const int nb = (a.S + BT - 1) / BT;
+    in.heads = heads;
+    in.nb = nb;
     hipLaunchKernelGGL(bwd_gate_kernel, dim3(heads), dim3(BW_THREADS), 0, a.stream, a.i_pre, a.f_pre, a.S, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -867,7 +896,7 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
             case 64: return launch_bwd_mfma<64, 64>(a, in, w);
             case 128: return launch_bwd_mfma<128, 64>(a, in, w);
             case 256: return launch_bwd_mfma<256, 64>(a, in, w);
-            case 384: return launch_bwd_mfma<384, 64>(a, in, w);
+            case 384: return launch_bwd_mfma<384, 32>(a, in, w);
             case 512: return launch_bwd_mfma<512, 32>(a, in, w);
             default: break;
         }

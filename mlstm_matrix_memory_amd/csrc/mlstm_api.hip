@@ -264,6 +264,8 @@ static mlstm_status check_bwd_sizes(int B, int NH, int S, int dqk, int dv, mlstm
     mlstm_status s = check_fwd_sizes(B, NH, S, dqk, dv, 16, dt, true);
     if (s != MLSTM_OK) return s;
     if (S > 65535 * 64) return fail(MLSTM_ERR_UNSUPPORTED, "S=%d exceeds the backward's %d tokens", S, 65535 * 64);
+    if ((long long)B * NH * ((S + 63) / 64) > 0x7fffffffLL)
+        return fail(MLSTM_ERR_UNSUPPORTED, "B*NH*ceil(S/64) exceeds the backward's grid");
     return MLSTM_OK;
 }
 
