@@ -7,7 +7,8 @@ never imports, links or calls it, and it shares no code with the HIP library.
 The arithmetic lives in ``mlstm_oracle.c`` (plain C, fp64, OpenMP over the
 independent heads): the stabilized mLSTM recurrence of "xLSTM: Extended Long
 Short-Term Memory", section 2.3 (eq. (18), the normalizer paragraph and the
-multi-head paragraph) with the stabilizer of section 2.2 (eq. (17)).  This module
+multi-head paragraph) with the stabilizer of section 2.2 (eq. (17)), the
+derivative of its parallel form, and the mLSTM block's epilogue (Figure 10).  This module
 only compiles it with gcc and marshals numpy arrays through ctypes.
 """
 from __future__ import annotations
@@ -42,6 +43,8 @@ def _bind(lib):
     lib.oracle_step_f64.argtypes = [dp] * 6 + [ctypes.c_int] * 4 + [dp] * 4
     lib.oracle_bwd_f64.restype = ctypes.c_int
     lib.oracle_bwd_f64.argtypes = [dp] * 7 + [ctypes.c_int] * 5 + [dp] * 6
+    lib.oracle_epilogue_f64.restype = ctypes.c_int
+    lib.oracle_epilogue_f64.argtypes = [dp] * 6 + [ctypes.c_int] * 4 + [ctypes.c_double, ctypes.c_int, dp]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     return lib
@@ -140,6 +143,23 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_bwd_f64 rejected its arguments")
         return tuple(out)
+
+    def epilogue(self, h, x, z, gn_w, gn_b, skip_w, eps, act):
+        """mLSTM block epilogue: per-head GroupNorm of h, plus skip_w * x, gated by act(z).
+
+        h, x, z [B,NH,S,dv]; gn_w, gn_b, skip_w [NH,dv]; act 0 = sigmoid, 1 = swish.
+        Returns y [B,NH,S,dv] in fp64.
+        """
+        h, x, z, gn_w, gn_b, skip_w = map(_f64, (h, x, z, gn_w, gn_b, skip_w))
+        B, NH, S, dv = h.shape
+        assert x.shape == h.shape and z.shape == h.shape
+        assert gn_w.shape == (NH, dv) and gn_b.shape == (NH, dv) and skip_w.shape == (NH, dv)
+        y = np.empty_like(h)
+        rc = self.lib.oracle_epilogue_f64(_ptr(h), _ptr(x), _ptr(z), _ptr(gn_w), _ptr(gn_b), _ptr(skip_w),
+                                          B, NH, S, dv, float(eps), int(act), _ptr(y))
+        if rc != 0:
+            raise ValueError("oracle_epilogue_f64 rejected its arguments")
+        return y
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())

@@ -278,6 +278,47 @@ int oracle_bwd_f64(const double *q, const double *k, const double *v,
 }
 
 /* Number of OpenMP threads a parallel region of the oracle would use. */
+/*
+ * mLSTM block epilogue (xLSTM paper, Figure 10 caption, the mLSTM block): the
+ * cell output h of each head is normalized by a GroupNorm with one group per
+ * head (a LayerNorm over that head's d_v channels, with a per-channel scale and
+ * shift), the learnable skip input is added, and the sum is gated component-wise
+ * by the external output gate:
+ *   mu = mean_r h_r,  var = mean_r (h_r - mu)^2            (over the head's d_v)
+ *   y_r = (gn_w_r (h_r - mu) / sqrt(var + eps) + gn_b_r + skip_w_r x_r) * act(z_r)
+ * The caption does not name the gate's activation: act = sigmoid (act = 0) or
+ * swish z sigmoid(z) (act = 1).  Per-channel parameters are [NH][dv]; h, x, z and
+ * y are [B][NH][S][dv].
+ */
+int oracle_epilogue_f64(const double *h, const double *x, const double *z,
+                        const double *gn_w, const double *gn_b, const double *skip_w,
+                        int B, int NH, int S, int dv, double eps, int act, double *y)
+{
+    if (B < 0 || NH < 0 || S < 0 || dv <= 0 || !(eps >= 0.0) || (act != 0 && act != 1))
+        return -1;
+    if (!h || !x || !z || !gn_w || !gn_b || !skip_w || !y)
+        return -1;
+    for (int b = 0; b < B; ++b)
+        for (int hd = 0; hd < NH; ++hd)
+            for (int t = 0; t < S; ++t) {
+                const size_t row = (((size_t)b * NH + hd) * S + t) * dv;
+                const double *hr = h + row;
+                double mu = 0.0;
+                for (int r = 0; r < dv; ++r) mu += hr[r];
+                mu /= dv;
+                double var = 0.0;
+                for (int r = 0; r < dv; ++r) var += (hr[r] - mu) * (hr[r] - mu);
+                var /= dv;
+                const double inv = 1.0 / sqrt(var + eps);
+                for (int r = 0; r < dv; ++r) {
+                    const size_t c = (size_t)hd * dv + r;
+                    const double g = act == 0 ? sigmoid(z[row + r]) : z[row + r] * sigmoid(z[row + r]);
+                    y[row + r] = (gn_w[c] * (hr[r] - mu) * inv + gn_b[c] + skip_w[c] * x[row + r]) * g;
+                }
+            }
+    return 0;
+}
+
 int oracle_num_threads(void)
 {
     int nt = 1;

@@ -395,6 +395,68 @@ def pin_bwd_linear_in_dh(orc):
         _close(c, 2.0 * a - 3.0 * b, rtol=1e-11, what="linearity in dh")
 
 
+# ---- mLSTM block epilogue (Figure 10 caption) --------------------------------
+def _epi_case(seed, B=2, NH=3, S=5, dv=8):
+    rng = np.random.default_rng(seed)
+    h = rng.standard_normal((B, NH, S, dv)) * 2.0 + 0.5
+    x = rng.standard_normal((B, NH, S, dv))
+    z = rng.standard_normal((B, NH, S, dv)) * 2.0
+    gw = 1.0 + 0.3 * rng.standard_normal((NH, dv))
+    gb = 0.3 * rng.standard_normal((NH, dv))
+    sw = 1.0 + 0.3 * rng.standard_normal((NH, dv))
+    return h, x, z, gw, gb, sw
+
+
+def pin_epilogue_library_group_norm(orc):
+    """GroupNorm with one group per head is torch's group_norm over a token's NH*dv
+    channels (head-major); the gate is torch's sigmoid / silu."""
+    import torch
+    h, x, z, gw, gb, sw = _epi_case(81)
+    B, NH, S, dv = h.shape
+    eps = 1e-3
+    tok = lambda a: torch.from_numpy(np.ascontiguousarray(a.transpose(0, 2, 1, 3).reshape(B * S, NH * dv)))
+    gn = torch.nn.functional.group_norm(tok(h), NH, torch.from_numpy(gw.reshape(-1)),
+                                        torch.from_numpy(gb.reshape(-1)), eps)
+    pre = gn + torch.from_numpy(sw.reshape(-1)) * tok(x)
+    for act, fn in ((0, torch.sigmoid), (1, torch.nn.functional.silu)):
+        want = (pre * fn(tok(z))).numpy().reshape(B, S, NH, dv).transpose(0, 2, 1, 3)
+        _close(orc.epilogue(h, x, z, gw, gb, sw, eps, act), want, rtol=1e-12, what=f"group_norm act={act}")
+
+
+def pin_epilogue_constant_head(orc):
+    """A head whose channels are all equal normalizes to zero: y = (gn_b + skip_w x) act(z)."""
+    h, x, z, gw, gb, sw = _epi_case(82)
+    h[:] = h[..., :1]
+    sig = 1.0 / (1.0 + np.exp(-z))
+    _close(orc.epilogue(h, x, z, gw, gb, sw, 1e-5, 0), (gb[None, :, None, :] + sw[None, :, None, :] * x) * sig,
+           rtol=1e-12, what="constant head")
+
+
+def pin_epilogue_shift_scale_invariance(orc):
+    """Without eps the normalization forgets any positive scale and shift of a head's row."""
+    h, x, z, gw, gb, sw = _epi_case(83)
+    a = 3.7 * np.ones_like(h)
+    a[:, 1] = 0.02
+    y0 = orc.epilogue(h, x, z, gw, gb, sw, 0.0, 1)
+    y1 = orc.epilogue(a * h - 11.0, x, z, gw, gb, sw, 0.0, 1)
+    _close(y1, y0, rtol=1e-9, what="shift/scale invariance")
+
+
+def pin_epilogue_swish_is_z_times_sigmoid(orc):
+    """The swish-gated output is the sigmoid-gated one times z."""
+    h, x, z, gw, gb, sw = _epi_case(84)
+    _close(orc.epilogue(h, x, z, gw, gb, sw, 1e-5, 1), orc.epilogue(h, x, z, gw, gb, sw, 1e-5, 0) * z,
+           rtol=1e-12, what="swish vs sigmoid")
+
+
+EPI_PINS = [
+    pin_epilogue_library_group_norm,
+    pin_epilogue_constant_head,
+    pin_epilogue_shift_scale_invariance,
+    pin_epilogue_swish_is_z_times_sigmoid,
+]
+
+
 BWD_PINS = [
     pin_bwd_finite_differences_floor_inactive,
     pin_bwd_finite_differences_floor_active,

@@ -10,7 +10,7 @@ import os
 import pytest
 
 import oracle
-from oracle_pins import ALL_PINS, BWD_PINS
+from oracle_pins import ALL_PINS, BWD_PINS, EPI_PINS
 
 MUTANTS = {
     "forget_gate_dropped_on_C": (
@@ -77,6 +77,25 @@ MUTANTS = {
     "bwd_log_sigmoid_derivative": (
         "dfh[j] = rev * sigmoid(-fh[j]);",
         "dfh[j] = rev * sigmoid(fh[j]);"),
+    # block epilogue
+    "epi_unbiased_variance": (
+        "var /= dv;",
+        "var /= (dv - 1);"),
+    "epi_shift_dropped": (
+        "* inv + gn_b[c] + skip_w[c]",
+        "* inv + skip_w[c]"),
+    "epi_skip_ungated": (
+        "(gn_w[c] * (hr[r] - mu) * inv + gn_b[c] + skip_w[c] * x[row + r]) * g;",
+        "(gn_w[c] * (hr[r] - mu) * inv + gn_b[c]) * g + skip_w[c] * x[row + r];"),
+    "epi_mean_not_subtracted": (
+        "gn_w[c] * (hr[r] - mu) * inv",
+        "gn_w[c] * hr[r] * inv"),
+    "epi_channel_ignores_head": (
+        "const size_t c = (size_t)hd * dv + r;",
+        "const size_t c = r;"),
+    "epi_swish_as_sigmoid": (
+        ": z[row + r] * sigmoid(z[row + r]);",
+        ": sigmoid(z[row + r]);"),
 }
 
 
@@ -91,7 +110,7 @@ def test_mutant_is_caught(name, tmp_path):
     oracle.build(str(mutated), lib_path)
     orc = oracle.Oracle(oracle.load(lib_path))
     failed = []
-    for pin in ALL_PINS + BWD_PINS:
+    for pin in ALL_PINS + BWD_PINS + EPI_PINS:
         try:
             pin(orc)
         except (AssertionError, FloatingPointError, ValueError):
