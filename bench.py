@@ -9,7 +9,8 @@ exactly --steps steps.  The same run also times the one-token decode step
 consecutive steps) and reports it under "decode", and the backward
 (mlstm_bwd_parallel: gradients of the same forward with respect to q, k, v and
 the three gate pre-activations, given dh) on the forward's workload under
-"backward".
+"backward", and the mLSTM block epilogue (mlstm_block_epilogue: per-head GroupNorm,
+learnable skip, external output gate) on the forward's h shape under "epilogue".
 
 Roofline: the dominant kernel of the forward is the scan; its duration is taken
 with HIP events recorded on the stream the kernels run on, and its algorithmic
@@ -67,6 +68,11 @@ def fwd_alg_bytes(w) -> float:
 
 def bwd_alg_flops(w) -> float:
     return float(w.B * w.NH) * w.S * (w.S + 1) / 2 * 6.0 * (w.dqk + w.dv)
+
+
+def epilogue_alg_bytes(w) -> float:
+    e = 2
+    return float(w.B * w.NH * w.S * w.dv) * 4 * e + float(w.NH * w.dv) * 12   # h, x, z, y + parameters
 
 
 def step_alg_bytes(w) -> float:
@@ -128,6 +134,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-epilogue", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
@@ -142,7 +149,8 @@ def main() -> int:
     import numpy as np
     import torch
 
-    from mlstm_matrix_memory_amd import (MLSTM_BF16, inputs, mlstm_bwd_parallel, mlstm_bwd_workspace_bytes,
+    from mlstm_matrix_memory_amd import (MLSTM_BF16, MLSTM_GATE_SWISH, inputs, mlstm_block_epilogue,
+                                         mlstm_bwd_parallel, mlstm_bwd_workspace_bytes,
                                          mlstm_fwd_prepare, mlstm_fwd_scan, mlstm_fwd_workspace_bytes, mlstm_step)
 
     dev = torch.device("cuda:0")
@@ -253,6 +261,37 @@ def main() -> int:
         del dh, bws, grads
         torch.cuda.empty_cache()
     del d
+
+    # ---------------- block epilogue ------------------------------------------
+    if not args.no_epilogue:
+        ex = inputs.epilogue_inputs(w)
+        de = {k: gpu(v, w.dtype if k in ("h", "x", "z") else "f32") for k, v in ex.items()}
+        del ex
+        y = torch.empty_like(de["h"])
+        ea = (de["h"], de["x"], de["z"], de["gn_w"], de["gn_b"], de["skip_w"])
+        for _ in range(3):
+            mlstm_block_epilogue(*ea, eps=1e-5, act=MLSTM_GATE_SWISH, y_out=y)
+        torch.cuda.synchronize()
+        n_ep = 20
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_ep):
+            mlstm_block_epilogue(*ea, eps=1e-5, act=MLSTM_GATE_SWISH, y_out=y)
+        e1.record()
+        torch.cuda.synchronize()
+        ep_ms = e0.elapsed_time(e1) / n_ep
+        ep_bytes = epilogue_alg_bytes(w)
+        ep_gbs = ep_bytes / (ep_ms / 1e3) / 1e9
+        out["epilogue"] = {
+            "workload": f"{w.name}: mlstm_block_epilogue B={w.B} NH={w.NH} S={w.S} d_v={w.dv} bf16 h/x/z/y, "
+                        "swish gate",
+            "us_per_call": ep_ms * 1e3,
+            "roofline": {"kernel": "epilogue_kernel", "bound": "hbm", "achieved": ep_gbs, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": ep_gbs / HBM_PEAK_GBS, "traffic": None,
+                         "alg_bytes_per_launch": ep_bytes},
+        }
+        del de, y, ea
+        torch.cuda.empty_cache()
 
     # ---------------- decode step ---------------------------------------------
     if not args.no_decode:

@@ -68,6 +68,12 @@ typedef enum mlstm_dtype {
     MLSTM_BF16 = 1
 } mlstm_dtype;
 
+/* activation of the mLSTM block's external output gate (mlstm_block_epilogue) */
+typedef enum mlstm_gate_act {
+    MLSTM_GATE_SIGMOID = 0,      /* sigmoid(z)        */
+    MLSTM_GATE_SWISH = 1         /* z * sigmoid(z)    */
+} mlstm_gate_act;
+
 /*
  * Bytes of device workspace a forward over these sizes needs (0 if none): what
  * mlstm_fwd_parallel (and its two stages) need when S is a multiple of chunk,
@@ -227,6 +233,40 @@ mlstm_status mlstm_bwd_parallel(const void *q, const void *k, const void *v,
                                 float *grad_q, float *grad_k, float *grad_v,
                                 float *grad_i, float *grad_f, float *grad_o,
                                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Epilogue of the mLSTM block ("xLSTM: Extended Long Short-Term Memory",
+ * Figure 10 and its caption): the cell output is normalized by a GroupNorm with
+ * one group per head (a LayerNorm over the head's d_v channels with a
+ * per-channel scale and shift), the learnable skip input is added, and the sum is
+ * gated component-wise by the external output gate.  Per (b, head, t):
+ *   mu = mean_r h_r,  var = mean_r (h_r - mu)^2     (population variance)
+ *   y_r = (gn_weight_r (h_r - mu) / sqrt(var + eps) + gn_bias_r
+ *          + skip_weight_r x_r) * act(z_r)
+ * The caption does not name the gate's activation; act selects sigmoid or swish.
+ *
+ * Arguments
+ *   h               [B,NH,S,d_v] dtype, the cell output (e.g. h_out of a forward)
+ *   x               [B,NH,S,d_v] dtype, the skip input of each head's channels
+ *   z               [B,NH,S,d_v] dtype, external output gate pre-activations
+ *   gn_weight, gn_bias, skip_weight
+ *                   [NH,d_v] fp32 per-channel parameters (channel r of head hd at
+ *                   hd*d_v + r)
+ *   B, NH, S        >= 1;  d_v a multiple of 16, <= 4096
+ *   eps             >= 0 (finite); a row with zero variance needs eps > 0
+ *   act             MLSTM_GATE_SIGMOID or MLSTM_GATE_SWISH
+ *   dtype           MLSTM_F32 or MLSTM_BF16 (of h, x, z and y_out)
+ *   y_out           [B,NH,S,d_v] dtype, written; may be the same buffer as h, x
+ *                   or z (each element is read before it is written, by the same
+ *                   thread), but must not partly overlap any of them
+ * All tensor pointers must be 16-byte aligned.
+ */
+mlstm_status mlstm_block_epilogue(const void *h, const void *x, const void *z,
+                                  const float *gn_weight, const float *gn_bias,
+                                  const float *skip_weight,
+                                  int B, int NH, int S, int d_v, float eps,
+                                  mlstm_gate_act act, mlstm_dtype dtype,
+                                  void *y_out, void *stream);
 
 /* Static description of a status code. */
 const char *mlstm_status_string(mlstm_status status);

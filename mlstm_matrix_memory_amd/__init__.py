@@ -9,15 +9,20 @@ Entry points (same names as include/mlstm.h):
   mlstm_step          one-token recurrent decode step, state updated in place
   mlstm_bwd_parallel  gradients of the zero-state forward with respect to all inputs
   mlstm_bwd_workspace_bytes
+  mlstm_block_epilogue
+                      the mLSTM block's per-head GroupNorm, learnable skip and external output gate
   mlstm_fwd_workspace_bytes, mlstm_status_string, mlstm_error_detail
 """
 from .binding import (  # noqa: F401
     MLSTM_BF16,
     MLSTM_F32,
+    MLSTM_GATE_SIGMOID,
+    MLSTM_GATE_SWISH,
     MlstmError,
     load_library,
     mlstm_bwd_parallel,
     mlstm_bwd_workspace_bytes,
+    mlstm_block_epilogue,
     mlstm_error_detail,
     mlstm_fwd_parallel,
     mlstm_fwd_parallel_state,

@@ -64,6 +64,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mlstm_bwd_parallel.restype = i
     lib.mlstm_bwd_parallel.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, i,
                                        fp, fp, fp, fp, fp, fp, vp, sz, vp]
+    lib.mlstm_block_epilogue.restype = i
+    lib.mlstm_block_epilogue.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, ctypes.c_float, i, i, vp, vp]
     lib.mlstm_step.restype = i
     lib.mlstm_step.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, fp, fp, fp, vp, vp]
     lib.mlstm_status_string.restype = ctypes.c_char_p
@@ -279,6 +281,41 @@ def mlstm_bwd_parallel(q, k, v, i_pre, f_pre, o_pre, dh, grads=None, workspace=N
     if st != MLSTM_OK:
         raise MlstmError("mlstm_bwd_parallel", st, mlstm_error_detail())
     return tuple(grads)
+
+
+MLSTM_GATE_SIGMOID = 0
+MLSTM_GATE_SWISH = 1
+
+
+def mlstm_block_epilogue(h, x, z, gn_weight, gn_bias, skip_weight, eps: float = 1e-5,
+                         act: int = MLSTM_GATE_SIGMOID, y_out=None, stream=None):
+    """Per-head GroupNorm of h, plus skip_weight * x, gated by act(z); returns y.
+
+    h, x, z [B,NH,S,d_v] float32 or bfloat16 (one dtype); gn_weight, gn_bias,
+    skip_weight [NH,d_v] float32; y_out like h (may be h, x or z itself).
+    """
+    import torch
+    lib = load_library()
+    if h.dim() != 4:
+        raise ValueError("h must be 4-D [B, NH, S, d_v]")
+    B, NH, S, dv = h.shape
+    dev = h.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    dt = _dtype_code(h)
+    for t, name in ((h, "h"), (x, "x"), (z, "z")):
+        _check(t, name, (B, NH, S, dv), h.dtype, dev)
+    for t, name in ((gn_weight, "gn_weight"), (gn_bias, "gn_bias"), (skip_weight, "skip_weight")):
+        _check(t, name, (NH, dv), torch.float32, dev)
+    if y_out is None:
+        y_out = torch.empty_like(h)
+    _check(y_out, "y_out", (B, NH, S, dv), h.dtype, dev)
+    st = lib.mlstm_block_epilogue(h.data_ptr(), x.data_ptr(), z.data_ptr(), gn_weight.data_ptr(),
+                                  gn_bias.data_ptr(), skip_weight.data_ptr(), B, NH, S, dv, float(eps), int(act),
+                                  dt, y_out.data_ptr(), _stream_handle(stream, dev))
+    if st != MLSTM_OK:
+        raise MlstmError("mlstm_block_epilogue", st, mlstm_error_detail())
+    return y_out
 
 
 def mlstm_step(q, k, v, i_pre, f_pre, o_pre, C, n, m, h_out=None, stream=None):

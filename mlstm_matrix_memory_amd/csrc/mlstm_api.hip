@@ -312,6 +312,40 @@ mlstm_status mlstm_bwd_parallel(const void* q, const void* k, const void* v,
     return ok();
 }
 
+mlstm_status mlstm_block_epilogue(const void* h, const void* x, const void* z,
+                                  const float* gn_weight, const float* gn_bias, const float* skip_weight,
+                                  int B, int NH, int S, int d_v, float eps, mlstm_gate_act act,
+                                  mlstm_dtype dtype, void* y_out, void* stream) {
+    if (B < 1 || NH < 1 || S < 1)
+        return fail(MLSTM_ERR_INVALID_ARG, "B=%d, NH=%d, S=%d must all be >= 1", B, NH, S);
+    if (d_v < 16 || d_v > MAX_DIM || d_v % 16 != 0)
+        return fail(MLSTM_ERR_INVALID_ARG, "d_v=%d must be a multiple of 16 in [16, %d]", d_v, MAX_DIM);
+    mlstm_status s = check_dtype(dtype);
+    if (s != MLSTM_OK) return s;
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(MLSTM_ERR_INVALID_ARG, "eps=%g must be finite and >= 0", eps);
+    if (act != MLSTM_GATE_SIGMOID && act != MLSTM_GATE_SWISH)
+        return fail(MLSTM_ERR_INVALID_ARG, "act=%d is neither MLSTM_GATE_SIGMOID nor MLSTM_GATE_SWISH", (int)act);
+    if ((long long)B * NH * S * d_v > (1LL << 40) || (long long)B * NH * S > 0x7fffffffLL * 4)
+        return fail(MLSTM_ERR_UNSUPPORTED, "tensor too large");
+    const void* ptrs[] = {h, x, z, gn_weight, gn_bias, skip_weight, y_out};
+    const char* names[] = {"h", "x", "z", "gn_weight", "gn_bias", "skip_weight", "y_out"};
+    for (int p = 0; p < 7; ++p) {
+        if (!ptrs[p]) return fail(MLSTM_ERR_INVALID_ARG, "%s is NULL", names[p]);
+        if (!aligned16(ptrs[p])) return fail(MLSTM_ERR_INVALID_ARG, "%s is not 16-byte aligned", names[p]);
+    }
+    const size_t bytes = (size_t)B * NH * S * d_v * (dtype == MLSTM_BF16 ? 2 : 4);
+    for (int p = 0; p < 3; ++p)
+        if (ptrs[p] != y_out && overlaps(ptrs[p], bytes, y_out, bytes))
+            return fail(MLSTM_ERR_INVALID_ARG, "y_out partly overlaps %s", names[p]);
+    mlstm::EpilogueArgs a = {};
+    a.h = h; a.x = x; a.z = z; a.gn_w = gn_weight; a.gn_b = gn_bias; a.skip_w = skip_weight;
+    a.B = B; a.NH = NH; a.S = S; a.dv = d_v; a.eps = eps; a.act = (int)act; a.dtype = dtype; a.y = y_out;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = mlstm::launch_epilogue(a);
+    if (e != hipSuccess) return fail(MLSTM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 const char* mlstm_status_string(mlstm_status status) {
     switch (status) {
         case MLSTM_OK: return "ok";

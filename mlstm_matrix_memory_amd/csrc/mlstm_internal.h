@@ -116,6 +116,19 @@ struct BwdArgs {
     hipStream_t stream;
 };
 
+struct EpilogueArgs {
+    const void* h; const void* x; const void* z;
+    const float* gn_w; const float* gn_b; const float* skip_w;
+    int B, NH, S, dv;
+    float eps;
+    int act;                 // 0 sigmoid, 1 swish
+    mlstm_dtype dtype;
+    void* y;
+    hipStream_t stream;
+};
+
+hipError_t launch_epilogue(const EpilogueArgs& a);
+
 hipError_t launch_step(const StepArgs& a);
 
 // generic chunkwise forward on the vector ALUs (any supported shape, fp32 or bf16)

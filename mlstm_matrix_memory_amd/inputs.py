@@ -14,7 +14,8 @@ Workloads (xLSTM language-model layer shapes; gate pre-activations fp32):
 
 Recipe (per workload, generator ``numpy.random.default_rng(seed)``):
   draw order q, k, v, i~, f~, o~ (then the spike positions, then the decode state);
-  the backward's dh ~ N(0,1) comes from a generator of its own (seed + 2000);
+  the backward's dh ~ N(0,1) comes from a generator of its own (seed + 2000), the
+  block epilogue's inputs from another (seed + 3000);
   normals drawn directly in float32; k scaled by 1/sqrt(d_qk) in fp32 for the
   forward workloads (decode keys are unscaled N(0,1)); q, k, v of bf16 workloads
   rounded to bf16 with round-to-nearest-even, kept here as float32 arrays that
@@ -131,6 +132,30 @@ def bwd_dh(w: Workload, seed: int | None = None, B: int | None = None, NH: int |
     rng = np.random.default_rng((w.seed if seed is None else seed) + 2000)
     dh = _normal(rng, (B, NH, S, dv))
     return bf16_round(dh) if w.dtype == "bf16" else dh
+
+
+def epilogue_inputs(w: Workload, seed: int | None = None, B: int | None = None, NH: int | None = None,
+                    S: int | None = None, dv: int | None = None):
+    """Inputs of the mLSTM block epilogue (generator seeded with seed + 3000).
+
+    h, x, z ~ N(0,1) [B,NH,S,dv] (bf16-rounded for bf16 workloads); per-channel
+    parameters [NH,dv] float32: gn_w ~ 1 + 0.1 N(0,1), gn_b ~ 0.1 N(0,1),
+    skip_w ~ 1 + 0.1 N(0,1) (away from 1 and 0, so a wrong channel index shows).
+    """
+    B = w.B if B is None else B
+    NH = w.NH if NH is None else NH
+    S = w.S if S is None else S
+    dv = w.dv if dv is None else dv
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 3000)
+    h = _normal(rng, (B, NH, S, dv))
+    x = _normal(rng, (B, NH, S, dv))
+    z = _normal(rng, (B, NH, S, dv))
+    gn_w = _normal(rng, (NH, dv), 1.0, 0.1)
+    gn_b = _normal(rng, (NH, dv), 0.0, 0.1)
+    skip_w = _normal(rng, (NH, dv), 1.0, 0.1)
+    if w.dtype == "bf16":
+        h, x, z = bf16_round(h), bf16_round(x), bf16_round(z)
+    return dict(h=h, x=x, z=z, gn_w=gn_w, gn_b=gn_b, skip_w=skip_w)
 
 
 def step_state(w: Workload, seed: int | None = None, B: int | None = None, NH: int | None = None,

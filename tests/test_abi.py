@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol(lib):
     names = b.header_symbols()
     assert {"mlstm_fwd_parallel", "mlstm_fwd_parallel_state", "mlstm_fwd_prepare", "mlstm_fwd_scan",
             "mlstm_step", "mlstm_fwd_workspace_bytes", "mlstm_status_string", "mlstm_error_detail",
-            "mlstm_bwd_parallel", "mlstm_bwd_workspace_bytes"} <= set(names)
+            "mlstm_bwd_parallel", "mlstm_bwd_workspace_bytes", "mlstm_block_epilogue"} <= set(names)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in include/mlstm.h but not exported"
 
@@ -148,7 +148,7 @@ def test_binding_has_same_names_as_abi():
     import mlstm_matrix_memory_amd as pkg
     for name in ("mlstm_fwd_parallel", "mlstm_fwd_parallel_state", "mlstm_fwd_prepare", "mlstm_fwd_scan",
                  "mlstm_step", "mlstm_fwd_workspace_bytes", "mlstm_status_string", "mlstm_error_detail",
-                 "mlstm_bwd_parallel", "mlstm_bwd_workspace_bytes"):
+                 "mlstm_bwd_parallel", "mlstm_bwd_workspace_bytes", "mlstm_block_epilogue"):
         assert callable(getattr(pkg, name))
 
 
@@ -223,3 +223,39 @@ def test_bwd_workspace_grows_with_the_sequence():
     # per token at least the fp64 cumulative gate and stabilizer and the fp32 dnum row
     assert large - small >= 2 * (640 - 64) * (16 + 48 * 4)
     assert b.mlstm_bwd_workspace_bytes(1, 1, 64, 24, 32, b.MLSTM_F32) == 0
+
+
+def _epi(lib, B=1, NH=2, S=8, dv=32, eps=1e-5, act=0, dt=b.MLSTM_BF16, ptrs=None):
+    p = [FAKE] * 7 if ptrs is None else ptrs
+    return lib.mlstm_block_epilogue(*p[:6], B, NH, S, dv, eps, act, dt, p[6], None)
+
+
+@pytest.mark.parametrize("kw,detail", [
+    (dict(S=0), "S=0"),
+    (dict(dv=40), "d_v=40"),
+    (dict(eps=-1.0), "eps"),
+    (dict(eps=float("nan")), "eps"),
+    (dict(act=2), "act=2"),
+    (dict(dt=9), "dtype=9"),
+])
+def test_epilogue_rejects_bad_arguments(lib, kw, detail):
+    assert _epi(lib, **kw) == b.MLSTM_ERR_INVALID_ARG
+    assert detail in b.mlstm_error_detail()
+
+
+@pytest.mark.parametrize("which", range(7))
+def test_epilogue_rejects_null_pointer(lib, which):
+    ptrs = [FAKE] * 7
+    ptrs[which] = None
+    assert _epi(lib, ptrs=ptrs) == b.MLSTM_ERR_INVALID_ARG
+    assert "NULL" in b.mlstm_error_detail()
+
+
+def test_epilogue_rejects_partial_overlap(lib):
+    # y_out may be h itself, but not a shifted view of it
+    ptrs = [0x100000, 0x200000, 0x300000, FAKE, FAKE, FAKE, 0x100000 + 64]
+    assert _epi(lib, ptrs=ptrs) == b.MLSTM_ERR_INVALID_ARG
+    assert "overlaps h" in b.mlstm_error_detail()
+    ptrs[3] = FAKE_MIS
+    assert _epi(lib, ptrs=ptrs) == b.MLSTM_ERR_INVALID_ARG
+    assert "aligned" in b.mlstm_error_detail()
