@@ -8,7 +8,8 @@ The arithmetic lives in ``mlstm_oracle.c`` (plain C, fp64, OpenMP over the
 independent heads): the stabilized mLSTM recurrence of "xLSTM: Extended Long
 Short-Term Memory", section 2.3 (eq. (18), the normalizer paragraph and the
 multi-head paragraph) with the stabilizer of section 2.2 (eq. (17)), the
-derivative of its parallel form, and the mLSTM block's epilogue (Figure 10).  This module
+derivative of its parallel form, the mLSTM block's epilogue (Figure 10), and
+the sLSTM recurrence with block-diagonal memory mixing (section 2.2).  This module
 only compiles it with gcc and marshals numpy arrays through ctypes.
 """
 from __future__ import annotations
@@ -45,6 +46,8 @@ def _bind(lib):
     lib.oracle_bwd_f64.argtypes = [dp] * 7 + [ctypes.c_int] * 5 + [dp] * 6
     lib.oracle_epilogue_f64.restype = ctypes.c_int
     lib.oracle_epilogue_f64.argtypes = [dp] * 6 + [ctypes.c_int] * 4 + [ctypes.c_double, ctypes.c_int, dp]
+    lib.oracle_slstm_f64.restype = ctypes.c_int
+    lib.oracle_slstm_f64.argtypes = [dp, dp] + [ctypes.c_int] * 5 + [dp] * 4 + [dp] * 5
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     return lib
@@ -160,6 +163,28 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle_epilogue_f64 rejected its arguments")
         return y
+
+    def slstm(self, x_pre, R, forget_exp=0, c0=None, n0=None, m0=None, h0=None):
+        """sLSTM recurrence.  x_pre [B,NH,S,4,dh] (gates z, i, f, o), R [NH,4,dh,dh].
+
+        Returns (h [B,NH,S,dh], c, n, m, h_last [B,NH,dh]) in fp64; the state is the
+        stabilized one.  All of c0, n0, m0, h0 None = zero state.
+        """
+        x_pre, R = _f64(x_pre), _f64(R)
+        B, NH, S, four, dh = x_pre.shape
+        assert four == 4 and R.shape == (NH, 4, dh, dh)
+        st = [c0, n0, m0, h0]
+        if any(a is not None for a in st):
+            st = [_f64(a) for a in st]
+            assert all(a.shape == (B, NH, dh) for a in st)
+        h = np.empty((B, NH, S, dh))
+        outs = [np.empty((B, NH, dh)) for _ in range(4)]
+        rc = self.lib.oracle_slstm_f64(_ptr(x_pre), _ptr(R), B, NH, S, dh, int(forget_exp),
+                                       *[_ptr(a) if a is not None else None for a in st],
+                                       _ptr(h), *[_ptr(a) for a in outs])
+        if rc != 0:
+            raise ValueError("oracle_slstm_f64 rejected its arguments")
+        return (h, *outs)
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())

@@ -319,6 +319,77 @@ int oracle_epilogue_f64(const double *h, const double *x, const double *z,
     return 0;
 }
 
+/*
+ * sLSTM recurrence with block-diagonal memory mixing (xLSTM paper, section 2.2:
+ * exponential gating with normalizer and stabilizer states, memory mixing through
+ * recurrent connections from the hidden state to the cell input and the gates,
+ * mixing within a head but not across heads; section 2.1 for the LSTM cell it
+ * extends).  The equations are not legible on the pages; this is the plainest
+ * reading of their description.  Per (b, head), cells r = 0..dh-1:
+ *   a_g = x_pre[t][g] + R_g h_{t-1}        g = z, i, f, o (R_g [dh][dh], row = output cell)
+ *   log i = a_i;  log f = log sigmoid(a_f)  (forget_exp = 0)  or  a_f  (forget_exp = 1)
+ *   m_t = max(log f + m_{t-1}, log i)
+ *   c_t = exp(log f + m_{t-1} - m_t) c_{t-1} + exp(log i - m_t) tanh(a_z)
+ *   n_t = exp(log f + m_{t-1} - m_t) n_{t-1} + exp(log i - m_t)
+ *   h_t = sigmoid(a_o) c_t / n_t
+ * (c, n are the stabilized states: the unstabilized ones times exp(-m_t), a factor
+ * that cancels in h.)  Layouts: x_pre [B][NH][S][4][dh] (gate order z, i, f, o),
+ * R [NH][4][dh][dh], states [B][NH][dh], h [B][NH][S][dh].  All of c0, n0, m0, h0
+ * NULL = the zero state (c = n = m = h = 0).
+ */
+int oracle_slstm_f64(const double *x_pre, const double *R, int B, int NH, int S, int dh, int forget_exp,
+                     const double *c0, const double *n0, const double *m0, const double *h0,
+                     double *h, double *c_out, double *n_out, double *m_out, double *h_out)
+{
+    if (B < 0 || NH < 0 || S < 0 || dh <= 0 || (forget_exp != 0 && forget_exp != 1))
+        return -1;
+    if (!x_pre || !R || !h || !c_out || !n_out || !m_out || !h_out)
+        return -1;
+    const int given = (c0 != NULL) + (n0 != NULL) + (m0 != NULL) + (h0 != NULL);
+    if (given != 0 && given != 4)
+        return -1;
+    const int heads = B * NH;
+
+    #pragma omp parallel for schedule(dynamic, 1)
+    for (int bh = 0; bh < heads; ++bh) {
+        const int hd = bh % NH;
+        const double *Rh = R + (size_t)hd * 4 * dh * dh;
+        double *c = c_out + (size_t)bh * dh, *n = n_out + (size_t)bh * dh;
+        double *m = m_out + (size_t)bh * dh, *hp = h_out + (size_t)bh * dh;
+        for (int r = 0; r < dh; ++r) {
+            c[r] = given ? c0[(size_t)bh * dh + r] : 0.0;
+            n[r] = given ? n0[(size_t)bh * dh + r] : 0.0;
+            m[r] = given ? m0[(size_t)bh * dh + r] : 0.0;
+            hp[r] = given ? h0[(size_t)bh * dh + r] : 0.0;
+        }
+        double *a = malloc(sizeof(double) * 4 * dh);
+        for (int t = 0; t < S; ++t) {
+            const double *xt = x_pre + ((size_t)bh * S + t) * 4 * dh;
+            for (int g = 0; g < 4; ++g)
+                for (int r = 0; r < dh; ++r) {
+                    double acc = xt[g * dh + r];
+                    const double *row = Rh + ((size_t)g * dh + r) * dh;
+                    for (int j = 0; j < dh; ++j) acc += row[j] * hp[j];
+                    a[g * dh + r] = acc;
+                }
+            double *ht = h + ((size_t)bh * S + t) * dh;
+            for (int r = 0; r < dh; ++r) {
+                const double az = a[r], ai = a[dh + r], af = a[2 * dh + r], ao = a[3 * dh + r];
+                const double log_f = forget_exp ? af : log_sigmoid(af);
+                const double m_t = fmax(log_f + m[r], ai);
+                const double fs = exp(log_f + m[r] - m_t), is = exp(ai - m_t);
+                c[r] = fs * c[r] + is * tanh(az);
+                n[r] = fs * n[r] + is;
+                m[r] = m_t;
+                ht[r] = sigmoid(ao) * c[r] / n[r];
+            }
+            for (int r = 0; r < dh; ++r) hp[r] = ht[r];
+        }
+        free(a);
+    }
+    return 0;
+}
+
 int oracle_num_threads(void)
 {
     int nt = 1;

@@ -457,6 +457,114 @@ EPI_PINS = [
 ]
 
 
+# ---- sLSTM recurrence (section 2.2) -------------------------------------------
+def _slstm_case(seed, B=2, NH=2, S=12, dh=6, rscale=0.3):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((B, NH, S, 4, dh))
+    x[..., 2, :] += 2.0                         # forget gates mostly open
+    R = rscale * rng.standard_normal((NH, 4, dh, dh))
+    return x, R
+
+
+def pin_slstm_unstabilized(orc):
+    """The stabilized recurrence equals the plain exponential-gated one (c = c' e^m, n = n' e^m)."""
+    x, R = _slstm_case(91)
+    B, NH, S, _, dh = x.shape
+    for fe in (0, 1):
+        h, c, n, m, hl = orc.slstm(x, R, fe)
+        for b in range(B):
+            for hd in range(NH):
+                cc, nn, hh = np.zeros(dh), np.zeros(dh), np.zeros(dh)
+                for t in range(S):
+                    a = x[b, hd, t] + R[hd] @ hh
+                    i_g = np.exp(a[1])
+                    f_g = np.exp(a[2]) if fe else 1.0 / (1.0 + np.exp(-a[2]))
+                    cc = f_g * cc + i_g * np.tanh(a[0])
+                    nn = f_g * nn + i_g
+                    hh = cc / nn / (1.0 + np.exp(-a[3]))
+                    _close(h[b, hd, t], hh, rtol=1e-10, what=f"slstm h fe={fe}")
+                _close(c[b, hd] * np.exp(m[b, hd]), cc, rtol=1e-10, what="slstm c")
+                _close(n[b, hd] * np.exp(m[b, hd]), nn, rtol=1e-10, what="slstm n")
+                _close(hl[b, hd], hh, rtol=1e-12, what="slstm last h")
+
+
+def pin_slstm_constant_cell_input(orc):
+    """With no mixing into the cell input and a constant cell input, c / n is the
+    normalized average of one value: h_t = sigmoid(a_o,t) tanh(z~) whatever the gates do."""
+    x, R = _slstm_case(92, S=20)
+    x[..., 0, :] = x[:, :, :1, 0, :]
+    R[:, 0] = 0.0
+    h, *_ = orc.slstm(x, R, 0)
+    hp = np.zeros(h.shape[:2] + h.shape[3:])
+    for t in range(h.shape[2]):
+        a_o = x[:, :, t, 3] + np.einsum("hrj,bhj->bhr", R[:, 3], hp)
+        _close(h[:, :, t], np.tanh(x[:, :, t, 0]) / (1.0 + np.exp(-a_o)), rtol=1e-12, what="constant z")
+        hp = h[:, :, t]
+
+
+def pin_slstm_memoryless(orc):
+    """An exponential forget gate at exp(-1e4) forgets everything: the cell is the RNN
+    h_t = sigmoid(a_o) tanh(a_z), a = x + R h_{t-1}."""
+    x, R = _slstm_case(93)
+    x[..., 2, :] = -1e4
+    R[:, 2] = 0.0
+    h, *_ = orc.slstm(x, R, 1)
+    hp = np.zeros(h.shape[:2] + h.shape[3:])
+    for t in range(h.shape[2]):
+        a = x[:, :, t] + np.einsum("hgrj,bhj->bhgr", R, hp)
+        hp = np.tanh(a[:, :, 0]) / (1.0 + np.exp(-a[:, :, 3]))
+        _close(h[:, :, t], hp, rtol=1e-12, what="memoryless")
+
+
+def pin_slstm_heads_are_diagonal_blocks(orc):
+    """NH heads of dh cells equal one head of NH*dh cells whose recurrent matrices are
+    block diagonal with the heads' matrices as blocks."""
+    x, R = _slstm_case(94, B=1, NH=3, dh=4)
+    NH, dh = 3, 4
+    h, c, n, m, hl = orc.slstm(x, R, 0)
+    xb = x.transpose(0, 2, 3, 1, 4).reshape(1, 1, x.shape[2], 4, NH * dh)
+    Rb = np.zeros((1, 4, NH * dh, NH * dh))
+    for hd in range(NH):
+        Rb[0, :, hd * dh:(hd + 1) * dh, hd * dh:(hd + 1) * dh] = R[hd]
+    hb, cb, nb, mb, hlb = orc.slstm(xb, Rb, 0)
+    _close(hb.reshape(1, x.shape[2], NH, dh).transpose(0, 2, 1, 3), h, rtol=1e-13, what="block diagonal h")
+    _close(cb.reshape(1, NH, dh), c, rtol=1e-13, what="block diagonal c")
+
+
+def pin_slstm_forget_sigmoid_as_exp(orc):
+    """Without mixing into the forget gate, the sigmoid forget gate on a_f is the
+    exponential one on log sigmoid(a_f)."""
+    x, R = _slstm_case(95)
+    R[:, 2] = 0.0
+    x2 = x.copy()
+    x2[..., 2, :] = -np.logaddexp(0.0, -x[..., 2, :])
+    a = orc.slstm(x, R, 0)
+    b = orc.slstm(x2, R, 1)
+    for u, v in zip(a, b):
+        _close(u, v, rtol=1e-12, what="forget sigmoid vs exp")
+
+
+def pin_slstm_continuation(orc):
+    """Running S1 tokens, then S2 from the returned state, equals one run of S1 + S2."""
+    x, R = _slstm_case(96, S=15)
+    full = orc.slstm(x, R, 0)
+    first = orc.slstm(x[:, :, :6], R, 0)
+    second = orc.slstm(x[:, :, 6:], R, 0, *first[1:])
+    _close(np.concatenate([first[0], second[0]], axis=2), full[0], rtol=1e-12, what="continued h")
+    for u, v in zip(second[1:], full[1:]):
+        _close(u, v, rtol=1e-12, what="continued state")
+
+
+SLSTM_PINS = [
+    pin_slstm_unstabilized,
+    pin_slstm_constant_cell_input,
+    pin_slstm_memoryless,
+    pin_slstm_heads_are_diagonal_blocks,
+    pin_slstm_forget_sigmoid_as_exp,
+    pin_slstm_continuation,
+]
+
+
 BWD_PINS = [
     pin_bwd_finite_differences_floor_inactive,
     pin_bwd_finite_differences_floor_active,

@@ -10,7 +10,7 @@ import os
 import pytest
 
 import oracle
-from oracle_pins import ALL_PINS, BWD_PINS, EPI_PINS
+from oracle_pins import ALL_PINS, BWD_PINS, EPI_PINS, SLSTM_PINS
 
 MUTANTS = {
     "forget_gate_dropped_on_C": (
@@ -96,6 +96,31 @@ MUTANTS = {
     "epi_swish_as_sigmoid": (
         ": z[row + r] * sigmoid(z[row + r]);",
         ": sigmoid(z[row + r]);"),
+    # sLSTM
+    "slstm_recurrent_transposed": (
+        "for (int j = 0; j < dh; ++j) acc += row[j] * hp[j];",
+        "for (int j = 0; j < dh; ++j) acc += Rh[((size_t)g * dh + j) * dh + r] * hp[j];"),
+    "slstm_gate_order": (
+        "ai = a[dh + r], af = a[2 * dh + r]",
+        "ai = a[2 * dh + r], af = a[dh + r]"),
+    "slstm_cell_input_not_squashed": (
+        "c[r] = fs * c[r] + is * tanh(az);",
+        "c[r] = fs * c[r] + is * az;"),
+    "slstm_normalizer_no_forget": (
+        "n[r] = fs * n[r] + is;",
+        "n[r] = n[r] + is;"),
+    "slstm_head_ignored": (
+        "const int hd = bh % NH;",
+        "const int hd = 0;"),
+    "slstm_stabilizer_max_dropped": (
+        "const double m_t = fmax(log_f + m[r], ai);",
+        "const double m_t = log_f + m[r];"),
+    "slstm_output_gate_dropped": (
+        "ht[r] = sigmoid(ao) * c[r] / n[r];",
+        "ht[r] = c[r] / n[r];"),
+    "slstm_hidden_not_fed_back": (
+        "            for (int r = 0; r < dh; ++r) hp[r] = ht[r];\n",
+        ""),
 }
 
 
@@ -110,7 +135,7 @@ def test_mutant_is_caught(name, tmp_path):
     oracle.build(str(mutated), lib_path)
     orc = oracle.Oracle(oracle.load(lib_path))
     failed = []
-    for pin in ALL_PINS + BWD_PINS + EPI_PINS:
+    for pin in ALL_PINS + BWD_PINS + EPI_PINS + SLSTM_PINS:
         try:
             pin(orc)
         except (AssertionError, FloatingPointError, ValueError):

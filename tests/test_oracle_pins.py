@@ -2,7 +2,7 @@
 import pytest
 
 import oracle
-from oracle_pins import ALL_PINS, BWD_PINS, EPI_PINS
+from oracle_pins import ALL_PINS, BWD_PINS, EPI_PINS, SLSTM_PINS
 
 
 @pytest.fixture(scope="module")
@@ -10,6 +10,6 @@ def orc():
     return oracle.Oracle()
 
 
-@pytest.mark.parametrize("pin", ALL_PINS + BWD_PINS + EPI_PINS, ids=lambda p: p.__name__)
+@pytest.mark.parametrize("pin", ALL_PINS + BWD_PINS + EPI_PINS + SLSTM_PINS, ids=lambda p: p.__name__)
 def test_pin(orc, pin):
     pin(orc)
