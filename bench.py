@@ -10,7 +10,9 @@ consecutive steps) and reports it under "decode", and the backward
 (mlstm_bwd_parallel: gradients of the same forward with respect to q, k, v and
 the three gate pre-activations, given dh) on the forward's workload under
 "backward", and the mLSTM block epilogue (mlstm_block_epilogue: per-head GroupNorm,
-learnable skip, external output gate) on the forward's h shape under "epilogue".
+learnable skip, external output gate) on the forward's h shape under "epilogue",
+and the sLSTM recurrence (slstm_fwd on slstm_125m: B=8, NH=4, S=2048, d_h=192,
+bf16 recurrent matrices) under "slstm".
 
 Roofline: the dominant kernel of the forward is the scan; its duration is taken
 with HIP events recorded on the stream the kernels run on, and its algorithmic
@@ -75,6 +77,10 @@ def epilogue_alg_bytes(w) -> float:
     return float(w.B * w.NH * w.S * w.dv) * 4 * e + float(w.NH * w.dv) * 12   # h, x, z, y + parameters
 
 
+def slstm_alg_flops(w) -> float:
+    return float(w.B * w.NH * w.S) * 4 * w.dqk * w.dqk * 2     # the four recurrent matrix-vector products
+
+
 def step_alg_bytes(w) -> float:
     e = 2
     per_head = 8 * w.dqk * w.dv + 8 * w.dqk + 8 + e * (2 * w.dqk + w.dv) + 8 + 4 * w.dv + e * w.dv
@@ -135,6 +141,7 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-epilogue", action="store_true")
+    ap.add_argument("--no-slstm", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
@@ -149,7 +156,7 @@ def main() -> int:
     import numpy as np
     import torch
 
-    from mlstm_matrix_memory_amd import (MLSTM_BF16, MLSTM_GATE_SWISH, inputs, mlstm_block_epilogue,
+    from mlstm_matrix_memory_amd import (MLSTM_BF16, MLSTM_GATE_SWISH, inputs, mlstm_block_epilogue, slstm_fwd,
                                          mlstm_bwd_parallel, mlstm_bwd_workspace_bytes,
                                          mlstm_fwd_prepare, mlstm_fwd_scan, mlstm_fwd_workspace_bytes, mlstm_step)
 
@@ -291,6 +298,37 @@ def main() -> int:
                          "alg_bytes_per_launch": ep_bytes},
         }
         del de, y, ea
+        torch.cuda.empty_cache()
+
+    # ---------------- sLSTM recurrence -----------------------------------------
+    if not args.no_slstm:
+        wsl = inputs.WORKLOADS["slstm_125m"]
+        xs = inputs.slstm_inputs(wsl)
+        xp, Rs = gpu(xs["x_pre"], "f32"), gpu(xs["R"], wsl.dtype)
+        del xs
+        so = slstm_fwd(xp, Rs)
+        torch.cuda.synchronize()
+        n_sl = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t_start = time.perf_counter()
+        e0.record()
+        for _ in range(n_sl):
+            slstm_fwd(xp, Rs, 0, None, None, None, None, *so)
+        e1.record()
+        torch.cuda.synchronize()
+        swall = time.perf_counter() - t_start
+        sl_ms = e0.elapsed_time(e1) / n_sl
+        sflops = slstm_alg_flops(wsl)
+        stf = sflops / (sl_ms / 1e3) / 1e12
+        out["slstm"] = {
+            "workload": f"slstm_125m: slstm_fwd B={wsl.B} NH={wsl.NH} S={wsl.S} d_h={wsl.dqk} bf16 R, fp32 gates",
+            "tokens_per_s": wsl.B * wsl.S * n_sl / swall, "ms_per_call": sl_ms,
+            "us_per_step": sl_ms * 1e3 / wsl.S, "workgroups": wsl.NH * ((wsl.B + 7) // 8),
+            "roofline": {"kernel": "slstm_kernel", "bound": "mfma", "achieved": stf, "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": stf / BF16_PEAK_TFLOPS, "traffic": None,
+                         "alg_flops_per_launch": sflops},
+        }
+        del xp, Rs, so
         torch.cuda.empty_cache()
 
     # ---------------- decode step ---------------------------------------------

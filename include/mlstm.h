@@ -68,6 +68,12 @@ typedef enum mlstm_dtype {
     MLSTM_BF16 = 1
 } mlstm_dtype;
 
+/* activation of the sLSTM forget gate (slstm_fwd) */
+typedef enum mlstm_forget_act {
+    MLSTM_FORGET_SIGMOID = 0,    /* log f = log sigmoid(a_f) */
+    MLSTM_FORGET_EXP = 1         /* log f = a_f              */
+} mlstm_forget_act;
+
 /* activation of the mLSTM block's external output gate (mlstm_block_epilogue) */
 typedef enum mlstm_gate_act {
     MLSTM_GATE_SIGMOID = 0,      /* sigmoid(z)        */
@@ -267,6 +273,47 @@ mlstm_status mlstm_block_epilogue(const void *h, const void *x, const void *z,
                                   int B, int NH, int S, int d_v, float eps,
                                   mlstm_gate_act act, mlstm_dtype dtype,
                                   void *y_out, void *stream);
+
+/*
+ * sLSTM recurrence with block-diagonal memory mixing ("xLSTM: Extended Long
+ * Short-Term Memory", section 2.2: exponential gating, the normalizer state that
+ * sums the input gate times all later forget gates, the stabilizer state m_t, and
+ * memory mixing through recurrent connections from the hidden state to the cell
+ * input and to the gates, within each head but not across heads; section 2.1 for
+ * the LSTM cell it extends).  The pages describe the equations in words; this is
+ * their plainest reading.  Per (b, head), cell r, with the head's recurrent
+ * matrices R_g (g = z, i, f, o) and a_g = x_pre_g + R_g h_{t-1}:
+ *   log i = a_i;  log f = log sigmoid(a_f) or a_f (forget);
+ *   m_t = max(log f + m_{t-1}, log i)
+ *   c_t = exp(log f + m_{t-1} - m_t) c_{t-1} + exp(log i - m_t) tanh(a_z)
+ *   n_t = exp(log f + m_{t-1} - m_t) n_{t-1} + exp(log i - m_t)
+ *   h_t = sigmoid(a_o) c_t / n_t
+ * (c, n are kept stabilized: the unstabilized states times exp(-m_t).)  The input
+ * projections x_pre = W x + b are computed by the caller (a dense GEMM).
+ *
+ * Arguments
+ *   x_pre           [B,NH,S,4,d_h] fp32, gate order z, i, f, o (read only)
+ *   R               [NH,4,d_h,d_h] dtype; R[hd][g][r][j] weighs h_{t-1}[j] into gate
+ *                   g of cell r (read only)
+ *   B, NH, S        >= 1;  d_h a multiple of 16, <= 192 (bf16) or <= 128 (fp32)
+ *   forget          MLSTM_FORGET_SIGMOID or MLSTM_FORGET_EXP
+ *   dtype           MLSTM_F32 or MLSTM_BF16: element type of R and h_out (the
+ *                   recurrent products run on bf16 MFMA; fp32 R is split into
+ *                   two bf16 parts, h into two bf16 parts)
+ *   c_init, n_init, m_init, h_init
+ *                   [B,NH,d_h] fp32 state entering token 0, all four or none
+ *                   (none = zero state, m = 0)
+ *   h_out           [B,NH,S,d_h] dtype, written
+ *   c_final, n_final, m_final, h_final
+ *                   [B,NH,d_h] fp32, written; each may be the same buffer as the
+ *                   matching initial one (in place), but no other overlap
+ * x_pre and R must be 16-byte aligned, the rest aligned to their element type.
+ */
+mlstm_status slstm_fwd(const float *x_pre, const void *R, int B, int NH, int S, int d_h,
+                       mlstm_forget_act forget, mlstm_dtype dtype,
+                       const float *c_init, const float *n_init, const float *m_init, const float *h_init,
+                       void *h_out, float *c_final, float *n_final, float *m_final, float *h_final,
+                       void *stream);
 
 /* Static description of a status code. */
 const char *mlstm_status_string(mlstm_status status);

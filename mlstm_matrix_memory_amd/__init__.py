@@ -11,11 +11,14 @@ Entry points (same names as include/mlstm.h):
   mlstm_bwd_workspace_bytes
   mlstm_block_epilogue
                       the mLSTM block's per-head GroupNorm, learnable skip and external output gate
+  slstm_fwd           the sLSTM recurrence with block-diagonal (per-head) memory mixing
   mlstm_fwd_workspace_bytes, mlstm_status_string, mlstm_error_detail
 """
 from .binding import (  # noqa: F401
     MLSTM_BF16,
     MLSTM_F32,
+    MLSTM_FORGET_EXP,
+    MLSTM_FORGET_SIGMOID,
     MLSTM_GATE_SIGMOID,
     MLSTM_GATE_SWISH,
     MlstmError,
@@ -31,4 +34,5 @@ from .binding import (  # noqa: F401
     mlstm_fwd_workspace_bytes,
     mlstm_status_string,
     mlstm_step,
+    slstm_fwd,
 )

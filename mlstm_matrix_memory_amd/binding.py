@@ -66,6 +66,8 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
                                        fp, fp, fp, fp, fp, fp, vp, sz, vp]
     lib.mlstm_block_epilogue.restype = i
     lib.mlstm_block_epilogue.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, ctypes.c_float, i, i, vp, vp]
+    lib.slstm_fwd.restype = i
+    lib.slstm_fwd.argtypes = [fp, vp, i, i, i, i, i, i, fp, fp, fp, fp, vp, fp, fp, fp, fp, vp]
     lib.mlstm_step.restype = i
     lib.mlstm_step.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, fp, fp, fp, vp, vp]
     lib.mlstm_status_string.restype = ctypes.c_char_p
@@ -81,7 +83,7 @@ def header_symbols(path: str = HEADER) -> list[str]:
     """Names of the functions include/mlstm.h declares."""
     text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(mlstm_[a-z_0-9]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b((?:mlstm|slstm)_[a-z_0-9]+)\s*\(", text)))
 
 
 def mlstm_status_string(status: int) -> str:
@@ -316,6 +318,49 @@ def mlstm_block_epilogue(h, x, z, gn_weight, gn_bias, skip_weight, eps: float = 
     if st != MLSTM_OK:
         raise MlstmError("mlstm_block_epilogue", st, mlstm_error_detail())
     return y_out
+
+
+MLSTM_FORGET_SIGMOID = 0
+MLSTM_FORGET_EXP = 1
+
+
+def slstm_fwd(x_pre, R, forget: int = MLSTM_FORGET_SIGMOID, c_init=None, n_init=None, m_init=None, h_init=None,
+              h_out=None, c_final=None, n_final=None, m_final=None, h_final=None, stream=None):
+    """sLSTM recurrence; returns (h [B,NH,S,d_h], c, n, m, h_last [B,NH,d_h]).
+
+    x_pre [B,NH,S,4,d_h] float32 (gates z, i, f, o); R [NH,4,d_h,d_h] float32 or
+    bfloat16 (also the dtype of h); states [B,NH,d_h] float32, all four or none.
+    """
+    import torch
+    lib = load_library()
+    if x_pre.dim() != 5 or x_pre.shape[3] != 4:
+        raise ValueError("x_pre must be [B, NH, S, 4, d_h]")
+    B, NH, S, _, dh = x_pre.shape
+    dev = x_pre.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    dt = _dtype_code(R)
+    _check(x_pre, "x_pre", (B, NH, S, 4, dh), torch.float32, dev)
+    _check(R, "R", (NH, 4, dh, dh), R.dtype, dev)
+    init = [c_init, n_init, m_init, h_init]
+    if any(t is not None for t in init):
+        if not all(t is not None for t in init):
+            raise ValueError("c_init, n_init, m_init and h_init must be given together")
+        for t, name in zip(init, ("c_init", "n_init", "m_init", "h_init")):
+            _check(t, name, (B, NH, dh), torch.float32, dev)
+    if h_out is None:
+        h_out = torch.empty((B, NH, S, dh), dtype=R.dtype, device=dev)
+    fin = [c_final, n_final, m_final, h_final]
+    fin = [torch.empty((B, NH, dh), dtype=torch.float32, device=dev) if t is None else t for t in fin]
+    _check(h_out, "h_out", (B, NH, S, dh), R.dtype, dev)
+    for t, name in zip(fin, ("c_final", "n_final", "m_final", "h_final")):
+        _check(t, name, (B, NH, dh), torch.float32, dev)
+    ptr = lambda t: t.data_ptr() if t is not None else None
+    st = lib.slstm_fwd(x_pre.data_ptr(), R.data_ptr(), B, NH, S, dh, int(forget), dt, *[ptr(t) for t in init],
+                       h_out.data_ptr(), *[t.data_ptr() for t in fin], _stream_handle(stream, dev))
+    if st != MLSTM_OK:
+        raise MlstmError("slstm_fwd", st, mlstm_error_detail())
+    return (h_out, *fin)
 
 
 def mlstm_step(q, k, v, i_pre, f_pre, o_pre, C, n, m, h_out=None, stream=None):

@@ -346,6 +346,62 @@ mlstm_status mlstm_block_epilogue(const void* h, const void* x, const void* z,
     return ok();
 }
 
+mlstm_status slstm_fwd(const float* x_pre, const void* R, int B, int NH, int S, int d_h,
+                       mlstm_forget_act forget, mlstm_dtype dtype,
+                       const float* c_init, const float* n_init, const float* m_init, const float* h_init,
+                       void* h_out, float* c_final, float* n_final, float* m_final, float* h_final,
+                       void* stream) {
+    if (B < 1 || NH < 1 || S < 1)
+        return fail(MLSTM_ERR_INVALID_ARG, "B=%d, NH=%d, S=%d must all be >= 1", B, NH, S);
+    mlstm_status s = check_dtype(dtype);
+    if (s != MLSTM_OK) return s;
+    const int dmax = dtype == MLSTM_BF16 ? 192 : 128;
+    if (d_h < 16 || d_h % 16 != 0 || d_h > dmax)
+        return fail(MLSTM_ERR_INVALID_ARG, "d_h=%d must be a multiple of 16 in [16, %d] for this dtype", d_h, dmax);
+    if (forget != MLSTM_FORGET_SIGMOID && forget != MLSTM_FORGET_EXP)
+        return fail(MLSTM_ERR_INVALID_ARG, "forget=%d is neither MLSTM_FORGET_SIGMOID nor MLSTM_FORGET_EXP",
+                    (int)forget);
+    if ((long long)NH * ((B + 7) / 8) > 0x7fffffffLL || (long long)B * NH * S * 4 * d_h > (1LL << 40))
+        return fail(MLSTM_ERR_UNSUPPORTED, "tensor too large");
+    const unsigned el = dtype == MLSTM_BF16 ? 2u : 4u;
+    const void* ptrs[] = {x_pre, R, h_out, c_final, n_final, m_final, h_final};
+    const char* names[] = {"x_pre", "R", "h_out", "c_final", "n_final", "m_final", "h_final"};
+    const unsigned align[] = {16, 16, el, 4, 4, 4, 4};
+    for (int p = 0; p < 7; ++p) {
+        if (!ptrs[p]) return fail(MLSTM_ERR_INVALID_ARG, "%s is NULL", names[p]);
+        if (!aligned(ptrs[p], align[p]))
+            return fail(MLSTM_ERR_INVALID_ARG, "%s is not %u-byte aligned", names[p], align[p]);
+    }
+    const int given = (c_init != nullptr) + (n_init != nullptr) + (m_init != nullptr) + (h_init != nullptr);
+    if (given != 0 && given != 4)
+        return fail(MLSTM_ERR_INVALID_ARG, "c_init, n_init, m_init and h_init must be given together (or all NULL)");
+    const size_t sb = (size_t)B * NH * d_h * 4;
+    const void* ins[] = {c_init, n_init, m_init, h_init};
+    const void* outs[] = {c_final, n_final, m_final, h_final};
+    for (int i = 0; i < 4; ++i) {
+        if (given && !aligned(ins[i], 4)) return fail(MLSTM_ERR_INVALID_ARG, "initial state is not 4-byte aligned");
+        for (int o = 0; o < 4; ++o) {
+            if (o != i && overlaps(outs[i], sb, outs[o], sb))
+                return fail(MLSTM_ERR_INVALID_ARG, "the final state buffers overlap each other");
+            if (given && overlaps(ins[i], sb, outs[o], sb) && !(i == o && ins[i] == outs[o]))
+                return fail(MLSTM_ERR_INVALID_ARG, "an initial state buffer overlaps a final one (other than in place)");
+        }
+    }
+    const size_t hb = (size_t)B * NH * S * d_h * el;
+    for (int i = 0; i < 4; ++i)
+        if (overlaps(h_out, hb, outs[i], sb) || (given && overlaps(h_out, hb, ins[i], sb)))
+            return fail(MLSTM_ERR_INVALID_ARG, "h_out overlaps a state buffer");
+    mlstm::SlstmArgs a = {};
+    a.x_pre = x_pre; a.R = R; a.B = B; a.NH = NH; a.S = S; a.dh = d_h;
+    a.forget_exp = forget == MLSTM_FORGET_EXP ? 1 : 0; a.dtype = dtype;
+    a.c0 = c_init; a.n0 = n_init; a.m0 = m_init; a.h0 = h_init;
+    a.h = h_out; a.c = c_final; a.n = n_final; a.m = m_final; a.hlast = h_final;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = mlstm::launch_slstm(a);
+    if (e != hipSuccess) return fail(MLSTM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
 const char* mlstm_status_string(mlstm_status status) {
     switch (status) {
         case MLSTM_OK: return "ok";

@@ -129,6 +129,18 @@ struct EpilogueArgs {
 
 hipError_t launch_epilogue(const EpilogueArgs& a);
 
+struct SlstmArgs {
+    const float* x_pre; const void* R;
+    int B, NH, S, dh;
+    int forget_exp;          // 0: log f = log sigmoid(a_f); 1: log f = a_f
+    mlstm_dtype dtype;       // of R and h
+    const float* c0; const float* n0; const float* m0; const float* h0;   // all null = zero state
+    void* h; float* c; float* n; float* m; float* hlast;
+    hipStream_t stream;
+};
+
+hipError_t launch_slstm(const SlstmArgs& a);
+
 hipError_t launch_step(const StepArgs& a);
 
 // generic chunkwise forward on the vector ALUs (any supported shape, fp32 or bf16)

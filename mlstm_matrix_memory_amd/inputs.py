@@ -11,11 +11,13 @@ Workloads (xLSTM language-model layer shapes; gate pre-activations fp32):
   lm_1_3b   B=4  NH=4 S=2048  d=1024 chunk=64  bf16 q/k/v
   long_ctx  B=1  NH=8 S=32768 d=256  chunk=128 bf16 q/k/v, i~ with 1% spikes at +40
   decode    batch 256, NH=4, d=512, 128 one-token steps from a random fp32 state
+  slstm_125m  sLSTM B=8 NH=4 S=2048 d_h=192, bf16 recurrent matrices
 
 Recipe (per workload, generator ``numpy.random.default_rng(seed)``):
   draw order q, k, v, i~, f~, o~ (then the spike positions, then the decode state);
   the backward's dh ~ N(0,1) comes from a generator of its own (seed + 2000), the
-  block epilogue's inputs from another (seed + 3000);
+  block epilogue's inputs from another (seed + 3000), the sLSTM's from another
+  (seed + 4000);
   normals drawn directly in float32; k scaled by 1/sqrt(d_qk) in fp32 for the
   forward workloads (decode keys are unscaled N(0,1)); q, k, v of bf16 workloads
   rounded to bf16 with round-to-nearest-even, kept here as float32 arrays that
@@ -65,6 +67,8 @@ WORKLOADS = {
     "long_ctx": Workload("long_ctx", "fwd", 1, 8, 32768, 256, 256, 128, "bf16",
                          i_mu=0.0, i_sd=8.0, f_mu=1.0, f_sd=2.0, spike_frac=0.01, seed=4),
     "decode": Workload("decode", "step", 256, 4, 128, 512, 512, 0, "bf16", scale_k=False, seed=5),
+    # sLSTM: d_qk = d_v = d_h, the cells per head (embedding 768 over 4 heads)
+    "slstm_125m": Workload("slstm_125m", "slstm", 8, 4, 2048, 192, 192, 0, "bf16", seed=6),
 }
 
 
@@ -156,6 +160,28 @@ def epilogue_inputs(w: Workload, seed: int | None = None, B: int | None = None, 
     if w.dtype == "bf16":
         h, x, z = bf16_round(h), bf16_round(x), bf16_round(z)
     return dict(h=h, x=x, z=z, gn_w=gn_w, gn_b=gn_b, skip_w=skip_w)
+
+
+def slstm_inputs(w: Workload, seed: int | None = None, B: int | None = None, NH: int | None = None,
+                 S: int | None = None, dh: int | None = None):
+    """Inputs of the sLSTM recurrence (generator seeded with seed + 4000).
+
+    x_pre [B,NH,S,4,dh] float32: z~, i~, o~ ~ N(0,1), f~ ~ N(f_mu, f_sd) (forget gates
+    mostly open); R [NH,4,dh,dh] ~ N(0,1)/sqrt(dh), so that R h is O(1), bf16-rounded
+    for bf16 workloads.
+    """
+    B = w.B if B is None else B
+    NH = w.NH if NH is None else NH
+    S = w.S if S is None else S
+    dh = w.dqk if dh is None else dh
+    rng = np.random.default_rng((w.seed if seed is None else seed) + 4000)
+    x = _normal(rng, (B, NH, S, 4, dh))
+    x[:, :, :, 2, :] = _normal(rng, (B, NH, S, dh), w.f_mu, w.f_sd)
+    R = _normal(rng, (NH, 4, dh, dh))
+    R *= np.float32(1.0 / math.sqrt(dh))
+    if w.dtype == "bf16":
+        R = bf16_round(R)
+    return dict(x_pre=x, R=R)
 
 
 def step_state(w: Workload, seed: int | None = None, B: int | None = None, NH: int | None = None,

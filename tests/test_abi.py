@@ -23,7 +23,7 @@ def test_exports_every_declared_symbol(lib):
     names = b.header_symbols()
     assert {"mlstm_fwd_parallel", "mlstm_fwd_parallel_state", "mlstm_fwd_prepare", "mlstm_fwd_scan",
             "mlstm_step", "mlstm_fwd_workspace_bytes", "mlstm_status_string", "mlstm_error_detail",
-            "mlstm_bwd_parallel", "mlstm_bwd_workspace_bytes", "mlstm_block_epilogue"} <= set(names)
+            "mlstm_bwd_parallel", "mlstm_bwd_workspace_bytes", "mlstm_block_epilogue", "slstm_fwd"} <= set(names)
     for name in names:
         assert hasattr(lib, name), f"{name} declared in include/mlstm.h but not exported"
 
@@ -148,7 +148,7 @@ def test_binding_has_same_names_as_abi():
     import mlstm_matrix_memory_amd as pkg
     for name in ("mlstm_fwd_parallel", "mlstm_fwd_parallel_state", "mlstm_fwd_prepare", "mlstm_fwd_scan",
                  "mlstm_step", "mlstm_fwd_workspace_bytes", "mlstm_status_string", "mlstm_error_detail",
-                 "mlstm_bwd_parallel", "mlstm_bwd_workspace_bytes", "mlstm_block_epilogue"):
+                 "mlstm_bwd_parallel", "mlstm_bwd_workspace_bytes", "mlstm_block_epilogue", "slstm_fwd"):
         assert callable(getattr(pkg, name))
 
 
@@ -259,3 +259,44 @@ def test_epilogue_rejects_partial_overlap(lib):
     ptrs[3] = FAKE_MIS
     assert _epi(lib, ptrs=ptrs) == b.MLSTM_ERR_INVALID_ARG
     assert "aligned" in b.mlstm_error_detail()
+
+
+def _sl(lib, B=2, NH=2, S=8, dh=64, forget=0, dt=b.MLSTM_BF16, init=(None,) * 4, outs=None):
+    o = [0x800000, 0x900000, 0xA00000, 0xB00000, 0xC00000] if outs is None else outs
+    return lib.slstm_fwd(FAKE, FAKE, B, NH, S, dh, forget, dt, *init, *o, None)
+
+
+@pytest.mark.parametrize("kw,detail", [
+    (dict(S=0), "S=0"),
+    (dict(dh=24), "d_h=24"),
+    (dict(dh=208), "d_h=208"),
+    (dict(dh=144, dt=b.MLSTM_F32), "d_h=144"),
+    (dict(forget=3), "forget=3"),
+    (dict(dt=4), "dtype=4"),
+])
+def test_slstm_rejects_bad_arguments(lib, kw, detail):
+    assert _sl(lib, **kw) == b.MLSTM_ERR_INVALID_ARG
+    assert detail in b.mlstm_error_detail()
+
+
+def test_slstm_state_rules(lib):
+    assert _sl(lib, init=(FAKE, None, None, None)) == b.MLSTM_ERR_INVALID_ARG
+    assert "together" in b.mlstm_error_detail()
+    # in place is allowed; an initial buffer overlapping another final one is not
+    outs = [0x800000, 0x900000, 0xA00000, 0xB00000, 0xC00000]
+    init = (outs[1] + 64, 0x100000, 0x200000, 0x300000)
+    assert _sl(lib, init=init, outs=outs) == b.MLSTM_ERR_INVALID_ARG
+    assert "overlaps" in b.mlstm_error_detail()
+    assert _sl(lib, outs=[outs[0], outs[1], outs[1] + 128, outs[3], outs[4]]) == b.MLSTM_ERR_INVALID_ARG
+    assert "overlap each other" in b.mlstm_error_detail()
+    assert _sl(lib, outs=[outs[1] - 64, outs[1], outs[2], outs[3], outs[4]]) == b.MLSTM_ERR_INVALID_ARG
+    assert "h_out overlaps" in b.mlstm_error_detail()
+
+
+def test_slstm_rejects_null_and_misaligned(lib):
+    assert lib.slstm_fwd(None, FAKE, 1, 1, 4, 64, 0, b.MLSTM_BF16, None, None, None, None,
+                         FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.MLSTM_ERR_INVALID_ARG
+    assert "x_pre is NULL" in b.mlstm_error_detail()
+    assert lib.slstm_fwd(FAKE, FAKE_MIS, 1, 1, 4, 64, 0, b.MLSTM_BF16, None, None, None, None,
+                         FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.MLSTM_ERR_INVALID_ARG
+    assert "R is not" in b.mlstm_error_detail()
