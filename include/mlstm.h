@@ -307,7 +307,8 @@ mlstm_status mlstm_block_epilogue(const void *h, const void *x, const void *z,
  *   c_final, n_final, m_final, h_final
  *                   [B,NH,d_h] fp32, written; each may be the same buffer as the
  *                   matching initial one (in place), but no other overlap
- * x_pre and R must be 16-byte aligned, the rest aligned to their element type.
+ * x_pre and R must be 16-byte aligned, the state buffers 8-byte aligned, h_out
+ * aligned to its element type.
  */
 mlstm_status slstm_fwd(const float *x_pre, const void *R, int B, int NH, int S, int d_h,
                        mlstm_forget_act forget, mlstm_dtype dtype,

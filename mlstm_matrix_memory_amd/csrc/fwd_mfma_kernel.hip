@@ -48,14 +48,6 @@
 namespace mlstm {
 namespace {
 
-// Workgroup barrier that orders LDS traffic only: this wave's LDS operations are
-// complete (lgkmcnt 0) before it signals, but global loads still in flight stay in
-// flight, so register prefetches issued before the barrier keep overlapping with
-// the work after it.  (The full __syncthreads fence would wait for them.)  The
-// memory clobber keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 __device__ __forceinline__ bf16x8 cvt8(f32x4 a, f32x4 b) {
     return bf16x8{(bf16)a[0], (bf16)a[1], (bf16)a[2], (bf16)a[3],

@@ -366,7 +366,7 @@ mlstm_status slstm_fwd(const float* x_pre, const void* R, int B, int NH, int S, 
     const unsigned el = dtype == MLSTM_BF16 ? 2u : 4u;
     const void* ptrs[] = {x_pre, R, h_out, c_final, n_final, m_final, h_final};
     const char* names[] = {"x_pre", "R", "h_out", "c_final", "n_final", "m_final", "h_final"};
-    const unsigned align[] = {16, 16, el, 4, 4, 4, 4};
+    const unsigned align[] = {16, 16, el, 8, 8, 8, 8};
     for (int p = 0; p < 7; ++p) {
         if (!ptrs[p]) return fail(MLSTM_ERR_INVALID_ARG, "%s is NULL", names[p]);
         if (!aligned(ptrs[p], align[p]))
@@ -379,7 +379,7 @@ mlstm_status slstm_fwd(const float* x_pre, const void* R, int B, int NH, int S, 
     const void* ins[] = {c_init, n_init, m_init, h_init};
     const void* outs[] = {c_final, n_final, m_final, h_final};
     for (int i = 0; i < 4; ++i) {
-        if (given && !aligned(ins[i], 4)) return fail(MLSTM_ERR_INVALID_ARG, "initial state is not 4-byte aligned");
+        if (given && !aligned(ins[i], 8)) return fail(MLSTM_ERR_INVALID_ARG, "initial state is not 8-byte aligned");
         for (int o = 0; o < 4; ++o) {
             if (o != i && overlaps(outs[i], sb, outs[o], sb))
                 return fail(MLSTM_ERR_INVALID_ARG, "the final state buffers overlap each other");

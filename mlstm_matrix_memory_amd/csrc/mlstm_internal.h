@@ -83,6 +83,15 @@ __device__ __forceinline__ bf16x8 cat(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Workgroup barrier that orders LDS traffic only: this wave's LDS operations are
+// complete (lgkmcnt 0) before it signals, but global loads and stores still in
+// flight stay in flight, so register prefetches issued before the barrier keep
+// overlapping with the work after it.  (The full __syncthreads fence would wait for
+// them.)  The memory clobber keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---- launchers (return hipSuccess or the launch error) --------------------
 struct FwdArgs {
     const void* q; const void* k; const void* v;

@@ -11,19 +11,20 @@
 //   h_t = sigmoid(a_o) c_t / n_t
 //
 // The recurrence is sequential in t, so a step's latency is what counts.  One
-// workgroup runs one head for a tile of up to 8 sequences, all steps:
-//   - the head's four recurrent matrices stay in registers for the whole sequence
-//     as bf16 MFMA A operands (rows = 4 * DH gate rows, 16-row blocks dealt to the
-//     waves; fp32 matrices are held as bf16 hi + lo pairs);
+// workgroup runs one head for a tile of up to 8 sequences, all steps, with one
+// wave per 16 cells (DHP / 16 waves):
+//   - the wave holds the rows of all four gates of its 16 cells of the head's
+//     recurrent matrices in registers, as bf16 MFMA A operands, for the whole
+//     sequence (an fp32 matrix is held as bf16 hi + lo pairs);
 //   - h_{t-1} of the tile sits in LDS as the B operand: columns 0..7 hold bf16(h)
-//     of the 8 sequences, columns 8..15 the rounding remainder h - bf16(h), so one
+//     of the 8 sequences, columns 8..15 the remainder h - bf16(h), so one
 //     16-column MFMA gives R bf16(h) and R (h - bf16(h)) side by side and a lane
 //     swap adds them (the split costs no extra MFMA);
-//   - R h goes through LDS to the thread that owns the cell's (c, n, m); that
-//     thread has loaded the step's input pre-activations of its cells while the
-//     products ran, updates the state in fp32 registers, and writes h_t out and
-//     back to LDS.
-// Two workgroup barriers per step.
+//   - the four gate sums of a cell land in the same lanes, which keep that cell's
+//     (c, n, m) for its sequence in registers and update it in place: no LDS
+//     round trip for the gates;
+//   - h goes to a second LDS buffer (ping-pong), so a step needs one barrier;
+//   - the input pre-activations are loaded several steps ahead.
 #include "mlstm_internal.h"
 
 namespace mlstm {
@@ -31,19 +32,23 @@ namespace {
 
 constexpr int SL_BT = 8;                   // sequences per workgroup
 
-// threads per workgroup: 16 waves, or 8 at d_h 192, where a wave's share of the
-// recurrent matrices needs more than the 128 registers a lane has at 16 waves
 template <int DHP>
-constexpr int sl_threads() { return DHP > 128 ? 512 : 1024; }
+constexpr int sl_threads() { return 4 * DHP; }    // one wave per 16 cells
+
+// steps of input pre-activations in flight (8 registers each), as many as the
+// registers left beside the recurrent matrices allow
+template <typename T, int DHP>
+constexpr int sl_prefetch() { return DHP > 128 ? 2 : 4; }
 
 template <int DHP>
 struct alignas(16) SlstmSmem {
-    bf16 hb[16 * (DHP + 8)];               // B operand: [column][cell], hi columns 0..7, lo 8..15
-    float gate[4 * DHP * SL_BT];           // [gate row][sequence]
+    bf16 hb[2][16 * (DHP + 8)];            // ping-pong B operand: [column][cell], hi 0..7, lo 8..15
 };
 
-__device__ __forceinline__ void store_h(float* p, float v) { *p = v; }
-__device__ __forceinline__ void store_h(bf16* p, float v) { *p = (bf16)v; }
+__device__ __forceinline__ void store_h4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void store_h4(bf16* p, f32x4 v) {
+    *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+}
 
 // A operand (8 consecutive columns of one R row) from bf16 or fp32 memory
 __device__ __forceinline__ void load_r(const bf16* p, bool ok, bf16x8& hi, bf16x8& lo) {
@@ -61,153 +66,182 @@ __device__ __forceinline__ void load_r(const float* p, bool ok, bf16x8& hi, bf16
     }
 }
 
+// gate math on the hardware exp / log / reciprocal (about 1 ulp each)
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_sigmoid(float x) { return fast_rcp(1.0f + __expf(-x)); }
+__device__ __forceinline__ float fast_log_sigmoid(float x) { return fminf(x, 0.0f) - __logf(1.0f + __expf(-fabsf(x))); }
+__device__ __forceinline__ float fast_tanh(float x) {
+    const float e = __expf(-2.0f * fabsf(x));
+    return copysignf((1.0f - e) * fast_rcp(1.0f + e), x);
+}
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+
+__device__ __forceinline__ f32x2 load2(const float* p) { return *reinterpret_cast<const f32x2*>(p); }
+__device__ __forceinline__ void store_h2(float* p, f32x2 v) { *reinterpret_cast<f32x2*>(p) = v; }
+__device__ __forceinline__ void store_h2(bf16* p, f32x2 v) {
+    *reinterpret_cast<unsigned*>(p) = (unsigned)__builtin_bit_cast(unsigned short, (bf16)v[0]) |
+                                      ((unsigned)__builtin_bit_cast(unsigned short, (bf16)v[1]) << 16);
+}
+
+// value of lane (l + 8) mod 16 of the same 16-lane row (DPP row rotate by 8, VALU only)
+__device__ __forceinline__ float row_swap8(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+}
+
 // T: dtype of R and h_out.  DHP: d_h rounded up to 64, 128 or (bf16) 192.
-template <typename T, int DHP>
+// FEXP: forget gate exp (log f = a_f) instead of sigmoid.
+//
+// Lane layout of a wave (16 cells, rows 16 w + 4 g + i of each gate): after the
+// products, lane l of 16-lane row g holds the four gate sums of cells 4g + i for
+// sequence l % 8 (lanes l and l + 8 hold the same sums once the bf16 remainder
+// column is added); lane l < 8 then updates cells 4g, 4g+1 and lane l + 8 cells
+// 4g+2, 4g+3, so all 16 lanes share the cell arithmetic.
+template <typename T, int DHP, bool FEXP>
 __global__ __launch_bounds__(sl_threads<DHP>()) void slstm_kernel(
-    const float* __restrict__ x_pre, const T* __restrict__ R, int B, int NH, int S, int dh, int forget_exp,
+    const float* __restrict__ x_pre, const T* __restrict__ R, int B, int NH, int S, int dh,
     const float* __restrict__ c0, const float* __restrict__ n0, const float* __restrict__ m0,
     const float* __restrict__ h0, T* __restrict__ h, float* __restrict__ cF, float* __restrict__ nF,
     float* __restrict__ mF, float* __restrict__ hF)
 {
-    constexpr int SL_THREADS = sl_threads<DHP>();
-    constexpr int SL_WAVES = SL_THREADS / 64;
     constexpr bool SPLIT = sizeof(T) == 4;             // fp32 R: hi + lo A operands
     constexpr int P = DHP + 8;
-    constexpr int RB = 4 * DHP / 16 / SL_WAVES;        // 16-row blocks per wave
     constexpr int KS = DHP / 32;                       // k-steps over the cells
-    constexpr int NITEM = DHP * SL_BT;                 // (sequence, cell) pairs of the tile
-    constexpr int IPT = (NITEM + SL_THREADS - 1) / SL_THREADS;
     __shared__ SlstmSmem<DHP> sm;
 
     const int hd = blockIdx.x % NH, b0 = (blockIdx.x / NH) * SL_BT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 15, g = lane >> 4;
+    const int half = ln >> 3, bl = ln & 7;             // lane updates cells 2*half, 2*half+1 of its 4
+    const int r0 = 16 * wave + 4 * g + 2 * half;       // first of this lane's 2 cells
+    const int b = b0 + bl;
+    const bool own = b < B && r0 < dh;                 // lane updates (and stores) these cells
 
-    // recurrent matrices of this head as A operands
-    bf16x8 ra[RB][KS], rl[SPLIT ? RB : 1][SPLIT ? KS : 1];
-    const T* Rh = R + (size_t)hd * 4 * dh * dh;
+    // rows of the four gates of this wave's 16 cells as A operands
+    bf16x8 ra[4][KS], rl[SPLIT ? 4 : 1][SPLIT ? KS : 1];
+    {
+        const T* Rh = R + (size_t)hd * 4 * dh * dh;
+        const int r = 16 * wave + ln;
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) {
-        const int row = 16 * (wave * RB + rb) + ln;    // gate row in the padded layout
-        const int gate = row / DHP, r = row % DHP;
+        for (int gt = 0; gt < 4; ++gt)
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const int c = 32 * kk + 8 * g;
-            bf16x8 hi, lo;
-            load_r(Rh + ((size_t)gate * dh + r) * dh + c, r < dh && c < dh, hi, lo);
-            ra[rb][kk] = hi;
-            if constexpr (SPLIT) rl[rb][kk] = lo;
-        }
+            for (int kk = 0; kk < KS; ++kk) {
+                const int c = 32 * kk + 8 * g;
+                bf16x8 hi, lo;
+                load_r(Rh + ((size_t)gt * dh + r) * dh + c, r < dh && c < dh, hi, lo);
+                ra[gt][kk] = hi;
+                if constexpr (SPLIT) rl[gt][kk] = lo;
+            }
     }
 
-    // state of the cells this thread updates: item = tid + SL_THREADS * j -> (sequence, cell)
-    float cs[IPT], ns[IPT], ms[IPT];
-    for (int e = tid; e < 16 * P; e += SL_THREADS) sm.hb[e] = (bf16)0.0f;
+    for (int e = tid; e < 2 * 16 * P; e += sl_threads<DHP>()) (&sm.hb[0][0])[e] = (bf16)0.0f;
     __syncthreads();
+    f32x2 cs = {0, 0}, ns = {0, 0}, ms = {0, 0}, hv = {0, 0};
+    const size_t st0 = ((size_t)b * NH + hd) * dh + r0;
+    if (own && c0) {
+        cs = load2(c0 + st0);
+        ns = load2(n0 + st0);
+        ms = load2(m0 + st0);
+        hv = load2(h0 + st0);
 #pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-        const int item = tid + SL_THREADS * j;
-        const int bb = item / DHP, r = item % DHP, b = b0 + bb;
-        cs[j] = ns[j] = ms[j] = 0.0f;
-        if (item < NITEM && r < dh && b < B) {
-            const size_t st = ((size_t)b * NH + hd) * dh + r;
-            float hv = 0.0f;
-            if (c0) { cs[j] = c0[st]; ns[j] = n0[st]; ms[j] = m0[st]; hv = h0[st]; }
-            const bf16 hi = (bf16)hv;
-            sm.hb[bb * P + r] = hi;
-            sm.hb[(SL_BT + bb) * P + r] = (bf16)(hv - (float)hi);
+        for (int i = 0; i < 2; ++i) {
+            const bf16 hi = (bf16)hv[i];
+            sm.hb[0][bl * P + r0 + i] = hi;
+            sm.hb[0][(SL_BT + bl) * P + r0 + i] = (bf16)(hv[i] - (float)hi);
         }
     }
 
-    for (int t = 0; t < S; ++t) {
-        // this step's input pre-activations of the thread's cells: issued before the
-        // barrier and the products, used after them
-        float xz[IPT], xi[IPT], xf[IPT], xo[IPT];
+    // Wait here for the matrix and state loads: inside the step loop the compiler
+    // cannot tell them from the loads in flight across iterations and would wait
+    // for every outstanding load before each step's first product.
+    __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0), expcnt and lgkmcnt unconstrained
+
+    // The step's input pre-activations (gate gt at x_pre[b][hd][t][gt][r0, r0+1])
+    // are loaded PD steps ahead into a ring of registers (the step loop is unrolled
+    // by PD so the ring index is static), so their memory latency hides behind PD
+    // steps.  They are loaded unconditionally from a valid address -- lanes that own
+    // no cell read the start of x_pre, steps past the end re-read the last -- so the
+    // loaded registers carry into their step without a select (which would make the
+    // compiler wait for them at once).
+    constexpr int PD = sl_prefetch<T, DHP>();
+    const float* xb = own ? x_pre + ((size_t)b * NH + hd) * S * 4 * dh + r0 : x_pre;
+    const size_t xstep = own ? (size_t)4 * dh : 0;
+    const int goff = own ? dh : 0;
+    f32x2 xr[PD][4];
 #pragma unroll
-        for (int j = 0; j < IPT; ++j) {
-            const int item = tid + SL_THREADS * j;
-            const int bb = item / DHP, r = item % DHP, b = b0 + bb;
-            xz[j] = xi[j] = xf[j] = xo[j] = 0.0f;
-            if (item < NITEM && r < dh && b < B) {
-                const float* xp = x_pre + (((size_t)b * NH + hd) * S + t) * 4 * dh + r;
-                xz[j] = xp[0];
-                xi[j] = xp[dh];
-                xf[j] = xp[2 * dh];
-                xo[j] = xp[3 * dh];
+    for (int u = 0; u < PD; ++u)
+#pragma unroll
+        for (int gt = 0; gt < 4; ++gt) xr[u][gt] = load2(xb + (size_t)min(u, S - 1) * xstep + gt * goff);
+
+    for (int t0 = 0; t0 < S; t0 += PD) {
+#pragma unroll
+        for (int u = 0; u < PD; ++u) {
+            const int t = t0 + u;
+            if (t >= S) break;
+            const int cur = t & 1;
+            lds_barrier();                             // h_{t-1} complete in hb[cur]; loads stay in flight
+            f32x4 acc[4];
+#pragma unroll
+            for (int gt = 0; gt < 4; ++gt) acc[gt] = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const bf16x8 hbv = *reinterpret_cast<const bf16x8*>(sm.hb[cur] + ln * P + 32 * kk + 8 * g);
+#pragma unroll
+                for (int gt = 0; gt < 4; ++gt) {
+                    acc[gt] = mfma(ra[gt][kk], hbv, acc[gt]);
+                    if constexpr (SPLIT) acc[gt] = mfma(rl[gt][kk], hbv, acc[gt]);
+                }
             }
-        }
-        __syncthreads();                               // h_{t-1} in LDS
-        f32x4 acc[RB];
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0, 0, 0, 0};
+            for (int i = 0; i < 2; ++i) {
+                // gate sums of cell r0 + i: this lane's rows 2*half + i, plus the remainder column
+                float a[4];
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-            const bf16x8 hbv = *reinterpret_cast<const bf16x8*>(sm.hb + ln * P + 32 * kk + 8 * g);
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb) {
-                acc[rb] = mfma(ra[rb][kk], hbv, acc[rb]);
-                if constexpr (SPLIT) acc[rb] = mfma(rl[rb][kk], hbv, acc[rb]);
+                for (int gt = 0; gt < 4; ++gt) {
+                    const float lo_i = half ? acc[gt][2 + i] : acc[gt][i];
+                    const float hi_i = half ? acc[gt][i] : acc[gt][2 + i];
+                    // lanes l and l + 8 exchange the pair the other one updates
+                    a[gt] = lo_i + row_swap8(hi_i) + xr[u][gt][i];
+                }
+                const float lf = FEXP ? a[2] : fast_log_sigmoid(a[2]);
+                const float mt = fmaxf(lf + ms[i], a[1]);
+                const float fs = __expf(lf + ms[i] - mt), is = __expf(a[1] - mt);
+                cs[i] = fs * cs[i] + is * fast_tanh(a[0]);
+                ns[i] = fs * ns[i] + is;
+                ms[i] = mt;
+                hv[i] = fast_sigmoid(a[3]) * cs[i] * fast_rcp(ns[i]);
             }
-        }
-        // column ln + 8 holds R (h - bf16(h)) of sequence ln: add it in
+            if (own) {
+                store_h2(h + (((size_t)b * NH + hd) * S + t) * dh + r0, hv);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[rb][i] += __shfl_xor(acc[rb][i], 8, 64);
-            if (ln < SL_BT) {
-                const int row = 16 * (wave * RB + rb) + 4 * g;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.gate[(row + i) * SL_BT + ln] = acc[rb][i];
+                for (int i = 0; i < 2; ++i) {
+                    const bf16 hi = (bf16)hv[i];
+                    sm.hb[cur ^ 1][bl * P + r0 + i] = hi;
+                    sm.hb[cur ^ 1][(SL_BT + bl) * P + r0 + i] = (bf16)(hv[i] - (float)hi);
+                }
             }
-        }
-        __syncthreads();                               // gate pre-activations complete
+            const size_t tn = (size_t)min(t + PD, S - 1) * xstep;
 #pragma unroll
-        for (int j = 0; j < IPT; ++j) {
-            const int item = tid + SL_THREADS * j;
-            const int bb = item / DHP, r = item % DHP, b = b0 + bb;
-            if (item < NITEM && r < dh && b < B) {
-                const float az = sm.gate[(0 * DHP + r) * SL_BT + bb] + xz[j];
-                const float ai = sm.gate[(1 * DHP + r) * SL_BT + bb] + xi[j];
-                const float af = sm.gate[(2 * DHP + r) * SL_BT + bb] + xf[j];
-                const float ao = sm.gate[(3 * DHP + r) * SL_BT + bb] + xo[j];
-                const float lf = forget_exp ? af : log_sigmoid(af);
-                const float mt = fmaxf(lf + ms[j], ai);
-                const float fs = expf(lf + ms[j] - mt), is = expf(ai - mt);
-                cs[j] = fs * cs[j] + is * tanhf(az);
-                ns[j] = fs * ns[j] + is;
-                ms[j] = mt;
-                const float hv = sigmoid(ao) * cs[j] / ns[j];
-                store_h(h + (((size_t)b * NH + hd) * S + t) * dh + r, hv);
-                const bf16 hi = (bf16)hv;
-                sm.hb[bb * P + r] = hi;
-                sm.hb[(SL_BT + bb) * P + r] = (bf16)(hv - (float)hi);
-            }
+            for (int gt = 0; gt < 4; ++gt) xr[u][gt] = load2(xb + tn + gt * goff);
         }
     }
-    // final state
-#pragma unroll
-    for (int j = 0; j < IPT; ++j) {
-        const int item = tid + SL_THREADS * j;
-        const int bb = item / DHP, r = item % DHP, b = b0 + bb;
-        if (item < NITEM && r < dh && b < B) {
-            const size_t st = ((size_t)b * NH + hd) * dh + r;
-            cF[st] = cs[j];
-            nF[st] = ns[j];
-            mF[st] = ms[j];
-            hF[st] = (float)sm.hb[bb * P + r] + (float)sm.hb[(SL_BT + bb) * P + r];
-        }
+    if (own) {
+        *reinterpret_cast<f32x2*>(cF + st0) = cs;
+        *reinterpret_cast<f32x2*>(nF + st0) = ns;
+        *reinterpret_cast<f32x2*>(mF + st0) = ms;
+        *reinterpret_cast<f32x2*>(hF + st0) = hv;
     }
 }
 
-template <typename T>
+template <typename T, bool FEXP>
 hipError_t launch_slstm_t(const SlstmArgs& a) {
     const dim3 grid((unsigned)(a.NH * ((a.B + SL_BT - 1) / SL_BT)));
     const T* R = (const T*)a.R;
     T* h = (T*)a.h;
-#define SL_CASE(D)                                                                                           \
-    if (a.dh <= D) {                                                                                         \
-        hipLaunchKernelGGL((slstm_kernel<T, D>), grid, dim3(sl_threads<D>()), 0, a.stream, a.x_pre, R, a.B, a.NH, \
-                           a.S, a.dh, a.forget_exp, a.c0, a.n0, a.m0, a.h0, h, a.c, a.n, a.m, a.hlast);     \
-        return hipGetLastError();                                                                            \
+#define SL_CASE(D)                                                                                               \
+    if (a.dh <= D) {                                                                                             \
+        hipLaunchKernelGGL((slstm_kernel<T, D, FEXP>), grid, dim3(sl_threads<D>()), 0, a.stream, a.x_pre, R, a.B, \
+                           a.NH, a.S, a.dh, a.c0, a.n0, a.m0, a.h0, h, a.c, a.n, a.m, a.hlast);                  \
+        return hipGetLastError();                                                                                \
     }
     SL_CASE(64)
     SL_CASE(128)
@@ -219,8 +253,8 @@ hipError_t launch_slstm_t(const SlstmArgs& a) {
 }  // namespace
 
 hipError_t launch_slstm(const SlstmArgs& a) {
-    if (a.dtype == MLSTM_BF16) return launch_slstm_t<bf16>(a);
-    return launch_slstm_t<float>(a);
+    if (a.dtype == MLSTM_BF16) return a.forget_exp ? launch_slstm_t<bf16, true>(a) : launch_slstm_t<bf16, false>(a);
+    return a.forget_exp ? launch_slstm_t<float, true>(a) : launch_slstm_t<float, false>(a);
 }
 
 }  // namespace mlstm
