@@ -40,6 +40,11 @@ constexpr int sl_threads() { return 4 * DHP; }    // one wave per 16 cells
 template <typename T, int DHP>
 constexpr int sl_prefetch() { return DHP > 128 ? 2 : 4; }
 
+// where lanes that own no cell store their (ignored) h, one 8-byte slot per lane,
+// and read their input pre-activations (zeros, never written)
+__device__ __align__(16) float slstm_sink[128];
+__device__ __align__(16) float slstm_zero[8];
+
 template <int DHP>
 struct alignas(16) SlstmSmem {
     bf16 hb[2][16 * (DHP + 8)];            // ping-pong B operand: [column][cell], hi 0..7, lo 8..15
@@ -159,11 +164,11 @@ __global__ __launch_bounds__(sl_threads<DHP>()) void slstm_kernel(
     // are loaded PD steps ahead into a ring of registers (the step loop is unrolled
     // by PD so the ring index is static), so their memory latency hides behind PD
     // steps.  They are loaded unconditionally from a valid address -- lanes that own
-    // no cell read the start of x_pre, steps past the end re-read the last -- so the
-    // loaded registers carry into their step without a select (which would make the
+    // no cell read zeros, steps past the end re-read the last -- so the loaded
+    // registers carry into their step without a select (which would make the
     // compiler wait for them at once).
     constexpr int PD = sl_prefetch<T, DHP>();
-    const float* xb = own ? x_pre + ((size_t)b * NH + hd) * S * 4 * dh + r0 : x_pre;
+    const float* xb = own ? x_pre + ((size_t)b * NH + hd) * S * 4 * dh + r0 : slstm_zero;
     const size_t xstep = own ? (size_t)4 * dh : 0;
     const int goff = own ? dh : 0;
     f32x2 xr[PD][4];
@@ -171,59 +176,71 @@ __global__ __launch_bounds__(sl_threads<DHP>()) void slstm_kernel(
     for (int u = 0; u < PD; ++u)
 #pragma unroll
         for (int gt = 0; gt < 4; ++gt) xr[u][gt] = load2(xb + (size_t)min(u, S - 1) * xstep + gt * goff);
+    // h of lanes that own no cell goes to a sink, so the store needs no branch
+    T* hrow = own ? h + ((size_t)b * NH + hd) * S * dh + r0 : reinterpret_cast<T*>(slstm_sink) + 2 * lane;
+    const size_t hstep = own ? (size_t)dh : 0;
 
-    for (int t0 = 0; t0 < S; t0 += PD) {
+    // One step; branch free, so that the compiler can count the loads in flight
+    // (a branch around a load or store makes it wait for all of them).  Lanes that
+    // own no cell compute on zero inputs: their values stay finite and only reach
+    // cells and sequences that are not stored (padded cells meet zero matrix columns).
+    // Gate arithmetic: with d = log f + m_{t-1} - log i, exactly one of the
+    // stabilized gates is 1 and the other exp(-|d|); sigmoid(a_o) c / n takes one
+    // reciprocal.
+    auto step = [&](int t, f32x2 (&xu)[4]) __attribute__((always_inline)) {
+        const int cur = t & 1;
+        lds_barrier();                                 // h_{t-1} complete in hb[cur]; loads stay in flight
+        f32x4 acc[4];
 #pragma unroll
-        for (int u = 0; u < PD; ++u) {
-            const int t = t0 + u;
-            if (t >= S) break;
-            const int cur = t & 1;
-            lds_barrier();                             // h_{t-1} complete in hb[cur]; loads stay in flight
-            f32x4 acc[4];
+        for (int gt = 0; gt < 4; ++gt) acc[gt] = f32x4{0, 0, 0, 0};
 #pragma unroll
-            for (int gt = 0; gt < 4; ++gt) acc[gt] = f32x4{0, 0, 0, 0};
+        for (int kk = 0; kk < KS; ++kk) {
+            const bf16x8 hbv = *reinterpret_cast<const bf16x8*>(sm.hb[cur] + ln * P + 32 * kk + 8 * g);
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const bf16x8 hbv = *reinterpret_cast<const bf16x8*>(sm.hb[cur] + ln * P + 32 * kk + 8 * g);
-#pragma unroll
-                for (int gt = 0; gt < 4; ++gt) {
-                    acc[gt] = mfma(ra[gt][kk], hbv, acc[gt]);
-                    if constexpr (SPLIT) acc[gt] = mfma(rl[gt][kk], hbv, acc[gt]);
-                }
+            for (int gt = 0; gt < 4; ++gt) {
+                acc[gt] = mfma(ra[gt][kk], hbv, acc[gt]);
+                if constexpr (SPLIT) acc[gt] = mfma(rl[gt][kk], hbv, acc[gt]);
             }
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                // gate sums of cell r0 + i: this lane's rows 2*half + i, plus the remainder column
-                float a[4];
-#pragma unroll
-                for (int gt = 0; gt < 4; ++gt) {
-                    const float lo_i = half ? acc[gt][2 + i] : acc[gt][i];
-                    const float hi_i = half ? acc[gt][i] : acc[gt][2 + i];
-                    // lanes l and l + 8 exchange the pair the other one updates
-                    a[gt] = lo_i + row_swap8(hi_i) + xr[u][gt][i];
-                }
-                const float lf = FEXP ? a[2] : fast_log_sigmoid(a[2]);
-                const float mt = fmaxf(lf + ms[i], a[1]);
-                const float fs = __expf(lf + ms[i] - mt), is = __expf(a[1] - mt);
-                cs[i] = fs * cs[i] + is * fast_tanh(a[0]);
-                ns[i] = fs * ns[i] + is;
-                ms[i] = mt;
-                hv[i] = fast_sigmoid(a[3]) * cs[i] * fast_rcp(ns[i]);
-            }
-            if (own) {
-                store_h2(h + (((size_t)b * NH + hd) * S + t) * dh + r0, hv);
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const bf16 hi = (bf16)hv[i];
-                    sm.hb[cur ^ 1][bl * P + r0 + i] = hi;
-                    sm.hb[cur ^ 1][(SL_BT + bl) * P + r0 + i] = (bf16)(hv[i] - (float)hi);
-                }
-            }
-            const size_t tn = (size_t)min(t + PD, S - 1) * xstep;
-#pragma unroll
-            for (int gt = 0; gt < 4; ++gt) xr[u][gt] = load2(xb + tn + gt * goff);
         }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            // gate sums of cell r0 + i: this lane's column of rows 2*half + i, plus the
+            // other half's column (lanes l and l + 8 exchange the pair the other updates)
+            float a[4];
+#pragma unroll
+            for (int gt = 0; gt < 4; ++gt) {
+                const float mine = half ? acc[gt][2 + i] : acc[gt][i];
+                const float other = half ? acc[gt][i] : acc[gt][2 + i];
+                a[gt] = mine + row_swap8(other) + xu[gt][i];
+            }
+            const float lf = FEXP ? a[2] : fast_log_sigmoid(a[2]);
+            const float d = lf + ms[i] - a[1];
+            const float e = __expf(-fabsf(d));
+            const float fs = d >= 0.0f ? 1.0f : e, is = d >= 0.0f ? e : 1.0f;
+            cs[i] = fs * cs[i] + is * fast_tanh(a[0]);
+            ns[i] = fs * ns[i] + is;
+            ms[i] = fmaxf(lf + ms[i], a[1]);
+            hv[i] = cs[i] * fast_rcp(ns[i] * (1.0f + __expf(-a[3])));
+        }
+        store_h2(hrow + (size_t)t * hstep, hv);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const bf16 hi = (bf16)hv[i];
+            sm.hb[cur ^ 1][bl * P + r0 + i] = hi;
+            sm.hb[cur ^ 1][(SL_BT + bl) * P + r0 + i] = (bf16)(hv[i] - (float)hi);
+        }
+        const size_t tn = (size_t)min(t + PD, S - 1) * xstep;
+#pragma unroll
+        for (int gt = 0; gt < 4; ++gt) xu[gt] = load2(xb + tn + gt * goff);
+    };
+    const int nfull = S - S % PD;
+    for (int t0 = 0; t0 < nfull; t0 += PD) {
+#pragma unroll
+        for (int u = 0; u < PD; ++u) step(t0 + u, xr[u]);
     }
+#pragma unroll
+    for (int u = 0; u < PD; ++u)
+        if (nfull + u < S) step(nfull + u, xr[u]);
     if (own) {
         *reinterpret_cast<f32x2*>(cF + st0) = cs;
         *reinterpret_cast<f32x2*>(nF + st0) = ns;
