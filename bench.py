@@ -51,6 +51,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 METRIC = "mLSTM fwd tokens/s + TFLOP/s (% bf16 MFMA peak); step tokens/s (% HBM BW)"
 SCAN_SOURCE = os.path.join(ROOT, "mlstm_matrix_memory_amd", "csrc", "fwd_mfma_kernel.hip")
 STEP_SOURCE = os.path.join(ROOT, "mlstm_matrix_memory_amd", "csrc", "step_kernel.hip")
+EPILOGUE_SOURCE = os.path.join(ROOT, "mlstm_matrix_memory_amd", "csrc", "epilogue_kernel.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
@@ -294,7 +295,8 @@ def main() -> int:
                         "swish gate",
             "us_per_call": ep_ms * 1e3,
             "roofline": {"kernel": "epilogue_kernel", "bound": "hbm", "achieved": ep_gbs, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": ep_gbs / HBM_PEAK_GBS, "traffic": None,
+                         "unit": "GB/s", "frac": ep_gbs / HBM_PEAK_GBS,
+                         "traffic": measured_traffic("epilogue_kernel", EPILOGUE_SOURCE, w.name),
                          "alg_bytes_per_launch": ep_bytes},
         }
         del de, y, ea
