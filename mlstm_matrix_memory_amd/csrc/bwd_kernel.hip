@@ -771,6 +771,20 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
     const bf16* dnh_g = reinterpret_cast<const bf16*>(ws.dnum);
     const bf16* dnl_g = dnh_g + (size_t)in.heads * S * dv;
 
+    // k_s and v_s as B operands (k-slot 8g + j <-> dimension 32 kk + 8g + j): held in
+    // registers across all query blocks up to width 384; at 512 they do not fit and
+    // are re-read (from cache) at every k-step
+    constexpr bool KV_REG = D <= 384;
+    auto kop = [&](int kk) { return ld8(in.k + (tokh + s) * dqk + 32 * kk + 8 * g, sval && 32 * kk + 8 * g < dqk); };
+    auto vop = [&](int kk) { return ld8(in.v + (tokh + s) * dv + 32 * kk + 8 * g, sval && 32 * kk + 8 * g < dv); };
+    bf16x8 kb[KV_REG ? KS : 1], vb[KV_REG ? KS : 1];
+    if constexpr (KV_REG) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            kb[kk] = kop(kk);
+            vb[kk] = vop(kk);
+        }
+    }
     f32x4 dka[NB], dva[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) dka[b] = dva[b] = f32x4{0, 0, 0, 0};
@@ -792,15 +806,14 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
         for (int tb = 0; tb < TB; ++tb) sc[tb] = da[tb] = f32x4{0, 0, 0, 0};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
-            // k_s and v_s as B operands: k-slot 8g + j <-> dimension 32 kk + 8g + j (cache-resident)
-            const bf16x8 kb = ld8(in.k + (tokh + s) * dqk + 32 * kk + 8 * g, sval && 32 * kk + 8 * g < dqk);
-            const bf16x8 vb = ld8(in.v + (tokh + s) * dv + 32 * kk + 8 * g, sval && 32 * kk + 8 * g < dv);
+            const bf16x8 kbk = KV_REG ? kb[KV_REG ? kk : 0] : kop(kk);
+            const bf16x8 vbk = KV_REG ? vb[KV_REG ? kk : 0] : vop(kk);
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
                 const int off = (16 * tb + ln) * P + 32 * kk + 8 * g;
-                sc[tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.q + off), kb, sc[tb]);
-                da[tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.dh + off), vb, da[tb]);
-                da[tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.dl + off), vb, da[tb]);
+                sc[tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.q + off), kbk, sc[tb]);
+                da[tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.dh + off), vbk, da[tb]);
+                da[tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.dl + off), vbk, da[tb]);
             }
         }
         // P = S (.) D', G = (dA + dden') (.) D', as hi/lo B operands over query slots
