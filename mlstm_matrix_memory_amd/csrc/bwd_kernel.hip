@@ -548,6 +548,8 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
 {
     constexpr int P = D + 8;
     constexpr int NB = D / 16, KS = D / 32;
+    constexpr int GB = 4;                       // value / key blocks whose operands are read together
+    static_assert(NB % GB == 0, "width must be a multiple of 64");
     __shared__ RowsSmem<D> sm;
     int bh, rb;
     grid_block(in.heads, bh, rb);
@@ -599,12 +601,20 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) st[sb] = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
+        for (int k0 = 0; k0 < KS; k0 += 2) {
+            bf16x8 a[2][4];
 #pragma unroll
-            for (int sb = 0; sb < 4; ++sb) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(sm.k + (16 * sb + ln) * P + 32 * kk + 8 * g);
-                st[sb] = mfma(a, qb[kk], st[sb]);
-            }
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb)
+                    a[j][sb] = k0 + j < KS ? *reinterpret_cast<const bf16x8*>(sm.k + (16 * sb + ln) * P + 32 * (k0 + j) + 8 * g)
+                                           : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb)
+                    if (k0 + j < KS) st[sb] = mfma(a[j][sb], qb[k0 + j < KS ? k0 + j : 0], st[sb]);
+        }
         float d[4][4];
         decay4(d, c0);
         bf16x8 ph[2], pl[2];
@@ -619,15 +629,26 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
                 ph[sb >> 1][4 * (sb & 1) + i] = hi;
                 pl[sb >> 1][4 * (sb & 1) + i] = lo;
             }
+        // operands of GB value blocks read together, then their products with
+        // consecutive MFMAs on independent accumulators (LDS latency overlaps)
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
+        for (int nb0 = 0; nb0 < NB; nb0 += GB) {
+            bf16x8 a[GB][2];
+#pragma unroll
+            for (int j = 0; j < GB; ++j)
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const bf16* vp = sm.v + (32 * pr + 4 * g + (ln >> 2)) * P + 16 * (nb0 + j) + 4 * (ln & 3);
+                    a[j][pr] = cat(lds_read_tr(vp), lds_read_tr(vp + 16 * P));
+                }
 #pragma unroll
             for (int pr = 0; pr < 2; ++pr) {
-                const bf16* vp = sm.v + (32 * pr + 4 * g + (ln >> 2)) * P + 16 * nb + 4 * (ln & 3);
-                const bf16x8 a = cat(lds_read_tr(vp), lds_read_tr(vp + 16 * P));
-                num[nb] = mfma(a, ph[pr], num[nb]);
-                num[nb] = mfma(a, pl[pr], num[nb]);
+#pragma unroll
+                for (int j = 0; j < GB; ++j) num[nb0 + j] = mfma(a[j][pr], ph[pr], num[nb0 + j]);
+#pragma unroll
+                for (int j = 0; j < GB; ++j) num[nb0 + j] = mfma(a[j][pr], pl[pr], num[nb0 + j]);
             }
+        }
     }
 
     // ---- per query: u, do~, dnum', dden' ------------------------------------
@@ -695,14 +716,18 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) da[sb] = f32x4{0, 0, 0, 0};
 #pragma unroll
-        for (int pr = 0; pr < NB / 2; ++pr)
+        for (int pr = 0; pr < NB / 2; ++pr) {
+            bf16x8 a[4];
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
                 const bf16* vp = sm.v + (16 * sb + ln) * P + 32 * pr + 4 * g;
-                const bf16x8 a = cat(*reinterpret_cast<const bf16x4*>(vp), *reinterpret_cast<const bf16x4*>(vp + 16));
-                da[sb] = mfma(a, dnh[pr], da[sb]);
-                da[sb] = mfma(a, dnl[pr], da[sb]);
+                a[sb] = cat(*reinterpret_cast<const bf16x4*>(vp), *reinterpret_cast<const bf16x4*>(vp + 16));
             }
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) da[sb] = mfma(a[sb], dnh[pr], da[sb]);
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) da[sb] = mfma(a[sb], dnl[pr], da[sb]);
+        }
         float d[4][4];
         decay4(d, c0);
         bf16x8 gh[2], gl[2];
@@ -716,14 +741,23 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
                 gl[sb >> 1][4 * (sb & 1) + i] = lo;
             }
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb)
+        for (int jb0 = 0; jb0 < NB; jb0 += GB) {
+            bf16x8 a[GB][2];
+#pragma unroll
+            for (int j = 0; j < GB; ++j)
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const bf16* kp = sm.k + (32 * pr + 4 * g + (ln >> 2)) * P + 16 * (jb0 + j) + 4 * (ln & 3);
+                    a[j][pr] = cat(lds_read_tr(kp), lds_read_tr(kp + 16 * P));
+                }
 #pragma unroll
             for (int pr = 0; pr < 2; ++pr) {
-                const bf16* kp = sm.k + (32 * pr + 4 * g + (ln >> 2)) * P + 16 * jb + 4 * (ln & 3);
-                const bf16x8 a = cat(lds_read_tr(kp), lds_read_tr(kp + 16 * P));
-                dqa[jb] = mfma(a, gh[pr], dqa[jb]);
-                dqa[jb] = mfma(a, gl[pr], dqa[jb]);
+#pragma unroll
+                for (int j = 0; j < GB; ++j) dqa[jb0 + j] = mfma(a[j][pr], gh[pr], dqa[jb0 + j]);
+#pragma unroll
+                for (int j = 0; j < GB; ++j) dqa[jb0 + j] = mfma(a[j][pr], gl[pr], dqa[jb0 + j]);
             }
+        }
     }
     float qdq = 0.0f;
 #pragma unroll
