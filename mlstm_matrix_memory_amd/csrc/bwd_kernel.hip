@@ -533,6 +533,56 @@ __device__ __forceinline__ void stage_rows(bf16* dst, const bf16* src, size_t to
     }
 }
 
+// K and V rows [row0, row0 + 64) into LDS (pitch P) with every load of both tiles
+// issued before the first store: one memory round trip per stage instead of one per
+// batch.  (Used up to width 384, where the 2 * D / 32 registers per thread fit beside
+// the live state; wider tiles go through stage_rows in batches.)
+template <int D, int P>
+__device__ __forceinline__ void stage_kv(bf16* dk_, bf16* dv_, const bf16* ks, const bf16* vs, size_t tok0,
+                                         int row0, int S, int dqk, int dv, int tid) {
+    constexpr int UPT = 64 * D / 8 / MB_THREADS;
+    bf16x8 rk[UPT], rv[UPT];
+#pragma unroll
+    for (int b = 0; b < UPT; ++b) {
+        const int u = tid + b * MB_THREADS;
+        const int r = u / (D / 8), c8 = 8 * (u % (D / 8));
+        rk[b] = ld8(ks + (tok0 + row0 + r) * dqk + c8, row0 + r < S && c8 < dqk);
+        rv[b] = ld8(vs + (tok0 + row0 + r) * dv + c8, row0 + r < S && c8 < dv);
+    }
+#pragma unroll
+    for (int b = 0; b < UPT; ++b) {
+        const int u = tid + b * MB_THREADS;
+        const int r = u / (D / 8), c8 = 8 * (u % (D / 8));
+        *reinterpret_cast<bf16x8*>(dk_ + r * P + c8) = rk[b];
+        *reinterpret_cast<bf16x8*>(dv_ + r * P + c8) = rv[b];
+    }
+}
+
+// Q, dnum' hi and dnum' lo rows [row0, row0 + R) into LDS with every load issued
+// before the first store (one memory round trip per stage)
+template <int R, int D, int P>
+__device__ __forceinline__ void stage_qd(bf16* dq_, bf16* dh_, bf16* dl_, const bf16* qs, const bf16* hs,
+                                         const bf16* ls, size_t tok0, int row0, int S, int dqk, int dv, int tid) {
+    constexpr int UPT = R * D / 8 / MB_THREADS;
+    bf16x8 rq[UPT], rh[UPT], rl[UPT];
+#pragma unroll
+    for (int b = 0; b < UPT; ++b) {
+        const int u = tid + b * MB_THREADS;
+        const int r = u / (D / 8), c8 = 8 * (u % (D / 8));
+        rq[b] = ld8(qs + (tok0 + row0 + r) * dqk + c8, row0 + r < S && c8 < dqk);
+        rh[b] = ld8(hs + (tok0 + row0 + r) * dv + c8, row0 + r < S && c8 < dv);
+        rl[b] = ld8(ls + (tok0 + row0 + r) * dv + c8, row0 + r < S && c8 < dv);
+    }
+#pragma unroll
+    for (int b = 0; b < UPT; ++b) {
+        const int u = tid + b * MB_THREADS;
+        const int r = u / (D / 8), c8 = 8 * (u % (D / 8));
+        *reinterpret_cast<bf16x8*>(dq_ + r * P + c8) = rq[b];
+        *reinterpret_cast<bf16x8*>(dh_ + r * P + c8) = rh[b];
+        *reinterpret_cast<bf16x8*>(dl_ + r * P + c8) = rl[b];
+    }
+}
+
 template <int D>
 struct alignas(16) RowsSmem {
     bf16 k[64 * (D + 8)];
@@ -570,8 +620,12 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
 
     auto stage = [&](int c0) {
         __syncthreads();
-        stage_rows<64, D, P, 8>(sm.k, in.k, tokh, c0, S, dqk, tid);
-        stage_rows<64, D, P, 8>(sm.v, in.v, tokh, c0, S, dv, tid);
+        if constexpr (D <= 384) {
+            stage_kv<D, P>(sm.k, sm.v, in.k, in.v, tokh, c0, S, dqk, dv, tid);
+        } else {
+            stage_rows<64, D, P, 8>(sm.k, in.k, tokh, c0, S, dqk, tid);
+            stage_rows<64, D, P, 8>(sm.v, in.v, tokh, c0, S, dv, tid);
+        }
         if (tid < 64) {
             const int s = min(c0 + tid, S - 1);
             sm.gs[tid] = ws.F[tokh + s] - (double)in.i_pre[tokh + s];
@@ -825,9 +879,13 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
 
     for (int r0 = c0; r0 < S; r0 += QB) {
         __syncthreads();
-        stage_rows<QB, D, P, 4>(sm.q, in.q, tokh, r0, S, dqk, tid);
-        stage_rows<QB, D, P, 4>(sm.dh, dnh_g, tokh, r0, S, dv, tid);
-        stage_rows<QB, D, P, 4>(sm.dl, dnl_g, tokh, r0, S, dv, tid);
+        if constexpr (QB * D <= 32 * 384) {
+            stage_qd<QB, D, P>(sm.q, sm.dh, sm.dl, in.q, dnh_g, dnl_g, tokh, r0, S, dqk, dv, tid);
+        } else {
+            stage_rows<QB, D, P, 4>(sm.q, in.q, tokh, r0, S, dqk, tid);
+            stage_rows<QB, D, P, 4>(sm.dh, dnh_g, tokh, r0, S, dv, tid);
+            stage_rows<QB, D, P, 4>(sm.dl, dnl_g, tokh, r0, S, dv, tid);
+        }
         if (tid < QB) {
             const int tt = min(r0 + tid, S - 1);
             sm.rt[tid] = ws.F[tokh + tt] - ws.m[tokh + tt];
