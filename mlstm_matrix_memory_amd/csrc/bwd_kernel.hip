@@ -846,6 +846,7 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
 {
     constexpr int P = D + 8;
     constexpr int NB = D / 16, KS = D / 32, TB = QB / 16;
+    constexpr int CB = 2;                       // key / value blocks whose operands are read together
     __shared__ ColsSmem<D, QB> sm;
     int bh, cb;
     grid_block(in.heads, bh, cb);               // the first key blocks have the most query blocks
@@ -924,20 +925,30 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
                 gh[tb >> 1][4 * (tb & 1) + i] = hi;
                 gl[tb >> 1][4 * (tb & 1) + i] = lo;
             }
-        // dk^T[j][s] += Q^T G ;  dv^T[n][s] += dnum'^T P
+        // dk^T[j][s] += Q^T G ;  dv^T[n][s] += dnum'^T P.  The operands of CB blocks are
+        // read together, then their MFMAs run on independent accumulators.
 #pragma unroll
-        for (int b = 0; b < NB; ++b)
+        for (int b0 = 0; b0 < NB; b0 += CB)
 #pragma unroll
             for (int pr = 0; pr < TB / 2; ++pr) {
-                const int off = (32 * pr + 4 * g + (ln >> 2)) * P + 16 * b + 4 * (ln & 3);
-                const bf16x8 aq = cat(lds_read_tr(sm.q + off), lds_read_tr(sm.q + off + 16 * P));
-                dka[b] = mfma(aq, gh[pr], dka[b]);
-                dka[b] = mfma(aq, gl[pr], dka[b]);
-                const bf16x8 ah = cat(lds_read_tr(sm.dh + off), lds_read_tr(sm.dh + off + 16 * P));
-                const bf16x8 al = cat(lds_read_tr(sm.dl + off), lds_read_tr(sm.dl + off + 16 * P));
-                dva[b] = mfma(ah, ph[pr], dva[b]);
-                dva[b] = mfma(ah, pl[pr], dva[b]);
-                dva[b] = mfma(al, ph[pr], dva[b]);
+                bf16x8 aq[CB], ah[CB], al[CB];
+#pragma unroll
+                for (int j = 0; j < CB; ++j) {
+                    const int off = (32 * pr + 4 * g + (ln >> 2)) * P + 16 * (b0 + j) + 4 * (ln & 3);
+                    aq[j] = cat(lds_read_tr(sm.q + off), lds_read_tr(sm.q + off + 16 * P));
+                    ah[j] = cat(lds_read_tr(sm.dh + off), lds_read_tr(sm.dh + off + 16 * P));
+                    al[j] = cat(lds_read_tr(sm.dl + off), lds_read_tr(sm.dl + off + 16 * P));
+                }
+#pragma unroll
+                for (int j = 0; j < CB; ++j) dka[b0 + j] = mfma(aq[j], gh[pr], dka[b0 + j]);
+#pragma unroll
+                for (int j = 0; j < CB; ++j) dva[b0 + j] = mfma(ah[j], ph[pr], dva[b0 + j]);
+#pragma unroll
+                for (int j = 0; j < CB; ++j) dka[b0 + j] = mfma(aq[j], gl[pr], dka[b0 + j]);
+#pragma unroll
+                for (int j = 0; j < CB; ++j) dva[b0 + j] = mfma(ah[j], pl[pr], dva[b0 + j]);
+#pragma unroll
+                for (int j = 0; j < CB; ++j) dva[b0 + j] = mfma(al[j], ph[pr], dva[b0 + j]);
             }
     }
     float kdk = 0.0f;
