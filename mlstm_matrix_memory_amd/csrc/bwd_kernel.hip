@@ -44,17 +44,56 @@ struct BwdWs {
     float* qdq;     // [heads][S] q_t . dq_t (MFMA path)
 };
 
+// States of the two-level form (MFMA path, long sequences): see bwd_state_walk
+struct SuperStates {
+    int LS;          // tokens per superchunk (multiple of 64)
+    int G;           // superchunks per head; states exist for g = 0 .. G - 2
+    bf16* C;         // [heads][G-1][2][d_v][d_qk]: bf16 hi, then lo
+    float* n;        // [heads][G-1][d_qk]
+    bf16* dC;        // gradients of the states, same layout
+    float* dn;       // [heads][G-1][d_qk]
+    float* part;     // per-superchunk sums, fp32 [heads][G-1][d_v d_qk + d_qk]
+};
+
+int mfma_bwd_width(const BwdArgs& a);
+
+// Superchunk length of the two-level form: the quadratic tiles shrink to a band of
+// LS tokens, at the price of one state product per 64-token block (about three
+// blocks' worth of band work) and a sequential walk over the sequence.  Short
+// sequences stay one superchunk (G = 1).
+inline int bwd_superchunk(const BwdArgs& a) {
+    const int S64 = (a.S + 63) / 64 * 64;
+    const int LS = 256;
+    // workgroups of the per-superchunk kernel and threads of the scan fit a 1-D grid
+    const long long heads = (long long)a.B * a.NH;
+    const long long local = heads * ((a.dv + 63) / 64) * ((a.dqk + 63) / 64) * ((a.S + LS - 1) / LS);
+    const long long scan = heads * (((long long)a.dv * a.dqk + a.dqk) / 4);
+    if (mfma_bwd_width(a) == 0 || a.S < 1024 || local > 0x7fffffffLL || scan > 0x7fffffffLL) return S64;
+    return LS;
+}
+
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline size_t bwd_ws_walk(char* base, size_t heads, size_t S, int dv, BwdWs* out) {
+inline size_t bwd_ws_walk(char* base, const BwdArgs& a, BwdWs* out, SuperStates* ss) {
+    const size_t heads = (size_t)a.B * a.NH, S = a.S;
     size_t off = 0;
     auto take = [&](size_t bytes) { char* p = base + off; off += a256(bytes); return p; };
     BwdWs w;
     w.F = (double*)take(heads * S * sizeof(double));
     w.m = (double*)take(heads * S * sizeof(double));
-    w.dnum = (float*)take(heads * S * dv * sizeof(float));
+    w.dnum = (float*)take(heads * S * a.dv * sizeof(float));
     w.dden = (float*)take(heads * S * sizeof(float));
     w.qdq = (float*)take(heads * S * sizeof(float));
+    SuperStates st;
+    st.LS = bwd_superchunk(a);
+    st.G = (a.S + st.LS - 1) / st.LS;
+    const size_t ns = heads * (size_t)(st.G - 1);
+    st.C = (bf16*)take(ns * 2 * a.dv * a.dqk * sizeof(bf16));
+    st.dC = (bf16*)take(ns * 2 * a.dv * a.dqk * sizeof(bf16));
+    st.n = (float*)take(ns * a.dqk * sizeof(float));
+    st.dn = (float*)take(ns * a.dqk * sizeof(float));
+    st.part = (float*)take(ns * ((size_t)a.dv * a.dqk + a.dqk) * sizeof(float));
     if (out) *out = w;
+    if (ss) *ss = st;
     return off;
 }
 
@@ -152,6 +191,7 @@ struct BwdIn {
     const float* i_pre; const float* f_pre; const float* o_pre;
     int S, dqk, dv;
     int heads, nb;          // heads and 64-token blocks per head
+    int LS, G;              // two-level form: tokens per superchunk and superchunks (G = 1: none)
 };
 
 // (head, block) of a workgroup of the 1-D grid over blocks x heads: all heads' block
@@ -533,6 +573,226 @@ __device__ __forceinline__ void stage_rows(bf16* dst, const bf16* src, size_t to
     }
 }
 
+// ===========================================================================
+// Two-level form: states at superchunk boundaries (long sequences)
+// ===========================================================================
+// With superchunks of LS tokens (g = 0, 1, ...; e_g = last token of g, mu_g = m at
+// e_g), every key s before superchunk g reaches a query t in g only through the
+// stabilized state at the end of superchunk g - 1:
+//   C~_g = sum_{s <= e_g} exp(F_{e_g} - F_s + i~_s - mu_g) v_s k_s^T   (n~_g likewise)
+//   sum_{s <= e_{g-1}} D'_ts S_ts v_s = beta_t C~_{g-1} q_t,
+//   beta_t = exp(F_t - F_{e_{g-1}} + mu_{g-1} - m_t) <= 1.
+// So a query needs key blocks of its own superchunk only (the existing tiles,
+// restricted to that band) plus beta_t C~_{g-1} q_t; its dq gains
+// beta_t (C~_{g-1}^T dnum'_t + n~_{g-1} dden'_t).  In reverse, the gradient of the
+// state at the end of superchunk g collects the queries of g + 1 and, decayed, the
+// gradient of the next state:
+//   dC~_g = sum_{t in g+1} beta_t dnum'_t q_t^T + gamma_{g+1} dC~_{g+1},
+//   gamma_{g+1} = exp(F_{e_{g+1}} - F_{e_g} + mu_g - mu_{g+1}) <= 1,
+// and a key s of superchunk g gains dv_s += omega_s dC~_g k_s and
+// dk_s += omega_s (dC~_g^T v_s + dn~_g), omega_s = exp(F_{e_g} - F_s + i~_s - mu_g).
+// Every weight is <= 1 since m is the running max of the log-weights.
+constexpr int WK_THREADS = 256;
+
+__device__ __forceinline__ size_t state_off(int bh, int g, int G, int dv, int dqk) {
+    return ((size_t)bh * (G - 1) + g) * 2 * (size_t)dv * dqk;
+}
+
+struct alignas(16) LocalSmem {
+    bf16 x[2][64 * 72];      // X tile [token][n] (hi; lo in reverse), pitch 72
+    bf16 y[64 * 72];         // Y tile [token][j]
+    float w[64];             // token weights
+    float dd[64];            // weights of the vector part
+    float t[64 * 68];        // the finished 64 x 64 tile, for 16-byte stores
+};
+
+// The contribution of one superchunk to one state, for one 64 x 64 tile of it:
+//   forward  L_g = sum_{s in g}     omega_s v_s k_s^T,        l_g = sum omega_s k_s
+//   reverse  R_g = sum_{t in g + 1} beta_t dnum'_t q_t^T,     r_g = sum beta_t dden'_t q_t
+// (omega and beta relative to the end of superchunk g, as in the states).  One
+// workgroup per (tile, state, head) of a 1-D grid, tile fastest; the next 64
+// tokens' loads are issued before the current tile's products, so memory latency
+// overlaps the MFMAs.  The sums go to `part` as fp32 [heads][G-1][d_v d_qk + d_qk]
+// (matrix rows n, then the vector), and the tiles with n0 == 0 also sum the vector.
+template <bool REV>
+__global__ __launch_bounds__(WK_THREADS) void bwd_state_local(BwdIn<bf16> in, BwdWs ws, SuperStates ss,
+                                                              float* __restrict__ part)
+{
+    __shared__ LocalSmem sm;
+    const int S = in.S, dqk = in.dqk, dv = in.dv, G = ss.G, LS = ss.LS;
+    const int tj = (dqk + 63) / 64, tiles = tj * ((dv + 63) / 64);
+    const int tile = blockIdx.x % tiles, gh = blockIdx.x / tiles;
+    const int g = gh % (G - 1), bh = gh / (G - 1);
+    const int n0 = 64 * (tile / tj), j0 = 64 * (tile % tj);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 15, g4 = lane >> 4;
+    const size_t tokh = (size_t)bh * S;
+    const bf16* dnh = reinterpret_cast<const bf16*>(ws.dnum);
+    const bf16* dnl = dnh + (size_t)in.heads * S * dv;
+    const bf16* xs = REV ? dnh : in.v;
+    const bf16* ys = REV ? in.q : in.k;
+    const bool vec = n0 == 0;
+    const int eg = (g + 1) * LS - 1;
+    const double Fe = ws.F[tokh + eg], mue = ws.m[tokh + eg];
+    const int ta = REV ? (g + 1) * LS : g * LS;
+    const int tb = REV ? min(S, (g + 2) * LS) : (g + 1) * LS;
+
+    // this thread's share of a 64-token step: rows r0 + 32 b (b = 0, 1), 8 columns
+    const int lr = tid / 8, lc = 8 * (tid % 8);
+    bf16x8 rx[2], rl[2], ry[2];
+    double wa = 0.0, wb = 0.0;              // per-token gate values (tid < 64)
+    float wdd = 0.0f;
+    bool wok = false;
+    auto load = [&](int s0) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            const int s = s0 + lr + 32 * b;
+            const bool ok = s < tb;
+            const size_t ts = tokh + (ok ? s : ta);
+            rx[b] = ld8(xs + ts * dv + n0 + lc, ok && n0 + lc < dv);
+            rl[b] = REV ? ld8(dnl + ts * dv + n0 + lc, ok && n0 + lc < dv) : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            ry[b] = ld8(ys + ts * dqk + j0 + lc, ok && j0 + lc < dqk);
+        }
+        if (tid < 64) {
+            const int s = s0 + tid;
+            const size_t ts = tokh + (s < tb ? s : ta);
+            wa = ws.F[ts];
+            wb = REV ? ws.m[ts] : (double)in.i_pre[ts];
+            wdd = REV ? ws.dden[ts] : 1.0f;
+            wok = s < tb;                    // weight 0 beyond the superchunk
+        }
+    };
+
+    f32x4 acc[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) acc[jb] = f32x4{0, 0, 0, 0};
+    float vpart = 0.0f;                     // vector partial: column tid % 64, tokens tid / 64 + 4 r
+    load(ta);
+    for (int s0 = ta; s0 < tb; s0 += 64) {
+        __syncthreads();                     // previous step's tiles consumed
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            *reinterpret_cast<bf16x8*>(sm.x[0] + (lr + 32 * b) * 72 + lc) = rx[b];
+            if (REV) *reinterpret_cast<bf16x8*>(sm.x[1] + (lr + 32 * b) * 72 + lc) = rl[b];
+            *reinterpret_cast<bf16x8*>(sm.y + (lr + 32 * b) * 72 + lc) = ry[b];
+        }
+        if (tid < 64) {
+            // omega_s = exp(F_e - F_s + i~_s - mu_e);  beta_t = exp(F_t - F_e + mu_e - m_t)
+            const float wgt = !wok ? 0.0f : REV ? exp_arg(wa - Fe + mue - wb) : exp_arg(Fe - wa + wb - mue);
+            sm.w[tid] = wgt;
+            sm.dd[tid] = wgt * wdd;
+        }
+        lds_barrier();
+        if (s0 + 64 < tb) load(s0 + 64);     // in flight during the products below
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const int trow = 32 * kk + 8 * g4 + (ln >> 2);
+            const bf16* xp = sm.x[0] + trow * 72 + 16 * wave + 4 * (ln & 3);
+            const bf16x8 xv = cat(lds_read_tr(xp), lds_read_tr(xp + 4 * 72));
+            bf16x8 xl = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            if (REV) {
+                const bf16* xq = sm.x[1] + trow * 72 + 16 * wave + 4 * (ln & 3);
+                xl = cat(lds_read_tr(xq), lds_read_tr(xq + 4 * 72));
+            }
+            const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sm.w[32 * kk + 8 * g4]);
+            const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sm.w[32 * kk + 8 * g4 + 4]);
+            bf16x8 ah, al;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xf = (float)xv[e] + (REV ? (float)xl[e] : 0.0f);
+                bf16 hi, lo;
+                hilo((e < 4 ? w0[e] : w1[e - 4]) * xf, hi, lo);
+                ah[e] = hi;
+                al[e] = lo;
+            }
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+                const bf16* yp = sm.y + trow * 72 + 16 * jb + 4 * (ln & 3);
+                const bf16x8 yv = cat(lds_read_tr(yp), lds_read_tr(yp + 4 * 72));
+                acc[jb] = mfma(ah, yv, acc[jb]);
+                acc[jb] = mfma(al, yv, acc[jb]);
+            }
+        }
+        if (vec) {
+#pragma unroll 4
+            for (int r = wave; r < 64; r += 4) vpart += sm.dd[r] * (float)sm.y[r * 72 + lane];
+        }
+    }
+    // the tile (and the vector) to `part`, 16-byte stores
+    __syncthreads();
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.t[(16 * wave + 4 * g4 + i) * 68 + 16 * jb + ln] = acc[jb][i];
+    __syncthreads();
+    const size_t E = (size_t)dv * dqk + dqk;
+    float* dst = part + ((size_t)bh * (G - 1) + g) * E;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int r = lr + 32 * b;
+        if (n0 + r < dv && j0 + lc < dqk) {
+            float* p = dst + (size_t)(n0 + r) * dqk + j0 + lc;
+            *reinterpret_cast<f32x4*>(p) = *reinterpret_cast<const f32x4*>(&sm.t[r * 68 + lc]);
+            *reinterpret_cast<f32x4*>(p + 4) = *reinterpret_cast<const f32x4*>(&sm.t[r * 68 + lc + 4]);
+        }
+    }
+    if (vec) {
+        __syncthreads();
+        sm.t[wave * 68 + lane] = vpart;
+        __syncthreads();
+        if (tid < 64 && j0 + tid < dqk)
+            dst[(size_t)dv * dqk + j0 + tid] = sm.t[tid] + sm.t[68 + tid] + sm.t[2 * 68 + tid] + sm.t[3 * 68 + tid];
+    }
+}
+
+// The states from the per-superchunk sums, element by element in superchunk order:
+//   forward  C~_g  = L_g + gamma_g C~_{g-1},     gamma_g = exp(F_{e_g} - F_{e_{g-1}} + mu_{g-1} - mu_g)
+//   reverse  dC~_g = R_g + gamma_{g+1} dC~_{g+1}
+// (the vectors likewise), stored as bf16 hi + lo (matrices) and fp32 (vectors).
+// One thread per 4 consecutive elements of a head's [d_v d_qk + d_qk]; the next
+// superchunk's sums are loaded before the current one is finished.
+template <bool REV>
+__global__ __launch_bounds__(WK_THREADS) void bwd_state_scan(BwdIn<bf16> in, BwdWs ws, SuperStates ss,
+                                                             const float* __restrict__ part, long long quads)
+{
+    const long long qd = (long long)blockIdx.x * WK_THREADS + threadIdx.x;
+    if (qd >= quads) return;
+    const int dqk = in.dqk, dv = in.dv, G = ss.G, LS = ss.LS;
+    const size_t M = (size_t)dv * dqk, E = M + dqk, EQ = E / 4;
+    const int bh = (int)(qd / EQ);
+    const size_t e = 4 * (size_t)(qd % EQ);
+    const size_t tokh = (size_t)bh * in.S;
+    const float* src = part + (size_t)bh * (G - 1) * E + e;
+    f32x4 c = f32x4{0, 0, 0, 0};
+    int g = REV ? G - 2 : 0;
+    f32x4 nxt = load4(src + (size_t)g * E);
+    for (int step = 0; step < G - 1; ++step, g += REV ? -1 : 1) {
+        const f32x4 cur = nxt;
+        if (step + 1 < G - 1) nxt = load4(src + (size_t)(REV ? g - 1 : g + 1) * E);
+        if (step > 0) {
+            const int ec = (g + 1) * LS - 1, ep = REV ? (g + 2) * LS - 1 : g * LS - 1;
+            const double Fc = ws.F[tokh + ec], mc = ws.m[tokh + ec];
+            const double Fp = ws.F[tokh + ep], mp = ws.m[tokh + ep];
+            c *= REV ? exp_arg(Fp - Fc + mc - mp) : exp_arg(Fc - Fp + mp - mc);
+        }
+        c += cur;
+        if (e < M) {
+            bf16* hp = (REV ? ss.dC : ss.C) + state_off(bh, g, G, dv, dqk) + e;
+            bf16x4 h4, l4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bf16 hi, lo;
+                hilo(c[i], hi, lo);
+                h4[i] = hi;
+                l4[i] = lo;
+            }
+            *reinterpret_cast<bf16x4*>(hp) = h4;
+            *reinterpret_cast<bf16x4*>(hp + M) = l4;
+        } else {
+            *reinterpret_cast<f32x4*>((REV ? ss.dn : ss.n) + ((size_t)bh * (G - 1) + g) * dqk + (e - M)) = c;
+        }
+    }
+}
+
 // K and V rows [row0, row0 + 64) into LDS (pitch P) with every load of both tiles
 // issued before the first store: one memory round trip per stage instead of one per
 // batch.  (Used up to width 384, where the 2 * D / 32 registers per thread fit beside
@@ -593,8 +853,8 @@ struct alignas(16) RowsSmem {
 // per (head, query block of 64): num', den' over key blocks <= it, then dnum', dden',
 // do~ (wave-local), then dq over the same key blocks, and q_t . dq_t
 template <int D>
-__global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdWs ws, float* __restrict__ dq,
-                                                          float* __restrict__ dout)
+__global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdWs ws, SuperStates ss,
+                                                          float* __restrict__ dq, float* __restrict__ dout)
 {
     constexpr int P = D + 8;
     constexpr int NB = D / 16, KS = D / 32;
@@ -612,6 +872,17 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
     const bool tval = t < S;
     const double Rt = tval ? ws.F[tokh + t] - ws.m[tokh + t] : 0.0;
     const float fl = tval ? exp_arg(-ws.m[tokh + t]) : 1.0f;
+    // two-level form: key blocks of this superchunk only, the earlier ones through the
+    // state at the end of the previous superchunk, weighted by beta_t
+    const int sg = rb * 64 / in.LS;                 // superchunk of this query block
+    const int cb_lo = sg * (in.LS / 64);
+    float beta = 0.0f;
+    size_t soff = 0;
+    if (sg > 0) {
+        const int ep = sg * in.LS - 1;
+        if (tval) beta = exp_arg(Rt - ws.F[tokh + ep] + ws.m[tokh + ep]);
+        soff = state_off(bh, sg - 1, in.G, dv, dqk);
+    }
 
     // q_t as B operands: k-slot 8g + j <-> key dimension 32 kk + 8g + j
     bf16x8 qb[KS];
@@ -632,6 +903,17 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
         }
         __syncthreads();
     };
+    // rows [64 sl, 64 sl + 64) of the d_v x d_qk state (hi into sm.k, lo into sm.v)
+    auto stage_state = [&](const bf16* hi, const bf16* lo, int sl) {
+        __syncthreads();
+        if constexpr (D <= 384) {
+            stage_kv<D, P>(sm.k, sm.v, hi, lo, 0, 64 * sl, dv, dqk, dqk, tid);
+        } else {
+            stage_rows<64, D, P, 8>(sm.k, hi, 0, 64 * sl, dv, dqk, tid);
+            stage_rows<64, D, P, 8>(sm.v, lo, 0, 64 * sl, dv, dqk, tid);
+        }
+        __syncthreads();
+    };
     // D'[s][t] for this lane's 16 entries of a tile pair (s = 16 sb + 4g + i)
     auto decay4 = [&](float (&d)[4][4], int c0) {
 #pragma unroll
@@ -648,7 +930,44 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) num[nb] = f32x4{0, 0, 0, 0};
     float den = 0.0f;
-    for (int cb = 0; cb <= rb; ++cb) {
+    if (sg > 0) {
+        // num'^T[n][t] = beta_t (C~ q_t)[n],  den'_t = beta_t n~ . q_t (lane partials);
+        // the state rows take the place of the key rows of a tile
+        const bf16* Chi = ss.C + soff;
+        const bf16* Clo = Chi + (size_t)dv * dqk;
+#pragma unroll
+        for (int sl = 0; sl < D / 64; ++sl) {
+            if (64 * sl >= dv) break;
+            stage_state(Chi, Clo, sl);
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                bf16x8 ah[4], al[4];
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) {
+                    const int off = (16 * sb + ln) * P + 32 * kk + 8 * g;
+                    ah[sb] = *reinterpret_cast<const bf16x8*>(sm.k + off);
+                    al[sb] = *reinterpret_cast<const bf16x8*>(sm.v + off);
+                }
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) num[4 * sl + sb] = mfma(ah[sb], qb[kk], num[4 * sl + sb]);
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb) num[4 * sl + sb] = mfma(al[sb], qb[kk], num[4 * sl + sb]);
+            }
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) num[nb] *= beta;
+        const float* nt = ss.n + ((size_t)bh * (in.G - 1) + sg - 1) * dqk;
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            const int j = 32 * kk + 8 * g;
+            if (j < dqk) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) den += nt[j + e] * (float)qb[kk][e];
+            }
+        }
+        den *= beta;
+    }
+    for (int cb = cb_lo; cb <= rb; ++cb) {
         const int c0 = 64 * cb;
         stage(c0);
         f32x4 st[4];
@@ -763,7 +1082,49 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
     f32x4 dqa[NB];
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) dqa[jb] = f32x4{0, 0, 0, 0};
-    for (int cb = 0; cb <= rb; ++cb) {
+    if (sg > 0) {
+        // dq^T[j][t] = beta_t (C~^T dnum'_t + n~ dden'_t)[j]: transposing reads of the
+        // staged state rows, whose n order follows dnum''s k-slots (as V's in pass 1)
+        const bf16* Chi = ss.C + soff;
+        const bf16* Clo = Chi + (size_t)dv * dqk;
+        const float* nt = ss.n + ((size_t)bh * (in.G - 1) + sg - 1) * dqk;
+#pragma unroll
+        for (int sl = 0; sl < D / 64; ++sl) {
+            if (64 * sl >= dv) break;
+            stage_state(Chi, Clo, sl);
+            constexpr int GI = D <= 256 ? GB : 2;   // fewer operands in flight at the widest tiles
+#pragma unroll
+            for (int jb0 = 0; jb0 < NB; jb0 += GI) {
+                bf16x8 ah[GI][2], al[GI][2];
+#pragma unroll
+                for (int j = 0; j < GI; ++j)
+#pragma unroll
+                    for (int pr = 0; pr < 2; ++pr) {
+                        const int off = (32 * pr + 4 * g + (ln >> 2)) * P + 16 * (jb0 + j) + 4 * (ln & 3);
+                        ah[j][pr] = cat(lds_read_tr(sm.k + off), lds_read_tr(sm.k + off + 16 * P));
+                        al[j][pr] = cat(lds_read_tr(sm.v + off), lds_read_tr(sm.v + off + 16 * P));
+                    }
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+                    for (int j = 0; j < GI; ++j) dqa[jb0 + j] = mfma(ah[j][pr], dnh[2 * sl + pr], dqa[jb0 + j]);
+#pragma unroll
+                    for (int j = 0; j < GI; ++j) dqa[jb0 + j] = mfma(ah[j][pr], dnl[2 * sl + pr], dqa[jb0 + j]);
+#pragma unroll
+                    for (int j = 0; j < GI; ++j) dqa[jb0 + j] = mfma(al[j][pr], dnh[2 * sl + pr], dqa[jb0 + j]);
+                }
+            }
+        }
+#pragma unroll
+        for (int jb = 0; jb < NB; ++jb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int jj = 16 * jb + 4 * g + i;
+                dqa[jb][i] = beta * (dqa[jb][i] + (jj < dqk ? nt[jj] * dd : 0.0f));
+            }
+        }
+    }
+    for (int cb = cb_lo; cb <= rb; ++cb) {
         const int c0 = 64 * cb;
         stage(c0);
         f32x4 da[4];
@@ -841,7 +1202,8 @@ struct alignas(16) ColsSmem {
 // per (head, key block of 64): dk, dv over query blocks >= it (QB queries at a
 // time), and k_s . dk_s (= di~_s)
 template <int D, int QB>
-__global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdWs ws, float* __restrict__ dk,
+__global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdWs ws, SuperStates ss,
+                                                          float* __restrict__ dk,
                                                           float* __restrict__ dvv, float* __restrict__ di)
 {
     constexpr int P = D + 8;
@@ -878,7 +1240,68 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
 #pragma unroll
     for (int b = 0; b < NB; ++b) dka[b] = dva[b] = f32x4{0, 0, 0, 0};
 
-    for (int r0 = c0; r0 < S; r0 += QB) {
+    // two-level form: query blocks of this superchunk only, the later ones through the
+    // gradient of the state at the end of this superchunk, weighted by omega_s
+    const int sg = c0 / in.LS;
+    const int r_hi = min(S, (sg + 1) * in.LS);
+    if (sg < in.G - 1) {
+        const int ep = (sg + 1) * in.LS - 1;
+        const float omega = sval ? exp_arg(ws.F[tokh + ep] - Qs - ws.m[tokh + ep]) : 0.0f;
+        const bf16* Nhi = ss.dC + state_off(bh, sg, in.G, dv, dqk);
+        const bf16* Nlo = Nhi + (size_t)dv * dqk;
+        const float* dnt = ss.dn + ((size_t)bh * (in.G - 1) + sg) * dqk;
+        // QB-row slices of dC~ (hi into sm.dh, lo into sm.dl):
+        //   dv^T[n][s] += dC~[n][j] k_s[j]   (direct reads of the slice's rows n)
+        //   dk^T[j][s] += dC~^T[j][n] v_s[n] (transposing reads, n within the slice)
+#pragma unroll
+        for (int sl = 0; sl < D / QB; ++sl) {
+            if (QB * sl >= dv) break;
+            __syncthreads();
+            stage_rows<QB, D, P, 4>(sm.dh, Nhi, 0, QB * sl, dv, dqk, tid);
+            stage_rows<QB, D, P, 4>(sm.dl, Nlo, 0, QB * sl, dv, dqk, tid);
+            __syncthreads();
+#pragma unroll
+            for (int kk = 0; kk < KS; ++kk) {
+                const bf16x8 kbk = KV_REG ? kb[KV_REG ? kk : 0] : kop(kk);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const int off = (16 * tb + ln) * P + 32 * kk + 8 * g;
+                    dva[TB * sl + tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.dh + off), kbk, dva[TB * sl + tb]);
+                    dva[TB * sl + tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.dl + off), kbk, dva[TB * sl + tb]);
+                }
+            }
+#pragma unroll
+            for (int kq = 0; kq < QB / 32; ++kq) {
+                const int kk = QB / 32 * sl + kq;
+                const bf16x8 vbk = KV_REG ? vb[KV_REG ? kk : 0] : vop(kk);
+#pragma unroll
+                for (int b0 = 0; b0 < NB; b0 += CB) {
+                    bf16x8 ah[CB], al[CB];
+#pragma unroll
+                    for (int j = 0; j < CB; ++j) {
+                        const int off = (32 * kq + 8 * g + (ln >> 2)) * P + 16 * (b0 + j) + 4 * (ln & 3);
+                        ah[j] = cat(lds_read_tr(sm.dh + off), lds_read_tr(sm.dh + off + 4 * P));
+                        al[j] = cat(lds_read_tr(sm.dl + off), lds_read_tr(sm.dl + off + 4 * P));
+                    }
+#pragma unroll
+                    for (int j = 0; j < CB; ++j) dka[b0 + j] = mfma(ah[j], vbk, dka[b0 + j]);
+#pragma unroll
+                    for (int j = 0; j < CB; ++j) dka[b0 + j] = mfma(al[j], vbk, dka[b0 + j]);
+                }
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int jj = 16 * b + 4 * g + i;
+                dka[b][i] = omega * (dka[b][i] + (jj < dqk ? dnt[jj] : 0.0f));
+                dva[b][i] *= omega;
+            }
+        }
+    }
+
+    for (int r0 = c0; r0 < r_hi; r0 += QB) {
         __syncthreads();
         if constexpr (QB * D <= 32 * 384) {
             stage_qd<QB, D, P>(sm.q, sm.dh, sm.dl, in.q, dnh_g, dnl_g, tokh, r0, S, dqk, dv, tid);
@@ -979,13 +1402,29 @@ int mfma_bwd_width(const BwdArgs& a) {
 }
 
 template <int D, int QB>
-hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdIn<bf16>& in, const BwdWs& w) {
+hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdIn<bf16>& in, const BwdWs& w, const SuperStates& ss) {
     const int heads = a.B * a.NH, nb = (a.S + 63) / 64;
-    hipLaunchKernelGGL((bwd_rows_mfma<D>), dim3(heads * nb), dim3(MB_THREADS), 0, a.stream, in, w, a.dq, a.dout);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_cols_mfma<D, QB>), dim3(heads * nb), dim3(MB_THREADS), 0, a.stream, in, w, a.dk, a.dvv,
-                       a.di);
+    const long long tiles = (long long)((a.dv + 63) / 64) * ((a.dqk + 63) / 64);
+    const dim3 lgrid((unsigned)(tiles * heads * (ss.G - 1)));
+    const long long quads = (long long)heads * (((long long)a.dv * a.dqk + a.dqk) / 4);
+    const dim3 sgrid((unsigned)((quads + WK_THREADS - 1) / WK_THREADS));
+    hipError_t e;
+    if (ss.G > 1) {
+        hipLaunchKernelGGL((bwd_state_local<false>), lgrid, dim3(WK_THREADS), 0, a.stream, in, w, ss, ss.part);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_state_scan<false>), sgrid, dim3(WK_THREADS), 0, a.stream, in, w, ss, ss.part, quads);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((bwd_rows_mfma<D>), dim3(heads * nb), dim3(MB_THREADS), 0, a.stream, in, w, ss, a.dq, a.dout);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ss.G > 1) {
+        hipLaunchKernelGGL((bwd_state_local<true>), lgrid, dim3(WK_THREADS), 0, a.stream, in, w, ss, ss.part);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL((bwd_state_scan<true>), sgrid, dim3(WK_THREADS), 0, a.stream, in, w, ss, ss.part, quads);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((bwd_cols_mfma<D, QB>), dim3(heads * nb), dim3(MB_THREADS), 0, a.stream, in, w, ss, a.dk,
+                       a.dvv, a.di);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_gates_kernel<bf16, true>), dim3(heads), dim3(BW_THREADS), 0, a.stream, in, a.dq, a.dk,
                        w.qdq, a.di, a.df);
@@ -996,7 +1435,8 @@ template <typename T>
 hipError_t launch_bwd_t(const BwdArgs& a) {
     const int heads = a.B * a.NH;
     BwdWs w;
-    bwd_ws_walk((char*)a.ws, (size_t)heads, a.S, a.dv, &w);
+    SuperStates ss;
+    bwd_ws_walk((char*)a.ws, a, &w, &ss);
     BwdIn<T> in;
     in.q = (const T*)a.q; in.k = (const T*)a.k; in.v = (const T*)a.v; in.dh = (const T*)a.dh;
     in.i_pre = a.i_pre; in.f_pre = a.f_pre; in.o_pre = a.o_pre;
@@ -1004,16 +1444,18 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
     const int nb = (a.S + BT - 1) / BT;
     in.heads = heads;
     in.nb = nb;
+    in.LS = ss.LS;
+    in.G = ss.G;
     hipLaunchKernelGGL(bwd_gate_kernel, dim3(heads), dim3(BW_THREADS), 0, a.stream, a.i_pre, a.f_pre, a.S, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if constexpr (sizeof(T) == 2) {
         switch (mfma_bwd_width(a)) {
-            case 64: return launch_bwd_mfma<64, 64>(a, in, w);
-            case 128: return launch_bwd_mfma<128, 64>(a, in, w);
-            case 256: return launch_bwd_mfma<256, 64>(a, in, w);
-            case 384: return launch_bwd_mfma<384, 32>(a, in, w);
-            case 512: return launch_bwd_mfma<512, 32>(a, in, w);
+            case 64: return launch_bwd_mfma<64, 64>(a, in, w, ss);
+            case 128: return launch_bwd_mfma<128, 64>(a, in, w, ss);
+            case 256: return launch_bwd_mfma<256, 64>(a, in, w, ss);
+            case 384: return launch_bwd_mfma<384, 32>(a, in, w, ss);
+            case 512: return launch_bwd_mfma<512, 32>(a, in, w, ss);
             default: break;
         }
     }
@@ -1029,7 +1471,7 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
 }  // namespace
 
 size_t bwd_workspace_bytes(const BwdArgs& a) {
-    return bwd_ws_walk(nullptr, (size_t)a.B * a.NH, a.S, a.dv, nullptr);
+    return bwd_ws_walk(nullptr, a, nullptr, nullptr);
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {

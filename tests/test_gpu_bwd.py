@@ -116,6 +116,40 @@ def test_bf16_mfma_widths(orc, name, over):
     _compare(orc, x, dh, "bf16")
 
 
+# the two-level form (sequences of 1024 tokens or more: superchunks of 256 tokens,
+# the earlier ones reached through the states at their ends) at every tile width,
+# with ragged last superchunks and tiles, unequal d_qk / d_v and the long-context
+# gates with input-gate spikes
+TWO_LEVEL_CASES = [
+    ("lm_125m", dict(B=1, NH=1, S=1090, dqk=64, dv=48)),
+    ("lm_125m", dict(B=2, NH=1, S=1030, dqk=128, dv=80)),
+    ("long_ctx", dict(B=1, NH=2, S=1100, dqk=256, dv=256)),
+    ("lm_125m", dict(B=1, NH=1, S=1300, dqk=384, dv=160)),
+    ("lm_125m", dict(B=1, NH=1, S=1024, dqk=512, dv=512)),
+    ("long_ctx", dict(B=1, NH=1, S=1200, dqk=112, dv=448)),
+    ("long_ctx", dict(B=1, NH=1, S=2200, dqk=256, dv=256)),
+]
+
+
+@pytest.mark.parametrize("name,over", TWO_LEVEL_CASES, ids=lambda v: str(v))
+def test_bf16_two_level(orc, name, over):
+    w = inputs.WORKLOADS[name]
+    announce(f"bwd bf16 two-level {name} {over}")
+    x = inputs.fwd_inputs(w, seed=450 + w.seed, **over)
+    dh = inputs.bwd_dh(w, seed=450 + w.seed, B=over["B"], NH=over["NH"], S=over["S"], dv=over["dv"])
+    _compare(orc, x, dh, "bf16")
+
+
+def test_bf16_two_level_normalizer_floor(orc):
+    # input gates lowered by 3: the floor is active on part of the rows, also where
+    # the denominator comes mostly through the superchunk states
+    w = inputs.WORKLOADS["lm_125m"]
+    announce("bwd bf16 two-level floor B=1 NH=2 S=1111 d=128")
+    x = inputs.fwd_inputs(w, seed=460, B=1, NH=2, S=1111, dqk=128, dv=128)
+    x["i_pre"] = (x["i_pre"] - np.float32(3.0)).astype(np.float32)
+    _compare(orc, x, inputs.bwd_dh(w, seed=460, B=1, NH=2, S=1111, dv=128), "bf16")
+
+
 def test_bf16_mfma_normalizer_floor(orc):
     # input gates lowered by 3: the floor is active on part of the rows
     w = inputs.WORKLOADS["lm_125m"]
