@@ -21,11 +21,11 @@
 // Tiled passes over 64-token blocks with fp32 accumulation and fp64 exponent
 // arguments (on the vector ALUs here; bf16 inputs with d_qk, d_v <= 512 take the
 // MFMA form of the two middle passes further down):
-//   bwd_gate_kernel   per head: F and m (prefix sum, prefix max), fp64
+//   bwd_gate_local/fix  per head: F and m (prefix sum, prefix max), fp64, by segments
 //   bwd_rows_kernel   per (query block, head): num', den' over key blocks <= it, then
 //                     dnum', dden', do~; then dq over the same key blocks
 //   bwd_cols_kernel   per (key block, head): dk, dv over query blocks >= it
-//   bwd_gates_kernel  per head: di~, df~ (reverse prefix sum)
+//   bwd_gates_kernel/fix  per head: di~, df~ (reverse prefix sum), by segments
 #include "mlstm_internal.h"
 
 namespace mlstm {
@@ -42,9 +42,12 @@ struct BwdWs {
                     // the MFMA path keeps dnum' there as bf16 hi [heads][S][dv], then lo
     float* dden;    // [heads][S] dden'
     float* qdq;     // [heads][S] q_t . dq_t (MFMA path)
+    double* seg;    // [heads][segments][2] per-segment totals of the two gate scans
 };
 
-// States of the two-level form (MFMA path, long sequences): see bwd_state_walk
+constexpr int GSEG = 1024;       // tokens per segment of the gate scans
+
+// States of the two-level form (MFMA path, long sequences): see bwd_state_local
 struct SuperStates {
     int LS;          // tokens per superchunk (multiple of 64)
     int G;           // superchunks per head; states exist for g = 0 .. G - 2
@@ -83,6 +86,7 @@ inline size_t bwd_ws_walk(char* base, const BwdArgs& a, BwdWs* out, SuperStates*
     w.dnum = (float*)take(heads * S * a.dv * sizeof(float));
     w.dden = (float*)take(heads * S * sizeof(float));
     w.qdq = (float*)take(heads * S * sizeof(float));
+    w.seg = (double*)take(heads * ((S + GSEG - 1) / GSEG) * 2 * sizeof(double));
     SuperStates st;
     st.LS = bwd_superchunk(a);
     st.G = (a.S + st.LS - 1) / st.LS;
@@ -99,16 +103,22 @@ inline size_t bwd_ws_walk(char* base, const BwdArgs& a, BwdWs* out, SuperStates*
 
 // ---- kernel 1: F and m per head --------------------------------------------
 // m_t = max(log f_t + m_{t-1}, i~_t) from m = 0 unrolls to F_t + max(0, max_{s<=t}(i~_s - F_s)).
-__global__ __launch_bounds__(BW_THREADS) void bwd_gate_kernel(const float* __restrict__ i_pre,
-                                                              const float* __restrict__ f_pre, int S, BwdWs ws)
+// Both are prefix scans; they run over segments of GSEG tokens in parallel
+// (bwd_gate_local: sums and maxima within the segment, and the segment's totals),
+// then bwd_gate_fix adds what the earlier segments carry in.  fp64 throughout.
+__global__ __launch_bounds__(BW_THREADS) void bwd_gate_local(const float* __restrict__ i_pre,
+                                                             const float* __restrict__ f_pre, int S, BwdWs ws)
 {
     __shared__ double part[BW_THREADS / 64];
-    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nseg = (S + GSEG - 1) / GSEG;
+    const int sg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t base = (size_t)bh * S;
-    double carry_sum = 0.0, carry_max = 0.0;     // max(0, ...) folds the zero initial state in
-    for (int t0 = 0; t0 < S; t0 += BW_THREADS) {
+    const int ta = sg * GSEG, tb = min(S, ta + GSEG);
+    double carry_sum = 0.0, carry_max = -INFINITY;
+    for (int t0 = ta; t0 < tb; t0 += BW_THREADS) {
         const int t = t0 + tid;
-        double x = t < S ? log_sigmoid_f64((double)f_pre[base + t]) : 0.0;
+        double x = t < tb ? log_sigmoid_f64((double)f_pre[base + t]) : 0.0;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const double y = __shfl_up(x, off, 64);
@@ -118,11 +128,11 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_gate_kernel(const float* __res
         __syncthreads();
         double pre = carry_sum;
         for (int w2 = 0; w2 < wave; ++w2) pre += part[w2];
-        const double F = pre + x;
+        const double F = pre + x;                       // within the segment
         double tot = carry_sum;
         for (int w2 = 0; w2 < BW_THREADS / 64; ++w2) tot += part[w2];
         __syncthreads();
-        double z = t < S ? (double)i_pre[base + t] - F : -INFINITY;
+        double z = t < tb ? (double)i_pre[base + t] - F : -INFINITY;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const double y = __shfl_up(z, off, 64);
@@ -132,16 +142,46 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_gate_kernel(const float* __res
         __syncthreads();
         double pm = carry_max;
         for (int w2 = 0; w2 < wave; ++w2) pm = fmax(pm, part[w2]);
-        const double M = fmax(pm, z);
         double tm = carry_max;
         for (int w2 = 0; w2 < BW_THREADS / 64; ++w2) tm = fmax(tm, part[w2]);
         __syncthreads();
-        if (t < S) {
+        if (t < tb) {
             ws.F[base + t] = F;
-            ws.m[base + t] = F + M;
+            ws.m[base + t] = fmax(pm, z);               // max over the segment's tokens <= t
         }
         carry_sum = tot;
         carry_max = tm;
+    }
+    if (tid == 0) {
+        ws.seg[((size_t)bh * nseg + sg) * 2] = carry_sum;
+        ws.seg[((size_t)bh * nseg + sg) * 2 + 1] = carry_max;
+    }
+}
+
+__global__ __launch_bounds__(BW_THREADS) void bwd_gate_fix(int S, BwdWs ws)
+{
+    __shared__ double cin[2];
+    const int nseg = (S + GSEG - 1) / GSEG;
+    const int sg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+    const size_t base = (size_t)bh * S;
+    if (threadIdx.x == 0) {
+        // F at the segment's start and max(0, max over earlier tokens of i~ - F)
+        double sum = 0.0, mx = 0.0;
+        for (int b = 0; b < sg; ++b) {
+            const double* p = ws.seg + ((size_t)bh * nseg + b) * 2;
+            mx = fmax(mx, p[1] - sum);
+            sum += p[0];
+        }
+        cin[0] = sum;
+        cin[1] = mx;
+    }
+    __syncthreads();
+    const double sum = cin[0], mx = cin[1];
+    const int ta = sg * GSEG, tb = min(S, ta + GSEG);
+    for (int t = ta + threadIdx.x; t < tb; t += BW_THREADS) {
+        const double F = sum + ws.F[base + t];
+        ws.F[base + t] = F;
+        ws.m[base + t] = F + fmax(mx, ws.m[base + t] - sum);
     }
 }
 
@@ -466,25 +506,30 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_cols_kernel(BwdIn<T> in, BwdWs
 
 // ---- kernel 4: gate gradients per head ----------------------------------------
 // di~_j = k_j . dk_j ;  dF_j = q_j . dq_j - k_j . dk_j ;  df~_j = sigmoid(-f~_j) sum_{t>=j} dF_t
-// DOTS: q . dq comes from the workspace and k . dk is already in di (MFMA path)
+// DOTS: q . dq comes from the workspace and k . dk is already in di (MFMA path).
+// The reverse prefix sum runs over segments of GSEG tokens in parallel: the
+// segment's own suffix sums go to ws.F (fp64; F is not needed any more) and its
+// total to ws.seg, then bwd_gates_fix adds the later segments' totals.
 template <typename T, bool DOTS>
-__global__ __launch_bounds__(BW_THREADS) void bwd_gates_kernel(BwdIn<T> in, const float* __restrict__ dq,
+__global__ __launch_bounds__(BW_THREADS) void bwd_gates_kernel(BwdIn<T> in, BwdWs ws, const float* __restrict__ dq,
                                                                const float* __restrict__ dk,
-                                                               const float* __restrict__ qdq_in,
-                                                               float* __restrict__ di, float* __restrict__ df)
+                                                               float* __restrict__ di)
 {
     __shared__ double part[BW_THREADS / 64];
-    const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int S = in.S, dqk = in.dqk;
+    const int nseg = (S + GSEG - 1) / GSEG;
+    const int sg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const size_t tokh = (size_t)bh * S;
+    const int ta = sg * GSEG, tb = min(S, ta + GSEG);
     double carry = 0.0;
-    // walk the sequence from the end; within a tile, thread tid holds token end - tid
-    for (int e0 = S - 1; e0 >= 0; e0 -= BW_THREADS) {
+    // walk the segment from its end; within a tile, thread tid holds token end - tid
+    for (int e0 = tb - 1; e0 >= ta; e0 -= BW_THREADS) {
         const int t = e0 - tid;
         double dF = 0.0;
-        if (t >= 0) {
+        if (t >= ta) {
             if (DOTS) {
-                dF = (double)qdq_in[tokh + t] - (double)di[tokh + t];
+                dF = (double)ws.qdq[tokh + t] - (double)di[tokh + t];
             } else {
                 double qdq = 0.0, kdk = 0.0;
                 for (int j = 0; j < dqk; ++j) {
@@ -508,11 +553,30 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_gates_kernel(BwdIn<T> in, cons
         double tot = carry;
         for (int w2 = 0; w2 < BW_THREADS / 64; ++w2) tot += part[w2];
         __syncthreads();
-        if (t >= 0) {
-            const double f = (double)in.f_pre[tokh + t];
-            df[tokh + t] = (float)((pre + x) / (1.0 + exp(f)));    // sigmoid(-f) = 1 / (1 + e^f)
-        }
+        if (t >= ta) ws.F[tokh + t] = pre + x;
         carry = tot;
+    }
+    if (tid == 0) ws.seg[((size_t)bh * nseg + sg) * 2] = carry;
+}
+
+template <typename T>
+__global__ __launch_bounds__(BW_THREADS) void bwd_gates_fix(BwdIn<T> in, BwdWs ws, float* __restrict__ df)
+{
+    __shared__ double cin;
+    const int S = in.S;
+    const int nseg = (S + GSEG - 1) / GSEG;
+    const int sg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
+    const size_t tokh = (size_t)bh * S;
+    if (threadIdx.x == 0) {
+        double sum = 0.0;                                // later segments, nearest first
+        for (int b = sg + 1; b < nseg; ++b) sum += ws.seg[((size_t)bh * nseg + b) * 2];
+        cin = sum;
+    }
+    __syncthreads();
+    const int ta = sg * GSEG, tb = min(S, ta + GSEG);
+    for (int t = ta + threadIdx.x; t < tb; t += BW_THREADS) {
+        const double f = (double)in.f_pre[tokh + t];
+        df[tokh + t] = (float)((ws.F[tokh + t] + cin) / (1.0 + exp(f)));    // sigmoid(-f) = 1 / (1 + e^f)
     }
 }
 
@@ -1391,6 +1455,16 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
     if (sval && g == 0) di[tokh + s] = kdk;
 }
 
+template <typename T, bool DOTS>
+hipError_t launch_gates(const BwdArgs& a, const BwdIn<T>& in, const BwdWs& w) {
+    const dim3 sgrid((unsigned)((size_t)a.B * a.NH * ((a.S + GSEG - 1) / GSEG)));
+    hipLaunchKernelGGL((bwd_gates_kernel<T, DOTS>), sgrid, dim3(BW_THREADS), 0, a.stream, in, w, a.dq, a.dk, a.di);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_gates_fix<T>), sgrid, dim3(BW_THREADS), 0, a.stream, in, w, a.df);
+    return hipGetLastError();
+}
+
 // smallest tile width covering both dimensions (0 = not on the MFMA path)
 int mfma_bwd_width(const BwdArgs& a) {
     if (a.dtype != MLSTM_BF16) return 0;
@@ -1426,9 +1500,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdIn<bf16>& in, const BwdWs&
     hipLaunchKernelGGL((bwd_cols_mfma<D, QB>), dim3(heads * nb), dim3(MB_THREADS), 0, a.stream, in, w, ss, a.dk,
                        a.dvv, a.di);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_gates_kernel<bf16, true>), dim3(heads), dim3(BW_THREADS), 0, a.stream, in, a.dq, a.dk,
-                       w.qdq, a.di, a.df);
-    return hipGetLastError();
+    return launch_gates<bf16, true>(a, in, w);
 }
 
 template <typename T>
@@ -1446,9 +1518,12 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
     in.nb = nb;
     in.LS = ss.LS;
     in.G = ss.G;
-    hipLaunchKernelGGL(bwd_gate_kernel, dim3(heads), dim3(BW_THREADS), 0, a.stream, a.i_pre, a.f_pre, a.S, w);
+    const dim3 sgrid((unsigned)((size_t)heads * ((a.S + GSEG - 1) / GSEG)));
+    hipLaunchKernelGGL(bwd_gate_local, sgrid, dim3(BW_THREADS), 0, a.stream, a.i_pre, a.f_pre, a.S, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(bwd_gate_fix, sgrid, dim3(BW_THREADS), 0, a.stream, a.S, w);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if constexpr (sizeof(T) == 2) {
         switch (mfma_bwd_width(a)) {
             case 64: return launch_bwd_mfma<64, 64>(a, in, w, ss);
@@ -1463,9 +1538,7 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_cols_kernel<T>), dim3(heads, nb), dim3(BW_THREADS), 0, a.stream, in, w, a.dk, a.dvv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL((bwd_gates_kernel<T, false>), dim3(heads), dim3(BW_THREADS), 0, a.stream, in, a.dq, a.dk,
-                       nullptr, a.di, a.df);
-    return hipGetLastError();
+    return launch_gates<T, false>(a, in, w);
 }
 
 }  // namespace

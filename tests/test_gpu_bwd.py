@@ -55,7 +55,7 @@ def test_tiny_fp32(orc, S):
     _compare(orc, x, inputs.bwd_dh(w, S=S), "f32")
 
 
-@pytest.mark.parametrize("S,dqk,dv", [(200, 48, 80), (100, 16, 16), (256, 128, 32)])
+@pytest.mark.parametrize("S,dqk,dv", [(200, 48, 80), (100, 16, 16), (256, 128, 32), (2100, 32, 48)])
 def test_fp32_medium(orc, S, dqk, dv):
     w = inputs.WORKLOADS["tiny"]
     announce(f"bwd fp32 B=2 NH=2 S={S} dqk={dqk} dv={dv}")
