@@ -69,7 +69,7 @@ inline int bwd_superchunk(const BwdArgs& a) {
     const int LS = 256;
     // workgroups of the per-superchunk kernel and threads of the scan fit a 1-D grid
     const long long heads = (long long)a.B * a.NH;
-    const long long local = heads * ((a.dv + 63) / 64) * ((a.dqk + 63) / 64) * ((a.S + LS - 1) / LS);
+    const long long local = heads * ((a.dv + 127) / 128) * ((a.dqk + 127) / 128) * ((a.S + LS - 1) / LS);
     const long long scan = heads * (((long long)a.dv * a.dqk + a.dqk) / 4);
     if (mfma_bwd_width(a) == 0 || a.S < 1024 || local > 0x7fffffffLL || scan > 0x7fffffffLL) return S64;
     return LS;
@@ -656,38 +656,44 @@ __device__ __forceinline__ void stage_rows(bf16* dst, const bf16* src, size_t to
 // and a key s of superchunk g gains dv_s += omega_s dC~_g k_s and
 // dk_s += omega_s (dC~_g^T v_s + dn~_g), omega_s = exp(F_{e_g} - F_s + i~_s - mu_g).
 // Every weight is <= 1 since m is the running max of the log-weights.
-constexpr int WK_THREADS = 256;
+constexpr int WK_THREADS = 256;         // the scan
+constexpr int LT = 128;                 // local sums: n and j extent of a workgroup's tile
+constexpr int LW = LT / 16;             // waves of a local-sum workgroup (one 16-row strip each)
+constexpr int LP = LT + 8;              // LDS pitch (bf16) of its token-major tiles
 
 __device__ __forceinline__ size_t state_off(int bh, int g, int G, int dv, int dqk) {
     return ((size_t)bh * (G - 1) + g) * 2 * (size_t)dv * dqk;
 }
 
 struct alignas(16) LocalSmem {
-    bf16 x[2][64 * 72];      // X tile [token][n] (hi; lo in reverse), pitch 72
-    bf16 y[64 * 72];         // Y tile [token][j]
+    bf16 x[2][64 * LP];      // X tile [token][n] (hi; lo in reverse)
+    bf16 y[64 * LP];         // Y tile [token][j]
     float w[64];             // token weights
     float dd[64];            // weights of the vector part
-    float t[64 * 68];        // the finished 64 x 64 tile, for 16-byte stores
+    float vs[4][LT];         // partial sums of the vector
 };
 
-// The contribution of one superchunk to one state, for one 64 x 64 tile of it:
+// The contribution of one superchunk to one state, for one LT x LT tile of it:
 //   forward  L_g = sum_{s in g}     omega_s v_s k_s^T,        l_g = sum omega_s k_s
 //   reverse  R_g = sum_{t in g + 1} beta_t dnum'_t q_t^T,     r_g = sum beta_t dden'_t q_t
 // (omega and beta relative to the end of superchunk g, as in the states).  One
-// workgroup per (tile, state, head) of a 1-D grid, tile fastest; the next 64
-// tokens' loads are issued before the current tile's products, so memory latency
-// overlaps the MFMAs.  The sums go to `part` as fp32 [heads][G-1][d_v d_qk + d_qk]
-// (matrix rows n, then the vector), and the tiles with n0 == 0 also sum the vector.
+// workgroup per (tile, state, head) of a 1-D grid, tile fastest; wave w owns rows
+// n0 + 16 w .. + 15 of the tile and all its columns.  The next 64 tokens' loads are
+// issued before the current tile's products, so memory latency overlaps the MFMAs.
+// The sums go to `part` as fp32 [heads][G-1][d_v d_qk + d_qk] (matrix rows n, then
+// the vector), and the tiles with n0 == 0 also sum the vector.
 template <bool REV>
-__global__ __launch_bounds__(WK_THREADS) void bwd_state_local(BwdIn<bf16> in, BwdWs ws, SuperStates ss,
-                                                              float* __restrict__ part)
+__global__ __launch_bounds__(64 * LW) void bwd_state_local(BwdIn<bf16> in, BwdWs ws, SuperStates ss,
+                                                           float* __restrict__ part)
 {
+    constexpr int NT = 64 * LW;                     // threads
+    constexpr int UPT = 64 * LT / 8 / NT;           // 16-byte units of a tile per thread
     __shared__ LocalSmem sm;
     const int S = in.S, dqk = in.dqk, dv = in.dv, G = ss.G, LS = ss.LS;
-    const int tj = (dqk + 63) / 64, tiles = tj * ((dv + 63) / 64);
+    const int tj = (dqk + LT - 1) / LT, tiles = tj * ((dv + LT - 1) / LT);
     const int tile = blockIdx.x % tiles, gh = blockIdx.x / tiles;
     const int g = gh % (G - 1), bh = gh / (G - 1);
-    const int n0 = 64 * (tile / tj), j0 = 64 * (tile % tj);
+    const int n0 = LT * (tile / tj), j0 = LT * (tile % tj);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 15, g4 = lane >> 4;
     const size_t tokh = (size_t)bh * S;
     const bf16* dnh = reinterpret_cast<const bf16*>(ws.dnum);
@@ -700,21 +706,20 @@ __global__ __launch_bounds__(WK_THREADS) void bwd_state_local(BwdIn<bf16> in, Bw
     const int ta = REV ? (g + 1) * LS : g * LS;
     const int tb = REV ? min(S, (g + 2) * LS) : (g + 1) * LS;
 
-    // this thread's share of a 64-token step: rows r0 + 32 b (b = 0, 1), 8 columns
-    const int lr = tid / 8, lc = 8 * (tid % 8);
-    bf16x8 rx[2], rl[2], ry[2];
+    bf16x8 rx[UPT], rl[UPT], ry[UPT];
     double wa = 0.0, wb = 0.0;              // per-token gate values (tid < 64)
     float wdd = 0.0f;
     bool wok = false;
     auto load = [&](int s0) {
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const int s = s0 + lr + 32 * b;
+        for (int b = 0; b < UPT; ++b) {
+            const int u = tid + NT * b, r = u / (LT / 8), c8 = 8 * (u % (LT / 8));
+            const int s = s0 + r;
             const bool ok = s < tb;
             const size_t ts = tokh + (ok ? s : ta);
-            rx[b] = ld8(xs + ts * dv + n0 + lc, ok && n0 + lc < dv);
-            rl[b] = REV ? ld8(dnl + ts * dv + n0 + lc, ok && n0 + lc < dv) : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
-            ry[b] = ld8(ys + ts * dqk + j0 + lc, ok && j0 + lc < dqk);
+            rx[b] = ld8(xs + ts * dv + n0 + c8, ok && n0 + c8 < dv);
+            rl[b] = REV ? ld8(dnl + ts * dv + n0 + c8, ok && n0 + c8 < dv) : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+            ry[b] = ld8(ys + ts * dqk + j0 + c8, ok && j0 + c8 < dqk);
         }
         if (tid < 64) {
             const int s = s0 + tid;
@@ -726,18 +731,21 @@ __global__ __launch_bounds__(WK_THREADS) void bwd_state_local(BwdIn<bf16> in, Bw
         }
     };
 
-    f32x4 acc[4];
+    f32x4 acc[LT / 16];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) acc[jb] = f32x4{0, 0, 0, 0};
-    float vpart = 0.0f;                     // vector partial: column tid % 64, tokens tid / 64 + 4 r
+    for (int jb = 0; jb < LT / 16; ++jb) acc[jb] = f32x4{0, 0, 0, 0};
+    float vpart[LT / 64];                   // vector partials: column lane + 64 c, tokens = wave (mod 4)
+#pragma unroll
+    for (int c = 0; c < LT / 64; ++c) vpart[c] = 0.0f;
     load(ta);
     for (int s0 = ta; s0 < tb; s0 += 64) {
         __syncthreads();                     // previous step's tiles consumed
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            *reinterpret_cast<bf16x8*>(sm.x[0] + (lr + 32 * b) * 72 + lc) = rx[b];
-            if (REV) *reinterpret_cast<bf16x8*>(sm.x[1] + (lr + 32 * b) * 72 + lc) = rl[b];
-            *reinterpret_cast<bf16x8*>(sm.y + (lr + 32 * b) * 72 + lc) = ry[b];
+        for (int b = 0; b < UPT; ++b) {
+            const int u = tid + NT * b, r = u / (LT / 8), c8 = 8 * (u % (LT / 8));
+            *reinterpret_cast<bf16x8*>(sm.x[0] + r * LP + c8) = rx[b];
+            if (REV) *reinterpret_cast<bf16x8*>(sm.x[1] + r * LP + c8) = rl[b];
+            *reinterpret_cast<bf16x8*>(sm.y + r * LP + c8) = ry[b];
         }
         if (tid < 64) {
             // omega_s = exp(F_e - F_s + i~_s - mu_e);  beta_t = exp(F_t - F_e + mu_e - m_t)
@@ -750,12 +758,12 @@ __global__ __launch_bounds__(WK_THREADS) void bwd_state_local(BwdIn<bf16> in, Bw
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int trow = 32 * kk + 8 * g4 + (ln >> 2);
-            const bf16* xp = sm.x[0] + trow * 72 + 16 * wave + 4 * (ln & 3);
-            const bf16x8 xv = cat(lds_read_tr(xp), lds_read_tr(xp + 4 * 72));
+            const bf16* xp = sm.x[0] + trow * LP + 16 * wave + 4 * (ln & 3);
+            const bf16x8 xv = cat(lds_read_tr(xp), lds_read_tr(xp + 4 * LP));
             bf16x8 xl = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
             if (REV) {
-                const bf16* xq = sm.x[1] + trow * 72 + 16 * wave + 4 * (ln & 3);
-                xl = cat(lds_read_tr(xq), lds_read_tr(xq + 4 * 72));
+                const bf16* xq = sm.x[1] + trow * LP + 16 * wave + 4 * (ln & 3);
+                xl = cat(lds_read_tr(xq), lds_read_tr(xq + 4 * LP));
             }
             const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sm.w[32 * kk + 8 * g4]);
             const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sm.w[32 * kk + 8 * g4 + 4]);
@@ -769,42 +777,45 @@ __global__ __launch_bounds__(WK_THREADS) void bwd_state_local(BwdIn<bf16> in, Bw
                 al[e] = lo;
             }
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
-                const bf16* yp = sm.y + trow * 72 + 16 * jb + 4 * (ln & 3);
-                const bf16x8 yv = cat(lds_read_tr(yp), lds_read_tr(yp + 4 * 72));
+            for (int jb = 0; jb < LT / 16; ++jb) {
+                const bf16* yp = sm.y + trow * LP + 16 * jb + 4 * (ln & 3);
+                const bf16x8 yv = cat(lds_read_tr(yp), lds_read_tr(yp + 4 * LP));
                 acc[jb] = mfma(ah, yv, acc[jb]);
                 acc[jb] = mfma(al, yv, acc[jb]);
             }
         }
-        if (vec) {
+        if (vec && wave < 4) {
 #pragma unroll 4
-            for (int r = wave; r < 64; r += 4) vpart += sm.dd[r] * (float)sm.y[r * 72 + lane];
+            for (int r = wave; r < 64; r += 4) {
+                const float d = sm.dd[r];
+#pragma unroll
+                for (int c = 0; c < LT / 64; ++c) vpart[c] += d * (float)sm.y[r * LP + lane + 64 * c];
+            }
         }
     }
-    // the tile (and the vector) to `part`, 16-byte stores
-    __syncthreads();
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.t[(16 * wave + 4 * g4 + i) * 68 + 16 * jb + ln] = acc[jb][i];
-    __syncthreads();
+    // the tile straight from the accumulators: rows n0 + 16 wave + 4 g4 + i, columns
+    // j0 + 16 jb + ln (16 consecutive floats per row and instruction)
     const size_t E = (size_t)dv * dqk + dqk;
     float* dst = part + ((size_t)bh * (G - 1) + g) * E;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int r = lr + 32 * b;
-        if (n0 + r < dv && j0 + lc < dqk) {
-            float* p = dst + (size_t)(n0 + r) * dqk + j0 + lc;
-            *reinterpret_cast<f32x4*>(p) = *reinterpret_cast<const f32x4*>(&sm.t[r * 68 + lc]);
-            *reinterpret_cast<f32x4*>(p + 4) = *reinterpret_cast<const f32x4*>(&sm.t[r * 68 + lc + 4]);
+    for (int i = 0; i < 4; ++i) {
+        const int n = n0 + 16 * wave + 4 * g4 + i;
+        if (n < dv) {
+#pragma unroll
+            for (int jb = 0; jb < LT / 16; ++jb) {
+                const int j = j0 + 16 * jb + ln;
+                if (j < dqk) dst[(size_t)n * dqk + j] = acc[jb][i];
+            }
         }
     }
     if (vec) {
+        if (wave < 4) {
+#pragma unroll
+            for (int c = 0; c < LT / 64; ++c) sm.vs[wave][lane + 64 * c] = vpart[c];
+        }
         __syncthreads();
-        sm.t[wave * 68 + lane] = vpart;
-        __syncthreads();
-        if (tid < 64 && j0 + tid < dqk)
-            dst[(size_t)dv * dqk + j0 + tid] = sm.t[tid] + sm.t[68 + tid] + sm.t[2 * 68 + tid] + sm.t[3 * 68 + tid];
+        if (tid < LT && j0 + tid < dqk)
+            dst[(size_t)dv * dqk + j0 + tid] = sm.vs[0][tid] + sm.vs[1][tid] + sm.vs[2][tid] + sm.vs[3][tid];
     }
 }
 
@@ -1478,13 +1489,13 @@ int mfma_bwd_width(const BwdArgs& a) {
 template <int D, int QB>
 hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdIn<bf16>& in, const BwdWs& w, const SuperStates& ss) {
     const int heads = a.B * a.NH, nb = (a.S + 63) / 64;
-    const long long tiles = (long long)((a.dv + 63) / 64) * ((a.dqk + 63) / 64);
+    const long long tiles = (long long)((a.dv + LT - 1) / LT) * ((a.dqk + LT - 1) / LT);
     const dim3 lgrid((unsigned)(tiles * heads * (ss.G - 1)));
     const long long quads = (long long)heads * (((long long)a.dv * a.dqk + a.dqk) / 4);
     const dim3 sgrid((unsigned)((quads + WK_THREADS - 1) / WK_THREADS));
     hipError_t e;
     if (ss.G > 1) {
-        hipLaunchKernelGGL((bwd_state_local<false>), lgrid, dim3(WK_THREADS), 0, a.stream, in, w, ss, ss.part);
+        hipLaunchKernelGGL((bwd_state_local<false>), lgrid, dim3(64 * LW), 0, a.stream, in, w, ss, ss.part);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL((bwd_state_scan<false>), sgrid, dim3(WK_THREADS), 0, a.stream, in, w, ss, ss.part, quads);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1492,7 +1503,7 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdIn<bf16>& in, const BwdWs&
     hipLaunchKernelGGL((bwd_rows_mfma<D>), dim3(heads * nb), dim3(MB_THREADS), 0, a.stream, in, w, ss, a.dq, a.dout);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ss.G > 1) {
-        hipLaunchKernelGGL((bwd_state_local<true>), lgrid, dim3(WK_THREADS), 0, a.stream, in, w, ss, ss.part);
+        hipLaunchKernelGGL((bwd_state_local<true>), lgrid, dim3(64 * LW), 0, a.stream, in, w, ss, ss.part);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL((bwd_state_scan<true>), sgrid, dim3(WK_THREADS), 0, a.stream, in, w, ss, ss.part, quads);
         if ((e = hipGetLastError()) != hipSuccess) return e;
