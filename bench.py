@@ -27,11 +27,16 @@ on is unchanged.
 cpu_baseline: the fp64 oracle (oracle/, plain C + OpenMP over heads) timed on the
 host on a bounded sample of the same workload.
 
-Backward: algorithmic FLOPs of the tiled quadratic form are, per head, the
-S(S+1)/2 causal (t, s) pairs times 6 (d_qk + d_v): scores and numerator
-recomputed, then dA, dq, dk and dv, one multiply-add each per pair and dimension.
-The whole call is timed with HIP events on its stream; its roofline is against
-the bf16 MFMA peak.
+Backward: sequences of 1024 tokens or more (bf16, d_qk, d_v <= 512) run the
+two-level form with superchunks of 256 tokens.  Its algorithmic FLOPs are, per
+head, the causal (t, s) pairs inside each superchunk times 6 (d_qk + d_v) (scores
+and numerator recomputed, then dA, dq, dk and dv, one multiply-add each per pair
+and dimension), plus 2 d_v d_qk (+ 2 d_qk for the normalizer) per token for each
+of the six state products: C~ q and C~^T dnum' for the queries after the first
+superchunk, dC~^T v and dC~ k for the keys before the last, and the two
+per-superchunk state sums.  Shorter sequences run the quadratic form over all
+S(S+1)/2 pairs.  The whole call is timed with HIP events on its stream; its
+roofline is against the bf16 MFMA peak.
 """
 from __future__ import annotations
 
@@ -69,8 +74,20 @@ def fwd_alg_bytes(w) -> float:
     return scan_alg_bytes(w) + float(w.B * w.NH * w.S) * 8  # + i~, f~ (fp32)
 
 
+BWD_SUPERCHUNK = 256            # the backward's superchunk length from 1024 tokens on
+
+
 def bwd_alg_flops(w) -> float:
-    return float(w.B * w.NH) * w.S * (w.S + 1) / 2 * 6.0 * (w.dqk + w.dv)
+    S, LS = w.S, BWD_SUPERCHUNK
+    pair = 6.0 * (w.dqk + w.dv)
+    if S < 1024 or max(w.dqk, w.dv) > 512 or w.dtype != "bf16":
+        return float(w.B * w.NH) * S * (S + 1) / 2 * pair
+    G = (S + LS - 1) // LS
+    band = sum(n * (n + 1) / 2 for n in [LS] * (G - 1) + [S - (G - 1) * LS])
+    prod = 2.0 * w.dv * w.dqk + 2.0 * w.dqk       # one state product for one token
+    later, earlier = S - LS, (G - 1) * LS          # queries after the first / keys before the last superchunk
+    per_head = band * pair + prod * (2 * later + 2 * earlier + earlier + later)
+    return float(w.B * w.NH) * per_head
 
 
 def epilogue_alg_bytes(w) -> float:
