@@ -61,9 +61,10 @@ struct SuperStates {
 int mfma_bwd_width(const BwdArgs& a);
 
 // Superchunk length of the two-level form: the quadratic tiles shrink to a band of
-// LS tokens, at the price of one state product per 64-token block (about three
-// blocks' worth of band work) and a sequential walk over the sequence.  Short
-// sequences stay one superchunk (G = 1).
+// LS tokens, at the price of the state products of every 64-token block (about
+// three blocks' worth of band work), the per-superchunk state sums and the scans
+// over superchunks.  256 measured best from 1024 tokens on (128, 512 and 1024 were
+// up to 40% slower); shorter sequences stay one superchunk (G = 1).
 inline int bwd_superchunk(const BwdArgs& a) {
     const int S64 = (a.S + 63) / 64 * 64;
     const int LS = 256;
@@ -928,12 +929,18 @@ struct alignas(16) RowsSmem {
 // per (head, query block of 64): num', den' over key blocks <= it, then dnum', dden',
 // do~ (wave-local), then dq over the same key blocks, and q_t . dq_t
 template <int D>
-__global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdWs ws, SuperStates ss,
+__global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(BwdIn<bf16> in, BwdWs ws, SuperStates ss,
                                                           float* __restrict__ dq, float* __restrict__ dout)
 {
     constexpr int P = D + 8;
     constexpr int NB = D / 16, KS = D / 32;
-    constexpr int GB = 4;                       // value / key blocks whose operands are read together
+    // Up to width 256 two workgroups share a CU (two waves per SIMD, 256 registers
+    // each), so one's staging overlaps the other's products: tiles are staged in
+    // batches of 4 loads per thread and fewer operands are read ahead.  Wider tiles
+    // keep the whole register file and stage with every load in flight (384) or in
+    // batches of 8 (512).
+    constexpr int GB = D <= 256 ? 2 : 4;        // value / key blocks whose operands are read together
+    constexpr int SMB = D <= 256 ? 4 : 8;       // loads per thread per staging batch
     static_assert(NB % GB == 0, "width must be a multiple of 64");
     __shared__ RowsSmem<D> sm;
     int bh, rb;
@@ -966,11 +973,11 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
 
     auto stage = [&](int c0) {
         __syncthreads();
-        if constexpr (D <= 384) {
+        if constexpr (D <= 384 && D > 256) {
             stage_kv<D, P>(sm.k, sm.v, in.k, in.v, tokh, c0, S, dqk, dv, tid);
         } else {
-            stage_rows<64, D, P, 8>(sm.k, in.k, tokh, c0, S, dqk, tid);
-            stage_rows<64, D, P, 8>(sm.v, in.v, tokh, c0, S, dv, tid);
+            stage_rows<64, D, P, SMB>(sm.k, in.k, tokh, c0, S, dqk, tid);
+            stage_rows<64, D, P, SMB>(sm.v, in.v, tokh, c0, S, dv, tid);
         }
         if (tid < 64) {
             const int s = min(c0 + tid, S - 1);
@@ -981,11 +988,11 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
     // rows [64 sl, 64 sl + 64) of the d_v x d_qk state (hi into sm.k, lo into sm.v)
     auto stage_state = [&](const bf16* hi, const bf16* lo, int sl) {
         __syncthreads();
-        if constexpr (D <= 384) {
+        if constexpr (D <= 384 && D > 256) {
             stage_kv<D, P>(sm.k, sm.v, hi, lo, 0, 64 * sl, dv, dqk, dqk, tid);
         } else {
-            stage_rows<64, D, P, 8>(sm.k, hi, 0, 64 * sl, dv, dqk, tid);
-            stage_rows<64, D, P, 8>(sm.v, lo, 0, 64 * sl, dv, dqk, tid);
+            stage_rows<64, D, P, SMB>(sm.k, hi, 0, 64 * sl, dv, dqk, tid);
+            stage_rows<64, D, P, SMB>(sm.v, lo, 0, 64 * sl, dv, dqk, tid);
         }
         __syncthreads();
     };
@@ -1048,17 +1055,18 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_rows_mfma(BwdIn<bf16> in, BwdW
         f32x4 st[4];
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) st[sb] = f32x4{0, 0, 0, 0};
+        constexpr int KB = D <= 256 ? 1 : 2;     // key slabs whose score operands are read together
 #pragma unroll
-        for (int k0 = 0; k0 < KS; k0 += 2) {
-            bf16x8 a[2][4];
+        for (int k0 = 0; k0 < KS; k0 += KB) {
+            bf16x8 a[KB][4];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < KB; ++j)
 #pragma unroll
                 for (int sb = 0; sb < 4; ++sb)
                     a[j][sb] = k0 + j < KS ? *reinterpret_cast<const bf16x8*>(sm.k + (16 * sb + ln) * P + 32 * (k0 + j) + 8 * g)
                                            : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < KB; ++j)
 #pragma unroll
                 for (int sb = 0; sb < 4; ++sb)
                     if (k0 + j < KS) st[sb] = mfma(a[j][sb], qb[k0 + j < KS ? k0 + j : 0], st[sb]);
