@@ -342,7 +342,7 @@ def main() -> int:
         out["slstm"] = {
             "workload": f"slstm_125m: slstm_fwd B={wsl.B} NH={wsl.NH} S={wsl.S} d_h={wsl.dqk} bf16 R, fp32 gates",
             "tokens_per_s": wsl.B * wsl.S * n_sl / swall, "ms_per_call": sl_ms,
-            "us_per_step": sl_ms * 1e3 / wsl.S, "workgroups": wsl.NH * ((wsl.B + 7) // 8),
+            "us_per_step": sl_ms * 1e3 / wsl.S, "workgroups": wsl.NH * ((wsl.B + 3) // 4),
             "roofline": {"kernel": "slstm_kernel", "bound": "mfma", "achieved": stf, "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": stf / BF16_PEAK_TFLOPS, "traffic": None,
                          "alg_flops_per_launch": sflops},

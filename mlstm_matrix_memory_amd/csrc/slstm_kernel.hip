@@ -11,15 +11,16 @@
 //   h_t = sigmoid(a_o) c_t / n_t
 //
 // The recurrence is sequential in t, so a step's latency is what counts.  One
-// workgroup runs one head for a tile of up to 8 sequences, all steps, with one
+// workgroup runs one head for a tile of up to 4 sequences, all steps, with one
 // wave per 16 cells (DHP / 16 waves):
 //   - the wave holds the rows of all four gates of its 16 cells of the head's
 //     recurrent matrices in registers, as bf16 MFMA A operands, for the whole
 //     sequence (an fp32 matrix is held as bf16 hi + lo pairs);
-//   - h_{t-1} of the tile sits in LDS as the B operand: columns 0..7 hold bf16(h)
-//     of the 8 sequences, columns 8..15 the remainder h - bf16(h), so one
-//     16-column MFMA gives R bf16(h) and R (h - bf16(h)) side by side and a lane
-//     swap adds them (the split costs no extra MFMA);
+//   - h_{t-1} of the tile sits in LDS as the B operand: columns s and s + 4 hold
+//     bf16(h) of sequence s, columns s + 8 and s + 12 the remainder h - bf16(h),
+//     so one 16-column MFMA gives R bf16(h) and R (h - bf16(h)) side by side, a
+//     lane swap adds them (the split costs no extra MFMA), and every (cell,
+//     sequence) pair of the wave has a lane of its own for the gate arithmetic;
 //   - the four gate sums of a cell land in the same lanes, which keep that cell's
 //     (c, n, m) for its sequence in registers and update it in place: no LDS
 //     round trip for the gates;
@@ -30,7 +31,7 @@
 namespace mlstm {
 namespace {
 
-constexpr int SL_BT = 8;                   // sequences per workgroup
+constexpr int SL_BT = 4;                   // sequences per workgroup
 
 template <int DHP>
 constexpr int sl_threads() { return 4 * DHP; }    // one wave per 16 cells
@@ -49,11 +50,6 @@ template <int DHP>
 struct alignas(16) SlstmSmem {
     bf16 hb[2][16 * (DHP + 8)];            // ping-pong B operand: [column][cell], hi 0..7, lo 8..15
 };
-
-__device__ __forceinline__ void store_h4(float* p, f32x4 v) { *reinterpret_cast<f32x4*>(p) = v; }
-__device__ __forceinline__ void store_h4(bf16* p, f32x4 v) {
-    *reinterpret_cast<bf16x4*>(p) = bf16x4{(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
-}
 
 // A operand (8 consecutive columns of one R row) from bf16 or fp32 memory
 __device__ __forceinline__ void load_r(const bf16* p, bool ok, bf16x8& hi, bf16x8& lo) {
@@ -80,15 +76,6 @@ __device__ __forceinline__ float fast_tanh(float x) {
     return copysignf((1.0f - e) * fast_rcp(1.0f + e), x);
 }
 
-typedef __attribute__((ext_vector_type(2))) float f32x2;
-
-__device__ __forceinline__ f32x2 load2(const float* p) { return *reinterpret_cast<const f32x2*>(p); }
-__device__ __forceinline__ void store_h2(float* p, f32x2 v) { *reinterpret_cast<f32x2*>(p) = v; }
-__device__ __forceinline__ void store_h2(bf16* p, f32x2 v) {
-    *reinterpret_cast<unsigned*>(p) = (unsigned)__builtin_bit_cast(unsigned short, (bf16)v[0]) |
-                                      ((unsigned)__builtin_bit_cast(unsigned short, (bf16)v[1]) << 16);
-}
-
 // value of lane (l + 8) mod 16 of the same 16-lane row (DPP row rotate by 8, VALU only)
 __device__ __forceinline__ float row_swap8(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
@@ -98,10 +85,10 @@ __device__ __forceinline__ float row_swap8(float x) {
 // FEXP: forget gate exp (log f = a_f) instead of sigmoid.
 //
 // Lane layout of a wave (16 cells, rows 16 w + 4 g + i of each gate): after the
-// products, lane l of 16-lane row g holds the four gate sums of cells 4g + i for
-// sequence l % 8 (lanes l and l + 8 hold the same sums once the bf16 remainder
-// column is added); lane l < 8 then updates cells 4g, 4g+1 and lane l + 8 cells
-// 4g+2, 4g+3, so all 16 lanes share the cell arithmetic.
+// products, lane l of 16-lane row g holds the bf16(h) (l % 16 < 8) or remainder
+// (l % 16 >= 8) part of the four gate sums of cells 4g + i for sequence l % 4;
+// lane l then updates cell 4g + (l % 16) / 4 of that sequence, taking the other
+// part from lane l + 8 (mod 16), which holds it for the same sequence.
 template <typename T, int DHP, bool FEXP>
 __global__ __launch_bounds__(sl_threads<DHP>()) void slstm_kernel(
     const float* __restrict__ x_pre, const T* __restrict__ R, int B, int NH, int S, int dh,
@@ -116,8 +103,8 @@ __global__ __launch_bounds__(sl_threads<DHP>()) void slstm_kernel(
 
     const int hd = blockIdx.x % NH, b0 = (blockIdx.x / NH) * SL_BT;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 15, g = lane >> 4;
-    const int half = ln >> 3, bl = ln & 7;             // lane updates cells 2*half, 2*half+1 of its 4
-    const int r0 = 16 * wave + 4 * g + 2 * half;       // first of this lane's 2 cells
+    const int ci = ln >> 2, bl = ln & 3;               // lane updates cell 4g + ci of sequence bl
+    const int r0 = 16 * wave + 4 * g + ci;             // this lane's cell
     const int b = b0 + bl;
     const bool own = b < B && r0 < dh;                 // lane updates (and stores) these cells
 
@@ -140,19 +127,22 @@ __global__ __launch_bounds__(sl_threads<DHP>()) void slstm_kernel(
 
     for (int e = tid; e < 2 * 16 * P; e += sl_threads<DHP>()) (&sm.hb[0][0])[e] = (bf16)0.0f;
     __syncthreads();
-    f32x2 cs = {0, 0}, ns = {0, 0}, ms = {0, 0}, hv = {0, 0};
+    float cs = 0.0f, ns = 0.0f, ms = 0.0f, hv = 0.0f;
     const size_t st0 = ((size_t)b * NH + hd) * dh + r0;
+    // h of sequence bl as bf16 hi (columns bl, bl + 4) and remainder (bl + 8, bl + 12)
+    auto put_h = [&](bf16* hb, float x) {
+        const bf16 hi = (bf16)x, lo = (bf16)(x - (float)hi);
+        hb[bl * P + r0] = hi;
+        hb[(bl + 4) * P + r0] = hi;
+        hb[(bl + 8) * P + r0] = lo;
+        hb[(bl + 12) * P + r0] = lo;
+    };
     if (own && c0) {
-        cs = load2(c0 + st0);
-        ns = load2(n0 + st0);
-        ms = load2(m0 + st0);
-        hv = load2(h0 + st0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const bf16 hi = (bf16)hv[i];
-            sm.hb[0][bl * P + r0 + i] = hi;
-            sm.hb[0][(SL_BT + bl) * P + r0 + i] = (bf16)(hv[i] - (float)hi);
-        }
+        cs = c0[st0];
+        ns = n0[st0];
+        ms = m0[st0];
+        hv = h0[st0];
+        put_h(sm.hb[0], hv);
     }
 
     // Wait here for the matrix and state loads: inside the step loop the compiler
@@ -171,13 +161,13 @@ __global__ __launch_bounds__(sl_threads<DHP>()) void slstm_kernel(
     const float* xb = own ? x_pre + ((size_t)b * NH + hd) * S * 4 * dh + r0 : slstm_zero;
     const size_t xstep = own ? (size_t)4 * dh : 0;
     const int goff = own ? dh : 0;
-    f32x2 xr[PD][4];
+    float xr[PD][4];
 #pragma unroll
     for (int u = 0; u < PD; ++u)
 #pragma unroll
-        for (int gt = 0; gt < 4; ++gt) xr[u][gt] = load2(xb + (size_t)min(u, S - 1) * xstep + gt * goff);
+        for (int gt = 0; gt < 4; ++gt) xr[u][gt] = xb[(size_t)min(u, S - 1) * xstep + gt * goff];
     // h of lanes that own no cell goes to a sink, so the store needs no branch
-    T* hrow = own ? h + ((size_t)b * NH + hd) * S * dh + r0 : reinterpret_cast<T*>(slstm_sink) + 2 * lane;
+    T* hrow = own ? h + ((size_t)b * NH + hd) * S * dh + r0 : reinterpret_cast<T*>(slstm_sink) + lane;
     const size_t hstep = own ? (size_t)dh : 0;
 
     // One step; branch free, so that the compiler can count the loads in flight
@@ -187,7 +177,7 @@ __global__ __launch_bounds__(sl_threads<DHP>()) void slstm_kernel(
     // Gate arithmetic: with d = log f + m_{t-1} - log i, exactly one of the
     // stabilized gates is 1 and the other exp(-|d|); sigmoid(a_o) c / n takes one
     // reciprocal.
-    auto step = [&](int t, f32x2 (&xu)[4]) __attribute__((always_inline)) {
+    auto step = [&](int t, float (&xu)[4]) __attribute__((always_inline)) {
         const int cur = t & 1;
         lds_barrier();                                 // h_{t-1} complete in hb[cur]; loads stay in flight
         f32x4 acc[4];
@@ -202,36 +192,31 @@ __global__ __launch_bounds__(sl_threads<DHP>()) void slstm_kernel(
                 if constexpr (SPLIT) acc[gt] = mfma(rl[gt][kk], hbv, acc[gt]);
             }
         }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            // gate sums of cell r0 + i: this lane's column of rows 2*half + i, plus the
-            // other half's column (lanes l and l + 8 exchange the pair the other updates)
+        {
+            // gate sums of cell 4g + ci: this lane's column of row ci, plus the partner
+            // column (lane l + 8 mod 16, the other part of the same sequence) of the same
+            // row, which the partner sends while receiving its own row ci ^ 2 from here
             float a[4];
 #pragma unroll
             for (int gt = 0; gt < 4; ++gt) {
-                const float mine = half ? acc[gt][2 + i] : acc[gt][i];
-                const float other = half ? acc[gt][i] : acc[gt][2 + i];
-                a[gt] = mine + row_swap8(other) + xu[gt][i];
+                const float mine = ci == 0 ? acc[gt][0] : ci == 1 ? acc[gt][1] : ci == 2 ? acc[gt][2] : acc[gt][3];
+                const float send = ci == 0 ? acc[gt][2] : ci == 1 ? acc[gt][3] : ci == 2 ? acc[gt][0] : acc[gt][1];
+                a[gt] = mine + row_swap8(send) + xu[gt];
             }
             const float lf = FEXP ? a[2] : fast_log_sigmoid(a[2]);
-            const float d = lf + ms[i] - a[1];
+            const float d = lf + ms - a[1];
             const float e = __expf(-fabsf(d));
             const float fs = d >= 0.0f ? 1.0f : e, is = d >= 0.0f ? e : 1.0f;
-            cs[i] = fs * cs[i] + is * fast_tanh(a[0]);
-            ns[i] = fs * ns[i] + is;
-            ms[i] = fmaxf(lf + ms[i], a[1]);
-            hv[i] = cs[i] * fast_rcp(ns[i] * (1.0f + __expf(-a[3])));
+            cs = fs * cs + is * fast_tanh(a[0]);
+            ns = fs * ns + is;
+            ms = fmaxf(lf + ms, a[1]);
+            hv = cs * fast_rcp(ns * (1.0f + __expf(-a[3])));
         }
-        store_h2(hrow + (size_t)t * hstep, hv);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const bf16 hi = (bf16)hv[i];
-            sm.hb[cur ^ 1][bl * P + r0 + i] = hi;
-            sm.hb[cur ^ 1][(SL_BT + bl) * P + r0 + i] = (bf16)(hv[i] - (float)hi);
-        }
+        hrow[(size_t)t * hstep] = from_f32<T>(hv);
+        put_h(sm.hb[cur ^ 1], hv);
         const size_t tn = (size_t)min(t + PD, S - 1) * xstep;
 #pragma unroll
-        for (int gt = 0; gt < 4; ++gt) xu[gt] = load2(xb + tn + gt * goff);
+        for (int gt = 0; gt < 4; ++gt) xu[gt] = xb[tn + gt * goff];
     };
     const int nfull = S - S % PD;
     for (int t0 = 0; t0 < nfull; t0 += PD) {
@@ -242,10 +227,10 @@ __global__ __launch_bounds__(sl_threads<DHP>()) void slstm_kernel(
     for (int u = 0; u < PD; ++u)
         if (nfull + u < S) step(nfull + u, xr[u]);
     if (own) {
-        *reinterpret_cast<f32x2*>(cF + st0) = cs;
-        *reinterpret_cast<f32x2*>(nF + st0) = ns;
-        *reinterpret_cast<f32x2*>(mF + st0) = ms;
-        *reinterpret_cast<f32x2*>(hF + st0) = hv;
+        cF[st0] = cs;
+        nF[st0] = ns;
+        mF[st0] = ms;
+        hF[st0] = hv;
     }
 }
 
