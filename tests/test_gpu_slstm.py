@@ -58,7 +58,7 @@ def test_fp32(orc, dh, forget):
 def test_bf16_widths(orc, dh):
     w = inputs.WORKLOADS["slstm_125m"]
     announce(f"slstm bf16 B=9 NH=2 S=120 dh={dh}")
-    # B=9: one full tile of 8 sequences and a tile with one
+    # B=9: two full tiles of 4 sequences and a tile with one
     x = inputs.slstm_inputs(w, seed=620 + dh, B=9, NH=2, S=120, dh=dh)
     _compare(orc, x, "bf16", 0)
 
