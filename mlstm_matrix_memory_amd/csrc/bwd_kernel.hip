@@ -26,6 +26,10 @@
 //                     dnum', dden', do~; then dq over the same key blocks
 //   bwd_cols_kernel   per (key block, head): dk, dv over query blocks >= it
 //   bwd_gates_kernel/fix  per head: di~, df~ (reverse prefix sum), by segments
+// From 1024 tokens on, the MFMA form restricts the middle passes to superchunks
+// of 256 tokens and reaches the earlier (later) ones through the stabilized state
+// (its gradient) at each superchunk boundary: bwd_state_local and bwd_state_scan
+// form those states, see the two-level section below.
 #include "mlstm_internal.h"
 
 namespace mlstm {
