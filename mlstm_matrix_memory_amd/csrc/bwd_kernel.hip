@@ -62,7 +62,22 @@ struct SuperStates {
     float* part;     // per-superchunk sums, fp32 [heads][G-1][d_v d_qk + d_qk]
 };
 
+// Buffers of the GEMM form (feature widths above 512): see its section below
+struct GemmWs {
+    int Sp;                  // S rounded up to 128 (the GEMM tile)
+    bf16* P;                 // [heads][Sp][Sp] decayed scores, bf16 hi, then lo (same layout)
+    bf16* G;                 // [heads][Sp][Sp] score gradients, hi then lo
+    float* num;              // [heads][S][d_v] num'
+    float* rowpart;          // [heads][S][2 Sp / 128] partial row sums of P
+};
+
 int mfma_bwd_width(const BwdArgs& a);
+
+// The GEMM form applies to bf16 with a feature width above 512 and sequences up to
+// 16384 tokens (its score-shaped matrices take 8 S_p^2 bytes per head).
+inline bool bwd_gemm_path(const BwdArgs& a) {
+    return a.dtype == MLSTM_BF16 && (a.dqk > 512 || a.dv > 512) && a.S <= 16384 && (long long)a.B * a.NH <= 65535;
+}
 
 // Superchunk length of the two-level form: the quadratic tiles shrink to a band of
 // LS tokens, at the price of the state products of every 64-token block (about
@@ -81,7 +96,7 @@ inline int bwd_superchunk(const BwdArgs& a) {
 }
 
 inline size_t a256(size_t x) { return (x + 255) & ~(size_t)255; }
-inline size_t bwd_ws_walk(char* base, const BwdArgs& a, BwdWs* out, SuperStates* ss) {
+inline size_t bwd_ws_walk(char* base, const BwdArgs& a, BwdWs* out, SuperStates* ss, GemmWs* gw) {
     const size_t heads = (size_t)a.B * a.NH, S = a.S;
     size_t off = 0;
     auto take = [&](size_t bytes) { char* p = base + off; off += a256(bytes); return p; };
@@ -101,8 +116,18 @@ inline size_t bwd_ws_walk(char* base, const BwdArgs& a, BwdWs* out, SuperStates*
     st.n = (float*)take(ns * a.dqk * sizeof(float));
     st.dn = (float*)take(ns * a.dqk * sizeof(float));
     st.part = (float*)take(ns * ((size_t)a.dv * a.dqk + a.dqk) * sizeof(float));
+    GemmWs gm = {};
+    if (bwd_gemm_path(a)) {
+        const size_t Sp = (S + 127) / 128 * 128;
+        gm.Sp = (int)Sp;
+        gm.P = (bf16*)take(2 * heads * Sp * Sp * sizeof(bf16));
+        gm.G = (bf16*)take(2 * heads * Sp * Sp * sizeof(bf16));
+        gm.num = (float*)take(heads * S * a.dv * sizeof(float));
+        gm.rowpart = (float*)take(heads * S * (2 * Sp / 128) * sizeof(float));
+    }
     if (out) *out = w;
     if (ss) *ss = st;
+    if (gw) *gw = gm;
     return off;
 }
 
@@ -1526,12 +1551,359 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdIn<bf16>& in, const BwdWs&
     return launch_gates<bf16, true>(a, in, w);
 }
 
+// ===========================================================================
+// GEMM form (bf16, max(d_qk, d_v) > 512): the score-shaped matrices materialized
+// ===========================================================================
+// Feature widths above 512 do not fit the per-query register tiles of the MFMA
+// form above.  For them the same quantities (readings of the header) are formed as
+// six causal GEMMs over [S_p x S_p] score-shaped matrices held in the workspace
+// (S_p = S rounded up to 128; zero above the diagonal and beyond S), each a tiled
+// bf16 MFMA product with fp32 accumulation and a fused epilogue:
+//   P   = (Q K^T) (.) D'                    (+ row sums = den')       tiles t >= s
+//   num'= P V                                                          s < tile end
+//   per query: u, do~, dnum', dden'        (bwd_gemm_query)
+//   G   = (dnum' V^T + dden') (.) D'                                   tiles t >= s
+//   dq  = G K,   dk = G^T Q,   dv = P^T dnum'
+// P, G and dnum' are computed values and enter their products as bf16 hi + lo.
+constexpr int GT = 128;                  // output tile, rows and columns
+constexpr int GK = 32;                   // k per step (one MFMA depth)
+constexpr int GTHREADS = 256;            // 2 x 2 waves, 64 x 64 each
+constexpr int GPR = GK + 8;              // LDS pitch of [row][k] tiles (bf16)
+constexpr int GPT = GT + 8;              // LDS pitch of [k][row] tiles
+
+enum GLayout { ROWK = 0, KROW = 1 };     // stored [row][k] (k contiguous) or [k][row]
+enum GEpi { EPI_F32 = 0, EPI_P = 1, EPI_G = 2 };
+enum GKRange { K_FULL = 0, K_UPTO = 1, K_FROM = 2 };   // k in [0,K), [0, tile end), [tile start, K)
+
+struct GOp {
+    const bf16* hi;
+    const bf16* lo;          // null for an exact operand
+    long long ld, hs;        // row stride and head stride, elements
+    int rows;                // valid rows (m or n); a multiple of 8 for KROW
+    int kv;                  // valid k; a multiple of 8 for ROWK
+};
+
+struct GEpiArgs {
+    float* out; long long ldo, hso; int Mv, Nv;       // EPI_F32
+    bf16* mat;                                         // EPI_P / EPI_G: P or G (hi; lo at + heads Sp^2)
+    float* rowpart;                                    // EPI_P
+    int S, Sp, heads;
+};
+
+template <int L>
+struct GTileSize { static constexpr int N = L == ROWK ? GT * GPR : GK * GPT; };
+
+// this thread's two 16-byte units of a 128 x 32 operand tile (global -> registers)
+template <int L>
+__device__ __forceinline__ void g_load(bf16x8 (&r)[2], const bf16* base, const GOp& op, int r0, int k0, int tid) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int id = tid + GTHREADS * u;
+        if constexpr (L == ROWK) {
+            const int row = id >> 2, k8 = 8 * (id & 3);
+            r[u] = ld8(base + (long long)(r0 + row) * op.ld + k0 + k8, r0 + row < op.rows && k0 + k8 < op.kv);
+        } else {
+            const int kr = id >> 4, c8 = 8 * (id & 15);
+            r[u] = ld8(base + (long long)(k0 + kr) * op.ld + r0 + c8, k0 + kr < op.kv && r0 + c8 < op.rows);
+        }
+    }
+}
+template <int L>
+__device__ __forceinline__ void g_store(const bf16x8 (&r)[2], bf16* tile, int tid) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const int id = tid + GTHREADS * u;
+        if constexpr (L == ROWK) *reinterpret_cast<bf16x8*>(tile + (id >> 2) * GPR + 8 * (id & 3)) = r[u];
+        else *reinterpret_cast<bf16x8*>(tile + (id >> 4) * GPT + 8 * (id & 15)) = r[u];
+    }
+}
+// MFMA operand (16 rows w0 + 16 b .. + 15, k-slots 8g .. 8g + 7 of the step)
+template <int L>
+__device__ __forceinline__ bf16x8 g_operand(const bf16* tile, int w0, int b, int ln, int g) {
+    if constexpr (L == ROWK) {
+        return *reinterpret_cast<const bf16x8*>(tile + (w0 + 16 * b + ln) * GPR + 8 * g);
+    } else {
+        const bf16* p = tile + (8 * g + (ln >> 2)) * GPT + w0 + 16 * b + 4 * (ln & 3);
+        return cat(lds_read_tr(p), lds_read_tr(p + 4 * GPT));
+    }
+}
+
+template <int LA, int LB, bool ALO, bool BLO>
+struct alignas(16) GemmSmem {
+    bf16 a[2][ALO ? 2 : 1][GTileSize<LA>::N];
+    bf16 b[2][BLO ? 2 : 1][GTileSize<LB>::N];
+};
+
+// One workgroup per (output tile, head).  TRI: only tiles with tn <= tm (the
+// causal lower triangle), enumerated in a 1-D grid; otherwise tiles in rows of
+// Nt, ordered so the ones with most k steps start first.
+template <int LA, int LB, bool ALO, bool BLO, int EPI, int KR, bool TRI>
+__global__ __launch_bounds__(GTHREADS) void bwd_gemm(GOp A, GOp B, int M, int N, int K, GEpiArgs ep, BwdWs ws,
+                                                     BwdIn<bf16> in)
+{
+    __shared__ GemmSmem<LA, LB, ALO, BLO> sm;
+    const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 15, g = lane >> 4;
+    const int Mt = (M + GT - 1) / GT, Nt = (N + GT - 1) / GT;
+    int tm, tn;
+    if constexpr (TRI) {
+        const int idx = blockIdx.x;
+        tm = (int)((sqrtf(8.0f * idx + 1.0f) - 1.0f) * 0.5f);
+        while ((long long)tm * (tm + 1) / 2 > idx) --tm;
+        while ((long long)(tm + 1) * (tm + 2) / 2 <= idx) ++tm;
+        tn = idx - tm * (tm + 1) / 2;
+    } else {
+        const int row = blockIdx.x / Nt;
+        tn = blockIdx.x % Nt;
+        tm = KR == K_UPTO ? Mt - 1 - row : row;        // most k steps first
+    }
+    const int m0 = GT * tm, n0 = GT * tn;
+    const int wm = 64 * (wave >> 1), wn = 64 * (wave & 1);
+    const int k_begin = KR == K_FROM ? m0 : 0;
+    const int k_end = KR == K_UPTO ? min(K, m0 + GT) : K;
+    const bf16* ah = A.hi + (long long)bh * A.hs;
+    const bf16* al = ALO ? A.lo + (long long)bh * A.hs : nullptr;
+    const bf16* bhp = B.hi + (long long)bh * B.hs;
+    const bf16* blp = BLO ? B.lo + (long long)bh * B.hs : nullptr;
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+
+    bf16x8 rah[2], ral[2], rbh[2], rbl[2];
+    auto load = [&](int k0) {
+        g_load<LA>(rah, ah, A, m0, k0, tid);
+        if constexpr (ALO) g_load<LA>(ral, al, A, m0, k0, tid);
+        g_load<LB>(rbh, bhp, B, n0, k0, tid);
+        if constexpr (BLO) g_load<LB>(rbl, blp, B, n0, k0, tid);
+    };
+    auto store = [&](int buf) {
+        g_store<LA>(rah, sm.a[buf][0], tid);
+        if constexpr (ALO) g_store<LA>(ral, sm.a[buf][1], tid);
+        g_store<LB>(rbh, sm.b[buf][0], tid);
+        if constexpr (BLO) g_store<LB>(rbl, sm.b[buf][1], tid);
+    };
+    if (k_begin < k_end) {
+        load(k_begin);
+        store(0);
+        __syncthreads();
+    }
+    for (int k0 = k_begin; k0 < k_end; k0 += GK) {
+        const int cur = ((k0 - k_begin) / GK) & 1;
+        const bool more = k0 + GK < k_end;
+        if (more) load(k0 + GK);                       // in flight during the products
+        bf16x8 bo[4], bol[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            bo[j] = g_operand<LB>(sm.b[cur][0], wn, j, ln, g);
+            if constexpr (BLO) bol[j] = g_operand<LB>(sm.b[cur][1], wn, j, ln, g);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bf16x8 ao = g_operand<LA>(sm.a[cur][0], wm, i, ln, g);
+            bf16x8 aol;
+            if constexpr (ALO) aol = g_operand<LA>(sm.a[cur][1], wm, i, ln, g);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                acc[i][j] = mfma(ao, bo[j], acc[i][j]);
+                if constexpr (ALO) acc[i][j] = mfma(aol, bo[j], acc[i][j]);
+                if constexpr (BLO) acc[i][j] = mfma(ao, bol[j], acc[i][j]);
+            }
+        }
+        if (more) store(cur ^ 1);                      // the other buffer, free since the last barrier
+        __syncthreads();
+    }
+
+    // epilogue: lane holds rows m0 + wm + 16 i + 4 g + e, column n0 + wn + 16 j + ln
+    const long long hsq = (long long)ep.Sp * ep.Sp;
+    if constexpr (EPI == EPI_F32) {
+        float* o = ep.out + (long long)bh * ep.hso;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int m = m0 + wm + 16 * i + 4 * g + e;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n = n0 + wn + 16 * j + ln;
+                    if (m < ep.Mv && n < ep.Nv) o[(long long)m * ep.ldo + n] = acc[i][j][e];
+                }
+            }
+    } else {
+        // P = S (.) D' or G = (dA + dden'_t) (.) D', with D'_ts = exp(F_t - m_t - (F_s - i~_s))
+        // for s <= t < S and 0 elsewhere (also beyond S, so the products can read whole tiles)
+        const size_t tokh = (size_t)bh * ep.S;
+        bf16* mh = ep.mat + (long long)bh * hsq;
+        bf16* ml = mh + (long long)ep.heads * hsq;
+        double qs[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int s = n0 + wn + 16 * j + ln;
+            qs[j] = s < ep.S ? ws.F[tokh + s] - (double)in.i_pre[tokh + s] : 0.0;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = m0 + wm + 16 * i + 4 * g + e;
+                const bool tv = t < ep.S;
+                const double rt = tv ? ws.F[tokh + t] - ws.m[tokh + t] : 0.0;
+                const float add = (EPI == EPI_G && tv) ? ws.dden[tokh + t] : 0.0f;
+                float rsum = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int s = n0 + wn + 16 * j + ln;
+                    const float d = (tv && s <= t) ? exp_arg(rt - qs[j]) : 0.0f;
+                    const float v = (acc[i][j][e] + add) * d;
+                    rsum += v;
+                    bf16 hi, lo;
+                    hilo(v, hi, lo);
+                    mh[(long long)t * ep.Sp + s] = hi;
+                    ml[(long long)t * ep.Sp + s] = lo;
+                }
+                if constexpr (EPI == EPI_P) {
+                    // sum over the 16 lanes of the row, then one partial per (row, wave column)
+#pragma unroll
+                    for (int off = 8; off > 0; off >>= 1) rsum += __shfl_xor(rsum, off, 64);
+                    if (ln == 0 && tv)
+                        ep.rowpart[(tokh + t) * (2 * ep.Sp / GT) + 2 * tn + (wave & 1)] = rsum;
+                }
+            }
+    }
+}
+
+// Per query t: den' from the row partials, then u, do~, dnum' (bf16 hi, lo) and dden',
+// with the arithmetic of the MFMA form's per-query phase.
+__global__ __launch_bounds__(BW_THREADS) void bwd_gemm_query(BwdIn<bf16> in, BwdWs ws, GemmWs gw,
+                                                            float* __restrict__ dout)
+{
+    __shared__ float red[BW_THREADS / 64];
+    __shared__ float bc;
+    const int t = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int S = in.S, dv = in.dv;
+    const size_t tok = (size_t)bh * S + t;
+    const int np = 2 * (t / GT + 1);                   // row partials of the tiles at or left of t's
+    if (wave == 0) {
+        float x = 0.0f;
+        for (int i = lane; i < np; i += 64) x += gw.rowpart[tok * (2 * gw.Sp / GT) + i];
+        x = wave_sum(x);
+        if (lane == 0) bc = x;
+    }
+    __syncthreads();
+    const float den = bc;
+    const float fl = exp_arg(-ws.m[tok]);
+    const float rN = 1.0f / fmaxf(fabsf(den), fl);
+    const float* nump = gw.num + tok * dv;
+    const float* op = in.o_pre + tok * dv;
+    const bf16* dhp = in.dh + tok * dv;
+    bf16* dnh = reinterpret_cast<bf16*>(ws.dnum) + tok * dv;
+    bf16* dnl = dnh + (size_t)in.heads * S * dv;
+    float duu = 0.0f;
+    for (int n = 4 * tid; n < dv; n += 4 * BW_THREADS) {
+        const f32x4 nm = load4(nump + n), o4 = load4(op + n), dh4 = load4(dhp + n);
+        f32x4 do4;
+        bf16x4 h4, l4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float u = nm[i] * rN;
+            const float gg = sigmoid(o4[i]);
+            do4[i] = dh4[i] * u * gg * (1.0f - gg);
+            const float du = dh4[i] * gg;
+            duu += du * u;
+            bf16 hi, lo;
+            hilo(du * rN, hi, lo);
+            h4[i] = hi;
+            l4[i] = lo;
+        }
+        *reinterpret_cast<f32x4*>(dout + tok * dv + n) = do4;
+        *reinterpret_cast<bf16x4*>(dnh + n) = h4;
+        *reinterpret_cast<bf16x4*>(dnl + n) = l4;
+    }
+    duu = wave_sum(duu);
+    if (lane == 0) red[wave] = duu;
+    __syncthreads();
+    if (tid == 0) {
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < BW_THREADS / 64; ++w) s += red[w];
+        ws.dden[tok] = fabsf(den) > fl ? -(den > 0.0f ? 1.0f : -1.0f) * s * rN : 0.0f;
+    }
+}
+
+template <int LA, int LB, bool ALO, bool BLO, int EPI, int KR, bool TRI>
+hipError_t launch_gemm(const BwdArgs& a, const GOp& A, const GOp& B, int M, int N, int K, const GEpiArgs& ep,
+                       const BwdWs& w, const BwdIn<bf16>& in) {
+    const int Mt = (M + GT - 1) / GT, Nt = (N + GT - 1) / GT;
+    const unsigned tiles = TRI ? (unsigned)(Mt * (Mt + 1) / 2) : (unsigned)(Mt * Nt);
+    hipLaunchKernelGGL((bwd_gemm<LA, LB, ALO, BLO, EPI, KR, TRI>), dim3(tiles, a.B * a.NH), dim3(GTHREADS), 0,
+                       a.stream, A, B, M, N, K, ep, w, in);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_gemm(const BwdArgs& a, const BwdIn<bf16>& in, const BwdWs& w, const GemmWs& gw) {
+    const int heads = a.B * a.NH, S = a.S, Sp = gw.Sp, dqk = a.dqk, dv = a.dv;
+    const long long hsq = (long long)Sp * Sp;
+    const bf16* q = in.q; const bf16* k = in.k; const bf16* v = in.v;
+    const bf16* dnh = reinterpret_cast<const bf16*>(w.dnum);
+    const bf16* dnl = dnh + (size_t)heads * S * dv;
+    GEpiArgs ep = {};
+    ep.S = S; ep.Sp = Sp; ep.heads = heads;
+    hipError_t e;
+    // P = (Q K^T) (.) D' and its row sums
+    {
+        GOp A = {q, nullptr, dqk, (long long)S * dqk, S, dqk};
+        GOp B = {k, nullptr, dqk, (long long)S * dqk, S, dqk};
+        GEpiArgs p = ep; p.mat = gw.P; p.rowpart = gw.rowpart;
+        if ((e = launch_gemm<ROWK, ROWK, false, false, EPI_P, K_FULL, true>(a, A, B, Sp, Sp, dqk, p, w, in)) != hipSuccess) return e;
+    }
+    // num' = P V
+    {
+        GOp A = {gw.P, gw.P + heads * hsq, Sp, hsq, Sp, Sp};
+        GOp B = {v, nullptr, dv, (long long)S * dv, dv, S};
+        GEpiArgs o = ep; o.out = gw.num; o.ldo = dv; o.hso = (long long)S * dv; o.Mv = S; o.Nv = dv;
+        if ((e = launch_gemm<ROWK, KROW, true, false, EPI_F32, K_UPTO, false>(a, A, B, S, dv, Sp, o, w, in)) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(bwd_gemm_query, dim3(S, heads), dim3(BW_THREADS), 0, a.stream, in, w, gw, a.dout);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // G = (dnum' V^T + dden') (.) D'
+    {
+        GOp A = {dnh, dnl, dv, (long long)S * dv, S, dv};
+        GOp B = {v, nullptr, dv, (long long)S * dv, S, dv};
+        GEpiArgs p = ep; p.mat = gw.G;
+        if ((e = launch_gemm<ROWK, ROWK, true, false, EPI_G, K_FULL, true>(a, A, B, Sp, Sp, dv, p, w, in)) != hipSuccess) return e;
+    }
+    // dq = G K
+    {
+        GOp A = {gw.G, gw.G + heads * hsq, Sp, hsq, Sp, Sp};
+        GOp B = {k, nullptr, dqk, (long long)S * dqk, dqk, S};
+        GEpiArgs o = ep; o.out = a.dq; o.ldo = dqk; o.hso = (long long)S * dqk; o.Mv = S; o.Nv = dqk;
+        if ((e = launch_gemm<ROWK, KROW, true, false, EPI_F32, K_UPTO, false>(a, A, B, S, dqk, Sp, o, w, in)) != hipSuccess) return e;
+    }
+    // dk = G^T Q
+    {
+        GOp A = {gw.G, gw.G + heads * hsq, Sp, hsq, Sp, Sp};
+        GOp B = {q, nullptr, dqk, (long long)S * dqk, dqk, S};
+        GEpiArgs o = ep; o.out = a.dk; o.ldo = dqk; o.hso = (long long)S * dqk; o.Mv = S; o.Nv = dqk;
+        if ((e = launch_gemm<KROW, KROW, true, false, EPI_F32, K_FROM, false>(a, A, B, S, dqk, Sp, o, w, in)) != hipSuccess) return e;
+    }
+    // dv = P^T dnum'
+    {
+        GOp A = {gw.P, gw.P + heads * hsq, Sp, hsq, Sp, Sp};
+        GOp B = {dnh, dnl, dv, (long long)S * dv, dv, S};
+        GEpiArgs o = ep; o.out = a.dvv; o.ldo = dv; o.hso = (long long)S * dv; o.Mv = S; o.Nv = dv;
+        if ((e = launch_gemm<KROW, KROW, true, true, EPI_F32, K_FROM, false>(a, A, B, S, dv, Sp, o, w, in)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 template <typename T>
 hipError_t launch_bwd_t(const BwdArgs& a) {
     const int heads = a.B * a.NH;
     BwdWs w;
     SuperStates ss;
-    bwd_ws_walk((char*)a.ws, a, &w, &ss);
+    GemmWs gw;
+    bwd_ws_walk((char*)a.ws, a, &w, &ss, &gw);
     BwdIn<T> in;
     in.q = (const T*)a.q; in.k = (const T*)a.k; in.v = (const T*)a.v; in.dh = (const T*)a.dh;
     in.i_pre = a.i_pre; in.f_pre = a.f_pre; in.o_pre = a.o_pre;
@@ -1548,6 +1920,10 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
     hipLaunchKernelGGL(bwd_gate_fix, sgrid, dim3(BW_THREADS), 0, a.stream, a.S, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if constexpr (sizeof(T) == 2) {
+        if (bwd_gemm_path(a)) {
+            if ((e = launch_bwd_gemm(a, in, w, gw)) != hipSuccess) return e;
+            return launch_gates<bf16, false>(a, in, w);
+        }
         switch (mfma_bwd_width(a)) {
             case 64: return launch_bwd_mfma<64, 64>(a, in, w, ss);
             case 128: return launch_bwd_mfma<128, 64>(a, in, w, ss);
@@ -1567,7 +1943,7 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
 }  // namespace
 
 size_t bwd_workspace_bytes(const BwdArgs& a) {
-    return bwd_ws_walk(nullptr, a, nullptr, nullptr);
+    return bwd_ws_walk(nullptr, a, nullptr, nullptr, nullptr);
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {

@@ -152,6 +152,36 @@ def test_bf16_two_level_normalizer_floor(orc):
     _compare(orc, x, inputs.bwd_dh(w, seed=460, B=1, NH=2, S=1111, dv=128), "bf16")
 
 
+# the GEMM form (feature width above 512): ragged sequence ends inside and beyond a
+# 128-token tile, unequal d_qk / d_v, two tokens, and the floor.  (With one token and
+# the floor inactive, u = sign(q.k) v and dq, dk vanish exactly, so any finite
+# precision leaves only a residual of the cancelling terms to compare; two tokens keep
+# that cancellation on the first query beside a second one of normal size.)
+GEMM_CASES = [
+    ("lm_1_3b", dict(B=1, NH=2, S=300, dqk=640, dv=640)),
+    ("lm_1_3b", dict(B=2, NH=1, S=130, dqk=528, dv=1024)),
+    ("lm_1_3b", dict(B=1, NH=1, S=2, dqk=1024, dv=1024)),
+    ("long_ctx", dict(B=1, NH=1, S=257, dqk=1024, dv=576)),
+]
+
+
+@pytest.mark.parametrize("name,over", GEMM_CASES, ids=lambda v: str(v))
+def test_bf16_gemm_form(orc, name, over):
+    w = inputs.WORKLOADS[name]
+    announce(f"bwd bf16 gemm form {name} {over}")
+    x = inputs.fwd_inputs(w, seed=470 + w.seed, **over)
+    dh = inputs.bwd_dh(w, seed=470 + w.seed, B=over["B"], NH=over["NH"], S=over["S"], dv=over["dv"])
+    _compare(orc, x, dh, "bf16")
+
+
+def test_bf16_gemm_form_normalizer_floor(orc):
+    w = inputs.WORKLOADS["lm_1_3b"]
+    announce("bwd bf16 gemm form floor B=1 NH=2 S=200 d=768")
+    x = inputs.fwd_inputs(w, seed=480, B=1, NH=2, S=200, dqk=768, dv=768)
+    x["i_pre"] = (x["i_pre"] - np.float32(3.0)).astype(np.float32)
+    _compare(orc, x, inputs.bwd_dh(w, seed=480, B=1, NH=2, S=200, dv=768), "bf16")
+
+
 def test_bf16_mfma_normalizer_floor(orc):
     # input gates lowered by 3: the floor is active on part of the rows
     w = inputs.WORKLOADS["lm_125m"]
