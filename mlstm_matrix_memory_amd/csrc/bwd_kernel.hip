@@ -535,18 +535,17 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_cols_kernel(BwdIn<T> in, BwdWs
 }
 
 // ---- kernel 4: gate gradients per head ----------------------------------------
-// di~_j = k_j . dk_j ;  dF_j = q_j . dq_j - k_j . dk_j ;  df~_j = sigmoid(-f~_j) sum_{t>=j} dF_t
-// DOTS: q . dq comes from the workspace and k . dk is already in di (MFMA path).
+// di~_j = k_j . dk_j ;  dF_j = q_j . dq_j - k_j . dk_j ;  df~_j = sigmoid(-f~_j) sum_{t>=j} dF_t,
+// with q . dq in ws.qdq and k . dk already in di (formed by the column pass of the
+// MFMA form, or by bwd_dots_kernel).
 // The reverse prefix sum runs over segments of GSEG tokens in parallel: the
 // segment's own suffix sums go to ws.F (fp64; F is not needed any more) and its
 // total to ws.seg, then bwd_gates_fix adds the later segments' totals.
-template <typename T, bool DOTS>
-__global__ __launch_bounds__(BW_THREADS) void bwd_gates_kernel(BwdIn<T> in, BwdWs ws, const float* __restrict__ dq,
-                                                               const float* __restrict__ dk,
-                                                               float* __restrict__ di)
+template <typename T>
+__global__ __launch_bounds__(BW_THREADS) void bwd_gates_kernel(BwdIn<T> in, BwdWs ws, const float* __restrict__ di)
 {
     __shared__ double part[BW_THREADS / 64];
-    const int S = in.S, dqk = in.dqk;
+    const int S = in.S;
     const int nseg = (S + GSEG - 1) / GSEG;
     const int sg = blockIdx.x % nseg, bh = blockIdx.x / nseg;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -556,20 +555,7 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_gates_kernel(BwdIn<T> in, BwdW
     // walk the segment from its end; within a tile, thread tid holds token end - tid
     for (int e0 = tb - 1; e0 >= ta; e0 -= BW_THREADS) {
         const int t = e0 - tid;
-        double dF = 0.0;
-        if (t >= ta) {
-            if (DOTS) {
-                dF = (double)ws.qdq[tokh + t] - (double)di[tokh + t];
-            } else {
-                double qdq = 0.0, kdk = 0.0;
-                for (int j = 0; j < dqk; ++j) {
-                    qdq += (double)to_f32(in.q[(tokh + t) * dqk + j]) * dq[(tokh + t) * dqk + j];
-                    kdk += (double)to_f32(in.k[(tokh + t) * dqk + j]) * dk[(tokh + t) * dqk + j];
-                }
-                di[tokh + t] = (float)kdk;
-                dF = qdq - kdk;
-            }
-        }
+        const double dF = t >= ta ? (double)ws.qdq[tokh + t] - (double)di[tokh + t] : 0.0;
         double x = dF;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -1503,12 +1489,52 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
     if (sval && g == 0) di[tokh + s] = kdk;
 }
 
+// q_t . dq_t (into ws.qdq) and k_t . dk_t (into di) for the paths that do not form
+// them in their own passes: one wave per token, 16-byte loads along the feature
+// axis, fp64 partial sums
+template <typename T>
+__global__ __launch_bounds__(BW_THREADS) void bwd_dots_kernel(BwdIn<T> in, BwdWs ws, const float* __restrict__ dq,
+                                                              const float* __restrict__ dk, float* __restrict__ di,
+                                                              long long tokens)
+{
+    const int lane = threadIdx.x & 63, dqk = in.dqk;
+    for (long long tok = (long long)blockIdx.x * (BW_THREADS / 64) + (threadIdx.x >> 6); tok < tokens;
+         tok += (long long)gridDim.x * (BW_THREADS / 64)) {
+        double a = 0.0, b = 0.0;
+        for (int j = 4 * lane; j < dqk; j += 256) {
+            const f32x4 q4 = load4(in.q + tok * dqk + j), g4 = load4(dq + tok * dqk + j);
+            const f32x4 k4 = load4(in.k + tok * dqk + j), h4 = load4(dk + tok * dqk + j);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                a += (double)q4[i] * g4[i];
+                b += (double)k4[i] * h4[i];
+            }
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) {
+            a += __shfl_xor(a, off, 64);
+            b += __shfl_xor(b, off, 64);
+        }
+        if (lane == 0) {
+            ws.qdq[tok] = (float)a;
+            di[tok] = (float)b;
+        }
+    }
+}
+
 template <typename T, bool DOTS>
 hipError_t launch_gates(const BwdArgs& a, const BwdIn<T>& in, const BwdWs& w) {
     const dim3 sgrid((unsigned)((size_t)a.B * a.NH * ((a.S + GSEG - 1) / GSEG)));
-    hipLaunchKernelGGL((bwd_gates_kernel<T, DOTS>), sgrid, dim3(BW_THREADS), 0, a.stream, in, w, a.dq, a.dk, a.di);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    hipError_t e;
+    if constexpr (!DOTS) {
+        const long long tokens = (long long)a.B * a.NH * a.S;
+        const long long blocks = (tokens + BW_THREADS / 64 - 1) / (BW_THREADS / 64);
+        hipLaunchKernelGGL((bwd_dots_kernel<T>), dim3((unsigned)(blocks < (1LL << 20) ? blocks : (1LL << 20))), dim3(BW_THREADS), 0,
+                           a.stream, in, w, a.dq, a.dk, a.di, tokens);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL((bwd_gates_kernel<T>), sgrid, dim3(BW_THREADS), 0, a.stream, in, w, a.di);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_gates_fix<T>), sgrid, dim3(BW_THREADS), 0, a.stream, in, w, a.df);
     return hipGetLastError();
 }
