@@ -1668,18 +1668,25 @@ __global__ __launch_bounds__(GTHREADS) void bwd_gemm(GOp A, GOp B, int M, int N,
                                                      BwdIn<bf16> in)
 {
     __shared__ GemmSmem<LA, LB, ALO, BLO> sm;
-    const int bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 15, g = lane >> 4;
+    // Workgroups are dealt to the 8 XCDs round robin; renumber them so each XCD
+    // takes a contiguous run of the (head, tile) order, whose neighbouring tiles
+    // share operand rows in that XCD's L2.
+    const unsigned total = gridDim.x * gridDim.y;
+    unsigned lin = blockIdx.x + blockIdx.y * gridDim.x;
+    if (total % 8 == 0) lin = (lin % 8) * (total / 8) + lin / 8;
+    const int bh = (int)(lin / gridDim.x), bid = (int)(lin % gridDim.x);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 15, g = lane >> 4;
     const int Mt = (M + GT - 1) / GT, Nt = (N + GT - 1) / GT;
     int tm, tn;
     if constexpr (TRI) {
-        const int idx = blockIdx.x;
+        const int idx = bid;
         tm = (int)((sqrtf(8.0f * idx + 1.0f) - 1.0f) * 0.5f);
         while ((long long)tm * (tm + 1) / 2 > idx) --tm;
         while ((long long)(tm + 1) * (tm + 2) / 2 <= idx) ++tm;
         tn = idx - tm * (tm + 1) / 2;
     } else {
-        const int row = blockIdx.x / Nt;
-        tn = blockIdx.x % Nt;
+        const int row = bid / Nt;
+        tn = bid % Nt;
         tm = KR == K_UPTO ? Mt - 1 - row : row;        // most k steps first
     }
     const int m0 = GT * tm, n0 = GT * tn;
