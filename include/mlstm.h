@@ -231,7 +231,10 @@ size_t mlstm_bwd_workspace_bytes(int B, int NH, int S, int d_qk, int d_v, mlstm_
  *                   From S = 1024 on (bf16, d_qk and d_v <= 512) the sums over
  *                   earlier keys are carried through the stabilized state at
  *                   every 256-token boundary, which the workspace holds too:
- *                   about 12 d_v d_qk bytes per boundary and head
+ *                   about 12 d_v d_qk bytes per boundary and head.  Above width
+ *                   512 (bf16, S <= 16384) it holds the causal score-shaped
+ *                   matrices instead: about 8 S_p^2 bytes per head, S_p = S
+ *                   rounded up to 128
  *   stream          hipStream_t or NULL
  * Every pointer must be 16-byte aligned except i_pre, f_pre, grad_i, grad_f
  * (4 bytes).  Outputs must not alias inputs, the workspace or each other.
