@@ -228,13 +228,13 @@ size_t mlstm_bwd_workspace_bytes(int B, int NH, int S, int d_qk, int d_v, mlstm_
  *   grad_o          [B,NH,S,d_v] fp32, written (gradient w.r.t. o_pre)
  *   workspace       device buffer of at least mlstm_bwd_workspace_bytes(...)
  *                   bytes, 16-byte aligned; contents on entry do not matter.
- *                   From S = 1024 on (bf16, d_qk and d_v <= 512) the sums over
- *                   earlier keys are carried through the stabilized state at
- *                   every 256-token boundary, which the workspace holds too:
- *                   about 12 d_v d_qk bytes per boundary and head.  Above width
- *                   512 (bf16, S <= 16384) it holds the causal score-shaped
- *                   matrices instead: about 8 S_p^2 bytes per head, S_p = S
- *                   rounded up to 128
+ *                   bf16 with a width above 384 and S <= 16384 holds the
+ *                   causal score-shaped matrices: about 8 S_p^2 bytes per
+ *                   head, S_p = S rounded up to 128.  Otherwise, from S = 1024
+ *                   on (bf16, d_qk and d_v <= 512), the sums over earlier keys
+ *                   are carried through the stabilized state at every
+ *                   256-token boundary, which the workspace holds too: about
+ *                   12 d_v d_qk bytes per boundary and head
  *   stream          hipStream_t or NULL
  * Every pointer must be 16-byte aligned except i_pre, f_pre, grad_i, grad_f
  * (4 bytes).  Outputs must not alias inputs, the workspace or each other.

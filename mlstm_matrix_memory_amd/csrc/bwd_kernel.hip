@@ -62,7 +62,7 @@ struct SuperStates {
     float* part;     // per-superchunk sums, fp32 [heads][G-1][d_v d_qk + d_qk]
 };
 
-// Buffers of the GEMM form (feature widths above 512): see its section below
+// Buffers of the GEMM form (feature widths above 384): see its section below
 struct GemmWs {
     int Sp;                  // S rounded up to 128 (the GEMM tile)
     bf16* P;                 // [heads][Sp][Sp] decayed scores, bf16 hi, then lo (same layout)
@@ -73,10 +73,12 @@ struct GemmWs {
 
 int mfma_bwd_width(const BwdArgs& a);
 
-// The GEMM form applies to bf16 with a feature width above 512 and sequences up to
-// 16384 tokens (its score-shaped matrices take 8 S_p^2 bytes per head).
+// The GEMM form applies to bf16 with a feature width above 384 and sequences up to
+// 16384 tokens (its score-shaped matrices take 8 S_p^2 bytes per head).  Above 512
+// the fused tiles do not fit; at 512 it measured 0.80 ms against 1.27 ms for them
+// (B=4, NH=4, S=2048), at 384 and below the fused forms are faster.
 inline bool bwd_gemm_path(const BwdArgs& a) {
-    return a.dtype == MLSTM_BF16 && (a.dqk > 512 || a.dv > 512) && a.S <= 16384 && (long long)a.B * a.NH <= 65535;
+    return a.dtype == MLSTM_BF16 && (a.dqk > 384 || a.dv > 384) && a.S <= 16384 && (long long)a.B * a.NH <= 65535;
 }
 
 // Superchunk length of the two-level form: the quadratic tiles shrink to a band of
@@ -1578,10 +1580,10 @@ hipError_t launch_bwd_mfma(const BwdArgs& a, const BwdIn<bf16>& in, const BwdWs&
 }
 
 // ===========================================================================
-// GEMM form (bf16, max(d_qk, d_v) > 512): the score-shaped matrices materialized
+// GEMM form (bf16, max(d_qk, d_v) > 384): the score-shaped matrices materialized
 // ===========================================================================
 // Feature widths above 512 do not fit the per-query register tiles of the MFMA
-// form above.  For them the same quantities (readings of the header) are formed as
+// form above, and at 512 they spill.  For widths above 384 the same quantities (readings of the header) are formed as
 // six causal GEMMs over [S_p x S_p] score-shaped matrices held in the workspace
 // (S_p = S rounded up to 128; zero above the diagonal and beyond S), each a tiled
 // bf16 MFMA product with fp32 accumulation and a fused epilogue:

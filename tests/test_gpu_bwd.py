@@ -203,30 +203,16 @@ def test_bf16_full_size_sampled_heads(orc, name, heads):
     _compare(orc, x, dh, "bf16", sel=sel)
 
 
-def test_bf16_long_ctx_full_size_directional(orc):
-    """The long-context workload at full size (B=1, NH=8, S=32768, d=256; 128
-    superchunks of the two-level form).  No oracle backward finishes at this
-    length, so one head is checked through a property that holds at any size: for
-    each input tensor X and a random direction delta, sum(dX . delta) is the
-    derivative of L = sum(dh . h) along delta, taken here by central differences of
-    the oracle's fp64 recurrent forward.  These gates make L strongly curved in q
-    and k (tokens whose normalizer nearly vanishes far above the floor), so the step
-    is 1e-9, where the estimate has converged to about 1e-6.  With delta ~ N(0, 1)
-    the difference is about the RMS error of dX, and it is bounded by the tolerance
-    times the norm of dX."""
-    w = inputs.WORKLOADS["long_ctx"]
-    announce("bwd bf16 long_ctx full size, head (0, 5), directional derivatives")
-    x = inputs.fwd_inputs(w)
-    dh = inputs.bwd_dh(w)
-    got = bwd_gpu(x, dh, "bf16")
-    for name, g in zip(NAMES, got):
-        assert np.all(np.isfinite(g)), f"{name} is not finite"
-    b, hd = 0, 5
+def _directional(orc, x, dh, got, b, hd, eps):
+    """For each input tensor X of head (b, hd) and a random direction delta, sum(dX .
+    delta) from the GPU gradients against the derivative of L = sum(dh . h) along
+    delta by central differences of the oracle's fp64 recurrent forward.  With delta
+    ~ N(0, 1) the difference is about the RMS error of dX, so it is bounded by the
+    tolerance times the norm of dX."""
     names = ("q", "k", "v", "i_pre", "f_pre", "o_pre")
     xs = {n: x[n][b:b + 1, hd:hd + 1].astype(np.float64) for n in names}
     dhs = dh[b:b + 1, hd:hd + 1].astype(np.float64)
     rng = np.random.default_rng(4242)
-    eps = 1e-9
     batch = {n: np.repeat(xs[n], 2 * len(names), axis=0) for n in names}
     dirs = {}
     for j, n in enumerate(names):
@@ -243,6 +229,40 @@ def test_bf16_long_ctx_full_size_directional(orc):
         e = abs(have - want) / max(scale, 1e-300)
         announce(f"  {NAMES[j]}: oracle {want:.6e} gpu {have:.6e} |diff|/|{NAMES[j]}| {e:.2e}")
         assert e <= TOL["bf16"], f"{NAMES[j]}: directional error {e:.3e} > {TOL['bf16']:.1e}"
+
+
+def test_bf16_long_ctx_full_size_directional(orc):
+    """The long-context workload at full size (B=1, NH=8, S=32768, d=256; 128
+    superchunks of the two-level form).  No oracle backward finishes at this
+    length, so one head is checked through directional derivatives (_directional).
+    These gates make L strongly curved in q and k (tokens whose normalizer nearly
+    vanishes far above the floor), so the step is 1e-9, where the difference
+    quotient has converged to about 1e-6."""
+    w = inputs.WORKLOADS["long_ctx"]
+    announce("bwd bf16 long_ctx full size, head (0, 5), directional derivatives")
+    x = inputs.fwd_inputs(w)
+    dh = inputs.bwd_dh(w)
+    got = bwd_gpu(x, dh, "bf16")
+    for name, g in zip(NAMES, got):
+        assert np.all(np.isfinite(g)), f"{name} is not finite"
+    _directional(orc, x, dh, got, 0, 5, 1e-9)
+
+
+def test_bf16_width512_long_directional(orc):
+    """Width 512 beyond 16384 tokens, where the fused tiles of the two-level form
+    run (shorter sequences at this width take the GEMM form): B=1, NH=2, S=16448,
+    checked on one head through directional derivatives of the oracle forward (at
+    this length even language-model gates curve L in k: the difference quotient
+    moves 1% from step 1e-6 to 1e-7 and agrees to 2e-8 from 1e-7 to 1e-8)."""
+    w = inputs.WORKLOADS["lm_125m"]
+    over = dict(B=1, NH=2, S=16448, dqk=512, dv=512)
+    announce(f"bwd bf16 width 512 {over}, head (0, 1), directional derivatives")
+    x = inputs.fwd_inputs(w, seed=490, **over)
+    dh = inputs.bwd_dh(w, seed=490, B=1, NH=2, S=16448, dv=512)
+    got = bwd_gpu(x, dh, "bf16")
+    for name, g in zip(NAMES, got):
+        assert np.all(np.isfinite(g)), f"{name} is not finite"
+    _directional(orc, x, dh, got, 0, 1, 1e-8)
 
 
 def test_deterministic():
