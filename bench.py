@@ -27,15 +27,16 @@ on is unchanged.
 cpu_baseline: the fp64 oracle (oracle/, plain C + OpenMP over heads) timed on the
 host on a bounded sample of the same workload.
 
-Backward: sequences of 1024 tokens or more (bf16, d_qk, d_v <= 512) run the
-two-level form with superchunks of 256 tokens.  Its algorithmic FLOPs are, per
+Backward: sequences of 1024 tokens or more (bf16, d_qk, d_v <= 512, and not the
+GEMM form that widths above 384 take up to 16384 tokens) run the two-level form
+with superchunks of 256 tokens.  Its algorithmic FLOPs are, per
 head, the causal (t, s) pairs inside each superchunk times 6 (d_qk + d_v) (scores
 and numerator recomputed, then dA, dq, dk and dv, one multiply-add each per pair
 and dimension), plus 2 d_v d_qk (+ 2 d_qk for the normalizer) per token for each
 of the six state products: C~ q and C~^T dnum' for the queries after the first
 superchunk, dC~^T v and dC~ k for the keys before the last, and the two
-per-superchunk state sums.  Shorter sequences run the quadratic form over all
-S(S+1)/2 pairs.  The whole call is timed with HIP events on its stream; its
+per-superchunk state sums.  Shorter sequences and the GEMM form run the
+quadratic form over all S(S+1)/2 pairs.  The whole call is timed with HIP events on its stream; its
 roofline is against the bf16 MFMA peak.
 """
 from __future__ import annotations
@@ -80,7 +81,9 @@ BWD_SUPERCHUNK = 256            # the backward's superchunk length from 1024 tok
 def bwd_alg_flops(w) -> float:
     S, LS = w.S, BWD_SUPERCHUNK
     pair = 6.0 * (w.dqk + w.dv)
-    if S < 1024 or max(w.dqk, w.dv) > 512 or w.dtype != "bf16":
+    d = max(w.dqk, w.dv)
+    gemm_form = w.dtype == "bf16" and d > 384 and S <= 16384
+    if gemm_form or S < 1024 or d > 512 or w.dtype != "bf16":
         return float(w.B * w.NH) * S * (S + 1) / 2 * pair
     G = (S + LS - 1) // LS
     band = sum(n * (n + 1) / 2 for n in [LS] * (G - 1) + [S - (G - 1) * LS])
