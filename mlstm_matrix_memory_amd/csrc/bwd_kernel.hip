@@ -677,7 +677,8 @@ __device__ __forceinline__ void stage_rows(bf16* dst, const bf16* src, size_t to
 constexpr int WK_THREADS = 256;         // the scan
 constexpr int LT = 128;                 // local sums: n and j extent of a workgroup's tile
 constexpr int LW = LT / 16;             // waves of a local-sum workgroup (one 16-row strip each)
-constexpr int LP = LT + 8;              // LDS pitch (bf16) of its token-major tiles
+constexpr int LP = LT + 16;             // LDS pitch (bf16) of its token-major tiles (read transposed only:
+                                        // 8 banks mod 64 between rows keeps those reads conflict free)
 
 __device__ __forceinline__ size_t state_off(int bh, int g, int G, int dv, int dqk) {
     return ((size_t)bh * (G - 1) + g) * 2 * (size_t)dv * dqk;
@@ -1597,7 +1598,8 @@ constexpr int GT = 128;                  // output tile, rows and columns
 constexpr int GK = 32;                   // k per step (one MFMA depth)
 constexpr int GTHREADS = 256;            // 2 x 2 waves, 64 x 64 each
 constexpr int GPR = GK + 8;              // LDS pitch of [row][k] tiles (bf16)
-constexpr int GPT = GT + 8;              // LDS pitch of [k][row] tiles
+constexpr int GPT = GT + 16;             // LDS pitch of [k][row] tiles: 8 banks mod 64 between rows, so the
+                                         // transposing reads (4 rows x 4 8-byte chunks per 16 lanes) never collide
 
 enum GLayout { ROWK = 0, KROW = 1 };     // stored [row][k] (k contiguous) or [k][row]
 enum GEpi { EPI_F32 = 0, EPI_P = 1, EPI_G = 2 };
