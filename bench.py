@@ -169,8 +169,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build runs on a single MI355X and has no "
-              "multi-GPU path (heads shard across GPUs with no communication; see the design notes). "
+        print("bench.py measures one GPU only: the library runs on a single MI355X and has no "
+              "multi-GPU path (heads would shard across GPUs with no communication). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
 
