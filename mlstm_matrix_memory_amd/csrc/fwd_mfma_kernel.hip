@@ -64,6 +64,35 @@ __device__ __forceinline__ float row16_sum(float x) {
     return x;
 }
 
+// Lane (quad lane b = lane & 3) reads x from quad lane (b + R) & 3 (DPP quad_perm).
+template <int R>
+__device__ __forceinline__ float quad_rotate(float x) {
+    constexpr int ctrl = ((0 + R) & 3) | (((1 + R) & 3) << 2) | (((2 + R) & 3) << 4) | (((3 + R) & 3) << 6);
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float pick4(f32x4 v, int i) {
+    return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
+}
+
+// 4 x 4 transpose within each quad of lanes.  In the MFMA accumulator layout, quad
+// lane b holds rows 4g..4g+3 (g = lane / 16) of column 4a + b (a = (lane % 16) / 4);
+// afterwards it holds row 4g + b at columns 4a..4a+3, so one 8-byte store writes it.
+__device__ __forceinline__ f32x4 quad_transpose(f32x4 y, int b) {
+    f32x4 yr;        // yr[r] = y[(b - r) & 3]: what this lane sends in round r
+#pragma unroll
+    for (int r = 0; r < 4; ++r) yr[r] = pick4(y, (b - r) & 3);
+    f32x4 got;       // got[r] came from quad lane (b + r) & 3, i.e. column (b + r) & 3
+    got[0] = yr[0];
+    got[1] = quad_rotate<1>(yr[1]);
+    got[2] = quad_rotate<2>(yr[2]);
+    got[3] = quad_rotate<3>(yr[3]);
+    f32x4 t;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t[j] = pick4(got, (j - b) & 3);
+    return t;
+}
+
 // inclusive scans over the lanes of one wave (64 lanes), fp64
 __device__ __forceinline__ double wave_scan_add(double x, int lane) {
 #pragma unroll
@@ -684,10 +713,11 @@ __device__ __forceinline__ void split8(f32x4 x0, f32x4 x1, bf16x8& hi, bf16x8& l
 // output-gate pre-activations and weights are in flight.  Q/K slabs are double
 // buffered in LDS, so a slab costs one barrier; a chunk adds two (partial sums of
 // Q C'^T over the key parts, and release of the chunk-level tiles).
-template <int L_, int DQ_, int NC_, int NK_, int SB_, int MINB_, int CW_>
+template <int L_, int DQ_, int NC_, int NK_, int SB_, int MINB_, int CW_, bool RS_>
 struct Scan2Cfg {
     static constexpr int L = L_, DQ = DQ_, NC = NC_, NK = NK_, SB = SB_, MINB = MINB_;
     static constexpr int CW = CW_;         // 16-column blocks per wave
+    static constexpr bool RS = RS_;        // h rows stored 4 columns per lane after a quad transpose
     static constexpr int W = NC * NK, THREADS = 64 * W, TV = 16 * NC * CW;
     static constexpr int DP = DQ / NK, NS = DP / SB, SW = NK * SB;
     static constexpr int QP = SW + 4;      // Q pitch: row stride = 2 (mod 32) dwords
@@ -924,7 +954,6 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
             // next loads in flight while this slab is multiplied
             if (s + 1 < NS) slab_load<C>(rs, tid, qh, kh, t0, s + 1);
             else if (c + 1 < nC) slab_load<C>(rs, tid, qh, kh, t0 + L, 0);
-            if (s == NS - 1 && c + 1 < nC) chunk_load<C>(rc, tid, chunk_src(c + 1), dv);
             if (s == 0) {
                 const float cand = sigma * sm.sc[5][0];
                 const bool rescale = cand < SIGMA_MIN;
@@ -1017,6 +1046,11 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
                 }
                 __builtin_amdgcn_sched_group_barrier(0x008, NMI + NMU - NKR, 0);
             }
+            // the next chunk's tiles are requested after this slab's products are issued
+            if (s == NS - 1 && c + 1 < nC) {
+                __builtin_amdgcn_sched_barrier(0);
+                chunk_load<C>(rc, tid, chunk_src(c + 1), dv);
+            }
         }
 
         // --- partial sums over key parts, then the rows each part owns --------
@@ -1060,6 +1094,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
                         intra[x] = mfma(alo, bop, intra[x]);
                     }
                 }
+                f32x4 y[CW];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tau = 16 * tb + 4 * lg + i;
@@ -1067,10 +1102,23 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
                     const float rden = __builtin_amdgcn_rcpf(fmaxf(fabsf(sm.sc[4][tau]), fl));
 #pragma unroll
                     for (int x = 0; x < CW; ++x) {
-                        if (!act[x]) continue;
                         const float num = ra * intra[x][i] + aa * inter[x][i];
                         const float og = __builtin_amdgcn_rcpf(1.0f + __expf(-sm.o[tau * OP + tcol + 16 * x + ln]));
-                        hh[(t0 + tau) * dv + vcol + 16 * x + ln] = (bf16)(og * num * rden);
+                        y[x][i] = og * num * rden;
+                    }
+                }
+#pragma unroll
+                for (int x = 0; x < CW; ++x) {
+                    if (!act[x]) continue;
+                    if constexpr (C::RS) {
+                        // one 8-byte store per lane: row 16 tb + 4 lg + (ln & 3), 4 columns
+                        const f32x4 t = quad_transpose(y[x], ln & 3);
+                        *reinterpret_cast<bf16x4*>(hh + (t0 + 16 * tb + 4 * lg + (ln & 3)) * dv + vcol + 16 * x +
+                                                   4 * (ln >> 2)) = bf16x4{(bf16)t[0], (bf16)t[1], (bf16)t[2], (bf16)t[3]};
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            hh[(t0 + 16 * tb + 4 * lg + i) * dv + vcol + 16 * x + ln] = (bf16)y[x][i];
                     }
                 }
             }
@@ -1153,9 +1201,9 @@ hipError_t launch_scan2(const FwdArgs& a, const Ws& w, int G) {
 
 // stage 0 = prepare (chunk_prep, gate_scan, den), stage 1 = scan (segments, chunk_scan2),
 // stage 2 = workspace size only
-template <int L, int DQ, int NC, int NK, int SB, int MINB, int CW>
+template <int L, int DQ, int NC, int NK, int SB, int MINB, int CW, bool RS>
 hipError_t run2(const FwdArgs& a, int stage, size_t* bytes) {
-    using C = Scan2Cfg<L, DQ, NC, NK, SB, MINB, CW>;
+    using C = Scan2Cfg<L, DQ, NC, NK, SB, MINB, CW, RS>;
     const int G = segments<C>(a);
     if (stage == 2) {
         *bytes = ws_bytes((size_t)a.B * a.NH, a.S, L, a.dqk, a.dv, G);
@@ -1169,23 +1217,26 @@ hipError_t run2(const FwdArgs& a, int stage, size_t* bytes) {
 typedef hipError_t (*RunFn)(const FwdArgs&, int, size_t*);
 
 // supported (chunk, d_qk) pairs and the tiling used for each:
-// (chunk, d_qk, column blocks, key parts, slab, workgroups per CU, column blocks per wave)
+// (chunk, d_qk, column blocks, key parts, slab, workgroups per CU, column blocks per wave,
+//  h stored as 4-column rows after a quad transpose instead of one column per lane)
 RunFn pick(int L, int dqk) {
-#define MLSTM_V2(L_, DQ_, NC_, NK_, SB_, MINB_, CW_) \
-    if (L == L_ && dqk == DQ_) return &run2<L_, DQ_, NC_, NK_, SB_, MINB_, CW_>;
+#define MLSTM_V2(L_, DQ_, NC_, NK_, SB_, MINB_, CW_, RS_) \
+    if (L == L_ && dqk == DQ_) return &run2<L_, DQ_, NC_, NK_, SB_, MINB_, CW_, RS_>;
     // Four waves per workgroup (one per SIMD) let the compiler use the whole
     // register file; eight waves (two per SIMD, key dimension split in two or
     // four parts) hide more latency behind the other wave's MFMAs.  Every entry
     // is chosen by measurement among the tilings that do not spill, except
     // d_qk 1024, whose eight-wave tiling spills a little and still measured
     // fastest (lm 1.3B-class layer shape: 618 us against 660 us for four waves).
-    MLSTM_V2(32, 128, 4, 1, 128, 1, 1)
-    MLSTM_V2(32, 384, 3, 1, 128, 1, 1)
-    MLSTM_V2(64, 128, 4, 1, 128, 1, 1)
-    MLSTM_V2(64, 256, 4, 2, 32, 1, 1)
-    MLSTM_V2(64, 384, 4, 2, 32, 1, 1)
-    MLSTM_V2(64, 512, 4, 2, 32, 1, 1)
-    MLSTM_V2(64, 1024, 2, 4, 32, 1, 1)
+    // The transposed row stores save the d_qk 1024 tiling about 7% (its store
+    // traffic per slab is the heaviest) and cost the narrower ones about 3%.
+    MLSTM_V2(32, 128, 4, 1, 128, 1, 1, false)
+    MLSTM_V2(32, 384, 3, 1, 128, 1, 1, false)
+    MLSTM_V2(64, 128, 4, 1, 128, 1, 1, false)
+    MLSTM_V2(64, 256, 4, 2, 32, 1, 1, false)
+    MLSTM_V2(64, 384, 4, 2, 32, 1, 1, false)
+    MLSTM_V2(64, 512, 4, 2, 32, 1, 1, false)
+    MLSTM_V2(64, 1024, 2, 4, 32, 1, 1, true)
 #undef MLSTM_V2
     return nullptr;
 }
