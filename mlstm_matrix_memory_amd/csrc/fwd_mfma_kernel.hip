@@ -133,9 +133,25 @@ struct Ws {
     float* nent;    // [heads][chunk][DQ]  normalizer n' entering each chunk
     float* nfin;    // [heads][DQ]  final normalizer
     float* mfin;    // [heads]      final stabilizer
-    float* cst;     // [heads][G][DV][DQ]  state entering each sequence segment (slot 0 unused)
+    float* cst;     // [heads][G][DV][DQ]  state entering each sequence segment (slot 0: the initial one)
+    float* cpart;   // [heads][G-1][SP][DV][DQ]  sums over the SP token parts of each segment but the last
+    int sp;         // token parts per segment in seg_state_kernel
 };
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Token parts per segment for the segment sums: enough workgroups for two per CU,
+// each part at least 4 chunks long.
+constexpr int SS_TILE = 128;           // key rows and value columns of a segment-sum workgroup's tile
+constexpr int SS_MAXP = 8;
+inline int seg_parts(size_t heads, size_t nC, int DQ, int DV, int G) {
+    if (G <= 1) return 1;
+    const size_t tiles = (size_t)(DQ / SS_TILE) * ((DV + SS_TILE - 1) / SS_TILE);
+    const size_t nCs = nC / G;
+    int P = 1;
+    while (2 * P <= SS_MAXP && tiles * (G - 1) * heads * P < 512 && nCs % (2 * P) == 0 && nCs / (2 * P) >= 4) P *= 2;
+    return P;
+}
+
 inline size_t ws_walk(void* base, size_t heads, size_t S, int L, int DQ, int DV, int G, Ws* out) {
     const size_t nC = S / L;
     char* p = (char*)base;
@@ -160,6 +176,8 @@ inline size_t ws_walk(void* base, size_t heads, size_t S, int L, int DQ, int DV,
     w.nfin = (float*)take(heads * DQ * sizeof(float));
     w.mfin = (float*)take(heads * sizeof(float));
     w.cst = G > 1 ? (float*)take(heads * G * (size_t)DV * DQ * sizeof(float)) : nullptr;
+    w.sp = seg_parts(heads, nC, DQ, DV, G);
+    w.cpart = G > 1 ? (float*)take(heads * (G - 1) * (size_t)w.sp * DV * DQ * sizeof(float)) : nullptr;
     if (out) *out = w;
     return off;
 }
@@ -554,7 +572,6 @@ __global__ __launch_bounds__(DEN_THREADS) void den_kernel(const bf16* __restrict
 // hi + lo as in the scan); seg_combine_kernel chains the segments.  The scan then
 // runs every segment in parallel from its own entering state.
 constexpr int SS_THREADS = 256;
-constexpr int SS_TILE = 128;           // key rows and value columns of a workgroup's tile
 constexpr int SS_P = SS_TILE + 16;     // LDS pitch (bf16) of the token-major tiles
 
 template <int L>
@@ -569,11 +586,12 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
 
     const int n_kt = dqk / SS_TILE;
     const int kt = blockIdx.x % n_kt, vt = blockIdx.x / n_kt;
-    const int g = blockIdx.y, bh = blockIdx.z;
+    const int g = blockIdx.y / ws.sp, part = blockIdx.y % ws.sp, bh = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 15, lg = lane >> 4;
     const int wr = wave >> 1, wc = wave & 1;                // 64 keys x 64 values per wave
-    const int nC = S / L, nCs = nC / G;
+    const int nC = S / L, nCs = nC / G, nCp = nCs / ws.sp;
+    const int c_first = g * nCs + part * nCp;              // first chunk of this part
     const int key0 = kt * SS_TILE, val0 = vt * SS_TILE;
     const size_t tokh = (size_t)bh * S, tinh = (size_t)bh * Sx;
 
@@ -582,7 +600,7 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
     bf16x8 rk[UPT], rv[UPT];
     float rw[UPT], ralpha = 1.0f;
     auto load = [&](int ci) {
-        const int c = g * nCs + ci;
+        const int c = c_first + ci;
         const size_t t0 = tokh + (size_t)c * L, ti0 = tinh + (size_t)c * L;
 #pragma unroll
         for (int u = 0; u < UPT; ++u) {
@@ -604,9 +622,9 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
 #pragma unroll
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
 
-    float A = 1.0f;          // product of alpha over the segment's chunks after the current one
-    load(nCs - 1);
-    for (int ci = nCs - 1; ci >= 0; --ci) {
+    float A = 1.0f;          // product of alpha over the part's chunks after the current one
+    load(nCp - 1);
+    for (int ci = nCp - 1; ci >= 0; --ci) {
         __syncthreads();     // previous tiles consumed
 #pragma unroll
         for (int u = 0; u < UPT; ++u) {
@@ -651,24 +669,27 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
                 }
         }
     }
-    // dC_g into slot g + 1: rows of the D layout are keys, columns are values
-    float* dst = ws.cst + ((size_t)bh * G + g + 1) * (size_t)dv * dqk;
+    // the decay of the segment's chunks after this part
+    float later = 1.0f;
+    for (int c = c_first + nCp; c < (g + 1) * nCs; ++c) later *= ws.alpha[(size_t)bh * nC + c];
+    // this part's share of dC_g: rows of the D layout are keys, columns are values
+    float* dst = ws.cpart + (((size_t)bh * (G - 1) + g) * ws.sp + part) * (size_t)dv * dqk;
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             const int col = val0 + 64 * wc + 16 * b + ln;
             if (col < dv)
-                *reinterpret_cast<f32x4*>(dst + (size_t)col * dqk + key0 + 64 * wr + 16 * a + 4 * lg) = acc[a][b];
+                *reinterpret_cast<f32x4*>(dst + (size_t)col * dqk + key0 + 64 * wr + 16 * a + 4 * lg) = later * acc[a][b];
         }
 }
 
 constexpr int SC_THREADS = 256;
 constexpr int SC_MAXG = 64;
 
-// C'_start(g + 1) = A_g C'_start(g) + dC_g, in place over slots 1 .. G-1; slot 0
-// receives a copy of the initial state (or zero), so no segment reads the
-// caller's buffer while another writes the final state.
+// C'_start(g + 1) = A_g C'_start(g) + dC_g, with dC_g the sum of its parts in part
+// order, into slots 1 .. G-1; slot 0 receives a copy of the initial state (or
+// zero), so no segment reads the caller's buffer while another writes the final state.
 __global__ __launch_bounds__(SC_THREADS) void seg_combine_kernel(Ws ws, int nC, int G, int dqk, int dv,
                                                                  const float* __restrict__ C0)
 {
@@ -687,10 +708,12 @@ __global__ __launch_bounds__(SC_THREADS) void seg_combine_kernel(Ws ws, int nC, 
     f32x4 c = C0 ? *reinterpret_cast<const f32x4*>(C0 + (size_t)bh * per + e) : f32x4{0, 0, 0, 0};
     float* base = ws.cst + (size_t)bh * G * per + e;
     *reinterpret_cast<f32x4*>(base) = c;      // the first segment starts from slot 0
+    const float* parts = ws.cpart + (size_t)bh * (G - 1) * ws.sp * per + e;
     for (int g = 0; g + 1 < G; ++g) {
-        f32x4* slot = reinterpret_cast<f32x4*>(base + (size_t)(g + 1) * per);
-        c = sA[g] * c + *slot;
-        *slot = c;
+        f32x4 d = *reinterpret_cast<const f32x4*>(parts + (size_t)g * ws.sp * per);
+        for (int pp = 1; pp < ws.sp; ++pp) d += *reinterpret_cast<const f32x4*>(parts + ((size_t)g * ws.sp + pp) * per);
+        c = sA[g] * c + d;
+        *reinterpret_cast<f32x4*>(base + (size_t)(g + 1) * per) = c;
     }
 }
 
@@ -1179,7 +1202,7 @@ hipError_t launch_scan2(const FwdArgs& a, const Ws& w, int G) {
     constexpr int L = C::L;
     const int heads = a.B * a.NH;
     if (G > 1) {
-        dim3 sgrid((a.dqk / SS_TILE) * ((a.dv + SS_TILE - 1) / SS_TILE), G - 1, heads);
+        dim3 sgrid((a.dqk / SS_TILE) * ((a.dv + SS_TILE - 1) / SS_TILE), (G - 1) * w.sp, heads);
         hipLaunchKernelGGL((seg_state_kernel<L>), sgrid, dim3(SS_THREADS), 0, a.stream,
                            (const bf16*)a.k, (const bf16*)a.v, w, a.S, a.Sx, a.dqk, a.dv, G);
         hipError_t e = hipGetLastError();

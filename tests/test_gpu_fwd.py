@@ -107,6 +107,26 @@ def test_bf16_segmented_sequence(orc, over, chunk):
     _compare(orc, x, chunk, "bf16")
 
 
+# Segments under forget gates close to one (f~ ~ N(8, 1): a chunk keeps about 98%
+# of the state), so every token part of a segment reaches the next segment's
+# entering state with a weight of order one: the per-part sums of the segment
+# states and their decay factors are visible in h and C.  With 256-wide heads the
+# first shape runs as 8 segments of 2 token parts each, the second (8 heads, two of
+# them compared) as 4 segments of 4 parts.
+SEGMENTED_SLOW_DECAY = [(dict(B=1, NH=1, S=4096, dqk=256, dv=256), None),
+                        (dict(B=1, NH=8, S=4096, dqk=256, dv=256), (np.array([[0, 0]]), np.array([[1, 6]])))]
+
+
+@pytest.mark.parametrize("over,sel", SEGMENTED_SLOW_DECAY, ids=["1head", "8heads"])
+def test_bf16_segmented_slow_decay(orc, over, sel):
+    w = inputs.WORKLOADS["lm_125m"]
+    announce(f"fwd bf16 segmented slow decay {over}")
+    x = inputs.fwd_inputs(w, seed=420 + over["NH"], **over)
+    x["f_pre"] = x["f_pre"] + np.float32(5.0)
+    errs = _compare(orc, x, 64, "bf16", sel=sel)
+    print(errs)
+
+
 FULL = [
     # (batch indices, head indices) of the sampled heads, shaped [1, n] so the
     # selection keeps the [B, NH] leading axes
