@@ -121,12 +121,13 @@ struct Ws {
     float* den;     // [heads][S]  row sums of the decayed scores (fp32, before rounding)
     float* wloc;    // [heads][S]  chunk-local update weights
     float* dn;      // [heads][chunk][DQ]  K^T w_loc of each chunk
-    // six per-token arrays in one allocation [6][heads][S], in this order:
+    // six per-token arrays in one allocation [6][heads][S], in this order (the scan
+    // stages the first four with every chunk):
     float* a;       // weight of the carried state in each row
     float* r;       // rescale of the chunk-local scores to the carried stabilizer
     float* fl;      // floor exp(-m_t) of the normalizer
+    float* den2;    // the full normalizer n'.q of each row (before the floor)
     float* w;       // update weights with the carried stabilizer
-    float* den2;    // copy of den (row sums of the decayed scores)
     float* alt;     // alpha of the token's chunk, repeated over its tokens
     size_t hs;      // heads * S: stride between the six arrays
     float* alpha;   // [heads][chunk]  decay of the carried state across the chunk
@@ -168,8 +169,8 @@ inline size_t ws_walk(void* base, size_t heads, size_t S, int L, int DQ, int DV,
     w.a = (float*)take(6 * heads * S * sizeof(float));
     w.r = w.a + w.hs;
     w.fl = w.a + 2 * w.hs;
-    w.w = w.a + 3 * w.hs;
-    w.den2 = w.a + 4 * w.hs;
+    w.den2 = w.a + 3 * w.hs;
+    w.w = w.a + 4 * w.hs;
     w.alt = w.a + 5 * w.hs;
     w.alpha = (float*)take(heads * nC * sizeof(float));
     w.nent = (float*)take(heads * nC * DQ * sizeof(float));
@@ -752,7 +753,7 @@ struct Scan2Cfg {
     // staged 16-byte units
     static constexpr int U_Q = L * SW / 8, U_SLAB = 2 * U_Q;
     static constexpr int U_V = L * TV / 8, U_P = 2 * L * L / 8, U_O = L * TV / 4;
-    static constexpr int U_SC = 6 * L / 4;
+    static constexpr int U_SC = 4 * L / 4;   // a, r, fl, den2
     static constexpr int U_CH = U_V + U_P + U_O + U_SC;
     static constexpr int NPS = (U_SLAB + THREADS - 1) / THREADS;
     static constexpr int NPC = (U_CH + THREADS - 1) / THREADS;
@@ -766,9 +767,11 @@ struct alignas(16) Scan2Smem {
     alignas(16) bf16 q[2][C::L * C::QP];
     alignas(16) bf16 k[2][C::L * C::KP];
     alignas(16) bf16 v[C::L * C::VP];
+    alignas(16) bf16 vwh[C::L * C::VP];  // (w / sigma') (.) V of the chunk, bf16 hi
+    alignas(16) bf16 vwl[C::L * C::VP];  // and lo
     alignas(16) bf16 p[2][C::L * C::PP];
     alignas(16) float o[C::L * C::OP];
-    alignas(16) float sc[6][C::L];       // a, r, fl, w, den (full normalizer), alpha (per chunk, repeated)
+    alignas(16) float sc[4][C::L];       // a, r, fl, den2 (the full normalizer)
     // The partial retrievals of the key parts are exchanged through the K slab
     // buffer the chunk's last slab did not use when they fit there: every wave is
     // past the barrier of that slab, and the next chunk's first slab is stored
@@ -836,18 +839,21 @@ __device__ __forceinline__ void slab_store(const f32x4 (&reg)[Pref<C>::NSL], Sca
 
 struct ChunkSrc {
     const bf16* v; const bf16* P; const float* o;
-    const float* sc;     // a of the chunk's first token; the other five arrays follow at stride hs
+    const float* sc;     // a of the chunk's first token; r, fl, den2, w, alt follow at stride hs
     size_t hs;
     int vcols;           // valid value columns of the tile
 };
 
 template <class C>
-__device__ __forceinline__ void chunk_load(f32x4 (&reg)[Pref<C>::NCH], int tid, const ChunkSrc& cs, int dv) {
+__device__ __forceinline__ void chunk_load(f32x4 (&reg)[Pref<C>::NCH], float (&wrow)[Pref<C>::NV], float& alpha,
+                                           int tid, const ChunkSrc& cs, int dv) {
     using PF = Pref<C>;
     for_units<C::THREADS, C::U_V, 0>(tid, [&](int idx, int u) {
         const int row = idx / (C::TV / 8), col = 8 * (idx % (C::TV / 8));
         reg[u] = (col < cs.vcols) ? *reinterpret_cast<const f32x4*>(cs.v + (size_t)row * dv + col) : f32x4{0, 0, 0, 0};
+        wrow[u] = cs.sc[4 * cs.hs + row];          // update weight w of the unit's token
     });
+    alpha = cs.sc[5 * cs.hs];                      // the chunk's decay (repeated per token)
     for_units<C::THREADS, C::U_P, PF::NV>(tid, [&](int idx, int u) {
         reg[u] = *reinterpret_cast<const f32x4*>(cs.P + 8 * idx);
     });
@@ -861,12 +867,26 @@ __device__ __forceinline__ void chunk_load(f32x4 (&reg)[Pref<C>::NCH], int tid, 
     });
 }
 
+// inv_sig = 1 / sigma' of the chunk: the V units are also stored as (w / sigma') (.) V,
+// split into bf16 hi + lo, the B operand of the state update
 template <class C>
-__device__ __forceinline__ void chunk_store(const f32x4 (&reg)[Pref<C>::NCH], Scan2Smem<C>& sm, int tid) {
+__device__ __forceinline__ void chunk_store(const f32x4 (&reg)[Pref<C>::NCH], const float (&wrow)[Pref<C>::NV],
+                                            float inv_sig, Scan2Smem<C>& sm, int tid) {
     using PF = Pref<C>;
     for_units<C::THREADS, C::U_V, 0>(tid, [&](int idx, int u) {
         const int row = idx / (C::TV / 8), col = 8 * (idx % (C::TV / 8));
         *reinterpret_cast<f32x4*>(sm.v + row * C::VP + col) = reg[u];
+        const bf16x8 vb = __builtin_bit_cast(bf16x8, reg[u]);
+        const float wi = wrow[u] * inv_sig;
+        bf16x8 h, l;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float xv = wi * (float)vb[e];
+            h[e] = (bf16)xv;
+            l[e] = (bf16)(xv - (float)h[e]);
+        }
+        *reinterpret_cast<bf16x8*>(sm.vwh + row * C::VP + col) = h;
+        *reinterpret_cast<bf16x8*>(sm.vwl + row * C::VP + col) = l;
     });
     for_units<C::THREADS, C::U_P, PF::NV>(tid, [&](int idx, int u) {
         const int half = idx / (C::L * C::L / 8), rem = idx % (C::L * C::L / 8);
@@ -954,20 +974,26 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
         }
 
     f32x4 rs[Pref<C>::NSL], rc[Pref<C>::NCH];
-    chunk_load<C>(rc, tid, chunk_src(0), dv);
+    float rw[Pref<C>::NV], ralpha;
+    chunk_load<C>(rc, rw, ralpha, tid, chunk_src(0), dv);
     slab_load<C>(rs, tid, qh, kh, 0, 0);
     float sigma = 1.0f;
 
     for (int c = 0; c < nC; ++c) {
         const size_t t0 = (size_t)c * L;
-        chunk_store<C>(rc, sm, tid);
+        // sigma' after this chunk's decay; the registers are rescaled instead when
+        // it would leave the comfortable range (every thread takes the same decision)
+        const float cand = sigma * ralpha;
+        const bool rescale = cand < SIGMA_MIN;
+        const float st_scale = rescale ? cand : 1.0f;
+        const float sig_new = rescale ? 1.0f : cand;
+        chunk_store<C>(rc, rw, 1.0f / sig_new, sm, tid);
         f32x4 acc_inter[LB][CW];
 #pragma unroll
         for (int tb = 0; tb < LB; ++tb)
 #pragma unroll
             for (int x = 0; x < CW; ++x) acc_inter[tb][x] = f32x4{0, 0, 0, 0};
         bf16x8 vwh[CW][L / 32], vwl[CW][L / 32];
-        float sig_new = 1.0f, st_scale = 1.0f;   // set after the first barrier (alpha is in LDS)
 
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
@@ -977,33 +1003,17 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
             // next loads in flight while this slab is multiplied
             if (s + 1 < NS) slab_load<C>(rs, tid, qh, kh, t0, s + 1);
             else if (c + 1 < nC) slab_load<C>(rs, tid, qh, kh, t0 + L, 0);
-            if (s == 0) {
-                const float cand = sigma * sm.sc[5][0];
-                const bool rescale = cand < SIGMA_MIN;
-                st_scale = rescale ? cand : 1.0f;
-                sig_new = rescale ? 1.0f : cand;
-            }
             if (active) {
                 if (s == 0) {
-                    // (w / sigma') (.) V for this wave's columns, split into bf16 hi + lo
-                    const float inv_sig = 1.0f / sig_new;
+                    // this wave's columns of (w / sigma') (.) V, hi and lo, as B operands
 #pragma unroll
-                    for (int kk = 0; kk < L / 32; ++kk) {
-                        const f32x4 w0 = *reinterpret_cast<const f32x4*>(&sm.sc[3][32 * kk + 8 * lg]) * inv_sig;
-                        const f32x4 w1 = *reinterpret_cast<const f32x4*>(&sm.sc[3][32 * kk + 8 * lg + 4]) * inv_sig;
+                    for (int kk = 0; kk < L / 32; ++kk)
 #pragma unroll
                         for (int x = 0; x < CW; ++x) {
                             const int vrow = (32 * kk + 8 * lg + (ln >> 2)) * VP + tcol + 16 * x + 4 * (ln & 3);
-                            const bf16x8 vb = cat(lds_read_tr(sm.v + vrow), lds_read_tr(sm.v + vrow + 4 * VP));
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                const float xv = (e < 4 ? w0[e & 3] : w1[e & 3]) * (float)vb[e];
-                                const bf16 hi = (bf16)xv;
-                                vwh[x][kk][e] = hi;
-                                vwl[x][kk][e] = (bf16)(xv - (float)hi);
-                            }
+                            vwh[x][kk] = cat(lds_read_tr(sm.vwh + vrow), lds_read_tr(sm.vwh + vrow + 4 * VP));
+                            vwl[x][kk] = cat(lds_read_tr(sm.vwl + vrow), lds_read_tr(sm.vwl + vrow + 4 * VP));
                         }
-                    }
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 // The slab's operands are read from LDS before the products that use
@@ -1072,7 +1082,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
             // the next chunk's tiles are requested after this slab's products are issued
             if (s == NS - 1 && c + 1 < nC) {
                 __builtin_amdgcn_sched_barrier(0);
-                chunk_load<C>(rc, tid, chunk_src(c + 1), dv);
+                chunk_load<C>(rc, rw, ralpha, tid, chunk_src(c + 1), dv);
             }
         }
 
@@ -1122,7 +1132,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
                 for (int i = 0; i < 4; ++i) {
                     const int tau = 16 * tb + 4 * lg + i;
                     const float aa = sm.sc[0][tau] * sigma, ra = sm.sc[1][tau], fl = sm.sc[2][tau];
-                    const float rden = __builtin_amdgcn_rcpf(fmaxf(fabsf(sm.sc[4][tau]), fl));
+                    const float rden = __builtin_amdgcn_rcpf(fmaxf(fabsf(sm.sc[3][tau]), fl));
 #pragma unroll
                     for (int x = 0; x < CW; ++x) {
                         const float num = ra * intra[x][i] + aa * inter[x][i];
