@@ -4,7 +4,13 @@
 // eq. (18), normalizer with floor, multi-head independence and the parallel form
 // of the recurrence) and section 2.2 (stabilizer m_t, eq. (17)).
 //
-// Two kernels, both on bf16 MFMA with fp32 accumulation:
+// Two stages.  The prepare stage is parallel over chunks: chunk_prep (below),
+// then gate_scan (the stabilizer and normalizer carried across chunks, which fix
+// every per-token weight) and den_kernel (the full normalizer n'.q of every row).
+// The scan stage is sequential over chunks: chunk_scan2, preceded for few heads
+// over long sequences by seg_state and seg_combine, which let independent
+// sequence segments start from their own entering states.  The two kernels that
+// carry the work, both on bf16 MFMA with fp32 accumulation:
 //
 // 1. chunk_prep (one workgroup per (head, chunk), all chunks in parallel)
 //      b_tau     = in-chunk cumulative sum of log sigmoid(f~)
@@ -14,8 +20,8 @@
 //    P_loc is stored in bf16 (it is the MFMA operand of the next kernel); every
 //    exponent is <= 0 so nothing overflows.
 //
-// 2. chunk_scan (one workgroup per (head, tile of TV value columns), sequential
-//    over the chunks of the head, state carried in MFMA accumulators)
+// 2. chunk_scan2 (one workgroup per (head, segment, tile of TV value columns),
+//    sequential over the chunks of the segment, state carried in MFMA accumulators)
 //      m_tau = max(b_tau + m_p, m_loc_tau)   a_tau = exp(b_tau + m_p - m_tau)
 //      r_tau = exp(m_loc_tau - m_tau)        (the exact recurrent stabilizer)
 //      num   = r (.) (P_loc V) + a (.) (Q C'^T),  den = r (.) den_loc + a (.) (Q n')
