@@ -23,10 +23,11 @@ def orc():
 KEYS = ("q", "k", "v", "i_pre", "f_pre", "o_pre")
 
 
-def _pieces(orc, w, dtype, over, cuts, chunk, seed):
+def _pieces(orc, w, dtype, over, cuts, chunk, seed, f_shift=0.0):
     import torch
     from mlstm_matrix_memory_amd import mlstm_fwd_parallel_state
     x = inputs.fwd_inputs(w, seed=seed, **over)
+    x["f_pre"] = x["f_pre"] + np.float32(f_shift)
     S = x["q"].shape[2]
     dev = {key: to_gpu(val, dtype if key in ("q", "k", "v") else "f32") for key, val in x.items()}
     bounds = [0] + list(cuts) + [S]
@@ -64,6 +65,18 @@ def test_pieces_continue_the_sequence(orc, name, over, cuts, chunk, dtype):
     announce(f"fwd_state pieces {name} {over} cuts={cuts} chunk={chunk} {dtype}")
     errs = _pieces(orc, w, dtype, over, cuts, chunk, seed=500 + w.seed)
     print(name, errs)
+
+
+def test_segments_from_a_state_under_slow_decay(orc):
+    # Forget gates close to one (f~ ~ N(8, 1)), so the state handed between pieces and
+    # every token part of every segment reach the later outputs.  With 8 heads of
+    # width 256 the second piece (2048 tokens through the MFMA path, then a ragged
+    # tail of 52) runs as 4 segments of 2 token parts each, from the first piece's state.
+    w = inputs.WORKLOADS["lm_125m"]
+    over = dict(B=1, NH=8, S=4100, dqk=256, dv=256)
+    announce(f"fwd_state pieces slow decay {over} cuts=(2000,) chunk=64 bf16")
+    errs = _pieces(orc, w, "bf16", over, (2000,), 64, seed=530, f_shift=5.0)
+    print(errs)
 
 
 def test_state_forward_from_zero_equals_the_plain_forward():
