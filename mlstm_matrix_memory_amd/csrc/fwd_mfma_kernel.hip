@@ -128,11 +128,11 @@ struct Ws {
     float* wloc;    // [heads][S]  chunk-local update weights
     float* dn;      // [heads][chunk][DQ]  K^T w_loc of each chunk
     // six per-token arrays in one allocation [6][heads][S], in this order (the scan
-    // stages the first four with every chunk):
+    // stages the first three with every chunk):
     float* a;       // weight of the carried state in each row
     float* r;       // rescale of the chunk-local scores to the carried stabilizer
+    float* rden;    // 1 / max(|n'.q|, exp(-m_t)): the divisor of each row, inverted
     float* fl;      // floor exp(-m_t) of the normalizer
-    float* den2;    // the full normalizer n'.q of each row (before the floor)
     float* w;       // update weights with the carried stabilizer
     float* alt;     // alpha of the token's chunk, repeated over its tokens
     size_t hs;      // heads * S: stride between the six arrays
@@ -174,8 +174,8 @@ inline size_t ws_walk(void* base, size_t heads, size_t S, int L, int DQ, int DV,
     w.hs = heads * S;
     w.a = (float*)take(6 * heads * S * sizeof(float));
     w.r = w.a + w.hs;
-    w.fl = w.a + 2 * w.hs;
-    w.den2 = w.a + 3 * w.hs;
+    w.rden = w.a + 2 * w.hs;
+    w.fl = w.a + 3 * w.hs;
     w.w = w.a + 4 * w.hs;
     w.alt = w.a + 5 * w.hs;
     w.alpha = (float*)take(heads * nC * sizeof(float));
@@ -535,7 +535,9 @@ __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int
 // ---------------------------------------------------------------------------
 // den_t = r_t den_loc_t + a_t (q_t . n'_entering), in fp32: this is the quantity the
 // retrieval divides by, and the one that cancels, so it is formed from exact bf16
-// q and the fp32 normalizer state (no bf16 rounding of computed values).
+// q and the fp32 normalizer state (no bf16 rounding of computed values).  What is
+// stored is the inverted divisor 1 / max(|den_t|, exp(-m_t)), which the scan's
+// output phase multiplies by.
 constexpr int DEN_THREADS = 256;
 
 template <int L>
@@ -562,7 +564,8 @@ __global__ __launch_bounds__(DEN_THREADS) void den_kernel(const bf16* __restrict
         acc = row16_sum(acc);
         if (lp == 0) {
             const size_t g = tok0 + row;
-            ws.den2[g] = ws.r[g] * ws.den[g] + ws.a[g] * acc;
+            const float den = ws.r[g] * ws.den[g] + ws.a[g] * acc;
+            ws.rden[g] = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), ws.fl[g]));
         }
     }
 }
@@ -759,7 +762,7 @@ struct Scan2Cfg {
     // staged 16-byte units
     static constexpr int U_Q = L * SW / 8, U_SLAB = 2 * U_Q;
     static constexpr int U_V = L * TV / 8, U_P = 2 * L * L / 8, U_O = L * TV / 4;
-    static constexpr int U_SC = 4 * L / 4;   // a, r, fl, den2
+    static constexpr int U_SC = 3 * L / 4;   // a, r, rden
     static constexpr int U_CH = U_V + U_P + U_O + U_SC;
     static constexpr int NPS = (U_SLAB + THREADS - 1) / THREADS;
     static constexpr int NPC = (U_CH + THREADS - 1) / THREADS;
@@ -777,7 +780,7 @@ struct alignas(16) Scan2Smem {
     alignas(16) bf16 vwl[C::L * C::VP];  // and lo
     alignas(16) bf16 p[2][C::L * C::PP];
     alignas(16) float o[C::L * C::OP];
-    alignas(16) float sc[4][C::L];       // a, r, fl, den2 (the full normalizer)
+    alignas(16) float sc[3][C::L];       // a, r, rden
     // The partial retrievals of the key parts are exchanged through the K slab
     // buffer the chunk's last slab did not use when they fit there: every wave is
     // past the barrier of that slab, and the next chunk's first slab is stored
@@ -845,7 +848,7 @@ __device__ __forceinline__ void slab_store(const f32x4 (&reg)[Pref<C>::NSL], Sca
 
 struct ChunkSrc {
     const bf16* v; const bf16* P; const float* o;
-    const float* sc;     // a of the chunk's first token; r, fl, den2, w, alt follow at stride hs
+    const float* sc;     // a of the chunk's first token; r, rden, fl, w, alt follow at stride hs
     size_t hs;
     int vcols;           // valid value columns of the tile
 };
@@ -1137,8 +1140,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int tau = 16 * tb + 4 * lg + i;
-                    const float aa = sm.sc[0][tau] * sigma, ra = sm.sc[1][tau], fl = sm.sc[2][tau];
-                    const float rden = __builtin_amdgcn_rcpf(fmaxf(fabsf(sm.sc[3][tau]), fl));
+                    const float aa = sm.sc[0][tau] * sigma, ra = sm.sc[1][tau], rden = sm.sc[2][tau];
 #pragma unroll
                     for (int x = 0; x < CW; ++x) {
                         const float num = ra * intra[x][i] + aa * inter[x][i];
