@@ -169,6 +169,9 @@ def main() -> int:
     ap.add_argument("--no-epilogue", action="store_true")
     ap.add_argument("--no-slstm", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=5)
+    ap.add_argument("--bwd-warmup", type=int, default=10,
+                    help="untimed backward calls first (the GPU idles while dh is generated on the host, "
+                         "and the first calls after that run slow)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
     args = ap.parse_args()
@@ -271,6 +274,8 @@ def main() -> int:
         bws = torch.empty(max(1, mlstm_bwd_workspace_bytes(w.B, w.NH, w.S, w.dqk, w.dv, MLSTM_BF16)),
                           dtype=torch.uint8, device=dev)
         grads = mlstm_bwd_parallel(*fa[:6], dh, workspace=bws)
+        for _ in range(max(0, args.bwd_warmup - 1)):
+            mlstm_bwd_parallel(*fa[:6], dh, grads=grads, workspace=bws)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t_start = time.perf_counter()
