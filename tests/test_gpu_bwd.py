@@ -95,6 +95,16 @@ def test_bf16_reduced(orc, name, over):
     _compare(orc, x, dh, "bf16")
 
 
+# the largest widths the boundary accepts (d_qk or d_v = 4096) against the narrowest
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dqk,dv", [(4096, 16), (16, 4096)], ids=lambda v: str(v))
+def test_maximum_widths(orc, dtype, dqk, dv):
+    w = inputs.WORKLOADS["tiny" if dtype == "f32" else "lm_125m"]
+    announce(f"bwd {dtype} maximum widths B=1 NH=1 S=70 dqk={dqk} dv={dv}")
+    x = inputs.fwd_inputs(w, seed=620 + dqk, B=1, NH=1, S=70, dqk=dqk, dv=dv)
+    _compare(orc, x, inputs.bwd_dh(w, seed=620 + dqk, B=1, NH=1, S=70, dv=dv), dtype)
+
+
 # every tile width of the bf16 MFMA form (the smallest of 64, 128, 256, 384, 512
 # covering max(d_qk, d_v)), with ragged sequence ends, unequal d_qk / d_v, d not a
 # multiple of 32, and the long-context gate distribution with input-gate spikes

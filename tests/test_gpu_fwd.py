@@ -93,6 +93,20 @@ def test_bf16_mfma_tilings(orc, chunk, dqk, dv):
     _compare(orc, x, chunk, "bf16")
 
 
+# the largest widths the boundary accepts (d_qk or d_v = 4096), each against the
+# narrowest other width, over three chunks
+MAX_WIDTHS = [(4096, 16), (16, 4096)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dqk,dv", MAX_WIDTHS, ids=lambda v: str(v))
+def test_maximum_widths(orc, dtype, dqk, dv):
+    w = inputs.WORKLOADS["tiny" if dtype == "f32" else "lm_125m"]
+    announce(f"fwd {dtype} maximum widths B=1 NH=2 S=96 dqk={dqk} dv={dv} chunk=32")
+    x = inputs.fwd_inputs(w, seed=610 + dqk, B=1, NH=2, S=96, dqk=dqk, dv=dv)
+    _compare(orc, x, 32, dtype)
+
+
 # few heads over a long sequence: the scan splits each head's sequence into
 # segments chained through their entering states (long-context gate statistics)
 SEGMENTED = [(dict(B=1, NH=1, S=2048, dqk=128, dv=96), 64), (dict(B=1, NH=2, S=1024, dqk=384, dv=384), 32),
