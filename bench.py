@@ -1,31 +1,42 @@
 """Benchmark of the mLSTM matrix-memory hot path on one MI355X.
 
-A timed step is one chunkwise parallel forward (mlstm_fwd_prepare + mlstm_fwd_scan,
-i.e. mlstm_fwd_parallel) over the lm_125m workload: B=8, NH=4, S=2048,
-d_qk=d_v=384, chunk 64, bf16 q/k/v, fp32 gate pre-activations, inputs resident in
-HBM.  `value` is forward tokens/s (B*S tokens per step) from the wall clock around
-exactly --steps steps.  The same run also times the one-token decode step
-(mlstm_step on the decode workload: batch 256, NH=4, d=512, fp32 state, 128
-consecutive steps) and reports it under "decode", and the backward
-(mlstm_bwd_parallel: gradients of the same forward with respect to q, k, v and
-the three gate pre-activations, given dh) on the forward's workload under
-"backward", and the mLSTM block epilogue (mlstm_block_epilogue: per-head GroupNorm,
-learnable skip, external output gate) on the forward's h shape under "epilogue",
-and the sLSTM recurrence (slstm_fwd on slstm_125m: B=8, NH=4, S=2048, d_h=192,
-bf16 recurrent matrices) under "slstm".
+A timed step is one chunkwise parallel forward (mlstm_fwd_prepare +
+mlstm_fwd_scan, i.e. mlstm_fwd_parallel) over the 1.3B-class layer, lm_1_3b:
+B=4, NH=4, S=2048, d_qk=d_v=1024, chunk 64, bf16 q/k/v, fp32 gate
+pre-activations, inputs resident in HBM.  `value` is forward tokens/s (B*S
+tokens per step) from the wall clock around exactly --steps steps.
 
-Roofline: the dominant kernel of the forward is the scan; its duration is taken
-with HIP events recorded on the stream the kernels run on, and its algorithmic
-bytes per launch are
-    B*NH*S*(2*(2*d_qk + d_v) + 4*d_v + 2*d_v) + B*NH*(4*d_qk*d_v + 4*d_qk + 4)
-(q, k, v and h in bf16, o~ in fp32, final state in fp32; the workspace the two
-stages exchange is not algorithmic).  Algorithmic FLOPs of the forward are
-B*NH*S*((chunk+1)*(d_qk+d_v) + 4*d_qk*d_v).  "traffic" is filled from the
-measured HBM counters in profiles/ only while the kernel source they were taken
-on is unchanged.
+The same run times, each under a key of its own:
+  "workloads"  the forward on the 125M-class layer (lm_125m: B=8, NH=4, S=2048,
+               d=384, chunk 64) and on the long-context stress (long_ctx: B=1,
+               NH=8, S=32768, d=256, chunk 128), each with its own roofline;
+  "decode"     128 consecutive one-token steps (mlstm_step, batch 256, NH=4,
+               d=512, fp32 state);
+  "backward"   mlstm_bwd_parallel (gradients with respect to q, k, v and the three
+               gate pre-activations, given dh) on lm_125m and long_ctx;
+  "epilogue"   mlstm_block_epilogue (per-head GroupNorm, learnable skip, external
+               output gate) on lm_125m's h shape;
+  "slstm"      slstm_fwd on slstm_125m (B=8, NH=4, S=2048, d_h=192).
+
+Forward roofline.  Algorithmic FLOPs per forward are
+    B*NH*S*((L+1)*(d_qk+d_v) + 4*d_qk*d_v)
+with L the chunk the kernels execute (a 128-token chunk runs as two 64-token
+chunks on the matrix cores, so long_ctx counts L = 64); algorithmic bytes are
+    B*NH*S*(2*(2*d_qk + d_v) + 8 + 4*d_v + 2*d_v) + B*NH*(4*d_qk*d_v + 4*d_qk + 4)
+(q, k, v and h in bf16, i~ and f~ and o~ in fp32, the final state in fp32; the
+workspace the two stages exchange is not algorithmic).  "roofline" is the whole
+forward call (all its kernels, timed with HIP events on the stream they run on):
+the MFMA fraction is reported as "frac" with "bound": "mfma" where the MFMA
+ceiling is within 10% of the HBM one (lm_1_3b sits at the ridge: 56.7 us at the
+bf16 peak against 58.8 us at the HBM peak), else the HBM fraction with "bound":
+"hbm"; both fractions are always given.  "traffic" is the sum over every forward
+kernel of the HBM bytes the TCC counters measured (profiles/hbm_traffic.json),
+filled only while the forward's kernel source is the one profiled; its ratio to
+the algorithmic bytes is "traffic_ratio".  "scan_roofline" is the dominant
+kernel, chunk_scan, alone.
 
 cpu_baseline: the fp64 oracle (oracle/, plain C + OpenMP over heads) timed on the
-host on a bounded sample of the same workload.
+host on a bounded sample of the headline workload.
 
 Backward: sequences of 1024 tokens or more (bf16, d_qk, d_v <= 512, and not the
 GEMM form that widths above 384 take up to 16384 tokens) run the two-level form
@@ -61,8 +72,13 @@ EPILOGUE_SOURCE = os.path.join(ROOT, "mlstm_matrix_memory_amd", "csrc", "epilogu
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
+def exec_chunk(w) -> int:
+    """Chunk the kernels execute: a 128-token chunk runs as two 64-token chunks."""
+    return 64 if (w.dtype == "bf16" and w.chunk == 128) else w.chunk
+
+
 def fwd_alg_flops(w) -> float:
-    return float(w.B * w.NH * w.S) * ((w.chunk + 1) * (w.dqk + w.dv) + 4.0 * w.dqk * w.dv)
+    return float(w.B * w.NH * w.S) * ((exec_chunk(w) + 1) * (w.dqk + w.dv) + 4.0 * w.dqk * w.dv)
 
 
 def scan_alg_bytes(w) -> float:
@@ -73,6 +89,29 @@ def scan_alg_bytes(w) -> float:
 
 def fwd_alg_bytes(w) -> float:
     return scan_alg_bytes(w) + float(w.B * w.NH * w.S) * 8  # + i~, f~ (fp32)
+
+
+def fwd_roofline(w, ms: float, kernel: str, flops: float, nbytes: float, traffic=None) -> dict:
+    """Roofline of one forward-shaped unit of work timed at ms per call."""
+    tflops = flops / (ms / 1e3) / 1e12
+    gbs = nbytes / (ms / 1e3) / 1e9
+    t_mfma = flops / (BF16_PEAK_TFLOPS * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    mfma_bound = t_mfma >= 0.9 * t_hbm
+    r = {"kernel": kernel, "bound": "mfma" if mfma_bound else "hbm",
+         "achieved": tflops if mfma_bound else gbs,
+         "peak": BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+         "unit": "TFLOP/s" if mfma_bound else "GB/s",
+         "frac": tflops / BF16_PEAK_TFLOPS if mfma_bound else gbs / HBM_PEAK_GBS,
+         "mfma_frac": tflops / BF16_PEAK_TFLOPS, "hbm_frac": gbs / HBM_PEAK_GBS,
+         "tflops_alg": tflops, "hbm_gbs_alg": gbs,
+         "alg_flops_per_launch": flops, "alg_bytes_per_launch": nbytes,
+         "traffic": None, "traffic_ratio": None}
+    if traffic is not None:
+        r["traffic"] = traffic["bytes"]
+        r["traffic_ratio"] = traffic["bytes"] / nbytes
+        r["traffic_kernels"] = traffic["kernels"]
+    return r
 
 
 BWD_SUPERCHUNK = 256            # the backward's superchunk length from 1024 tokens on
@@ -112,17 +151,30 @@ def source_hash(path: str) -> str:
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
+def _traffic_records():
+    if not os.path.exists(TRAFFIC_FILE):
+        return {}
+    try:
+        return json.load(open(TRAFFIC_FILE))
+    except (ValueError, OSError):
+        return {}
+
+
 def measured_traffic(kernel: str, source: str, workload: str):
     """HBM bytes per launch from committed counter runs, if taken on this exact source and workload."""
-    if not os.path.exists(TRAFFIC_FILE):
-        return None
-    try:
-        rec = json.load(open(TRAFFIC_FILE)).get(f"{kernel}:{workload}")
-    except (ValueError, OSError):
-        return None
+    rec = _traffic_records().get(f"{kernel}:{workload}")
     if not rec or rec.get("source_sha") != source_hash(source):
         return None
     return rec.get("bytes_per_launch")
+
+
+def forward_traffic(workload: str):
+    """HBM bytes of one whole forward (every kernel it launches), from committed counter
+    runs taken on this exact forward source, or None."""
+    rec = _traffic_records().get(f"forward:{workload}")
+    if not rec or rec.get("source_sha") != source_hash(SCAN_SOURCE):
+        return None
+    return {"bytes": rec["bytes_per_call"], "kernels": rec["kernels"]}
 
 
 def cpu_baseline(w, x, budget_s: float = 12.0):
@@ -161,8 +213,11 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=30,
-                    help="untimed steps first (about 7 ms on lm_125m; fewer leave the clocks below steady state)")
-    ap.add_argument("--workload", default="lm_125m")
+                    help="untimed steps first (fewer leave the clocks below steady state)")
+    ap.add_argument("--workload", default="lm_1_3b")
+    ap.add_argument("--extra-workloads", default="lm_125m,long_ctx",
+                    help="forward workloads timed besides the headline one (comma list, '' for none)")
+    ap.add_argument("--bwd-workloads", default="lm_125m,long_ctx")
     ap.add_argument("--decode-steps", type=int, default=128)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -197,55 +252,69 @@ def main() -> int:
         t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
         return t.to(torch.bfloat16) if dt == "bf16" else t
 
+    def describe(w):
+        return (f"{w.name}: mLSTM fwd B={w.B} NH={w.NH} S={w.S} d_qk={w.dqk} d_v={w.dv} "
+                f"chunk={w.chunk} bf16 q/k/v, fp32 gates")
+
     # ---------------- forward ------------------------------------------------
+    def time_forward(w, x, steps, warmup):
+        """Warm up, then time exactly `steps` forwards (prepare + scan) on the current stream."""
+        d = {k: gpu(v, w.dtype if k in ("q", "k", "v") else "f32") for k, v in x.items()}
+        ws = torch.empty(max(1, mlstm_fwd_workspace_bytes(w.B, w.NH, w.S, w.dqk, w.dv, w.chunk, MLSTM_BF16)),
+                         dtype=torch.uint8, device=dev)
+        h = torch.empty((w.B, w.NH, w.S, w.dv), dtype=torch.bfloat16, device=dev)
+        C = torch.empty((w.B, w.NH, w.dv, w.dqk), dtype=torch.float32, device=dev)
+        n = torch.empty((w.B, w.NH, w.dqk), dtype=torch.float32, device=dev)
+        m = torch.empty((w.B, w.NH), dtype=torch.float32, device=dev)
+        fa = (d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"], w.chunk)
+        for _ in range(warmup):
+            mlstm_fwd_prepare(*fa, workspace=ws)
+            mlstm_fwd_scan(*fa, h, C, n, m, workspace=ws)
+        torch.cuda.synchronize()
+        # events on the current stream, the one the binding launches every kernel on
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for s in range(steps):
+            evs[s][0].record()
+            mlstm_fwd_prepare(*fa, workspace=ws)
+            evs[s][1].record()
+            mlstm_fwd_scan(*fa, h, C, n, m, workspace=ws)
+            evs[s][2].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        res = {"ms_per_step": wall * 1e3 / steps,
+               "prepare_ms": sum(e[0].elapsed_time(e[1]) for e in evs) / steps,
+               "scan_ms": sum(e[1].elapsed_time(e[2]) for e in evs) / steps,
+               "event_ms": sum(e[0].elapsed_time(e[2]) for e in evs) / steps}
+        del d, ws, h, C, n, m
+        torch.cuda.empty_cache()
+        return res
+
+    def fwd_record(w, t):
+        flops, nbytes = fwd_alg_flops(w), fwd_alg_bytes(w)
+        rec = {"workload": describe(w), "ms_per_step": t["ms_per_step"],
+               "tokens_per_s": w.B * w.S / (t["ms_per_step"] / 1e3),
+               "event_ms": t["event_ms"], "prepare_ms": t["prepare_ms"], "scan_ms": t["scan_ms"],
+               "executed_chunk": exec_chunk(w),
+               "roofline": fwd_roofline(w, t["event_ms"], "forward (all kernels of mlstm_fwd_parallel)",
+                                        flops, nbytes, forward_traffic(w.name)),
+               "scan_roofline": fwd_roofline(w, t["scan_ms"], "chunk_scan", flops, scan_alg_bytes(w),
+                                             None)}
+        tr = measured_traffic("chunk_scan", SCAN_SOURCE, w.name)
+        if tr is not None:
+            rec["scan_roofline"]["traffic"] = tr
+            rec["scan_roofline"]["traffic_ratio"] = tr / scan_alg_bytes(w)
+        return rec
+
     w = inputs.WORKLOADS[args.workload]
     x = inputs.fwd_inputs(w)
-    d = {k: gpu(v, w.dtype if k in ("q", "k", "v") else "f32") for k, v in x.items()}
-    ws = torch.empty(max(1, mlstm_fwd_workspace_bytes(w.B, w.NH, w.S, w.dqk, w.dv, w.chunk, MLSTM_BF16)),
-                     dtype=torch.uint8, device=dev)
-    h = torch.empty((w.B, w.NH, w.S, w.dv), dtype=torch.bfloat16, device=dev)
-    C = torch.empty((w.B, w.NH, w.dv, w.dqk), dtype=torch.float32, device=dev)
-    n = torch.empty((w.B, w.NH, w.dqk), dtype=torch.float32, device=dev)
-    m = torch.empty((w.B, w.NH), dtype=torch.float32, device=dev)
-    fa = (d["q"], d["k"], d["v"], d["i_pre"], d["f_pre"], d["o_pre"], w.chunk)
-
-    def prepare():
-        mlstm_fwd_prepare(*fa, workspace=ws)
-
-    def scan():
-        mlstm_fwd_scan(*fa, h, C, n, m, workspace=ws)
-
-    for _ in range(args.warmup):
-        prepare()
-        scan()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for s in range(args.steps):
-        evs[s][0].record()
-        prepare()
-        evs[s][1].record()
-        scan()
-        evs[s][2].record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms_per_step = wall * 1e3 / args.steps
-    prep_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    scan_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-    fwd_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
-    tokens = w.B * w.S
-    value = tokens / (ms_per_step / 1e3)
-    flops = fwd_alg_flops(w)
-    tflops = flops / (ms_per_step / 1e3) / 1e12
-    fwd_gbs = fwd_alg_bytes(w) / (ms_per_step / 1e3) / 1e9
-    scan_bytes = scan_alg_bytes(w)
-    scan_gbs = scan_bytes / (scan_ms / 1e3) / 1e9
-    traffic = measured_traffic("chunk_scan", SCAN_SOURCE, w.name)
-
+    t = time_forward(w, x, args.steps, args.warmup)
+    head = fwd_record(w, t)
+    ms_per_step = t["ms_per_step"]
     out = {
         "metric": METRIC,
-        "value": value,
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -256,53 +325,69 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": f"{w.name}: mLSTM fwd B={w.B} NH={w.NH} S={w.S} d_qk={w.dqk} d_v={w.dv} "
-                               f"chunk={w.chunk} bf16 q/k/v, fp32 gates",
+        "config": {"workload": describe(w),
                    "B": w.B, "NH": w.NH, "S": w.S, "d_qk": w.dqk, "d_v": w.dv, "chunk": w.chunk},
-        "fwd": {"tflops_alg": tflops, "mfma_frac": tflops / BF16_PEAK_TFLOPS,
-                "hbm_gbs_alg": fwd_gbs, "hbm_frac": fwd_gbs / HBM_PEAK_GBS,
-                "event_ms": fwd_ms, "prepare_ms": prep_ms, "scan_ms": scan_ms},
-        "roofline": {"kernel": "chunk_scan", "bound": "hbm", "achieved": scan_gbs, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": scan_gbs / HBM_PEAK_GBS, "traffic": traffic,
-                     "alg_bytes_per_launch": scan_bytes},
+        "fwd": {"tflops_alg": head["roofline"]["tflops_alg"], "mfma_frac": head["roofline"]["mfma_frac"],
+                "hbm_gbs_alg": head["roofline"]["hbm_gbs_alg"], "hbm_frac": head["roofline"]["hbm_frac"],
+                "event_ms": t["event_ms"], "prepare_ms": t["prepare_ms"], "scan_ms": t["scan_ms"],
+                "executed_chunk": exec_chunk(w)},
+        "roofline": head["roofline"],
+        "scan_roofline": head["scan_roofline"],
     }
+    head_x = x
+    del x
+
+    extra = [nm for nm in args.extra_workloads.split(",") if nm and nm != w.name]
+    if extra:
+        out["workloads"] = {}
+        for nm in extra:
+            we = inputs.WORKLOADS[nm]
+            xe = inputs.fwd_inputs(we)
+            te = time_forward(we, xe, args.steps, args.warmup)
+            del xe
+            out["workloads"][nm] = fwd_record(we, te)
 
     # ---------------- backward ------------------------------------------------
-    del ws, h, C, n, m
-    torch.cuda.empty_cache()
     if not args.no_bwd:
-        dh = gpu(inputs.bwd_dh(w), w.dtype)
-        bws = torch.empty(max(1, mlstm_bwd_workspace_bytes(w.B, w.NH, w.S, w.dqk, w.dv, MLSTM_BF16)),
-                          dtype=torch.uint8, device=dev)
-        grads = mlstm_bwd_parallel(*fa[:6], dh, workspace=bws)
-        for _ in range(max(0, args.bwd_warmup - 1)):
-            mlstm_bwd_parallel(*fa[:6], dh, grads=grads, workspace=bws)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t_start = time.perf_counter()
-        e0.record()
-        for _ in range(args.bwd_steps):
-            mlstm_bwd_parallel(*fa[:6], dh, grads=grads, workspace=bws)
-        e1.record()
-        torch.cuda.synchronize()
-        bwall = time.perf_counter() - t_start
-        bwd_ms = e0.elapsed_time(e1) / args.bwd_steps
-        bflops = bwd_alg_flops(w)
-        btf = bflops / (bwd_ms / 1e3) / 1e12
-        out["backward"] = {
-            "workload": f"{w.name}: mlstm_bwd_parallel B={w.B} NH={w.NH} S={w.S} d_qk={w.dqk} d_v={w.dv} "
-                        "bf16 q/k/v/dh, fp32 gradients",
-            "tokens_per_s": tokens * args.bwd_steps / bwall, "ms_per_call": bwd_ms,
-            "roofline": {"kernel": "mlstm_bwd_parallel (whole call)", "bound": "mfma", "achieved": btf,
-                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": btf / BF16_PEAK_TFLOPS,
-                         "traffic": None, "alg_flops_per_call": bflops},
-        }
-        del dh, bws, grads
-        torch.cuda.empty_cache()
-    del d
+        out["backward"] = {}
+        for nm in [b for b in args.bwd_workloads.split(",") if b]:
+            wb = inputs.WORKLOADS[nm]
+            xb = head_x if nm == w.name else inputs.fwd_inputs(wb)
+            db = {k: gpu(v, wb.dtype if k in ("q", "k", "v") else "f32") for k, v in xb.items()}
+            del xb
+            fb = (db["q"], db["k"], db["v"], db["i_pre"], db["f_pre"], db["o_pre"])
+            dh = gpu(inputs.bwd_dh(wb), wb.dtype)
+            bws = torch.empty(max(1, mlstm_bwd_workspace_bytes(wb.B, wb.NH, wb.S, wb.dqk, wb.dv, MLSTM_BF16)),
+                              dtype=torch.uint8, device=dev)
+            grads = mlstm_bwd_parallel(*fb, dh, workspace=bws)
+            for _ in range(max(0, args.bwd_warmup - 1)):
+                mlstm_bwd_parallel(*fb, dh, grads=grads, workspace=bws)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            t_start = time.perf_counter()
+            e0.record()
+            for _ in range(args.bwd_steps):
+                mlstm_bwd_parallel(*fb, dh, grads=grads, workspace=bws)
+            e1.record()
+            torch.cuda.synchronize()
+            bwall = time.perf_counter() - t_start
+            bwd_ms = e0.elapsed_time(e1) / args.bwd_steps
+            bflops = bwd_alg_flops(wb)
+            btf = bflops / (bwd_ms / 1e3) / 1e12
+            out["backward"][nm] = {
+                "workload": f"{wb.name}: mlstm_bwd_parallel B={wb.B} NH={wb.NH} S={wb.S} d_qk={wb.dqk} "
+                            f"d_v={wb.dv} bf16 q/k/v/dh, fp32 gradients",
+                "tokens_per_s": wb.B * wb.S * args.bwd_steps / bwall, "ms_per_call": bwd_ms,
+                "roofline": {"kernel": "mlstm_bwd_parallel (whole call)", "bound": "mfma", "achieved": btf,
+                             "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": btf / BF16_PEAK_TFLOPS,
+                             "traffic": None, "alg_flops_per_call": bflops},
+            }
+            del db, fb, dh, bws, grads
+            torch.cuda.empty_cache()
 
     # ---------------- block epilogue ------------------------------------------
     if not args.no_epilogue:
+        w = inputs.WORKLOADS["lm_125m"]
         ex = inputs.epilogue_inputs(w)
         de = {k: gpu(v, w.dtype if k in ("h", "x", "z") else "f32") for k, v in ex.items()}
         del ex
@@ -419,7 +504,7 @@ def main() -> int:
 
     # ---------------- CPU baseline (oracle) ------------------------------------
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, x)
+        out["cpu_baseline"] = cpu_baseline(inputs.WORKLOADS[args.workload], head_x)
 
     print(json.dumps(out), flush=True)
     return 0

@@ -42,6 +42,10 @@
  *     human-readable reason for the last failure on the calling thread.  NaN or
  *     Inf in the inputs are propagated, not checked.
  *   - Outputs must not alias inputs (except where an entry point says "in place").
+ *     mlstm_fwd_parallel, mlstm_fwd_parallel_state, mlstm_fwd_prepare,
+ *     mlstm_fwd_scan and mlstm_step check it: a buffer they write (h_out, the
+ *     final or in-place state, the workspace) that shares a byte with any other
+ *     buffer of the call is rejected with MLSTM_ERR_INVALID_ARG.
  *   - Alignment: tensors the kernels access with vector loads or stores must be
  *     16-byte aligned (fwd: q, k, v, o_pre, h_out, C_final, n_final; step: q, k,
  *     C, n); every other pointer needs the alignment of its element type.
@@ -189,6 +193,8 @@ mlstm_status mlstm_fwd_scan(const void *q, const void *k, const void *v,
  *   B, NH           >= 1;  d_qk, d_v multiples of 16, <= 4096
  *   C, n, m         [B,NH,d_v,d_qk], [B,NH,d_qk], [B,NH] fp32, in place
  *   h_out           [B,NH,d_v] dtype, written
+ * The dot products n'.q and C'q are accumulated in fp64 over exactly the fp32
+ * state values written back, so h_out is the retrieval from the returned state.
  */
 mlstm_status mlstm_step(const void *q, const void *k, const void *v,
                         const float *i_pre, const float *f_pre, const float *o_pre,

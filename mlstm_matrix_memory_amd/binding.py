@@ -124,7 +124,21 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _fwd_args(q, k, v, i_pre, f_pre, o_pre, chunk, h_out, C_final, n_final, m_final, workspace, need_outputs):
+def _keep_for_stream(stream, device, tensors):
+    """Tensors a wrapper allocated itself (workspace, outputs) are allocated on the
+    current stream but used by kernels enqueued on `stream`.  When that is another
+    stream, tell torch's caching allocator, so that it does not hand their memory to
+    a later allocation on the current stream while those kernels still run."""
+    import torch
+    if stream is None or stream == torch.cuda.current_stream(device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
+def _fwd_args(q, k, v, i_pre, f_pre, o_pre, chunk, h_out, C_final, n_final, m_final, workspace, need_outputs,
+              stream=None):
     """Checks the forward's tensors, allocates what is missing; returns the argument tuple."""
     import torch
     lib = load_library()
@@ -142,15 +156,20 @@ def _fwd_args(q, k, v, i_pre, f_pre, o_pre, chunk, h_out, C_final, n_final, m_fi
     _check(i_pre, "i_pre", (B, NH, S), torch.float32, dev)
     _check(f_pre, "f_pre", (B, NH, S), torch.float32, dev)
     _check(o_pre, "o_pre", (B, NH, S, dv), torch.float32, dev)
+    owned = []            # tensors allocated here, used by kernels on `stream`
     if need_outputs:
         if h_out is None:
             h_out = torch.empty((B, NH, S, dv), dtype=q.dtype, device=dev)
+            owned.append(h_out)
         if C_final is None:
             C_final = torch.empty((B, NH, dv, dqk), dtype=torch.float32, device=dev)
+            owned.append(C_final)
         if n_final is None:
             n_final = torch.empty((B, NH, dqk), dtype=torch.float32, device=dev)
+            owned.append(n_final)
         if m_final is None:
             m_final = torch.empty((B, NH), dtype=torch.float32, device=dev)
+            owned.append(m_final)
         _check(h_out, "h_out", (B, NH, S, dv), q.dtype, dev)
         _check(C_final, "C_final", (B, NH, dv, dqk), torch.float32, dev)
         _check(n_final, "n_final", (B, NH, dqk), torch.float32, dev)
@@ -158,6 +177,8 @@ def _fwd_args(q, k, v, i_pre, f_pre, o_pre, chunk, h_out, C_final, n_final, m_fi
     need = int(lib.mlstm_fwd_workspace_bytes(B, NH, S, dqk, dv, chunk, dt))
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        owned.append(workspace)
+    _keep_for_stream(stream, dev, owned)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     return (B, NH, S, dqk, dv, dt, h_out, C_final, n_final, m_final, workspace, ws_ptr, ws_bytes, dev)
@@ -174,7 +195,7 @@ def mlstm_fwd_parallel(q, k, v, i_pre, f_pre, o_pre, chunk: int,
     """
     lib = load_library()
     (B, NH, S, dqk, dv, dt, h_out, C_final, n_final, m_final, workspace, ws_ptr, ws_bytes, dev) = _fwd_args(
-        q, k, v, i_pre, f_pre, o_pre, chunk, h_out, C_final, n_final, m_final, workspace, True)
+        q, k, v, i_pre, f_pre, o_pre, chunk, h_out, C_final, n_final, m_final, workspace, True, stream)
     st = lib.mlstm_fwd_parallel(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                 i_pre.data_ptr(), f_pre.data_ptr(), o_pre.data_ptr(),
                                 B, NH, S, dqk, dv, int(chunk), dt,
@@ -197,7 +218,7 @@ def mlstm_fwd_parallel_state(q, k, v, i_pre, f_pre, o_pre, chunk: int, C_init=No
     import torch
     lib = load_library()
     (B, NH, S, dqk, dv, dt, h_out, C_final, n_final, m_final, workspace, ws_ptr, ws_bytes, dev) = _fwd_args(
-        q, k, v, i_pre, f_pre, o_pre, chunk, h_out, C_final, n_final, m_final, workspace, True)
+        q, k, v, i_pre, f_pre, o_pre, chunk, h_out, C_final, n_final, m_final, workspace, True, stream)
     given = [t is not None for t in (C_init, n_init, m_init)]
     if any(given):
         if not all(given):
@@ -221,7 +242,7 @@ def mlstm_fwd_prepare(q, k, v, i_pre, f_pre, o_pre, chunk: int, workspace, strea
     """First stage of mlstm_fwd_parallel (per-chunk gates and decayed scores into workspace)."""
     lib = load_library()
     (B, NH, S, dqk, dv, dt, _, _, _, _, workspace, ws_ptr, ws_bytes, dev) = _fwd_args(
-        q, k, v, i_pre, f_pre, o_pre, chunk, None, None, None, None, workspace, False)
+        q, k, v, i_pre, f_pre, o_pre, chunk, None, None, None, None, workspace, False, stream)
     st = lib.mlstm_fwd_prepare(q.data_ptr(), k.data_ptr(), i_pre.data_ptr(), f_pre.data_ptr(),
                                B, NH, S, dqk, dv, int(chunk), dt, ws_ptr, ws_bytes, _stream_handle(stream, dev))
     if st != MLSTM_OK:
@@ -233,7 +254,7 @@ def mlstm_fwd_scan(q, k, v, i_pre, f_pre, o_pre, chunk: int, h_out, C_final, n_f
     """Second stage of mlstm_fwd_parallel (sequential pass over chunks); outputs given."""
     lib = load_library()
     (B, NH, S, dqk, dv, dt, h_out, C_final, n_final, m_final, workspace, ws_ptr, ws_bytes, dev) = _fwd_args(
-        q, k, v, i_pre, f_pre, o_pre, chunk, h_out, C_final, n_final, m_final, workspace, True)
+        q, k, v, i_pre, f_pre, o_pre, chunk, h_out, C_final, n_final, m_final, workspace, True, stream)
     st = lib.mlstm_fwd_scan(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                             i_pre.data_ptr(), f_pre.data_ptr(), o_pre.data_ptr(),
                             B, NH, S, dqk, dv, int(chunk), dt,
@@ -268,13 +289,17 @@ def mlstm_bwd_parallel(q, k, v, i_pre, f_pre, o_pre, dh, grads=None, workspace=N
     for t, name, shp, tdt in zip((q, k, v, i_pre, f_pre, o_pre, dh), ("q", "k", "v", "i_pre", "f_pre", "o_pre", "dh"),
                                  shapes + [(B, NH, S, dv)], [q.dtype] * 3 + [torch.float32] * 3 + [q.dtype]):
         _check(t, name, shp, tdt, dev)
+    owned = []
     if grads is None:
         grads = tuple(torch.empty(shp, dtype=torch.float32, device=dev) for shp in shapes)
+        owned.extend(grads)
     for t, name, shp in zip(grads, ("grad_q", "grad_k", "grad_v", "grad_i", "grad_f", "grad_o"), shapes):
         _check(t, name, shp, torch.float32, dev)
     need = int(lib.mlstm_bwd_workspace_bytes(B, NH, S, dqk, dv, dt))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        owned.append(workspace)
+    _keep_for_stream(stream, dev, owned)
     st = lib.mlstm_bwd_parallel(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                 i_pre.data_ptr(), f_pre.data_ptr(), o_pre.data_ptr(), dh.data_ptr(),
                                 B, NH, S, dqk, dv, dt, *[g.data_ptr() for g in grads],
@@ -311,6 +336,7 @@ def mlstm_block_epilogue(h, x, z, gn_weight, gn_bias, skip_weight, eps: float = 
         _check(t, name, (NH, dv), torch.float32, dev)
     if y_out is None:
         y_out = torch.empty_like(h)
+        _keep_for_stream(stream, dev, [y_out])
     _check(y_out, "y_out", (B, NH, S, dv), h.dtype, dev)
     st = lib.mlstm_block_epilogue(h.data_ptr(), x.data_ptr(), z.data_ptr(), gn_weight.data_ptr(),
                                   gn_bias.data_ptr(), skip_weight.data_ptr(), B, NH, S, dv, float(eps), int(act),
@@ -348,10 +374,16 @@ def slstm_fwd(x_pre, R, forget: int = MLSTM_FORGET_SIGMOID, c_init=None, n_init=
             raise ValueError("c_init, n_init, m_init and h_init must be given together")
         for t, name in zip(init, ("c_init", "n_init", "m_init", "h_init")):
             _check(t, name, (B, NH, dh), torch.float32, dev)
+    owned = []
     if h_out is None:
         h_out = torch.empty((B, NH, S, dh), dtype=R.dtype, device=dev)
+        owned.append(h_out)
     fin = [c_final, n_final, m_final, h_final]
-    fin = [torch.empty((B, NH, dh), dtype=torch.float32, device=dev) if t is None else t for t in fin]
+    for j, t in enumerate(fin):
+        if t is None:
+            fin[j] = torch.empty((B, NH, dh), dtype=torch.float32, device=dev)
+            owned.append(fin[j])
+    _keep_for_stream(stream, dev, owned)
     _check(h_out, "h_out", (B, NH, S, dh), R.dtype, dev)
     for t, name in zip(fin, ("c_final", "n_final", "m_final", "h_final")):
         _check(t, name, (B, NH, dh), torch.float32, dev)
@@ -390,6 +422,7 @@ def mlstm_step(q, k, v, i_pre, f_pre, o_pre, C, n, m, h_out=None, stream=None):
     _check(m, "m", (B, NH), torch.float32, dev)
     if h_out is None:
         h_out = torch.empty((B, NH, dv), dtype=q.dtype, device=dev)
+        _keep_for_stream(stream, dev, [h_out])
     _check(h_out, "h_out", (B, NH, dv), q.dtype, dev)
     st = lib.mlstm_step(q.data_ptr(), k.data_ptr(), v.data_ptr(),
                         i_pre.data_ptr(), f_pre.data_ptr(), o_pre.data_ptr(),

@@ -104,6 +104,28 @@ bool overlaps(const void* p, size_t pb, const void* q, size_t qb) {
     return a < b + qb && b < a + pb;
 }
 
+// A buffer of a call: its address, size in bytes and name (null or empty = absent).
+struct Buf {
+    const void* p;
+    size_t bytes;
+    const char* name;
+};
+
+// Every buffer the call writes (the first n_out of `bufs`) must share no byte with
+// any other buffer of the call: the kernels read inputs after writing outputs of
+// earlier chunks or rows, so an alias would corrupt results without an error.
+mlstm_status check_disjoint(const Buf* bufs, int n, int n_out) {
+    for (int o = 0; o < n_out; ++o) {
+        if (!bufs[o].p || bufs[o].bytes == 0) continue;
+        for (int i = 0; i < n; ++i) {
+            if (i == o || !bufs[i].p || bufs[i].bytes == 0) continue;
+            if (overlaps(bufs[o].p, bufs[o].bytes, bufs[i].p, bufs[i].bytes))
+                return fail(MLSTM_ERR_INVALID_ARG, "%s overlaps %s", bufs[o].name, bufs[i].name);
+        }
+    }
+    return MLSTM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -158,6 +180,26 @@ static mlstm_status fwd_common(const void* q, const void* k, const void* v,
         if (!workspace || workspace_bytes < need)
             return fail(MLSTM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
         if (!aligned16(workspace)) return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    }
+    {
+        // outputs first: the workspace, h and the final state are written
+        const size_t el = dtype == MLSTM_BF16 ? 2 : 4;
+        const size_t tok = heads * (size_t)S;
+        const bool scan = (stages & 2) != 0;
+        const Buf bufs[] = {
+            {need > 0 ? workspace : nullptr, need, "workspace"},
+            {scan ? h_out : nullptr, tok * d_v * el, "h_out"},
+            {scan ? C_final : nullptr, heads * d_v * d_qk * 4, "C_final"},
+            {scan ? n_final : nullptr, heads * d_qk * 4, "n_final"},
+            {scan ? m_final : nullptr, heads * 4, "m_final"},
+            {q, tok * d_qk * el, "q"}, {k, tok * d_qk * el, "k"},
+            {scan ? v : nullptr, tok * d_v * el, "v"},
+            {i_pre, tok * 4, "i_pre"}, {f_pre, tok * 4, "f_pre"},
+            {scan ? o_pre : nullptr, tok * d_v * 4, "o_pre"},
+            {C_init, heads * d_v * d_qk * 4, "C_init"}, {n_init, heads * d_qk * 4, "n_init"},
+            {m_init, heads * 4, "m_init"},
+        };
+        if ((s = check_disjoint(bufs, (int)(sizeof(bufs) / sizeof(bufs[0])), 5)) != MLSTM_OK) return s;
     }
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
@@ -248,6 +290,18 @@ mlstm_status mlstm_step(const void* q, const void* k, const void* v,
         if (!ptrs[p]) return fail(MLSTM_ERR_INVALID_ARG, "%s is NULL", names[p]);
         if (!aligned(ptrs[p], align[p]))
             return fail(MLSTM_ERR_INVALID_ARG, "%s is not %u-byte aligned", names[p], align[p]);
+    }
+    {
+        // C, n and m are updated in place (each element read and written by one
+        // thread) and h is written: none of them may share memory with anything else
+        const size_t heads = (size_t)B * NH;
+        const Buf bufs[] = {
+            {C, heads * d_v * d_qk * 4, "C"}, {n, heads * d_qk * 4, "n"}, {m, heads * 4, "m"},
+            {h_out, heads * d_v * el, "h_out"},
+            {q, heads * d_qk * el, "q"}, {k, heads * d_qk * el, "k"}, {v, heads * d_v * el, "v"},
+            {i_pre, heads * 4, "i_pre"}, {f_pre, heads * 4, "f_pre"}, {o_pre, heads * d_v * 4, "o_pre"},
+        };
+        if ((s = check_disjoint(bufs, (int)(sizeof(bufs) / sizeof(bufs[0])), 4)) != MLSTM_OK) return s;
     }
     mlstm::StepArgs a = {};
     a.q = q; a.k = k; a.v = v; a.i_pre = i_pre; a.f_pre = f_pre; a.o_pre = o_pre;

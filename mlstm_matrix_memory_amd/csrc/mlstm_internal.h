@@ -53,6 +53,11 @@ __device__ __forceinline__ float wave_sum(float x) {
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
     return x;
 }
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));

@@ -47,23 +47,30 @@ __global__ __launch_bounds__(STEP_THREADS) void step_kernel(
     const T* kb = k + (size_t)bh * dqk;
 
     // s3: n' <- f' n' + i' k ; den = n' . q   (same thread reads and writes n'[j])
-    __shared__ float red[STEP_WAVES];
+    // The two dot products of the step (n'.q here, C'q below) are accumulated in
+    // fp64: when q is nearly orthogonal to a memory dominated by a few stored
+    // pairs, both cancel, and fp32 accumulation error alone then exceeds the
+    // fp32 path's tolerance.  The updated state elements themselves are fp32 (the
+    // state's storage type), and the dot products are taken of exactly the values
+    // stored, so h is the retrieval from the returned state.  The kernel is bound
+    // by the state's HBM traffic; the fp64 arithmetic hides under it.
+    __shared__ double red[STEP_WAVES];
     float* nb = n + (size_t)bh * dqk;
-    float part = 0.0f;
+    double part = 0.0;
     for (int j = tid * 4; j < dqk; j += STEP_THREADS * 4) {
         f32x4 kk = load4(kb + j), qq = load4(qb + j);
         f32x4 nn = *reinterpret_cast<const f32x4*>(nb + j);
         nn = fs * nn + is * kk;
         *reinterpret_cast<f32x4*>(nb + j) = nn;
-        part += nn[0] * qq[0] + nn[1] * qq[1] + nn[2] * qq[2] + nn[3] * qq[3];
+        part += (double)nn[0] * qq[0] + (double)nn[1] * qq[1] + (double)nn[2] * qq[2] + (double)nn[3] * qq[3];
     }
-    part = wave_sum(part);
+    part = wave_sum_f64(part);
     if (lane == 0) red[wave] = part;
     __syncthreads();  // all reads of m[bh] and n are done past this point
-    float den = 0.0f;
+    double den = 0.0;
 #pragma unroll
     for (int w = 0; w < STEP_WAVES; ++w) den += red[w];
-    const float inv_denom = 1.0f / fmaxf(fabsf(den), exp_arg(-m_t));
+    const double inv_denom = 1.0 / fmax(fabs(den), exp(-m_t));
 
     // this lane's key and query columns, kept in registers for all rows
     f32x4 kr[NJ], qr[NJ];
@@ -97,17 +104,18 @@ __global__ __launch_bounds__(STEP_THREADS) void step_kernel(
                     c[rr][u] = f32x4{0, 0, 0, 0};
             }
         }
-        float acc[STEP_ROWS];
+        double acc[STEP_ROWS];
 #pragma unroll
         for (int rr = 0; rr < STEP_ROWS; ++rr) {
             const int r = r0 + rr;
             const float ivr = (r < dv) ? is * to_f32(vb[r]) : 0.0f;
-            float a = 0.0f;
+            double a = 0.0;
 #pragma unroll
             for (int u = 0; u < NJ; ++u) {
                 f32x4 cn = fs * c[rr][u] + ivr * kr[u];
                 c[rr][u] = cn;
-                a += cn[0] * qr[u][0] + cn[1] * qr[u][1] + cn[2] * qr[u][2] + cn[3] * qr[u][3];
+                a += (double)cn[0] * qr[u][0] + (double)cn[1] * qr[u][1] + (double)cn[2] * qr[u][2] +
+                     (double)cn[3] * qr[u][3];
             }
             acc[rr] = a;
         }
@@ -123,13 +131,13 @@ __global__ __launch_bounds__(STEP_THREADS) void step_kernel(
             }
         }
 #pragma unroll
-        for (int rr = 0; rr < STEP_ROWS; ++rr) acc[rr] = wave_sum(acc[rr]);
+        for (int rr = 0; rr < STEP_ROWS; ++rr) acc[rr] = wave_sum_f64(acc[rr]);
         if (lane < STEP_ROWS) {
-            float mine = acc[0];
+            double mine = acc[0];
 #pragma unroll
             for (int rr = 1; rr < STEP_ROWS; ++rr) if (lane == rr) mine = acc[rr];
             const int r = r0 + lane;
-            if (r < dv) hb[r] = from_f32<T>(sigmoid(ob[r]) * mine * inv_denom);
+            if (r < dv) hb[r] = from_f32<T>(sigmoid(ob[r]) * (float)(mine * inv_denom));
         }
     }
     if (tid == 0) m[bh] = (float)m_t;

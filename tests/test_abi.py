@@ -300,3 +300,66 @@ def test_slstm_rejects_null_and_misaligned(lib):
     assert lib.slstm_fwd(FAKE, FAKE_MIS, 1, 1, 4, 64, 0, b.MLSTM_BF16, None, None, None, None,
                          FAKE, FAKE, FAKE, FAKE, FAKE, None) == b.MLSTM_ERR_INVALID_ARG
     assert "R is not" in b.mlstm_error_detail()
+
+
+def test_long_single_head_runs_as_sequence_segments():
+    """One head of width 256 over 4096 tokens at chunk 128 (the shape the GPU gate-regime
+    tests call "segmented") runs as 8 sequence segments: its workspace holds the 8
+    entering states on top of 16 times the per-token arrays of a 256-token run, which
+    has no segments."""
+    with_seg = b.mlstm_fwd_workspace_bytes(1, 1, 4096, 256, 256, 128, b.MLSTM_BF16)
+    short = b.mlstm_fwd_workspace_bytes(1, 1, 256, 256, 256, 128, b.MLSTM_BF16)
+    assert with_seg - 16 * short >= 8 * 256 * 256 * 4
+
+
+def _fwd_ptrs(lib, ptrs, ws=None, ws_bytes=0):
+    return lib.mlstm_fwd_parallel(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], ptrs[5], 1, 2, 128, 128, 128, 64,
+                                  b.MLSTM_BF16, ptrs[6], ptrs[7], ptrs[8], ptrs[9], ws, ws_bytes, None)
+
+
+# distinct, aligned, far-apart fake addresses for q, k, v, i, f, o, h, C, n, m
+SPREAD = [0x1000000 * (j + 1) for j in range(10)]
+
+
+@pytest.mark.parametrize("out,inp", [(6, 0), (6, 2), (6, 5), (6, 7), (7, 1), (8, 3), (9, 4), (7, 8)])
+def test_fwd_rejects_an_output_overlapping_another_buffer(lib, out, inp):
+    ptrs = list(SPREAD)
+    ptrs[out] = ptrs[inp] + 16          # the output starts inside the other buffer (all hold >= 1 KiB)
+    need = b.mlstm_fwd_workspace_bytes(1, 2, 128, 128, 128, 64, b.MLSTM_BF16)
+    assert _fwd_ptrs(lib, ptrs, ws=0x40000000, ws_bytes=need) == b.MLSTM_ERR_INVALID_ARG
+    assert "overlaps" in b.mlstm_error_detail()
+
+
+def test_fwd_accepts_disjoint_buffers_up_to_the_workspace(lib):
+    # all disjoint: validation passes the alias checks and stops at the workspace
+    need = b.mlstm_fwd_workspace_bytes(1, 2, 128, 128, 128, 64, b.MLSTM_BF16)
+    if need == 0:
+        pytest.skip("this configuration needs no workspace")
+    assert _fwd_ptrs(lib, list(SPREAD)) == b.MLSTM_ERR_WORKSPACE
+
+
+@pytest.mark.parametrize("inp", [0, 2, 5, 6])
+def test_fwd_rejects_a_workspace_overlapping_a_tensor(lib, inp):
+    need = b.mlstm_fwd_workspace_bytes(1, 2, 128, 128, 128, 64, b.MLSTM_BF16)
+    if need == 0:
+        pytest.skip("this configuration needs no workspace")
+    ptrs = list(SPREAD)
+    assert _fwd_ptrs(lib, ptrs, ws=ptrs[inp] + 256, ws_bytes=need) == b.MLSTM_ERR_INVALID_ARG
+    assert "workspace overlaps" in b.mlstm_error_detail()
+
+
+def _step_ptrs(lib, ptrs):
+    return lib.mlstm_step(ptrs[0], ptrs[1], ptrs[2], ptrs[3], ptrs[4], ptrs[5], 2, 2, 64, 32, b.MLSTM_BF16,
+                          ptrs[6], ptrs[7], ptrs[8], ptrs[9], None)
+
+
+@pytest.mark.parametrize("out,inp", [(9, 6), (9, 0), (6, 7), (7, 1), (8, 3), (6, 2)])
+def test_step_rejects_state_or_output_overlapping_another_buffer(lib, out, inp):
+    ptrs = list(SPREAD)          # q, k, v, i, f, o, C, n, m, h
+    # inside the other buffer, at an offset that keeps the alignment the output needs
+    # (C and n: 16 bytes; the smallest buffers, i, f and m, hold 4 floats = 16 bytes)
+    ptrs[out] = ptrs[inp] + (16 if inp not in (3, 4, 8) and out in (6, 7) else 4)
+    if out in (6, 7) and inp in (3, 4, 8):
+        ptrs[out] = ptrs[inp]
+    assert _step_ptrs(lib, ptrs) == b.MLSTM_ERR_INVALID_ARG
+    assert "overlaps" in b.mlstm_error_detail()

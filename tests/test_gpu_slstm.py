@@ -36,9 +36,11 @@ def _compare(orc, x, dtype, forget=0, state=None):
     if dtype == "bf16":
         ref[0] = inputs.bf16_round(ref[0].astype(np.float32)).astype(np.float64)   # h is stored in bf16
     errs = {}
-    # c and n are stabilized states whose scale follows m; compare the ratio c/n
-    # (what h is made of) and m itself, then h and the last hidden state
+    # c and n are the stabilized states (c e^{-m}, n e^{-m}); once m matches, each is
+    # fixed on its own, so each is compared, and so is their ratio (what h is made of)
     check("h", got[0], ref[0], TOL[dtype], errs)
+    check("c", got[1], ref[1], TOL[dtype], errs)
+    check("n", got[2], ref[2], TOL[dtype], errs)
     check("c/n", got[1] / got[2], ref[1] / ref[2], TOL[dtype], errs)
     check("m", got[3], ref[3], TOL[dtype], errs)
     check("h_last", got[4], ref[4], TOL[dtype], errs)

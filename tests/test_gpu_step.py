@@ -34,6 +34,9 @@ def _run_steps(orc, w, steps, dtype, B, NH, dqk, dv, seed, sample_heads=None):
     torch.cuda.synchronize()
     h_gpu = np.stack([to_np(h) for h in hs])
     C_gpu, n_gpu, m_gpu = to_np(C), to_np(n), to_np(m)
+    # every head, sampled by the oracle or not, stays finite through all the steps
+    for name, a in (("h", h_gpu), ("C", C_gpu), ("n", n_gpu), ("m", m_gpu)):
+        assert np.all(np.isfinite(a)), f"{name} is not finite"
     # oracle, optionally on a subset of heads
     if sample_heads is None:
         sel = (slice(None), slice(None))
