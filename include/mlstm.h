@@ -129,6 +129,33 @@ mlstm_status mlstm_fwd_parallel(const void *q, const void *k, const void *v,
                                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * mlstm_fwd_parallel for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, layouts, results and rules as mlstm_fwd_parallel, without the
+ * workspace: the kernels use instead a scratch array the library holds in device
+ * memory, one per GPU, of mlstm_fwd_noalloc_scratch_bytes() bytes (64 MiB),
+ * kept from the first call on that GPU until the process ends.  The call itself
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine); the
+ * first call on a device looks up that device's copy of the array once.
+ *   - A forward whose workspace (mlstm_fwd_workspace_bytes) exceeds the scratch
+ *     is rejected with MLSTM_ERR_UNSUPPORTED before anything is enqueued (the
+ *     1.3B-class layer, B=4 NH=4 S=2048 d=1024, needs about 13 MB).
+ *   - Every call on one GPU shares its array: calls that overlap in time on one
+ *     GPU (two streams, or two threads) race and corrupt each other's results.
+ *     Serialize them.  The scratch needs no clearing between calls (every byte
+ *     the kernels read is written first by the same call).
+ *   - The current HIP device must be the GPU the tensors and stream belong to.
+ */
+size_t mlstm_fwd_noalloc_scratch_bytes(void);
+mlstm_status mlstm_fwd_parallel_noalloc(const void *q, const void *k, const void *v,
+                                        const float *i_pre, const float *f_pre, const float *o_pre,
+                                        int B, int NH, int S, int d_qk, int d_v, int chunk,
+                                        mlstm_dtype dtype,
+                                        void *h_out, float *C_final, float *n_final, float *m_final,
+                                        void *stream);
+
+/*
  * Chunkwise parallel forward that continues from a given stabilized state and
  * accepts any sequence length (section 2.3: the recurrence carried across the
  * chunks of the parallel form; a sequence split anywhere and run piece by piece,

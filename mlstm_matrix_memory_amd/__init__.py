@@ -4,6 +4,8 @@ Entry points (same names as include/mlstm.h):
   mlstm_fwd_parallel  chunkwise parallel forward over whole sequences
   mlstm_fwd_parallel_state
                       the same from a given state, for any sequence length
+  mlstm_fwd_parallel_noalloc, mlstm_fwd_noalloc_scratch_bytes
+                      mlstm_fwd_parallel for callers that cannot allocate (a per-GPU scratch array)
   mlstm_fwd_prepare, mlstm_fwd_scan
                       the two stages of mlstm_fwd_parallel, for callers that schedule them apart
   mlstm_step          one-token recurrent decode step, state updated in place
@@ -27,7 +29,9 @@ from .binding import (  # noqa: F401
     mlstm_bwd_workspace_bytes,
     mlstm_block_epilogue,
     mlstm_error_detail,
+    mlstm_fwd_noalloc_scratch_bytes,
     mlstm_fwd_parallel,
+    mlstm_fwd_parallel_noalloc,
     mlstm_fwd_parallel_state,
     mlstm_fwd_prepare,
     mlstm_fwd_scan,

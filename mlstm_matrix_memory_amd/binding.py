@@ -54,6 +54,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mlstm_fwd_parallel_state.restype = i
     lib.mlstm_fwd_parallel_state.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, i,
                                              fp, fp, fp, vp, fp, fp, fp, vp, sz, vp]
+    lib.mlstm_fwd_noalloc_scratch_bytes.restype = sz
+    lib.mlstm_fwd_noalloc_scratch_bytes.argtypes = []
+    lib.mlstm_fwd_parallel_noalloc.restype = i
+    lib.mlstm_fwd_parallel_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, i, i, i,
+                                               vp, fp, fp, fp, vp]
     lib.mlstm_fwd_prepare.restype = i
     lib.mlstm_fwd_prepare.argtypes = [vp, vp, fp, fp, i, i, i, i, i, i, i, vp, sz, vp]
     lib.mlstm_fwd_scan.restype = i
@@ -203,6 +208,46 @@ def mlstm_fwd_parallel(q, k, v, i_pre, f_pre, o_pre, chunk: int,
                                 ws_ptr, ws_bytes, _stream_handle(stream, dev))
     if st != MLSTM_OK:
         raise MlstmError("mlstm_fwd_parallel", st, mlstm_error_detail())
+    return h_out, C_final, n_final, m_final
+
+
+def mlstm_fwd_noalloc_scratch_bytes() -> int:
+    return int(load_library().mlstm_fwd_noalloc_scratch_bytes())
+
+
+def mlstm_fwd_parallel_noalloc(q, k, v, i_pre, f_pre, o_pre, chunk: int, h_out, C_final, n_final, m_final,
+                               stream=None):
+    """mlstm_fwd_parallel without a workspace: the library's per-GPU scratch array
+    serves instead, and nothing is allocated here either (outputs are required).
+    Calls that overlap in time on one GPU race on that array."""
+    import torch
+    lib = load_library()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, NH, S, d]")
+    B, NH, S, dqk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    dt = _dtype_code(q)
+    for t, name, shp, tdt in ((q, "q", (B, NH, S, dqk), q.dtype), (k, "k", (B, NH, S, dqk), q.dtype),
+                              (v, "v", (B, NH, S, dv), q.dtype), (i_pre, "i_pre", (B, NH, S), torch.float32),
+                              (f_pre, "f_pre", (B, NH, S), torch.float32),
+                              (o_pre, "o_pre", (B, NH, S, dv), torch.float32),
+                              (h_out, "h_out", (B, NH, S, dv), q.dtype),
+                              (C_final, "C_final", (B, NH, dv, dqk), torch.float32),
+                              (n_final, "n_final", (B, NH, dqk), torch.float32),
+                              (m_final, "m_final", (B, NH), torch.float32)):
+        if t is None:
+            raise ValueError(f"{name} is required (this entry point allocates nothing)")
+        _check(t, name, shp, tdt, dev)
+    st = lib.mlstm_fwd_parallel_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                        i_pre.data_ptr(), f_pre.data_ptr(), o_pre.data_ptr(),
+                                        B, NH, S, dqk, dv, int(chunk), dt,
+                                        h_out.data_ptr(), C_final.data_ptr(), n_final.data_ptr(),
+                                        m_final.data_ptr(), _stream_handle(stream, dev))
+    if st != MLSTM_OK:
+        raise MlstmError("mlstm_fwd_parallel_noalloc", st, mlstm_error_detail())
     return h_out, C_final, n_final, m_final
 
 

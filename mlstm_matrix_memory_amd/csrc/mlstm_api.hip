@@ -5,6 +5,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "mlstm_internal.h"
 
 namespace {
@@ -123,6 +125,41 @@ mlstm_status check_disjoint(const Buf* bufs, int n, int n_out) {
                 return fail(MLSTM_ERR_INVALID_ARG, "%s overlaps %s", bufs[o].name, bufs[i].name);
         }
     }
+    return MLSTM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free forward (mlstm_fwd_parallel_noalloc)
+// ---------------------------------------------------------------------------
+// One file-scope device array per GPU, held until the process ends.  In host code
+// the name `scratch` is only a stand-in for the symbol: its device address, which
+// differs per GPU, is looked up once per device with hipGetSymbolAddress and only
+// that address is ever handed to kernels.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of this GPU's scratch array (the current device), or an error.
+mlstm_status scratch_for_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(MLSTM_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= MAX_DEVICES)
+        return fail(MLSTM_ERR_UNSUPPORTED, "device %d is beyond the %d devices the scratch table covers", dev,
+                    MAX_DEVICES);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(MLSTM_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                        hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
     return MLSTM_OK;
 }
 
@@ -254,6 +291,29 @@ mlstm_status mlstm_fwd_parallel_state(const void* q, const void* k, const void* 
                                       void* workspace, size_t workspace_bytes, void* stream) {
     return fwd_common(q, k, v, i_pre, f_pre, o_pre, B, NH, S, d_qk, d_v, chunk, dtype, C_init, n_init, m_init,
                       h_out, C_final, n_final, m_final, workspace, workspace_bytes, stream, 3, true);
+}
+
+size_t mlstm_fwd_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+mlstm_status mlstm_fwd_parallel_noalloc(const void* q, const void* k, const void* v,
+                                        const float* i_pre, const float* f_pre, const float* o_pre,
+                                        int B, int NH, int S, int d_qk, int d_v, int chunk,
+                                        mlstm_dtype dtype,
+                                        void* h_out, float* C_final, float* n_final, float* m_final,
+                                        void* stream) {
+    // sizes first: a call the scratch array cannot serve is rejected before any HIP call
+    mlstm_status s = check_fwd_sizes(B, NH, S, d_qk, d_v, chunk, dtype, false);
+    if (s != MLSTM_OK) return s;
+    const size_t need = plan_fwd(B, NH, S, d_qk, d_v, chunk, dtype).total();
+    if (need > NOALLOC_SCRATCH_BYTES)
+        return fail(MLSTM_ERR_UNSUPPORTED,
+                    "this forward needs %zu bytes of scratch; the allocation-free entry point holds %zu "
+                    "(use mlstm_fwd_parallel with a caller-provided workspace)",
+                    need, NOALLOC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if (need > 0 && (s = scratch_for_current_device(&ws)) != MLSTM_OK) return s;
+    return fwd_common(q, k, v, i_pre, f_pre, o_pre, B, NH, S, d_qk, d_v, chunk, dtype, nullptr, nullptr, nullptr,
+                      h_out, C_final, n_final, m_final, ws, need > 0 ? NOALLOC_SCRATCH_BYTES : 0, stream, 3, false);
 }
 
 mlstm_status mlstm_fwd_prepare(const void* q, const void* k, const float* i_pre, const float* f_pre,
