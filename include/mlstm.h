@@ -103,6 +103,15 @@ size_t mlstm_fwd_workspace_bytes(int B, int NH, int S, int d_qk, int d_v, int ch
  * from chunk to chunk.  Results agree with the token-by-token recurrence up to
  * rounding for every chunk size.
  *
+ * Where it runs: bf16 inputs with d_qk a multiple of 64 up to 1024 run on the
+ * matrix cores (MFMA), in chunks of 64 tokens (also for chunk = 128, and for
+ * chunk = 16 or 32 except d_qk 128 and 384 at chunk 32, which have tilings of
+ * their own); when S is not a multiple of that, the last S mod 64 tokens run on
+ * the vector-ALU kernel.  fp32 inputs and every other d_qk run entirely on the
+ * vector ALUs, which is correct at every size but two to three orders of
+ * magnitude slower on wide heads (d_qk = 2048: about 0.7 TFLOP/s).  Only the
+ * matrix-core path uses the workspace.
+ *
  * Arguments
  *   q, k, v         inputs, dtype, layouts above (read only)
  *   i_pre, f_pre    input / forget gate pre-activations [B,NH,S] fp32

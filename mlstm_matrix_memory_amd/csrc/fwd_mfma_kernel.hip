@@ -77,26 +77,21 @@ __device__ __forceinline__ float quad_rotate(float x) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xF, 0xF, false));
 }
 
-__device__ __forceinline__ float pick4(f32x4 v, int i) {
-    return i == 0 ? v[0] : i == 1 ? v[1] : i == 2 ? v[2] : v[3];
-}
-
 // 4 x 4 transpose within each quad of lanes.  In the MFMA accumulator layout, quad
 // lane b holds rows 4g..4g+3 (g = lane / 16) of column 4a + b (a = (lane % 16) / 4);
 // afterwards it holds row 4g + b at columns 4a..4a+3, so one 8-byte store writes it.
+// Two exchange stages: lanes b and b ^ 2 swap the registers whose index differs from
+// b in bit 1, then lanes b and b ^ 1 those that differ in bit 0 (a swap of two
+// registers each way per stage: two DPP moves and six selects).
 __device__ __forceinline__ f32x4 quad_transpose(f32x4 y, int b) {
-    f32x4 yr;        // yr[r] = y[(b - r) & 3]: what this lane sends in round r
-#pragma unroll
-    for (int r = 0; r < 4; ++r) yr[r] = pick4(y, (b - r) & 3);
-    f32x4 got;       // got[r] came from quad lane (b + r) & 3, i.e. column (b + r) & 3
-    got[0] = yr[0];
-    got[1] = quad_rotate<1>(yr[1]);
-    got[2] = quad_rotate<2>(yr[2]);
-    got[3] = quad_rotate<3>(yr[3]);
-    f32x4 t;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) t[j] = pick4(got, (j - b) & 3);
-    return t;
+    const bool b2 = (b & 2) != 0, b1 = (b & 1) != 0;
+    const float s0 = b2 ? y[0] : y[2], s1 = b2 ? y[1] : y[3];
+    const float r0 = quad_rotate<2>(s0), r1 = quad_rotate<2>(s1);     // from lane b ^ 2
+    const f32x4 z = {b2 ? r0 : y[0], b2 ? r1 : y[1], b2 ? y[2] : r0, b2 ? y[3] : r1};
+    const float u0 = b1 ? z[0] : z[1], u1 = b1 ? z[2] : z[3];
+    const float q0 = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, u0), 0xB1, 0xF, 0xF, false));
+    const float q1 = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, u1), 0xB1, 0xF, 0xF, false));
+    return f32x4{b1 ? q0 : z[0], b1 ? z[1] : q0, b1 ? q1 : z[2], b1 ? z[3] : q1};   // from lane b ^ 1
 }
 
 // inclusive scans over the lanes of one wave (64 lanes), fp64
@@ -233,7 +228,7 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     __shared__ PrepSmem<L> sm;
 
     const int c = blockIdx.x, bh = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int ln = lane & 15, lg = lane >> 4;
     const size_t tok0 = (size_t)bh * S + (size_t)c * L;     // workspace token index
     const size_t tin0 = (size_t)bh * Sx + (size_t)c * L;    // input token index
@@ -406,7 +401,7 @@ __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int
     __shared__ float salpha[GS_TILE], srl[GS_TILE];
     __shared__ float spart[GS_WAVES][GS_COLS], sprod[GS_WAVES], sfin[GS_COLS];
     const int part = blockIdx.x, nparts = gridDim.x, bh = blockIdx.y;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int nC = S / L;
     const size_t tokh = (size_t)bh * S;
     const int j = part * GS_COLS + lane;
@@ -597,7 +592,7 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
     const int n_kt = dqk / SS_TILE;
     const int kt = blockIdx.x % n_kt, vt = blockIdx.x / n_kt;
     const int g = blockIdx.y / ws.sp, part = blockIdx.y % ws.sp, bh = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int ln = lane & 15, lg = lane >> 4;
     const int wr = wave >> 1, wc = wave & 1;                // 64 keys x 64 values per wave
     const int nC = S / L, nCs = nC / G, nCp = nCs / ws.sp;
@@ -937,7 +932,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
     }
     // workgroup -> (head, sequence segment, value tile)
     const int bh = wg / (G * n_vt), seg = (wg / n_vt) % G, vt = wg % n_vt;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int cb = wave % NC, kq = wave / NC;
     const int ln = lane & 15, lg = lane >> 4;
     // this wave's CW column blocks: tile columns 16 * (CW * cb + x), x < CW
@@ -1270,13 +1265,25 @@ RunFn pick(int L, int dqk) {
     // d_qk 1024, whose eight-wave tiling spills a little and still measured
     // fastest (lm 1.3B-class layer shape: 618 us against 660 us for four waves).
     // The transposed row stores save the d_qk 1024 tiling about 7% (its store
-    // traffic per slab is the heaviest) and cost the narrower ones about 3%.
+    // traffic per slab is the heaviest) and make no measurable difference on the
+    // narrower ones.
     MLSTM_V2(32, 128, 4, 1, 128, 1, 1, false)
     MLSTM_V2(32, 384, 3, 1, 128, 1, 1, false)
+    MLSTM_V2(64, 64, 4, 1, 64, 1, 1, false)
     MLSTM_V2(64, 128, 4, 1, 128, 1, 1, false)
+    MLSTM_V2(64, 192, 4, 2, 32, 1, 1, false)
     MLSTM_V2(64, 256, 4, 2, 32, 1, 1, false)
+    MLSTM_V2(64, 320, 4, 2, 32, 1, 1, false)
     MLSTM_V2(64, 384, 4, 2, 32, 1, 1, false)
+    MLSTM_V2(64, 448, 4, 2, 32, 1, 1, false)
     MLSTM_V2(64, 512, 4, 2, 32, 1, 1, false)
+    MLSTM_V2(64, 576, 4, 2, 32, 1, 1, false)
+    MLSTM_V2(64, 640, 2, 4, 32, 1, 1, true)
+    MLSTM_V2(64, 704, 4, 2, 32, 1, 1, false)
+    MLSTM_V2(64, 768, 2, 4, 32, 1, 1, true)
+    MLSTM_V2(64, 832, 4, 2, 32, 1, 1, false)
+    MLSTM_V2(64, 896, 2, 4, 32, 1, 1, true)
+    MLSTM_V2(64, 960, 4, 2, 32, 1, 1, false)
     MLSTM_V2(64, 1024, 2, 4, 32, 1, 1, true)
 #undef MLSTM_V2
     return nullptr;
@@ -1284,13 +1291,26 @@ RunFn pick(int L, int dqk) {
 
 // The chunk size only sets how the recurrence is re-associated: every chunk size
 // gives the same result up to rounding.  A 128-token chunk is computed as two
-// consecutive 64-token chunks, whose tiles fit the LDS and register budget.
-int mfma_chunk(const FwdArgs& a) { return a.chunk == 128 ? 64 : a.chunk; }
+// consecutive 64-token chunks, whose tiles fit the LDS and register budget; a
+// 16- or 32-token chunk for a width with no tiling at that chunk is computed in
+// 64-token chunks.
+int mfma_chunk(const FwdArgs& a) {
+    if (a.chunk == 128) return 64;
+    if (pick(a.chunk, a.dqk) != nullptr) return a.chunk;
+    return 64;
+}
 
 }  // namespace
 
+int mfma_fwd_chunk(const FwdArgs& a) {
+    if (a.dtype != MLSTM_BF16) return 0;
+    const int L = mfma_chunk(a);
+    return pick(L, a.dqk) != nullptr ? L : 0;
+}
+
 bool mfma_fwd_supported(const FwdArgs& a) {
-    return a.dtype == MLSTM_BF16 && a.S % a.chunk == 0 && pick(mfma_chunk(a), a.dqk) != nullptr;
+    const int L = mfma_fwd_chunk(a);
+    return L > 0 && a.S % L == 0;
 }
 
 size_t mfma_fwd_workspace_bytes(const FwdArgs& a) {

@@ -73,10 +73,11 @@ mlstm::FwdArgs make_fwd_args(int B, int NH, int S, int dqk, int dv, int chunk, m
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// How a forward over S tokens runs: the longest multiple of the chunk on the bf16
-// MFMA path when it covers the shape, the rest (a ragged tail, or everything on
-// the fp32 path and on shapes the MFMA path does not cover) on the VALU kernel.
-// Between the two, the state passes through the workspace.
+// How a forward over S tokens runs: the longest multiple of the chunk the bf16
+// MFMA path executes (see mfma_fwd_chunk) on that path when it covers the shape,
+// the rest (a ragged tail, or everything on the fp32 path and on shapes the MFMA
+// path does not cover) on the VALU kernel.  Between the two, the state passes
+// through the workspace.
 struct FwdPlan {
     int S_main;             // tokens on the MFMA path (0 = none)
     bool tail;              // the VALU kernel runs over [S_main, S)
@@ -87,7 +88,8 @@ struct FwdPlan {
 
 FwdPlan plan_fwd(int B, int NH, int S, int dqk, int dv, int chunk, mlstm_dtype dt) {
     FwdPlan pl = {};
-    const int S_main = S - S % chunk;
+    const int L = mlstm::mfma_fwd_chunk(make_fwd_args(B, NH, S, dqk, dv, chunk, dt));
+    const int S_main = L > 0 ? S - S % L : 0;
     mlstm::FwdArgs a = make_fwd_args(B, NH, S_main, dqk, dv, chunk, dt);
     if (S_main > 0 && dt == MLSTM_BF16 && mlstm::mfma_fwd_supported(a)) {
         pl.S_main = S_main;

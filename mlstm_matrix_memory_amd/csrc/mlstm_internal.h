@@ -48,6 +48,11 @@ __device__ __forceinline__ double log_sigmoid_f64(double x) {
 __device__ __forceinline__ float exp_arg(double x) { return expf((float)x); }
 
 // ---- wavefront helpers (64 lanes) ------------------------------------------
+// Index of the calling wave in its workgroup as a wave-uniform (scalar) value:
+// branches and addresses that depend only on it then compile to scalar code,
+// not to per-lane exec-mask manipulation.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
@@ -162,6 +167,7 @@ size_t valu_fwd_workspace_bytes(const FwdArgs& a);
 hipError_t launch_fwd_valu(const FwdArgs& a);
 
 // chunkwise forward on bf16 MFMA (bf16 inputs, shapes it supports)
+int mfma_fwd_chunk(const FwdArgs& a);          // chunk the MFMA path executes for these widths, 0 = none
 bool mfma_fwd_supported(const FwdArgs& a);
 size_t mfma_fwd_workspace_bytes(const FwdArgs& a);
 hipError_t launch_fwd_mfma_prepare(const FwdArgs& a);

@@ -363,3 +363,16 @@ def test_step_rejects_state_or_output_overlapping_another_buffer(lib, out, inp):
         ptrs[out] = ptrs[inp]
     assert _step_ptrs(lib, ptrs) == b.MLSTM_ERR_INVALID_ARG
     assert "overlaps" in b.mlstm_error_detail()
+
+
+@pytest.mark.parametrize("S,dqk,chunk", [(256, 256, 16), (256, 768, 16), (256, 640, 64), (256, 896, 64),
+                                         (256, 1024, 32), (300, 384, 16), (256, 64, 64), (256, 960, 128)])
+def test_bf16_widths_with_a_tiling_take_the_matrix_core_path(S, dqk, chunk):
+    # only the MFMA path uses a workspace; chunks without a tiling of their own at a
+    # width run as 64-token chunks (S = 300: 256 tokens there, a 44-token tail after)
+    assert b.mlstm_fwd_workspace_bytes(1, 2, S, dqk, 64, chunk, b.MLSTM_BF16) > 0
+
+
+@pytest.mark.parametrize("dqk,chunk,dt", [(2048, 64, b.MLSTM_BF16), (96, 64, b.MLSTM_BF16), (256, 64, b.MLSTM_F32)])
+def test_shapes_without_a_tiling_run_on_the_vector_alus(dqk, chunk, dt):
+    assert b.mlstm_fwd_workspace_bytes(1, 2, 256, dqk, 64, chunk, dt) == 0

@@ -79,7 +79,12 @@ def test_bf16_chunk_sweep(orc, chunk):
 # every (chunk, d_qk) the bf16 MFMA path has a tiling for, each with a d_v that
 # leaves a partial value tile (d_v not a multiple of the tile width)
 MFMA_SHAPES = [(32, 128, 80), (32, 384, 112), (64, 128, 96), (64, 256, 272), (64, 384, 400),
-               (64, 512, 80), (64, 1024, 48), (128, 128, 96), (128, 256, 144)]
+               (64, 512, 80), (64, 640, 64), (64, 768, 96), (64, 896, 32), (64, 1024, 48), (128, 128, 96),
+               (64, 64, 48), (64, 192, 208), (64, 320, 64), (64, 448, 96), (64, 576, 80), (64, 704, 32),
+               (64, 832, 64), (64, 960, 112),
+               (128, 256, 144),
+               # chunks with no tiling of their own at that width run as 64-token chunks
+               (16, 256, 80), (16, 768, 48), (32, 1024, 64)]
 
 
 @pytest.mark.parametrize("chunk,dqk,dv", MFMA_SHAPES, ids=lambda v: str(v))
