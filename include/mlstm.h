@@ -110,7 +110,9 @@ size_t mlstm_fwd_workspace_bytes(int B, int NH, int S, int d_qk, int d_v, int ch
  * the vector-ALU kernel.  fp32 inputs and every other d_qk run entirely on the
  * vector ALUs, which is correct at every size but two to three orders of
  * magnitude slower on wide heads (d_qk = 2048: about 0.7 TFLOP/s).  Only the
- * matrix-core path uses the workspace.
+ * matrix-core path uses the workspace; at d_qk 512 and 1024 it also holds copies
+ * of q and k in the order the matrix-core operands are read (2 * B*NH*S*d_qk
+ * bf16 elements).
  *
  * Arguments
  *   q, k, v         inputs, dtype, layouts above (read only)
@@ -143,7 +145,7 @@ mlstm_status mlstm_fwd_parallel(const void *q, const void *k, const void *v,
  *
  * Same arguments, layouts, results and rules as mlstm_fwd_parallel, without the
  * workspace: the kernels use instead a scratch array the library holds in device
- * memory, one per GPU, of mlstm_fwd_noalloc_scratch_bytes() bytes (64 MiB),
+ * memory, one per GPU, of mlstm_fwd_noalloc_scratch_bytes() bytes (160 MiB),
  * kept from the first call on that GPU until the process ends.  The call itself
  * allocates nothing (no hipMalloc, hipFree or allocating library routine); the
  * first call on a device looks up that device's copy of the array once.

@@ -7,10 +7,11 @@
 // Two stages.  The prepare stage is parallel over chunks: chunk_prep (below),
 // then gate_scan (the stabilizer and normalizer carried across chunks, which fix
 // every per-token weight) and den_kernel (the full normalizer n'.q of every row).
-// The scan stage is sequential over chunks: chunk_scan2, preceded for few heads
-// over long sequences by seg_state and seg_combine, which let independent
-// sequence segments start from their own entering states.  The two kernels that
-// carry the work, both on bf16 MFMA with fp32 accumulation:
+// The scan stage is sequential over chunks: chunk_scan2 (pipelined form), or at
+// d_qk 512 and 1024 chunk_scan4 (streaming form, see its comment), preceded for
+// few heads over long sequences by seg_state and seg_combine, which let
+// independent sequence segments start from their own entering states.  The two
+// kernels that carry the work, both on bf16 MFMA with fp32 accumulation:
 //
 // 1. chunk_prep (one workgroup per (head, chunk), all chunks in parallel)
 //      b_tau     = in-chunk cumulative sum of log sigmoid(f~)
@@ -50,6 +51,8 @@
 // hi = bf16(x), lo = bf16(x - hi) (about 2^-17 relative together) and its
 // product is taken as two MFMAs sharing the exact operand.
 #include "mlstm_internal.h"
+#include <climits>
+#include <type_traits>
 
 namespace mlstm {
 namespace {
@@ -138,6 +141,11 @@ struct Ws {
     float* cst;     // [heads][G][DV][DQ]  state entering each sequence segment (slot 0: the initial one)
     float* cpart;   // [heads][G-1][SP][DV][DQ]  sums over the SP token parts of each segment but the last
     int sp;         // token parts per segment in seg_state_kernel
+    // Q and K of each 64-token chunk in MFMA operand order (streaming scan only, else
+    // null): [heads][chunk][DQ/32][4][64 lanes][8], one 1 KB fragment per 32-key step
+    // and operand block, so that a wave reads each fragment as one contiguous load
+    bf16* qs;
+    bf16* ks;
 };
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -154,7 +162,7 @@ inline int seg_parts(size_t heads, size_t nC, int DQ, int DV, int G) {
     return P;
 }
 
-inline size_t ws_walk(void* base, size_t heads, size_t S, int L, int DQ, int DV, int G, Ws* out) {
+inline size_t ws_walk(void* base, size_t heads, size_t S, int L, int DQ, int DV, int G, bool kt, Ws* out) {
     const size_t nC = S / L;
     char* p = (char*)base;
     size_t off = 0;
@@ -180,16 +188,18 @@ inline size_t ws_walk(void* base, size_t heads, size_t S, int L, int DQ, int DV,
     w.cst = G > 1 ? (float*)take(heads * G * (size_t)DV * DQ * sizeof(float)) : nullptr;
     w.sp = seg_parts(heads, nC, DQ, DV, G);
     w.cpart = G > 1 ? (float*)take(heads * (G - 1) * (size_t)w.sp * DV * DQ * sizeof(float)) : nullptr;
+    w.qs = kt ? (bf16*)take(heads * S * DQ * sizeof(bf16)) : nullptr;
+    w.ks = kt ? (bf16*)take(heads * S * DQ * sizeof(bf16)) : nullptr;
     if (out) *out = w;
     return off;
 }
-inline Ws ws_layout(void* base, size_t heads, size_t S, int L, int DQ, int DV, int G) {
+inline Ws ws_layout(void* base, size_t heads, size_t S, int L, int DQ, int DV, int G, bool kt) {
     Ws w;
-    ws_walk(base, heads, S, L, DQ, DV, G, &w);
+    ws_walk(base, heads, S, L, DQ, DV, G, kt, &w);
     return w;
 }
-inline size_t ws_bytes(size_t heads, size_t S, int L, int DQ, int DV, int G) {
-    return ws_walk(nullptr, heads, S, L, DQ, DV, G, nullptr);
+inline size_t ws_bytes(size_t heads, size_t S, int L, int DQ, int DV, int G, bool kt) {
+    return ws_walk(nullptr, heads, S, L, DQ, DV, G, kt, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -304,6 +314,28 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
         }
         __syncthreads();
         if (j0 + PREP_SB < dqk) slab_load(reg, j0 + PREP_SB);
+        if (L == 64 && ws.qs != nullptr) {
+            // the slab's fragments in MFMA operand order (64-token chunks): per 32-key
+            // step ks, Q block tb (lane (ln, lg): row 16 tb + ln, keys 8 lg .. + 7) and
+            // K^T block (jt, kk) (lane: key 8 (ln / 4) + 4 jt + ln % 4, tokens
+            // 32 kk + 8 lg .. + 7, from two transposing reads)
+            const size_t fr0 = (tok0 * dqk + (size_t)j0 * L) * 2;        // bytes
+#pragma unroll
+            for (int pr = wave; pr < 2 * (PREP_SB / 32) * 4; pr += NW) {
+                const int isk = pr / ((PREP_SB / 32) * 4), rem = pr % ((PREP_SB / 32) * 4);
+                const int kst = rem / 4, f = rem % 4;
+                bf16x8 frag;
+                if (!isk) {
+                    frag = *reinterpret_cast<const bf16x8*>(sm.q + (16 * f + ln) * PREP_KP + 32 * kst + 8 * lg);
+                } else {
+                    const int jt = f / 2, kk = f % 2;
+                    const bf16* kp = sm.k + (32 * kk + 8 * lg + (ln >> 2)) * PREP_KP + 32 * kst + 8 * (ln & 3) + 4 * jt;
+                    frag = cat(lds_read_tr(kp), lds_read_tr(kp + 4 * PREP_KP));
+                }
+                char* dst = reinterpret_cast<char*>(isk ? ws.ks : ws.qs) + fr0 + ((size_t)kst * 4 + f) * 1024 + lane * 16;
+                *reinterpret_cast<bf16x8*>(dst) = frag;
+            }
+        }
         // raw scores of this wave's causal blocks, contracted over the slab
 #pragma unroll
         for (int r = 0; r < TBW; ++r) {
@@ -816,7 +848,7 @@ __device__ __forceinline__ void slab_load(f32x4 (&reg)[Pref<C>::NSL], int tid, c
     constexpr int NQ = Pref<C>::NQ;
     auto src_off = [&](int idx) {
         const int row = idx / (C::SW / 8), c8 = 8 * (idx % (C::SW / 8));
-        return (t0 + row) * C::DQ + (c8 / C::SB) * C::DP + s * C::SB + (c8 % C::SB);
+        return (t0 + row) * C::DQ + s * C::SW + c8;
     };
     for_units<C::THREADS, C::U_Q, 0>(tid, [&](int idx, int u) {
         reg[u] = *reinterpret_cast<const f32x4*>(qh + src_off(idx));
@@ -915,7 +947,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
     bf16* __restrict__ h, float* __restrict__ Cout, float* __restrict__ nout, float* __restrict__ mout)
 {
     constexpr int L = C::L, DQ = C::DQ, NC = C::NC, NK = C::NK, SB = C::SB, CW = C::CW;
-    constexpr int THREADS = C::THREADS, TV = C::TV, DP = C::DP, NS = C::NS;
+    constexpr int THREADS = C::THREADS, TV = C::TV, NS = C::NS;
     constexpr int QP = C::QP, KP = C::KP, VP = C::VP, PP = C::PP, OP = C::OP;
     constexpr int LB = C::LB, SBB = C::SBB, NSB = C::NSB;
     // Lazy decay: the registers hold C^ = C' / sigma; each chunk's decay alpha is
@@ -965,7 +997,9 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
         return cs;
     };
 
-    // state: st[x][jb] holds key rows j = kq*DP + 16*jb + 4*lg + i, value column vcol + 16x + ln
+    // state: st[x][jb] holds key rows j = s*SW + kq*SB + 16*jj + 4*lg + i (jb = s*SBB + jj), value
+    // column vcol + 16x + ln.  A slab is NK*SB consecutive keys, so its rows are read as
+    // whole cache lines, and key part kq takes its SB columns.
     f32x4 st[CW][NSB];
 #pragma unroll
     for (int x = 0; x < CW; ++x)
@@ -974,7 +1008,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
             st[x][jb] = f32x4{0, 0, 0, 0};
             if (Cin && act[x])
                 st[x][jb] = *reinterpret_cast<const f32x4*>(
-                    Cin + (size_t)(vcol + 16 * x + ln) * DQ + kq * DP + 16 * jb + 4 * lg);
+                    Cin + (size_t)(vcol + 16 * x + ln) * DQ + (jb / SBB) * C::SW + kq * SB + 16 * (jb % SBB) + 4 * lg);
         }
 
     f32x4 rs[Pref<C>::NSL], rc[Pref<C>::NCH];
@@ -1169,8 +1203,389 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
         if (!act[x]) continue;
 #pragma unroll
         for (int jb = 0; jb < NSB; ++jb)
-            *reinterpret_cast<f32x4*>(Cout + ((size_t)bh * dv + vcol + 16 * x + ln) * DQ + kq * DP + 16 * jb + 4 * lg) =
+            *reinterpret_cast<f32x4*>(Cout + ((size_t)bh * dv + vcol + 16 * x + ln) * DQ + (jb / SBB) * C::SW + kq * SB +
+                                      16 * (jb % SBB) + 4 * lg) =
                 st[x][jb] * sigma;
+    }
+    if (vt == 0) {
+        for (int j = tid; j < DQ; j += THREADS) nout[(size_t)bh * DQ + j] = ws.nfin[(size_t)bh * DQ + j];
+        if (tid == 0) mout[bh] = ws.mfin[bh];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// kernel 2, streaming form (64-token chunks)
+// ---------------------------------------------------------------------------
+// Every wave owns all TV value columns of the tile and DP = DQ/NK key rows of C'^T,
+// so each element of Q and K is needed by exactly one wave: both come from global
+// memory (L2) straight into that wave's MFMA operand registers, in the
+// operand-ordered copies chunk_prep writes (one contiguous 1 KB load per operand
+// block), and the key dimension needs no LDS staging and no barriers.  Per chunk a
+// wave makes two sweeps over its key rows: the retrieval Q C'^T of the state
+// entering the chunk, then the update C' += K^T ((w / sigma') V).  The partial
+// retrievals of the NK key parts go to LDS; each wave finishes the output rows of
+// the blocks it owns during the next chunk's retrieval sweep, so the one barrier
+// per chunk sits at its end.  The chunk's V tile and (w / sigma') (.) V, split into
+// bf16 hi + lo, are formed once per workgroup at the end of the previous chunk.
+//
+// Key order.  The state block pair (2s, 2s+1) of a wave covers its key rows
+// 32s .. 32s+31; block 2s + jt holds key 32s + 8(r/4) + 4jt + r%4 in accumulator
+// row r.  Lane l then holds keys 32s + 8(l/16) .. + 7 of the pair (rows 4(l/16)+i
+// of both blocks), which is exactly the B operand layout of the retrieval against
+// 8 consecutive keys of a Q row, and the update's A operand row r of block 2s + jt
+// is the token-contiguous K^T row of that key.
+//
+// Loads are branch free (indices past the last chunk are clamped to it) and each
+// step's prefetch is pinned before its products, so the compiler can count the
+// loads in flight instead of draining them at every step.
+template <int DQ_, int NK_, int CW_, int MINB_, int PD_, bool OP_ = true>
+struct Scan4Cfg {
+    static constexpr int L = 64, DQ = DQ_, NK = NK_, CW = CW_, MINB = MINB_;
+    static constexpr bool OUT_PREFETCH = OP_;   // output operands loaded a chunk ahead
+    static constexpr int PD = PD_;              // operand steps in flight ahead of the one multiplied
+    static constexpr int THREADS = 64 * NK, TV = 16 * CW;
+    static constexpr int DP = DQ / NK;          // key rows per wave
+    static constexpr int NS = DP / 32;          // 32-key steps per wave
+    static constexpr int LB = L / 16;           // 16-row blocks of the chunk
+    static constexpr int NB = LB * CW;          // output blocks of the tile
+    static constexpr int NOWN = (NB + NK - 1) / NK;
+    static constexpr int VP = TV + 16;          // tile pitch: 4 rows of a transposing read hit distinct banks
+    static constexpr int U_V = L * TV / 8;      // 16-byte units of the V tile
+    static constexpr int NPV = (U_V + THREADS - 1) / THREADS;
+    static constexpr int RED = NB * (NK - 1) * 256;   // floats of one partial-sum buffer (owners keep theirs)
+    static constexpr size_t TILES = 7 * (size_t)L * VP * 2;
+    static_assert(MINB * (TILES + 2 * (size_t)RED * 4) <= 160 * 1024, "LDS");
+    static_assert(DQ % NK == 0 && DP % 32 == 0, "key parts of whole 32-key steps");
+    static_assert(TV % 32 == 0, "tile pitch");
+    static_assert(THREADS <= 1024, "workgroup too large");
+    static_assert(PD >= 1 && PD <= 2 * NS, "prefetch depth within one chunk's steps");
+};
+
+// raw buffer loads (16 bytes): descriptor word 3 of an untyped buffer on gfx9-family
+// parts; reads past the descriptor's byte count return zeros
+constexpr int BUF_DWORD3 = 0x00020000;
+__device__ __forceinline__ bf16x8 buf_load16(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+template <class C>
+struct alignas(16) Scan4Smem {
+    alignas(16) bf16 v[3][C::L * C::VP];     // V tile of the chunk
+    alignas(16) bf16 vwh[2][C::L * C::VP];   // (w / sigma') (.) V, bf16 hi
+    alignas(16) bf16 vwl[2][C::L * C::VP];   // and lo
+    alignas(16) float red[2][C::RED];
+};
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan4_kernel(
+    const bf16* __restrict__ q, const bf16* __restrict__ v,
+    const float* __restrict__ o_pre, Ws ws, int S, int Sx, int G, int dv, int n_vt, int remap,
+    const float* __restrict__ C0,
+    bf16* __restrict__ h, float* __restrict__ Cout, float* __restrict__ nout, float* __restrict__ mout)
+{
+    constexpr int L = C::L, DQ = C::DQ, NK = C::NK, CW = C::CW;
+    constexpr int THREADS = C::THREADS, TV = C::TV, DP = C::DP, NS = C::NS;
+    constexpr int LB = C::LB, NB = C::NB, VP = C::VP, PD = C::PD;
+    constexpr float SIGMA_MIN = 0x1p-60f;
+    __shared__ Scan4Smem<C> sm;
+
+    int wg = blockIdx.x;
+    if (remap) {
+        const int NG = gridDim.x;
+        wg = (wg % 8) * (NG / 8) + wg / 8;
+    }
+    const int bh = wg / (G * n_vt), seg = (wg / n_vt) % G, vt = wg % n_vt;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int ln = lane & 15, lg = lane >> 4;
+    const int vcol = vt * TV;
+    const int vcols = min(TV, dv - vcol);
+    const int nC = S / L / G;
+    const int nCh = S / L;
+
+    const size_t tokh = (size_t)bh * S + (size_t)seg * (S / G);
+    const size_t tinh = (size_t)bh * Sx + (size_t)seg * (S / G);
+    const size_t ch0 = (size_t)bh * nCh + (size_t)seg * nC;       // global chunk index of chunk 0
+    const float* Cin = G == 1 ? (C0 ? C0 + (size_t)bh * dv * DQ : nullptr)
+                              : ws.cst + ((size_t)bh * G + seg) * (size_t)dv * DQ;
+    const int kw = wave * DP;                                      // this wave's first key row
+    // Q and K^T come in the operand-ordered copies chunk_prep writes: the fragment of
+    // 32-key step ks and block f of chunk c is 1 KB at ((c * DQ/32 + ks) * 4 + f) KB of
+    // the segment, lane l's 16 bytes at l * 16.  Q block tb: row 16 tb + ln, keys
+    // 32 ks + 8 lg .. + 7; K^T block 2 jt + kk: key 32 ks + 8 (ln / 4) + 4 jt + ln % 4,
+    // tokens 32 kk + 8 lg .. + 7.  Buffer descriptors keep every offset but the lane's
+    // in scalar registers.
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(ws.qs + tokh * DQ), (short)0, (int)((size_t)nC * L * DQ * 2), BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(ws.ks + tokh * DQ), (short)0, (int)((size_t)nC * L * DQ * 2), BUF_DWORD3);
+    const int vl = lane * 16;
+    constexpr int KSTEPS = DQ / 32;
+
+    // state: st[x][2s + jt][i] = C^[key kw + 32s + 8lg + 4jt + i][column vcol + 16x + ln]
+    f32x4 st[CW][2 * NS];
+#pragma unroll
+    for (int x = 0; x < CW; ++x)
+#pragma unroll
+        for (int b = 0; b < 2 * NS; ++b) {
+            st[x][b] = f32x4{0, 0, 0, 0};
+            if (Cin && 16 * x < vcols)
+                st[x][b] = *reinterpret_cast<const f32x4*>(
+                    Cin + (size_t)(vcol + 16 * x + ln) * DQ + kw + 32 * (b / 2) + 8 * lg + 4 * (b % 2));
+        }
+
+    // operand stream: step t < NS of a chunk is Q step t, NS <= t < 2NS is K^T step
+    // t - NS; PD steps are in flight while one is multiplied
+    auto load_step = [&](bf16x8 (&r)[4], int c, int t) {
+        const bool isq = t < NS;
+        const int so = ((c * KSTEPS + wave * NS + (isq ? t : t - NS)) * 4) * 1024;
+#pragma unroll
+        for (int f = 0; f < 4; ++f) r[f] = buf_load16(isq ? rq : rk, vl, so + f * 1024);
+    };
+    bf16x8 ring[PD][4];
+#pragma unroll
+    for (int p = 0; p < PD; ++p) load_step(ring[p], 0, p);
+    auto advance = [&](bf16x8 (&cur)[4], int c, int cn, int t) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cur[i] = ring[0][i];
+#pragma unroll
+        for (int p = 0; p + 1 < PD; ++p)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ring[p][i] = ring[p + 1][i];
+        const int tn = t + PD;
+        if (tn < 2 * NS) load_step(ring[PD - 1], c, tn);
+        else load_step(ring[PD - 1], cn, tn - 2 * NS);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // V tile and w of a chunk: loaded into registers one chunk ahead; stored as V
+    // (three buffers: the output rows of chunk c read it during chunk c + 1) and as
+    // (w / sigma') (.) V split into bf16 hi + lo (two buffers)
+    auto load_v = [&](f32x4 (&rv)[C::NPV], float (&rw)[C::NPV], int c) {
+        const size_t t0 = (size_t)c * L;
+#pragma unroll
+        for (int u = 0; u < C::NPV; ++u) {
+            const int idx = min(tid + u * THREADS, C::U_V - 1);
+            const int row = idx / (TV / 8), col = min(8 * (idx % (TV / 8)), vcols - 8);
+            rv[u] = *reinterpret_cast<const f32x4*>(v + (tinh + t0 + row) * dv + vcol + col);
+            rw[u] = ws.w[tokh + t0 + row];
+        }
+    };
+    auto store_v = [&](const f32x4 (&rv)[C::NPV], const float (&rw)[C::NPV], float inv_sig, int c) {
+        bf16* vr = sm.v[c % 3];
+        bf16* vh = sm.vwh[c & 1];
+        bf16* vl2 = sm.vwl[c & 1];
+#pragma unroll
+        for (int u = 0; u < C::NPV; ++u) {
+            const int idx = tid + u * THREADS;
+            if ((C::U_V % THREADS == 0) || idx < C::U_V) {
+                const int row = idx / (TV / 8), col = 8 * (idx % (TV / 8));
+                // columns past d_v hold zeros (their products are never stored)
+                const f32x4 val = col < vcols ? rv[u] : f32x4{0, 0, 0, 0};
+                *reinterpret_cast<f32x4*>(vr + row * VP + col) = val;
+                const bf16x8 vb8 = __builtin_bit_cast(bf16x8, val);
+                const float wi = rw[u] * inv_sig;
+                bf16x8 hh, ll;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float xv = wi * (float)vb8[e];
+                    hh[e] = (bf16)xv;
+                    ll[e] = (bf16)(xv - (float)hh[e]);
+                }
+                *reinterpret_cast<bf16x8*>(vh + row * VP + col) = hh;
+                *reinterpret_cast<bf16x8*>(vl2 + row * VP + col) = ll;
+            }
+        }
+    };
+
+    // sigma: scale of the registers (C^ = C' / sigma) during a chunk's retrieval;
+    // cand, resc, sig_new: the chunk's decay folded in, and whether the registers
+    // are rescaled instead (every thread takes the same decision)
+    float sigma = 1.0f;
+    float cand = ws.alpha[ch0];
+    bool resc = cand < SIGMA_MIN;
+    float sig_new = resc ? 1.0f : cand;
+    {
+        f32x4 rv0[C::NPV];
+        float rw0[C::NPV];
+        load_v(rv0, rw0, 0);
+        store_v(rv0, rw0, 1.0f / sig_new, 0);
+    }
+    f32x4 rv[C::NPV];
+    float rw[C::NPV];
+    load_v(rv, rw, min(1, nC - 1));
+    float alpha_n = ws.alpha[ch0 + min(1, nC - 1)];
+    lds_barrier();
+
+    // Output rows of a chunk are finished during the next chunk's retrieval sweep
+    // (after its first step), from the partial sums the key parts left in LDS, so
+    // that no wave waits for the others between the two sweeps: the one barrier per
+    // chunk is at its end.  Operands of the owned blocks, loaded during the chunk:
+    f32x4 own[C::NOWN];                 // this wave's own partial retrieval
+    bf16x8 pa[C::NOWN][2][2];           // P_loc rows, hi and lo
+    f32x4 ga[C::NOWN], gr[C::NOWN], gd[C::NOWN];
+    float og[C::NOWN][4];
+    float osig = 1.0f;                  // sigma of that chunk's retrieval
+    auto load_out = [&](int c) {
+        const size_t t0 = (size_t)c * L;
+#pragma unroll
+        for (int j = 0; j < C::NOWN; ++j) {
+            const int b = min(wave + NK * j, NB - 1);
+            const int tb = b / CW, x = b % CW;
+            const bf16* P = ws.P + 2 * (tokh + t0) * L + (size_t)(16 * tb + ln) * L + 8 * lg;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                pa[j][kk][0] = *reinterpret_cast<const bf16x8*>(P + 32 * kk);
+                pa[j][kk][1] = *reinterpret_cast<const bf16x8*>(P + L * L + 32 * kk);
+            }
+            const size_t tk = tokh + t0 + 16 * tb + 4 * lg;
+            ga[j] = *reinterpret_cast<const f32x4*>(ws.a + tk);
+            gr[j] = *reinterpret_cast<const f32x4*>(ws.r + tk);
+            gd[j] = *reinterpret_cast<const f32x4*>(ws.rden + tk);
+            const int col = vcol + min(16 * x, vcols - 16) + ln;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) og[j][i] = o_pre[(tinh + t0 + 16 * tb + 4 * lg + i) * dv + col];
+        }
+    };
+    auto output = [&](int c) {
+        const size_t t0 = (size_t)c * L;
+        const float* red = sm.red[c & 1];
+        const bf16* vr = sm.v[c % 3];
+        if (!C::OUT_PREFETCH) load_out(c);
+#pragma unroll
+        for (int j = 0; j < C::NOWN; ++j) {
+            const int b = wave + NK * j;
+            if (b >= NB) continue;
+            const int tb = b / CW, x = b % CW;
+            f32x4 inter = own[j], intra = {0, 0, 0, 0};
+#pragma unroll
+            for (int p = 0; p < NK - 1; ++p)
+                inter += *reinterpret_cast<const f32x4*>(red + (b * (NK - 1) + p) * 256 + lane * 4);
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const bf16* vp = vr + (32 * kk + 8 * lg + (ln >> 2)) * VP + 16 * x + 4 * (ln & 3);
+                const bf16x8 bop = cat(lds_read_tr(vp), lds_read_tr(vp + 4 * VP));
+                intra = mfma(pa[j][kk][0], bop, intra);
+                intra = mfma(pa[j][kk][1], bop, intra);
+            }
+            f32x4 y;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float num = gr[j][i] * intra[i] + ga[j][i] * osig * inter[i];
+                const float o = __builtin_amdgcn_rcpf(1.0f + __expf(-og[j][i]));
+                y[i] = o * num * gd[j][i];
+            }
+            const f32x4 tq = quad_transpose(y, ln & 3);
+            const int col = 16 * x + 4 * (ln >> 2);
+            if (col < vcols)
+                *reinterpret_cast<bf16x4*>(h + (tinh + t0 + 16 * tb + 4 * lg + (ln & 3)) * dv + vcol + col) =
+                    bf16x4{(bf16)tq[0], (bf16)tq[1], (bf16)tq[2], (bf16)tq[3]};
+        }
+    };
+
+    for (int c = 0; c < nC; ++c) {
+        const int cn = min(c + 1, nC - 1);         // chunk whose operands are prefetched at the end
+
+        // --- retrieval sweep: acc = Q C^ over this wave's key rows -------------
+        f32x4 acc[LB][CW];
+#pragma unroll
+        for (int tb = 0; tb < LB; ++tb)
+#pragma unroll
+            for (int x = 0; x < CW; ++x) acc[tb][x] = f32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+            bf16x8 cur[4];
+            advance(cur, c, cn, s);
+            bf16x8 bhi[CW], blo[CW];
+#pragma unroll
+            for (int x = 0; x < CW; ++x) split8(st[x][2 * s], st[x][2 * s + 1], bhi[x], blo[x]);
+#pragma unroll
+            for (int tb = 0; tb < LB; ++tb)
+#pragma unroll
+                for (int x = 0; x < CW; ++x) {
+                    acc[tb][x] = mfma(cur[tb], bhi[x], acc[tb][x]);
+                    acc[tb][x] = mfma(cur[tb], blo[x], acc[tb][x]);
+                }
+            if (s == 0 && c > 0) output(c - 1);
+        }
+        osig = sigma;
+        if (C::OUT_PREFETCH) load_out(c);
+        // partial sums of the blocks other waves own (owner of block b: wave b % NK);
+        // the owner keeps its own
+        {
+            float* red = sm.red[c & 1];
+#pragma unroll
+            for (int tb = 0; tb < LB; ++tb)
+#pragma unroll
+                for (int x = 0; x < CW; ++x) {
+                    const int b = tb * CW + x, owner = b % NK;
+                    if (owner != wave) {
+                        const int slot = wave < owner ? wave : wave - 1;
+                        *reinterpret_cast<f32x4*>(red + (b * (NK - 1) + slot) * 256 + lane * 4) = acc[tb][x];
+                    } else {
+                        own[b / NK] = acc[tb][x];
+                    }
+                }
+        }
+
+        // --- update sweep: C^ += K^T ((w / sigma') V)_{hi+lo} -------------------
+        if (resc) {
+#pragma unroll
+            for (int x = 0; x < CW; ++x)
+#pragma unroll
+                for (int b = 0; b < 2 * NS; ++b) st[x][b] *= cand;
+        }
+        {
+            bf16x8 vwh[CW][2], vwl[CW][2];
+            const bf16* vh = sm.vwh[c & 1];
+            const bf16* vl2 = sm.vwl[c & 1];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int x = 0; x < CW; ++x) {
+                    const int off = (32 * kk + 8 * lg + (ln >> 2)) * VP + 16 * x + 4 * (ln & 3);
+                    vwh[x][kk] = cat(lds_read_tr(vh + off), lds_read_tr(vh + off + 4 * VP));
+                    vwl[x][kk] = cat(lds_read_tr(vl2 + off), lds_read_tr(vl2 + off + 4 * VP));
+                }
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+                bf16x8 cur[4];
+                advance(cur, c, cn, NS + s);
+#pragma unroll
+                for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                        for (int x = 0; x < CW; ++x) {
+                            st[x][2 * s + jt] = mfma(cur[2 * jt + kk], vwh[x][kk], st[x][2 * s + jt]);
+                            st[x][2 * s + jt] = mfma(cur[2 * jt + kk], vwl[x][kk], st[x][2 * s + jt]);
+                        }
+            }
+        }
+        sigma = sig_new;
+        // the next chunk's tiles: (w / sigma') (.) V into the half chunk c - 1's update
+        // read, V into the buffer chunk c - 2's output rows read (both before the last
+        // barrier).  (After the last chunk this rewrites buffers nobody reads.)
+        cand = sigma * alpha_n;
+        resc = cand < SIGMA_MIN;
+        sig_new = resc ? 1.0f : cand;
+        store_v(rv, rw, 1.0f / sig_new, c + 1);
+        load_v(rv, rw, min(c + 2, nC - 1));
+        alpha_n = ws.alpha[ch0 + min(c + 2, nC - 1)];
+        // every wave's partial sums and the next chunk's tiles are in LDS before any
+        // wave reads them; the sums of chunk c - 1 (read during this chunk) are
+        // overwritten only after the next barrier
+        lds_barrier();
+    }
+    output(nC - 1);
+
+    if (seg != G - 1) return;
+#pragma unroll
+    for (int x = 0; x < CW; ++x) {
+        if (16 * x >= vcols) continue;
+#pragma unroll
+        for (int b = 0; b < 2 * NS; ++b)
+            *reinterpret_cast<f32x4*>(Cout + ((size_t)bh * dv + vcol + 16 * x + ln) * DQ + kw + 32 * (b / 2) + 8 * lg +
+                                      4 * (b % 2)) = st[x][b] * sigma;
     }
     if (vt == 0) {
         for (int j = tid; j < DQ; j += THREADS) nout[(size_t)bh * DQ + j] = ws.nfin[(size_t)bh * DQ + j];
@@ -1235,6 +1650,49 @@ hipError_t launch_scan2(const FwdArgs& a, const Ws& w, int G) {
     return hipGetLastError();
 }
 
+template <class C>
+hipError_t launch_scan4(const FwdArgs& a, const Ws& w, int G) {
+    constexpr int L = C::L;
+    const int heads = a.B * a.NH;
+    if (G > 1) {
+        dim3 sgrid((a.dqk / SS_TILE) * ((a.dv + SS_TILE - 1) / SS_TILE), (G - 1) * w.sp, heads);
+        hipLaunchKernelGGL((seg_state_kernel<L>), sgrid, dim3(SS_THREADS), 0, a.stream,
+                           (const bf16*)a.k, (const bf16*)a.v, w, a.S, a.Sx, a.dqk, a.dv, G);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const size_t quads = (size_t)a.dv * a.dqk / 4;
+        hipLaunchKernelGGL(seg_combine_kernel, dim3((unsigned)((quads + SC_THREADS - 1) / SC_THREADS), heads),
+                           dim3(SC_THREADS), 0, a.stream, w, a.S / L, G, a.dqk, a.dv, a.C0);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int n_vt = (a.dv + C::TV - 1) / C::TV;
+    const int nwg = heads * G * n_vt;
+    const int remap = (nwg % 8 == 0) ? 1 : 0;
+    hipLaunchKernelGGL((chunk_scan4_kernel<C>), dim3(nwg), dim3(C::THREADS), 0, a.stream,
+                       (const bf16*)a.q, (const bf16*)a.v, a.o_pre, w, a.S, a.Sx, G, a.dv, n_vt, remap,
+                       a.C0, (bf16*)a.h, a.C, a.n, a.m);
+    return hipGetLastError();
+}
+
+typedef hipError_t (*RunFn)(const FwdArgs&, int, size_t*);
+RunFn pick_pipelined(int L, int dqk);
+
+template <int DQ, int NK, int CW, int MINB, int PD, bool OP>
+hipError_t run4(const FwdArgs& a, int stage, size_t* bytes) {
+    using C = Scan4Cfg<DQ, NK, CW, MINB, PD, OP>;
+    // the operand copies of one head are addressed with 32-bit buffer offsets
+    if ((size_t)a.S * DQ * sizeof(bf16) > (size_t)INT_MAX) return pick_pipelined(C::L, DQ)(a, stage, bytes);
+    const int G = segments<C>(a);
+    if (stage == 2) {
+        *bytes = ws_bytes((size_t)a.B * a.NH, a.S, C::L, a.dqk, a.dv, G, true);
+        return hipSuccess;
+    }
+    Ws w = ws_layout(a.ws, (size_t)a.B * a.NH, a.S, C::L, a.dqk, a.dv, G, true);
+    if (stage == 0) return launch_prep<C::L>(a, w);
+    return launch_scan4<C>(a, w, G);
+}
+
 // stage 0 = prepare (chunk_prep, gate_scan, den), stage 1 = scan (segments, chunk_scan2),
 // stage 2 = workspace size only
 template <int L, int DQ, int NC, int NK, int SB, int MINB, int CW, bool RS>
@@ -1242,20 +1700,18 @@ hipError_t run2(const FwdArgs& a, int stage, size_t* bytes) {
     using C = Scan2Cfg<L, DQ, NC, NK, SB, MINB, CW, RS>;
     const int G = segments<C>(a);
     if (stage == 2) {
-        *bytes = ws_bytes((size_t)a.B * a.NH, a.S, L, a.dqk, a.dv, G);
+        *bytes = ws_bytes((size_t)a.B * a.NH, a.S, L, a.dqk, a.dv, G, false);
         return hipSuccess;
     }
-    Ws w = ws_layout(a.ws, (size_t)a.B * a.NH, a.S, L, a.dqk, a.dv, G);
+    Ws w = ws_layout(a.ws, (size_t)a.B * a.NH, a.S, L, a.dqk, a.dv, G, false);
     if (stage == 0) return launch_prep<L>(a, w);
     return launch_scan2<C>(a, w, G);
 }
 
-typedef hipError_t (*RunFn)(const FwdArgs&, int, size_t*);
-
 // supported (chunk, d_qk) pairs and the tiling used for each:
 // (chunk, d_qk, column blocks, key parts, slab, workgroups per CU, column blocks per wave,
 //  h stored as 4-column rows after a quad transpose instead of one column per lane)
-RunFn pick(int L, int dqk) {
+RunFn pick_pipelined(int L, int dqk) {
 #define MLSTM_V2(L_, DQ_, NC_, NK_, SB_, MINB_, CW_, RS_) \
     if (L == L_ && dqk == DQ_) return &run2<L_, DQ_, NC_, NK_, SB_, MINB_, CW_, RS_>;
     // Four waves per workgroup (one per SIMD) let the compiler use the whole
@@ -1287,6 +1743,23 @@ RunFn pick(int L, int dqk) {
     MLSTM_V2(64, 1024, 2, 4, 32, 1, 1, true)
 #undef MLSTM_V2
     return nullptr;
+}
+
+// The streaming scan where it measured faster than the pipelined one: d_qk 1024
+// (1.3B-class layer shape: 381 against 481 us for the scan, 468 against 545 us for
+// the whole forward) and d_qk 512 (B=4, NH=4, S=2048: 190 against 229 us).  At
+// d_qk 640 to 896 its partial-sum exchange and output operands push it past the
+// register file (spills), and at d_qk 384 and below it cannot keep two waves per
+// SIMD within the LDS, so those stay pipelined.
+RunFn pick(int L, int dqk) {
+#define MLSTM_V4(DQ_, NK_, CW_, MINB_, PD_, OP_) \
+    if (L == 64 && dqk == DQ_) return &run4<DQ_, NK_, CW_, MINB_, PD_, OP_>;
+    // (d_qk, key parts = waves, 16-column blocks per wave, workgroups per CU,
+    //  operand steps in flight, output operands loaded a chunk ahead)
+    MLSTM_V4(1024, 8, 2, 1, 2, true)
+    MLSTM_V4(512, 8, 2, 1, 2, true)
+#undef MLSTM_V4
+    return pick_pipelined(L, dqk);
 }
 
 // The chunk size only sets how the recurrence is re-associated: every chunk size

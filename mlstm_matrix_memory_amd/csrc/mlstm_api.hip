@@ -137,7 +137,7 @@ mlstm_status check_disjoint(const Buf* bufs, int n, int n_out) {
 // the name `scratch` is only a stand-in for the symbol: its device address, which
 // differs per GPU, is looked up once per device with hipGetSymbolAddress and only
 // that address is ever handed to kernels.
-constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)160 << 20;
 static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
 
 constexpr int MAX_DEVICES = 64;

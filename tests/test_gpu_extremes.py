@@ -94,6 +94,8 @@ SHAPES = [
     # one head of width 256 over 4096 tokens: the scan runs it as 8 sequence
     # segments of 512 tokens, each from its own entering state
     ("segmented", "long_ctx", dict(B=1, NH=1, S=4096, dqk=256, dv=256), 128, "bf16", 512),
+    # width 512 (the streaming form of the scan) over 2048 tokens: 8 segments of 256
+    ("streaming_segmented", "lm_1_3b", dict(B=1, NH=1, S=2048, dqk=512, dv=512), 64, "bf16", 256),
     # the fp32 path
     ("fp32_c64", "tiny", dict(B=1, NH=2, S=256, dqk=48, dv=80), 64, "f32", None),
     ("fp32_c16", "tiny", dict(B=1, NH=2, S=256, dqk=48, dv=80), 16, "f32", None),

@@ -115,7 +115,9 @@ def test_maximum_widths(orc, dtype, dqk, dv):
 # few heads over a long sequence: the scan splits each head's sequence into
 # segments chained through their entering states (long-context gate statistics)
 SEGMENTED = [(dict(B=1, NH=1, S=2048, dqk=128, dv=96), 64), (dict(B=1, NH=2, S=1024, dqk=384, dv=384), 32),
-             (dict(B=1, NH=1, S=4096, dqk=256, dv=256), 128)]
+             (dict(B=1, NH=1, S=4096, dqk=256, dv=256), 128),
+             # the streaming form of the scan (widths 512 and 1024), one with a ragged value tile
+             (dict(B=1, NH=1, S=2048, dqk=512, dv=512), 64), (dict(B=1, NH=2, S=1024, dqk=1024, dv=112), 64)]
 
 
 @pytest.mark.parametrize("over,chunk", SEGMENTED, ids=lambda v: str(v))

@@ -53,6 +53,7 @@ CASES = [
     ("lm_125m", dict(B=1, NH=2, S=700), (512,), 64, "bf16"),          # MFMA part + ragged tail
     ("lm_125m", dict(B=2, NH=1, S=333, dqk=128, dv=96), (100, 260), 32, "bf16"),  # every piece ragged
     ("lm_1_3b", dict(B=1, NH=1, S=300), (64,), 64, "bf16"),
+    ("lm_1_3b", dict(B=1, NH=2, S=1100, dqk=512, dv=512), (320,), 64, "bf16"),   # streaming scan from a state
     ("long_ctx", dict(B=1, NH=1, S=3000, dqk=256, dv=256), (1024,), 64, "bf16"),  # segments from a state
     ("long_ctx", dict(B=1, NH=2, S=1100), (129,), 128, "bf16"),
     ("tiny", dict(B=2, NH=2, S=150, dqk=48, dv=80), (37, 100), 16, "f32"),
