@@ -1249,14 +1249,15 @@ struct Scan4Cfg {
     static constexpr int LB = L / 16;           // 16-row blocks of the chunk
     static constexpr int NB = LB * CW;          // output blocks of the tile
     static constexpr int NOWN = (NB + NK - 1) / NK;
-    static constexpr int VP = TV + 16;          // tile pitch: 4 rows of a transposing read hit distinct banks
+    // tile pitch (bf16): 16 or 48 mod 64, so that the 4 rows of a transposing read
+    // start 8 or 24 banks apart and hit distinct banks
+    static constexpr int VP = (TV % 64 == 16 || TV % 64 == 48) ? TV : TV + 16;
     static constexpr int U_V = L * TV / 8;      // 16-byte units of the V tile
     static constexpr int NPV = (U_V + THREADS - 1) / THREADS;
     static constexpr int RED = NB * (NK - 1) * 256;   // floats of one partial-sum buffer (owners keep theirs)
     static constexpr size_t TILES = 7 * (size_t)L * VP * 2;
     static_assert(MINB * (TILES + 2 * (size_t)RED * 4) <= 160 * 1024, "LDS");
     static_assert(DQ % NK == 0 && DP % 32 == 0, "key parts of whole 32-key steps");
-    static_assert(TV % 32 == 0, "tile pitch");
     static_assert(THREADS <= 1024, "workgroup too large");
     static_assert(PD >= 1 && PD <= 2 * NS, "prefetch depth within one chunk's steps");
 };
