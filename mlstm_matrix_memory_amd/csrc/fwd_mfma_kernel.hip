@@ -421,9 +421,11 @@ constexpr int GS_BATCH = 16;     // loads issued together before their results a
 // The normalizer recurrence n' <- alpha n' + rl dn is affine too: each wave
 // carries it over its own range of chunks from zero, the ranges are chained
 // through LDS, and each wave then walks its range again from the true value.
-// Grid (key-column groups, heads): every workgroup of a head repeats the short
-// stabilizer scan, carries the normalizer for its 64 key columns and writes the
-// per-token weights of its share of the tokens.
+// Grid (parts, heads): every workgroup of a head repeats the short stabilizer
+// scan and writes the per-token weights of its share of the tokens; the first
+// d_qk/64 parts also carry the normalizer for their 64 key columns.  There are at
+// least enough parts for one workgroup per CU (few heads over long sequences would
+// otherwise leave the per-token work to a handful of workgroups).
 template <int L>
 __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int dqk,
                                                                const float* __restrict__ n0,
@@ -513,7 +515,9 @@ __global__ __launch_bounds__(GS_THREADS) void gate_scan_kernel(Ws ws, int S, int
         if (part == 0)
             for (int i = tid; i < nt; i += GS_THREADS) ws.alpha[(size_t)bh * nC + c0 + i] = salpha[i];
         // normalizer entering each chunk: n' <- alpha n' + rl K^T w_loc, one key column per lane,
-        // wave q over chunks [q0, q1) of the tile
+        // wave q over chunks [q0, q1) of the tile (workgroups past the key columns only
+        // write per-token weights)
+        if (part * GS_COLS >= dqk) continue;
         const int qrun = (nt + GS_WAVES - 1) / GS_WAVES;
         const int q0 = min(nt, wave * qrun), q1 = min(nt, q0 + qrun);
         const float* dnp = ws.dn + ((size_t)bh * nC + c0) * dqk + j;
@@ -578,20 +582,32 @@ __global__ __launch_bounds__(DEN_THREADS) void den_kernel(const bf16* __restrict
     __syncthreads();
     const size_t tok0 = (size_t)bh * S + (size_t)c * L;
     const int lp = tid & 15;
-    for (int row = tid >> 4; row < L; row += DEN_THREADS / 16) {
-        const bf16* qr = q + ((size_t)bh * Sx + (size_t)c * L + row) * dqk;
-        float acc = 0.0f;
-        for (int j0 = lp * 8; j0 < dqk; j0 += 128) {
-            const bf16x8 q8 = *reinterpret_cast<const bf16x8*>(qr + j0);
-            const f32x4 n0 = *reinterpret_cast<const f32x4*>(sn + j0);
-            const f32x4 n1 = *reinterpret_cast<const f32x4*>(sn + j0 + 4);
-            acc += (float)q8[0] * n0[0] + (float)q8[1] * n0[1] + (float)q8[2] * n0[2] + (float)q8[3] * n0[3]
-                 + (float)q8[4] * n1[0] + (float)q8[5] * n1[1] + (float)q8[6] * n1[2] + (float)q8[7] * n1[3];
-        }
-        acc = row16_sum(acc);
+    // each 16-lane group takes rows tid/16 + 16 i; the rows' loads of one step are
+    // issued together
+    constexpr int RPT = L / (DEN_THREADS / 16);
+    const bf16* qr = q + ((size_t)bh * Sx + (size_t)c * L + (tid >> 4)) * dqk;
+    float acc[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) acc[i] = 0.0f;
+#pragma unroll 2
+    for (int j0 = lp * 8; j0 < dqk; j0 += 128) {
+        bf16x8 q8[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) q8[i] = *reinterpret_cast<const bf16x8*>(qr + (size_t)16 * i * dqk + j0);
+        const f32x4 n0 = *reinterpret_cast<const f32x4*>(sn + j0);
+        const f32x4 n1 = *reinterpret_cast<const f32x4*>(sn + j0 + 4);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            acc[i] += (float)q8[i][0] * n0[0] + (float)q8[i][1] * n0[1] + (float)q8[i][2] * n0[2] +
+                      (float)q8[i][3] * n0[3] + (float)q8[i][4] * n1[0] + (float)q8[i][5] * n1[1] +
+                      (float)q8[i][6] * n1[2] + (float)q8[i][7] * n1[3];
+    }
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const float tot = row16_sum(acc[i]);
         if (lp == 0) {
-            const size_t g = tok0 + row;
-            const float den = ws.r[g] * ws.den[g] + ws.a[g] * acc;
+            const size_t g = tok0 + (tid >> 4) + 16 * i;
+            const float den = ws.r[g] * ws.den[g] + ws.a[g] * tot;
             ws.rden[g] = __builtin_amdgcn_rcpf(fmaxf(fabsf(den), ws.fl[g]));
         }
     }
@@ -1604,7 +1620,9 @@ hipError_t launch_prep(const FwdArgs& a, const Ws& w) {
                        (const bf16*)a.q, (const bf16*)a.k, a.i_pre, a.f_pre, a.S, a.Sx, a.dqk, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((gate_scan_kernel<L>), dim3((a.dqk + GS_COLS - 1) / GS_COLS, a.B * a.NH), dim3(GS_THREADS), 0, a.stream,
+    const int heads = a.B * a.NH;
+    const int gs_parts = max((a.dqk + GS_COLS - 1) / GS_COLS, min(64, (256 + heads - 1) / heads));
+    hipLaunchKernelGGL((gate_scan_kernel<L>), dim3(gs_parts, heads), dim3(GS_THREADS), 0, a.stream,
                        w, a.S, a.dqk, a.n0, a.m0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
