@@ -224,7 +224,7 @@ struct alignas(16) PrepSmem {
 // registers while the current one is multiplied.  Wave w owns the 16-row blocks
 // tb = w, w + 4, ... of the score matrix with all their causal column blocks, so
 // every row sum is formed inside one wave in a fixed order.
-template <int L>
+template <int L, bool FRAG>
 __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k,
     const float* __restrict__ i_pre, const float* __restrict__ f_pre,
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
         }
         __syncthreads();
         if (j0 + PREP_SB < dqk) slab_load(reg, j0 + PREP_SB);
-        if (L == 64 && ws.qs != nullptr) {
+        if constexpr (FRAG) {
             // the slab's fragments in MFMA operand order (64-token chunks): per 32-key
             // step ks, Q block tb (lane (ln, lg): row 16 tb + ln, keys 8 lg .. + 7) and
             // K^T block (jt, kk) (lane: key 8 (ln / 4) + 4 jt + ln % 4, tokens
@@ -370,7 +370,10 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
         }
     }
 
-    // decay, row sums (fp32, before rounding), and P_loc out as bf16 hi then lo
+    // decay, row sums (fp32, before rounding), and P_loc out as bf16 hi then lo:
+    // row-major, or for the streaming scan in MFMA operand order, staged through the
+    // (now free) Q and K tiles
+    constexpr bool frag = FRAG;
     bf16* Pout = ws.P + 2 * tok0 * L;
 #pragma unroll
     for (int r = 0; r < TBW; ++r) {
@@ -387,15 +390,32 @@ __global__ __launch_bounds__(PREP_THREADS) void chunk_prep_kernel(
                 if (sbk <= tb && s <= tau)
                     p = acc[r][sbk][i] * exp_arg(sm.sb[tau] - sm.sb[s] + (double)sm.si[s] - sm.sml[tau]);
                 den4[i] += p;
-                const bf16 hi = (bf16)p;
-                Pout[(size_t)tau * L + s] = hi;
-                Pout[(size_t)L * L + (size_t)tau * L + s] = (bf16)(p - (float)hi);
+                const bf16 hi = (bf16)p, lo = (bf16)(p - (float)hi);
+                if constexpr (frag) {
+                    sm.q[tau * PREP_KP + s] = hi;
+                    sm.k[tau * PREP_KP + s] = lo;
+                } else {
+                    Pout[(size_t)tau * L + s] = hi;
+                    Pout[(size_t)L * L + (size_t)tau * L + s] = lo;
+                }
             }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const float d = row16_sum(den4[i]);
             if (ln == 0) ws.den[tok0 + 16 * tb + 4 * lg + i] = d;
+        }
+    }
+    if constexpr (frag) {
+        // fragment (tb, kk, hl) at ((tb * 2 + kk) * 2 + hl) KB of the chunk's 16 KB:
+        // lane (ln, lg) holds row 16 tb + ln, columns 32 kk + 8 lg .. + 7
+        __syncthreads();
+#pragma unroll
+        for (int f = wave; f < 16; f += NW) {
+            const int tb = f / 4, kk = (f / 2) % 2, hl = f % 2;
+            const bf16* src = (hl ? sm.k : sm.q) + (16 * tb + ln) * PREP_KP + 32 * kk + 8 * lg;
+            *reinterpret_cast<bf16x8*>(reinterpret_cast<char*>(Pout) + f * 1024 + lane * 16) =
+                *reinterpret_cast<const bf16x8*>(src);
         }
     }
 }
@@ -1448,11 +1468,12 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan4_kernel(
         for (int j = 0; j < C::NOWN; ++j) {
             const int b = min(wave + NK * j, NB - 1);
             const int tb = b / CW, x = b % CW;
-            const bf16* P = ws.P + 2 * (tokh + t0) * L + (size_t)(16 * tb + ln) * L + 8 * lg;
+            // P_loc in operand order: fragment (tb, kk, hi/lo) is 1 KB at ((tb*2+kk)*2+hl) KB
+            const char* P = reinterpret_cast<const char*>(ws.P + 2 * (tokh + t0) * L) + lane * 16;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                pa[j][kk][0] = *reinterpret_cast<const bf16x8*>(P + 32 * kk);
-                pa[j][kk][1] = *reinterpret_cast<const bf16x8*>(P + L * L + 32 * kk);
+                pa[j][kk][0] = *reinterpret_cast<const bf16x8*>(P + ((tb * 2 + kk) * 2) * 1024);
+                pa[j][kk][1] = *reinterpret_cast<const bf16x8*>(P + ((tb * 2 + kk) * 2 + 1) * 1024);
             }
             const size_t tk = tokh + t0 + 16 * tb + 4 * lg;
             ga[j] = *reinterpret_cast<const f32x4*>(ws.a + tk);
@@ -1616,8 +1637,13 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan4_kernel(
 template <int L>
 hipError_t launch_prep(const FwdArgs& a, const Ws& w) {
     dim3 grid(a.S / L, a.B * a.NH);
-    hipLaunchKernelGGL((chunk_prep_kernel<L>), grid, dim3(PREP_THREADS), 0, a.stream,
-                       (const bf16*)a.q, (const bf16*)a.k, a.i_pre, a.f_pre, a.S, a.Sx, a.dqk, w);
+    // the streaming scan's operand-ordered copies (64-token chunks only)
+    if (L == 64 && w.qs != nullptr)
+        hipLaunchKernelGGL((chunk_prep_kernel<L, true>), grid, dim3(PREP_THREADS), 0, a.stream,
+                           (const bf16*)a.q, (const bf16*)a.k, a.i_pre, a.f_pre, a.S, a.Sx, a.dqk, w);
+    else
+        hipLaunchKernelGGL((chunk_prep_kernel<L, false>), grid, dim3(PREP_THREADS), 0, a.stream,
+                           (const bf16*)a.q, (const bf16*)a.k, a.i_pre, a.f_pre, a.S, a.Sx, a.dqk, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int heads = a.B * a.NH;
