@@ -1315,7 +1315,7 @@ struct alignas(16) Scan4Smem {
 
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan4_kernel(
-    const bf16* __restrict__ q, const bf16* __restrict__ v,
+    const bf16* __restrict__ v,
     const float* __restrict__ o_pre, Ws ws, int S, int Sx, int G, int dv, int n_vt, int remap,
     const float* __restrict__ C0,
     bf16* __restrict__ h, float* __restrict__ Cout, float* __restrict__ nout, float* __restrict__ mout)
@@ -1715,7 +1715,7 @@ hipError_t launch_scan4(const FwdArgs& a, const Ws& w, int G) {
     const int nwg = heads * G * n_vt;
     const int remap = (nwg % 8 == 0) ? 1 : 0;
     hipLaunchKernelGGL((chunk_scan4_kernel<C>), dim3(nwg), dim3(C::THREADS), 0, a.stream,
-                       (const bf16*)a.q, (const bf16*)a.v, a.o_pre, w, a.S, a.Sx, G, a.dv, n_vt, remap,
+                       (const bf16*)a.v, a.o_pre, w, a.S, a.Sx, G, a.dv, n_vt, remap,
                        a.C0, (bf16*)a.h, a.C, a.n, a.m);
     return hipGetLastError();
 }

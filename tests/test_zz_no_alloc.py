@@ -48,6 +48,14 @@ def test_noalloc_two_calls_second_smaller():
     _run_both(dict(B=1, NH=2, S=256, dqk=128, dv=96), 32, 821)
 
 
+def test_noalloc_streaming_scan_two_calls_second_smaller():
+    # widths 1024 and 512 run the streaming form of the scan, whose workspace also
+    # holds the operand-ordered copies of q and k
+    announce("fwd noalloc: B=1 NH=4 S=512 d=1024 chunk=64, then B=1 NH=2 S=256 d=512 chunk=64")
+    _run_both(dict(B=1, NH=4, S=512, dqk=1024, dv=1024), 64, 822)
+    _run_both(dict(B=1, NH=2, S=256, dqk=512, dv=512), 64, 823)
+
+
 def test_noalloc_rejects_a_forward_larger_than_its_scratch():
     from mlstm_matrix_memory_amd import MLSTM_BF16, binding
     lib = binding.load_library()
