@@ -32,6 +32,9 @@
 // form those states, see the two-level section below.
 #include "mlstm_internal.h"
 
+#include <type_traits>
+#include <utility>
+
 namespace mlstm {
 namespace {
 
@@ -47,6 +50,8 @@ struct BwdWs {
     float* dden;    // [heads][S] dden'
     float* qdq;     // [heads][S] q_t . dq_t (MFMA path)
     double* seg;    // [heads][segments][2] per-segment totals of the two gate scans
+    double* gk;     // [heads][S] F_s - i~_s (the key side of the decay's exponent)
+    double* rt;     // [heads][S] F_t - m_t (its query side)
 };
 
 constexpr int GSEG = 1024;       // tokens per segment of the gate scans
@@ -109,6 +114,8 @@ inline size_t bwd_ws_walk(char* base, const BwdArgs& a, BwdWs* out, SuperStates*
     w.dden = (float*)take(heads * S * sizeof(float));
     w.qdq = (float*)take(heads * S * sizeof(float));
     w.seg = (double*)take(heads * ((S + GSEG - 1) / GSEG) * 2 * sizeof(double));
+    w.gk = (double*)take(heads * S * sizeof(double));
+    w.rt = (double*)take(heads * S * sizeof(double));
     SuperStates st;
     st.LS = bwd_superchunk(a);
     st.G = (a.S + st.LS - 1) / st.LS;
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_gate_local(const float* __rest
     }
 }
 
-__global__ __launch_bounds__(BW_THREADS) void bwd_gate_fix(int S, BwdWs ws)
+__global__ __launch_bounds__(BW_THREADS) void bwd_gate_fix(const float* __restrict__ i_pre, int S, BwdWs ws)
 {
     __shared__ double cin[2];
     const int nseg = (S + GSEG - 1) / GSEG;
@@ -212,8 +219,11 @@ __global__ __launch_bounds__(BW_THREADS) void bwd_gate_fix(int S, BwdWs ws)
     const int ta = sg * GSEG, tb = min(S, ta + GSEG);
     for (int t = ta + threadIdx.x; t < tb; t += BW_THREADS) {
         const double F = sum + ws.F[base + t];
+        const double m = F + fmax(mx, ws.m[base + t] - sum);
         ws.F[base + t] = F;
-        ws.m[base + t] = F + fmax(mx, ws.m[base + t] - sum);
+        ws.m[base + t] = m;
+        ws.gk[base + t] = F - (double)i_pre[base + t];
+        ws.rt[base + t] = F - m;
     }
 }
 
@@ -887,65 +897,110 @@ __global__ __launch_bounds__(WK_THREADS) void bwd_state_scan(BwdIn<bf16> in, Bwd
     }
 }
 
-// K and V rows [row0, row0 + 64) into LDS (pitch P) with every load of both tiles
-// issued before the first store: one memory round trip per stage instead of one per
-// batch.  (Used up to width 384, where the 2 * D / 32 registers per thread fit beside
-// the live state; wider tiles go through stage_rows in batches.)
-template <int D, int P>
-__device__ __forceinline__ void stage_kv(bf16* dk_, bf16* dv_, const bf16* ks, const bf16* vs, size_t tok0,
-                                         int row0, int S, int dqk, int dv, int tid) {
-    constexpr int UPT = 64 * D / 8 / MB_THREADS;
-    bf16x8 rk[UPT], rv[UPT];
-#pragma unroll
-    for (int b = 0; b < UPT; ++b) {
-        const int u = tid + b * MB_THREADS;
-        const int r = u / (D / 8), c8 = 8 * (u % (D / 8));
-        rk[b] = ld8(ks + (tok0 + row0 + r) * dqk + c8, row0 + r < S && c8 < dqk);
-        rv[b] = ld8(vs + (tok0 + row0 + r) * dv + c8, row0 + r < S && c8 < dv);
-    }
-#pragma unroll
-    for (int b = 0; b < UPT; ++b) {
-        const int u = tid + b * MB_THREADS;
-        const int r = u / (D / 8), c8 = 8 * (u % (D / 8));
-        *reinterpret_cast<bf16x8*>(dk_ + r * P + c8) = rk[b];
-        *reinterpret_cast<bf16x8*>(dv_ + r * P + c8) = rv[b];
-    }
+// ---- staging by buffer loads that write LDS directly ----------------------------
+// The row and column passes keep one wave per SIMD at the wider tiles, so a load
+// round trip through registers leaves the matrix cores idle.  Buffer loads with the
+// LDS flag write their 16 bytes per lane straight into LDS (lane l of a wave fills
+// bytes 16 l .. 16 l + 15 of a 1 KB run that starts at the LDS address in M0); they
+// need no registers, so the next tile's loads are issued before the products on the
+// current one and waited for with a partial vmcnt.  They are written as inline
+// assembly: the compiler would otherwise order every LDS read after every such load
+// still in flight (it does not tell the two LDS buffers apart), which serializes
+// exactly the overlap they are for.  Every wait on them is therefore explicit: a
+// vmcnt that leaves only younger loads outstanding, then a barrier.
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>): a loop whose index
+// is a compile-time constant in every copy (register arrays indexed by it stay registers)
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-// Q, dnum' hi and dnum' lo rows [row0, row0 + R) into LDS with every load issued
-// before the first store (one memory round trip per stage)
-template <int R, int D, int P>
-__device__ __forceinline__ void stage_qd(bf16* dq_, bf16* dh_, bf16* dl_, const bf16* qs, const bf16* hs,
-                                         const bf16* ls, size_t tok0, int row0, int S, int dqk, int dv, int tid) {
-    constexpr int UPT = R * D / 8 / MB_THREADS;
-    bf16x8 rq[UPT], rh[UPT], rl[UPT];
-#pragma unroll
-    for (int b = 0; b < UPT; ++b) {
-        const int u = tid + b * MB_THREADS;
-        const int r = u / (D / 8), c8 = 8 * (u % (D / 8));
-        rq[b] = ld8(qs + (tok0 + row0 + r) * dqk + c8, row0 + r < S && c8 < dqk);
-        rh[b] = ld8(hs + (tok0 + row0 + r) * dv + c8, row0 + r < S && c8 < dv);
-        rl[b] = ld8(ls + (tok0 + row0 + r) * dv + c8, row0 + r < S && c8 < dv);
-    }
-#pragma unroll
-    for (int b = 0; b < UPT; ++b) {
-        const int u = tid + b * MB_THREADS;
-        const int r = u / (D / 8), c8 = 8 * (u % (D / 8));
-        *reinterpret_cast<bf16x8*>(dq_ + r * P + c8) = rq[b];
-        *reinterpret_cast<bf16x8*>(dh_ + r * P + c8) = rh[b];
-        *reinterpret_cast<bf16x8*>(dl_ + r * P + c8) = rl[b];
-    }
+// raw buffer descriptor over [base, base + bytes): loads past the range return zeros
+__device__ __forceinline__ u32x4 span_rsrc(const void* base, unsigned bytes) {
+    const unsigned long long a = (unsigned long long)base;
+    u32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((unsigned)a);
+    r[1] = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32) & 0xffffu);
+    r[2] = __builtin_amdgcn_readfirstlane(bytes);
+    r[3] = 0x00020000u;
+    return r;
 }
 
-template <int D>
-struct alignas(16) RowsSmem {
-    bf16 k[64 * (D + 8)];
-    bf16 v[64 * (D + 8)];
-    double gs[64];       // F_s - i~_s of the key block
+// this lane's 16 bytes at byte offset voff of the descriptor's range into LDS at
+// dst + 16 * lane (dst is the wave's, so uniform).  M0 is saved and restored around
+// the load (the compiler keeps it as its own); one wait state between the M0 write
+// and the load that reads it.
+__device__ __forceinline__ void dma16(void* dst, unsigned voff, u32x4 rs) {
+    const unsigned la = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_ptr)dst);
+    unsigned keep;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
+                 "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
+                 : "=&s"(keep) : "s"(la), "v"(voff), "s"(rs) : "memory");
+}
+
+// wait until at most N of this wave's vector memory operations are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// A tile of R rows x D columns in LDS with pitch D + 8 bf16: D / 8 + 1 granules of 16
+// bytes per row, the last one padding.  It is filled in LDS order in runs of 1 KB
+// (64 granules), dealt to the four waves round robin.
+template <int R, int D>
+struct DmaTile {
+    static constexpr int GR = D / 8 + 1;
+    static constexpr int TOT = R * GR;
+    static constexpr int NCH = (TOT + 63) / 64;
+    static constexpr int MIN_PER_WAVE = NCH / 4;      // loads every wave issues for one tile, at least
 };
 
+// Rows [0, R) of a row-major bf16 block (row stride d elements, `rows` of them present)
+// into LDS at dst, columns [0, D).  Granules past the present rows or past column d,
+// and the padding granules, are read beyond the descriptor's range and land as zeros.
+template <int R, int D>
+__device__ __forceinline__ void dma_tile(bf16* dst, const bf16* src, int rows, int d, int wave, int lane) {
+    using T = DmaTile<R, D>;
+    const unsigned bytes = rows > 0 ? (unsigned)(rows < R ? rows : R) * (unsigned)d * 2u : 0u;
+    const u32x4 rs = span_rsrc(src, bytes);
+    // the lane's offsets are recomputed at every call rather than held in registers
+    // across the kernel (they are a few integer operations per load)
+    int l = lane;
+    asm volatile("" : "+v"(l));
+#pragma unroll
+    for (int c0 = 0; c0 < T::NCH; c0 += 4) {
+        const int c = c0 + wave;
+        if (c < T::NCH) {
+            const int u = 64 * c + l;
+            const int r = u / T::GR, gc = u - r * T::GR;
+            const unsigned off = (gc < D / 8 && 8 * gc < d) ? (unsigned)(r * d + 8 * gc) * 2u : 0x80000000u;
+            if (T::TOT % 64 == 0 || u < T::TOT) dma16(dst + 512 * c, off, rs);
+        }
+    }
+}
+
+// n16 granules (n16 <= 64) of 16 bytes from src into LDS at dst by one wave; bytes past
+// `bytes` land as zeros
+__device__ __forceinline__ void dma_span(void* dst, const void* src, unsigned bytes, int n16, int lane) {
+    const u32x4 rs = span_rsrc(src, bytes);
+    if (lane < n16) dma16(dst, 16u * lane, rs);
+}
+
 // per (head, query block of 64): num', den' over key blocks <= it, then dnum', dden',
-// do~ (wave-local), then dq over the same key blocks, and q_t . dq_t
+// do~ (wave-local), then dq over the same key blocks, and q_t . dq_t.
+// Each pass walks a list of tile pairs: first the 64-row slices of the state (two-level
+// form), then the key blocks of the band.  The two tiles of a pair go to the two LDS
+// buffers; the products on one buffer run while the next pair's tile loads into the
+// other (pass 1: K or state hi into sk, then V or state lo into sv; pass 2 the other
+// way round, because dA needs V before dq needs K).
 template <int D>
 __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(BwdIn<bf16> in, BwdWs ws, SuperStates ss,
                                                           float* __restrict__ dq, float* __restrict__ dout)
@@ -953,109 +1008,94 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
     constexpr int P = D + 8;
     constexpr int NB = D / 16, KS = D / 32;
     // Up to width 256 two workgroups share a CU (two waves per SIMD, 256 registers
-    // each), so one's staging overlaps the other's products: tiles are staged in
-    // batches of 4 loads per thread and fewer operands are read ahead.  Wider tiles
-    // keep the whole register file and stage with every load in flight (384) or in
-    // batches of 8 (512).
+    // each): fewer operands are read ahead there.
     constexpr int GB = D <= 256 ? 2 : 4;        // value / key blocks whose operands are read together
-    constexpr int SMB = D <= 256 ? 4 : 8;       // loads per thread per staging batch
+    constexpr int NW = DmaTile<64, D>::MIN_PER_WAVE;
     static_assert(NB % GB == 0, "width must be a multiple of 64");
-    __shared__ RowsSmem<D> sm;
+    __shared__ __attribute__((aligned(16))) bf16 sk[64 * P];
+    __shared__ __attribute__((aligned(16))) bf16 sv[64 * P];
+    __shared__ __attribute__((aligned(16))) double sgs[2][64];   // F_s - i~_s of a key block, by its parity
     int bh, rb;
     grid_block(in.heads, bh, rb);
     rb = in.nb - 1 - rb;                        // the last query blocks have the most key blocks
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int S = in.S, dqk = in.dqk, dv = in.dv;
     const size_t tokh = (size_t)bh * S;
     const int r0 = rb * 64;
     const int t = r0 + 16 * wave + ln;          // this lane's query
     const bool tval = t < S;
-    const double Rt = tval ? ws.F[tokh + t] - ws.m[tokh + t] : 0.0;
+    const double Rt = tval ? ws.rt[tokh + t] : 0.0;
     const float fl = tval ? exp_arg(-ws.m[tokh + t]) : 1.0f;
     // two-level form: key blocks of this superchunk only, the earlier ones through the
     // state at the end of the previous superchunk, weighted by beta_t
     const int sg = rb * 64 / in.LS;                 // superchunk of this query block
     const int cb_lo = sg * (in.LS / 64);
     float beta = 0.0f;
-    size_t soff = 0;
+    const bf16* Chi = ss.C;
+    const bf16* Clo = ss.C;
+    int nsl = 0;                                    // state slices of 64 rows
     if (sg > 0) {
         const int ep = sg * in.LS - 1;
         if (tval) beta = exp_arg(Rt - ws.F[tokh + ep] + ws.m[tokh + ep]);
-        soff = state_off(bh, sg - 1, in.G, dv, dqk);
+        Chi = ss.C + state_off(bh, sg - 1, in.G, dv, dqk);
+        Clo = Chi + (size_t)dv * dqk;
+        nsl = (dv + 63) / 64;
     }
+    const int np = nsl + rb - cb_lo + 1;            // tile pairs of each pass
+
+    // loads of the tiles of pair p: state rows (hi, lo) or key block rows (K, V); the
+    // key block's F_s - i~_s goes with the tile whose products come first
+    auto dma_state = [&](bf16* dst, const bf16* base, int p) __attribute__((always_inline)) {
+        dma_tile<64, D>(dst, base + (size_t)64 * p * dqk, dv - 64 * p, dqk, wave, lane);
+    };
+    auto dma_keys = [&](bf16* dst, const bf16* x, int d, int cb, bool with_gs) __attribute__((always_inline)) {
+        dma_tile<64, D>(dst, x + (tokh + 64 * cb) * d, S - 64 * cb, d, wave, lane);
+        if (with_gs && wave == 1)
+            dma_span(sgs[cb & 1], ws.gk + tokh + 64 * cb, 8u * (unsigned)min(64, S - 64 * cb), 32, lane);
+    };
+    auto issue1_first = [&](int p) __attribute__((always_inline)) {
+        if (p >= np) return;
+        if (p < nsl) dma_state(sk, Chi, p);
+        else dma_keys(sk, in.k, dqk, cb_lo + p - nsl, true);
+    };
+    auto issue1_second = [&](int p) __attribute__((always_inline)) {
+        if (p >= np) return;
+        if (p < nsl) dma_state(sv, Clo, p);
+        else dma_keys(sv, in.v, dv, cb_lo + p - nsl, false);
+    };
+    auto issue2_first = [&](int p) __attribute__((always_inline)) {
+        if (p >= np) return;
+        if (p < nsl) dma_state(sv, Clo, p);
+        else dma_keys(sv, in.v, dv, cb_lo + p - nsl, true);
+    };
+    auto issue2_second = [&](int p) __attribute__((always_inline)) {
+        if (p >= np) return;
+        if (p < nsl) dma_state(sk, Chi, p);
+        else dma_keys(sk, in.k, dqk, cb_lo + p - nsl, false);
+    };
+    // the first tile of pair p has landed once no more than the second one's loads are
+    // outstanding; the second once no more than the next pair's first
+    auto wait_first = [&]() __attribute__((always_inline)) {
+        wait_vm<NW>();
+        __syncthreads();
+    };
+    auto wait_second = [&](int p) __attribute__((always_inline)) {
+        if (p + 1 < np) wait_vm<NW>();
+        else wait_vm<0>();
+        __syncthreads();
+    };
+    issue1_first(0);
+    issue1_second(0);
 
     // q_t as B operands: k-slot 8g + j <-> key dimension 32 kk + 8g + j
     bf16x8 qb[KS];
 #pragma unroll
     for (int kk = 0; kk < KS; ++kk) qb[kk] = ld8(in.q + (tokh + t) * dqk + 32 * kk + 8 * g, tval && 32 * kk + 8 * g < dqk);
-
-    auto stage = [&](int c0) {
-        __syncthreads();
-        if constexpr (D <= 384 && D > 256) {
-            stage_kv<D, P>(sm.k, sm.v, in.k, in.v, tokh, c0, S, dqk, dv, tid);
-        } else {
-            stage_rows<64, D, P, SMB>(sm.k, in.k, tokh, c0, S, dqk, tid);
-            stage_rows<64, D, P, SMB>(sm.v, in.v, tokh, c0, S, dv, tid);
-        }
-        if (tid < 64) {
-            const int s = min(c0 + tid, S - 1);
-            sm.gs[tid] = ws.F[tokh + s] - (double)in.i_pre[tokh + s];
-        }
-        __syncthreads();
-    };
-    // rows [64 sl, 64 sl + 64) of the d_v x d_qk state (hi into sm.k, lo into sm.v)
-    auto stage_state = [&](const bf16* hi, const bf16* lo, int sl) {
-        __syncthreads();
-        if constexpr (D <= 384 && D > 256) {
-            stage_kv<D, P>(sm.k, sm.v, hi, lo, 0, 64 * sl, dv, dqk, dqk, tid);
-        } else {
-            stage_rows<64, D, P, SMB>(sm.k, hi, 0, 64 * sl, dv, dqk, tid);
-            stage_rows<64, D, P, SMB>(sm.v, lo, 0, 64 * sl, dv, dqk, tid);
-        }
-        __syncthreads();
-    };
-    // D'[s][t] for this lane's 16 entries of a tile pair (s = 16 sb + 4g + i)
-    auto decay4 = [&](float (&d)[4][4], int c0) {
-#pragma unroll
-        for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int sl = 16 * sb + 4 * g + i;
-                d[sb][i] = (tval && c0 + sl <= t) ? exp_arg(Rt - sm.gs[sl]) : 0.0f;
-            }
-    };
-
-    // ---- pass 1: num'^T[n][t] and den_t -------------------------------------
-    f32x4 num[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) num[nb] = f32x4{0, 0, 0, 0};
+    // den'_t starts from beta_t n~ . q_t (lane partials; loaded here, before the pipeline
+    // has loads of its own in flight)
     float den = 0.0f;
     if (sg > 0) {
-        // num'^T[n][t] = beta_t (C~ q_t)[n],  den'_t = beta_t n~ . q_t (lane partials);
-        // the state rows take the place of the key rows of a tile
-        const bf16* Chi = ss.C + soff;
-        const bf16* Clo = Chi + (size_t)dv * dqk;
-#pragma unroll
-        for (int sl = 0; sl < D / 64; ++sl) {
-            if (64 * sl >= dv) break;
-            stage_state(Chi, Clo, sl);
-#pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                bf16x8 ah[4], al[4];
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb) {
-                    const int off = (16 * sb + ln) * P + 32 * kk + 8 * g;
-                    ah[sb] = *reinterpret_cast<const bf16x8*>(sm.k + off);
-                    al[sb] = *reinterpret_cast<const bf16x8*>(sm.v + off);
-                }
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb) num[4 * sl + sb] = mfma(ah[sb], qb[kk], num[4 * sl + sb]);
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb) num[4 * sl + sb] = mfma(al[sb], qb[kk], num[4 * sl + sb]);
-            }
-        }
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) num[nb] *= beta;
         const float* nt = ss.n + ((size_t)bh * (in.G - 1) + sg - 1) * dqk;
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
@@ -1067,9 +1107,58 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
         }
         den *= beta;
     }
+
+    // D'[s][t] for this lane's 16 entries of a tile pair (s = 16 sb + 4g + i)
+    auto decay4 = [&](float (&d)[4][4], int c0, const double* gs) {
+#pragma unroll
+        for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int sl = 16 * sb + 4 * g + i;
+                d[sb][i] = (tval && c0 + sl <= t) ? exp_arg(Rt - gs[sl]) : 0.0f;
+            }
+    };
+
+    // ---- pass 1: num'^T[n][t] and den_t -------------------------------------
+    f32x4 num[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) num[nb] = f32x4{0, 0, 0, 0};
+    // num'^T[n][t] = beta_t (C~ q_t)[n] over the state slices (the state rows take the
+    // place of key rows)
+    static_for<D / 64>([&](auto slc) __attribute__((always_inline)) {
+        constexpr int sl = decltype(slc)::value;
+        if (sl >= nsl) return;
+        wait_first();
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            bf16x8 a[4];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) a[sb] = *reinterpret_cast<const bf16x8*>(sk + (16 * sb + ln) * P + 32 * kk + 8 * g);
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) num[4 * sl + sb] = mfma(a[sb], qb[kk], num[4 * sl + sb]);
+        }
+        __syncthreads();
+        issue1_first(sl + 1);
+        wait_second(sl);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) {
+            bf16x8 a[4];
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) a[sb] = *reinterpret_cast<const bf16x8*>(sv + (16 * sb + ln) * P + 32 * kk + 8 * g);
+#pragma unroll
+            for (int sb = 0; sb < 4; ++sb) num[4 * sl + sb] = mfma(a[sb], qb[kk], num[4 * sl + sb]);
+        }
+        __syncthreads();
+        issue1_second(sl + 1);
+    });
+    if (sg > 0) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) num[nb] *= beta;
+    }
     for (int cb = cb_lo; cb <= rb; ++cb) {
+        const int p = nsl + cb - cb_lo;
         const int c0 = 64 * cb;
-        stage(c0);
+        wait_first();
         f32x4 st[4];
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) st[sb] = f32x4{0, 0, 0, 0};
@@ -1081,7 +1170,7 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
             for (int j = 0; j < KB; ++j)
 #pragma unroll
                 for (int sb = 0; sb < 4; ++sb)
-                    a[j][sb] = k0 + j < KS ? *reinterpret_cast<const bf16x8*>(sm.k + (16 * sb + ln) * P + 32 * (k0 + j) + 8 * g)
+                    a[j][sb] = k0 + j < KS ? *reinterpret_cast<const bf16x8*>(sk + (16 * sb + ln) * P + 32 * (k0 + j) + 8 * g)
                                            : bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
             for (int j = 0; j < KB; ++j)
@@ -1090,19 +1179,22 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
                     if (k0 + j < KS) st[sb] = mfma(a[j][sb], qb[k0 + j < KS ? k0 + j : 0], st[sb]);
         }
         float d[4][4];
-        decay4(d, c0);
+        decay4(d, c0, sgs[cb & 1]);
+        __syncthreads();
+        issue1_first(p + 1);
         bf16x8 ph[2], pl[2];
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float p = st[sb][i] * d[sb][i];
-                den += p;
+                const float pv = st[sb][i] * d[sb][i];
+                den += pv;
                 bf16 hi, lo;
-                hilo(p, hi, lo);
+                hilo(pv, hi, lo);
                 ph[sb >> 1][4 * (sb & 1) + i] = hi;
                 pl[sb >> 1][4 * (sb & 1) + i] = lo;
             }
+        wait_second(p);
         // operands of GB value blocks read together, then their products with
         // consecutive MFMAs on independent accumulators (LDS latency overlaps)
 #pragma unroll
@@ -1112,7 +1204,7 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
             for (int j = 0; j < GB; ++j)
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {
-                    const bf16* vp = sm.v + (32 * pr + 4 * g + (ln >> 2)) * P + 16 * (nb0 + j) + 4 * (ln & 3);
+                    const bf16* vp = sv + (32 * pr + 4 * g + (ln >> 2)) * P + 16 * (nb0 + j) + 4 * (ln & 3);
                     a[j][pr] = cat(lds_read_tr(vp), lds_read_tr(vp + 16 * P));
                 }
 #pragma unroll
@@ -1123,7 +1215,12 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
                 for (int j = 0; j < GB; ++j) num[nb0 + j] = mfma(a[j][pr], pl[pr], num[nb0 + j]);
             }
         }
+        __syncthreads();
+        issue1_second(p + 1);
     }
+    // both buffers are free: pass 2's first pair loads during the per-query phase
+    issue2_first(0);
+    issue2_second(0);
 
     // ---- per query: u, do~, dnum', dden' ------------------------------------
     den += __shfl_xor(den, 16, 64);
@@ -1183,51 +1280,64 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
     f32x4 dqa[NB];
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) dqa[jb] = f32x4{0, 0, 0, 0};
-    if (sg > 0) {
-        // dq^T[j][t] = beta_t (C~^T dnum'_t + n~ dden'_t)[j]: transposing reads of the
-        // staged state rows, whose n order follows dnum''s k-slots (as V's in pass 1)
-        const bf16* Chi = ss.C + soff;
-        const bf16* Clo = Chi + (size_t)dv * dqk;
-        const float* nt = ss.n + ((size_t)bh * (in.G - 1) + sg - 1) * dqk;
+    // the stores above are outstanding too: wait for everything once
+    wait_vm<0>();
+    __syncthreads();
+    // dq^T[j][t] = beta_t (C~^T dnum'_t + n~ dden'_t)[j]: transposing reads of the
+    // state slices, whose n order follows dnum''s k-slots (as V's in pass 1); the lo
+    // slice (in sv) first, then the hi one (in sk)
+    constexpr int GI = D <= 256 ? GB : 2;   // fewer operands in flight at the widest tiles
+    static_for<D / 64>([&](auto slc) __attribute__((always_inline)) {
+        constexpr int sl = decltype(slc)::value;
+        if (sl >= nsl) return;
+        if (sl > 0) wait_first();
 #pragma unroll
-        for (int sl = 0; sl < D / 64; ++sl) {
-            if (64 * sl >= dv) break;
-            stage_state(Chi, Clo, sl);
-            constexpr int GI = D <= 256 ? GB : 2;   // fewer operands in flight at the widest tiles
+        for (int jb0 = 0; jb0 < NB; jb0 += GI) {
+            bf16x8 a[GI][2];
 #pragma unroll
-            for (int jb0 = 0; jb0 < NB; jb0 += GI) {
-                bf16x8 ah[GI][2], al[GI][2];
-#pragma unroll
-                for (int j = 0; j < GI; ++j)
-#pragma unroll
-                    for (int pr = 0; pr < 2; ++pr) {
-                        const int off = (32 * pr + 4 * g + (ln >> 2)) * P + 16 * (jb0 + j) + 4 * (ln & 3);
-                        ah[j][pr] = cat(lds_read_tr(sm.k + off), lds_read_tr(sm.k + off + 16 * P));
-                        al[j][pr] = cat(lds_read_tr(sm.v + off), lds_read_tr(sm.v + off + 16 * P));
-                    }
+            for (int j = 0; j < GI; ++j)
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {
-#pragma unroll
-                    for (int j = 0; j < GI; ++j) dqa[jb0 + j] = mfma(ah[j][pr], dnh[2 * sl + pr], dqa[jb0 + j]);
-#pragma unroll
-                    for (int j = 0; j < GI; ++j) dqa[jb0 + j] = mfma(ah[j][pr], dnl[2 * sl + pr], dqa[jb0 + j]);
-#pragma unroll
-                    for (int j = 0; j < GI; ++j) dqa[jb0 + j] = mfma(al[j][pr], dnh[2 * sl + pr], dqa[jb0 + j]);
+                    const int off = (32 * pr + 4 * g + (ln >> 2)) * P + 16 * (jb0 + j) + 4 * (ln & 3);
+                    a[j][pr] = cat(lds_read_tr(sv + off), lds_read_tr(sv + off + 16 * P));
                 }
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr)
+#pragma unroll
+                for (int j = 0; j < GI; ++j) dqa[jb0 + j] = mfma(a[j][pr], dnh[2 * sl + pr], dqa[jb0 + j]);
+        }
+        __syncthreads();
+        issue2_first(sl + 1);
+        wait_second(sl);
+#pragma unroll
+        for (int jb0 = 0; jb0 < NB; jb0 += GI) {
+            bf16x8 a[GI][2];
+#pragma unroll
+            for (int j = 0; j < GI; ++j)
+#pragma unroll
+                for (int pr = 0; pr < 2; ++pr) {
+                    const int off = (32 * pr + 4 * g + (ln >> 2)) * P + 16 * (jb0 + j) + 4 * (ln & 3);
+                    a[j][pr] = cat(lds_read_tr(sk + off), lds_read_tr(sk + off + 16 * P));
+                }
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+                for (int j = 0; j < GI; ++j) dqa[jb0 + j] = mfma(a[j][pr], dnh[2 * sl + pr], dqa[jb0 + j]);
+#pragma unroll
+                for (int j = 0; j < GI; ++j) dqa[jb0 + j] = mfma(a[j][pr], dnl[2 * sl + pr], dqa[jb0 + j]);
             }
         }
+        __syncthreads();
+        issue2_second(sl + 1);
+    });
+    if (sg > 0) {
 #pragma unroll
-        for (int jb = 0; jb < NB; ++jb) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int jj = 16 * jb + 4 * g + i;
-                dqa[jb][i] = beta * (dqa[jb][i] + (jj < dqk ? nt[jj] * dd : 0.0f));
-            }
-        }
+        for (int jb = 0; jb < NB; ++jb) dqa[jb] *= beta;
     }
     for (int cb = cb_lo; cb <= rb; ++cb) {
+        const int p = nsl + cb - cb_lo;
         const int c0 = 64 * cb;
-        stage(c0);
+        if (p > 0) wait_first();
         f32x4 da[4];
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) da[sb] = f32x4{0, 0, 0, 0};
@@ -1236,7 +1346,7 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
             bf16x8 a[4];
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) {
-                const bf16* vp = sm.v + (16 * sb + ln) * P + 32 * pr + 4 * g;
+                const bf16* vp = sv + (16 * sb + ln) * P + 32 * pr + 4 * g;
                 a[sb] = cat(*reinterpret_cast<const bf16x4*>(vp), *reinterpret_cast<const bf16x4*>(vp + 16));
             }
 #pragma unroll
@@ -1245,7 +1355,9 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
             for (int sb = 0; sb < 4; ++sb) da[sb] = mfma(a[sb], dnl[pr], da[sb]);
         }
         float d[4][4];
-        decay4(d, c0);
+        decay4(d, c0, sgs[cb & 1]);
+        __syncthreads();
+        issue2_first(p + 1);
         bf16x8 gh[2], gl[2];
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb)
@@ -1256,6 +1368,7 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
                 gh[sb >> 1][4 * (sb & 1) + i] = hi;
                 gl[sb >> 1][4 * (sb & 1) + i] = lo;
             }
+        wait_second(p);
 #pragma unroll
         for (int jb0 = 0; jb0 < NB; jb0 += GB) {
             bf16x8 a[GB][2];
@@ -1263,7 +1376,7 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
             for (int j = 0; j < GB; ++j)
 #pragma unroll
                 for (int pr = 0; pr < 2; ++pr) {
-                    const bf16* kp = sm.k + (32 * pr + 4 * g + (ln >> 2)) * P + 16 * (jb0 + j) + 4 * (ln & 3);
+                    const bf16* kp = sk + (32 * pr + 4 * g + (ln >> 2)) * P + 16 * (jb0 + j) + 4 * (ln & 3);
                     a[j][pr] = cat(lds_read_tr(kp), lds_read_tr(kp + 16 * P));
                 }
 #pragma unroll
@@ -1274,12 +1387,18 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
                 for (int j = 0; j < GB; ++j) dqa[jb0 + j] = mfma(a[j][pr], gl[pr], dqa[jb0 + j]);
             }
         }
+        __syncthreads();
+        issue2_second(p + 1);
     }
+    // the state's share beta_t n~ dden'_t, loaded now that no tile loads are in flight
+    const float bdd = beta * dd;
+    const float* nt = ss.n + ((size_t)bh * (in.G - 1) + (sg > 0 ? sg - 1 : 0)) * dqk;
     float qdq = 0.0f;
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) {
         const int j0 = 16 * jb + 4 * g;
         if (tval && j0 < dqk) {
+            if (sg > 0) dqa[jb] += bdd * load4(nt + j0);
             *reinterpret_cast<f32x4*>(dq + (tokh + t) * dqk + j0) = dqa[jb];
             const f32x4 q4 = load4(in.q + (tokh + t) * dqk + j0);
 #pragma unroll
@@ -1291,17 +1410,11 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
     if (tval && g == 0) ws.qdq[tokh + t] = qdq;
 }
 
-template <int D, int QB>
-struct alignas(16) ColsSmem {
-    bf16 q[QB * (D + 8)];
-    bf16 dh[QB * (D + 8)];      // dnum' hi
-    bf16 dl[QB * (D + 8)];      // dnum' lo
-    double rt[QB];              // F_t - m_t of the query block
-    float dd[QB];               // dden'_t
-};
-
 // per (head, key block of 64): dk, dv over query blocks >= it (QB queries at a
-// time), and k_s . dk_s (= di~_s)
+// time), and k_s . dk_s (= di~_s).  Items: first the QB-row slices of the state
+// gradient (two-level form; hi and lo), then the query slabs of the band (Q, dnum' hi,
+// dnum' lo and the slab's F_t - m_t and dden'_t).  With two LDS sets (all widths up to
+// 384) the next item loads into one set while the products run on the other.
 template <int D, int QB>
 __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdWs ws, SuperStates ss,
                                                           float* __restrict__ dk,
@@ -1310,18 +1423,78 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
     constexpr int P = D + 8;
     constexpr int NB = D / 16, KS = D / 32, TB = QB / 16;
     constexpr int CB = 2;                       // key / value blocks whose operands are read together
-    __shared__ ColsSmem<D, QB> sm;
+    constexpr int NBUF = 2 * 3 * QB * P * 2 <= 152 * 1024 ? 2 : 1;
+    constexpr int NW = DmaTile<QB, D>::MIN_PER_WAVE;
+    static_assert(TB % 2 == 0, "query slabs are whole MFMA k-steps");
+    __shared__ __attribute__((aligned(16))) bf16 sq[NBUF][QB * P];
+    __shared__ __attribute__((aligned(16))) bf16 sdh[NBUF][QB * P];    // dnum' hi, or state gradient hi
+    __shared__ __attribute__((aligned(16))) bf16 sdl[NBUF][QB * P];    // dnum' lo, or state gradient lo
+    __shared__ __attribute__((aligned(16))) double srt[NBUF][QB];      // F_t - m_t of the slab
+    __shared__ __attribute__((aligned(16))) float sdd[NBUF][QB];       // dden'_t
     int bh, cb;
     grid_block(in.heads, bh, cb);               // the first key blocks have the most query blocks
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, ln = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x, lane = tid & 63, ln = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int S = in.S, dqk = in.dqk, dv = in.dv;
     const size_t tokh = (size_t)bh * S;
     const int c0 = cb * 64;
     const int s = c0 + 16 * wave + ln;           // this lane's key
     const bool sval = s < S;
-    const double Qs = sval ? ws.F[tokh + s] - (double)in.i_pre[tokh + s] : 0.0;
+    const double Qs = sval ? ws.gk[tokh + s] : 0.0;
     const bf16* dnh_g = reinterpret_cast<const bf16*>(ws.dnum);
     const bf16* dnl_g = dnh_g + (size_t)in.heads * S * dv;
+
+    // two-level form: query blocks of this superchunk only, the later ones through the
+    // gradient of the state at the end of this superchunk, weighted by omega_s
+    const int sg = c0 / in.LS;
+    const int r_hi = min(S, (sg + 1) * in.LS);
+    const bf16* Nhi = ss.dC;
+    const bf16* Nlo = ss.dC;
+    int nsl = 0;
+    float omega = 0.0f;
+    if (sg < in.G - 1) {
+        Nhi = ss.dC + state_off(bh, sg, in.G, dv, dqk);
+        Nlo = Nhi + (size_t)dv * dqk;
+        nsl = (dv + QB - 1) / QB;
+        const int ep = (sg + 1) * in.LS - 1;
+        if (sval) omega = exp_arg(ws.F[tokh + ep] - Qs - ws.m[tokh + ep]);
+    }
+    const int np = nsl + (r_hi - c0 + QB - 1) / QB;
+
+    auto issue = [&](int p) __attribute__((always_inline)) {
+        if (p >= np) return;
+        const int b = NBUF == 2 ? (p & 1) : 0;
+        if (p < nsl) {
+            dma_tile<QB, D>(sdh[b], Nhi + (size_t)QB * p * dqk, dv - QB * p, dqk, wave, lane);
+            dma_tile<QB, D>(sdl[b], Nlo + (size_t)QB * p * dqk, dv - QB * p, dqk, wave, lane);
+        } else {
+            const int r0 = c0 + QB * (p - nsl);
+            dma_tile<QB, D>(sq[b], in.q + (tokh + r0) * dqk, S - r0, dqk, wave, lane);
+            dma_tile<QB, D>(sdh[b], dnh_g + (tokh + r0) * dv, S - r0, dv, wave, lane);
+            dma_tile<QB, D>(sdl[b], dnl_g + (tokh + r0) * dv, S - r0, dv, wave, lane);
+            const unsigned nq = (unsigned)min(QB, S - r0);
+            if (wave == 1) dma_span(srt[b], ws.rt + tokh + r0, 8u * nq, QB / 2, lane);
+            if (wave == 2) dma_span(sdd[b], ws.dden + tokh + r0, 4u * nq, QB / 4, lane);
+        }
+    };
+    // at item p: wait for its loads (the next item's may stay outstanding)
+    auto begin = [&](int p) __attribute__((always_inline)) {
+        if constexpr (NBUF == 2) {
+            __syncthreads();                    // item p - 1, the other set's user, is done
+            issue(p + 1);
+            if (p + 1 < nsl) wait_vm<2 * NW>();
+            else if (p + 1 < np) wait_vm<3 * NW>();
+            else wait_vm<0>();
+        } else {
+            if (p > 0) {
+                __syncthreads();
+                issue(p);
+            }
+            wait_vm<0>();
+        }
+        __syncthreads();
+    };
+    issue(0);
 
     // k_s and v_s as B operands (k-slot 8g + j <-> dimension 32 kk + 8g + j): held in
     // registers across all query blocks up to width 384; at 512 they do not fit and
@@ -1341,82 +1514,62 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
 #pragma unroll
     for (int b = 0; b < NB; ++b) dka[b] = dva[b] = f32x4{0, 0, 0, 0};
 
-    // two-level form: query blocks of this superchunk only, the later ones through the
-    // gradient of the state at the end of this superchunk, weighted by omega_s
-    const int sg = c0 / in.LS;
-    const int r_hi = min(S, (sg + 1) * in.LS);
-    if (sg < in.G - 1) {
-        const int ep = (sg + 1) * in.LS - 1;
-        const float omega = sval ? exp_arg(ws.F[tokh + ep] - Qs - ws.m[tokh + ep]) : 0.0f;
-        const bf16* Nhi = ss.dC + state_off(bh, sg, in.G, dv, dqk);
-        const bf16* Nlo = Nhi + (size_t)dv * dqk;
-        const float* dnt = ss.dn + ((size_t)bh * (in.G - 1) + sg) * dqk;
-        // QB-row slices of dC~ (hi into sm.dh, lo into sm.dl):
-        //   dv^T[n][s] += dC~[n][j] k_s[j]   (direct reads of the slice's rows n)
-        //   dk^T[j][s] += dC~^T[j][n] v_s[n] (transposing reads, n within the slice)
+    // QB-row slices of dC~ (hi, lo):
+    //   dv^T[n][s] += dC~[n][j] k_s[j]   (direct reads of the slice's rows n)
+    //   dk^T[j][s] += dC~^T[j][n] v_s[n] (transposing reads, n within the slice)
+    static_for<D / QB>([&](auto slc) __attribute__((always_inline)) {
+        constexpr int sl = decltype(slc)::value;
+        if (sl >= nsl) return;
+        begin(sl);
+        const bf16* th = sdh[NBUF == 2 ? (sl & 1) : 0];
+        const bf16* tl_ = sdl[NBUF == 2 ? (sl & 1) : 0];
 #pragma unroll
-        for (int sl = 0; sl < D / QB; ++sl) {
-            if (QB * sl >= dv) break;
-            __syncthreads();
-            stage_rows<QB, D, P, 4>(sm.dh, Nhi, 0, QB * sl, dv, dqk, tid);
-            stage_rows<QB, D, P, 4>(sm.dl, Nlo, 0, QB * sl, dv, dqk, tid);
-            __syncthreads();
+        for (int kk = 0; kk < KS; ++kk) {
+            const bf16x8 kbk = KV_REG ? kb[KV_REG ? kk : 0] : kop(kk);
 #pragma unroll
-            for (int kk = 0; kk < KS; ++kk) {
-                const bf16x8 kbk = KV_REG ? kb[KV_REG ? kk : 0] : kop(kk);
-#pragma unroll
-                for (int tb = 0; tb < TB; ++tb) {
-                    const int off = (16 * tb + ln) * P + 32 * kk + 8 * g;
-                    dva[TB * sl + tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.dh + off), kbk, dva[TB * sl + tb]);
-                    dva[TB * sl + tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.dl + off), kbk, dva[TB * sl + tb]);
-                }
-            }
-#pragma unroll
-            for (int kq = 0; kq < QB / 32; ++kq) {
-                const int kk = QB / 32 * sl + kq;
-                const bf16x8 vbk = KV_REG ? vb[KV_REG ? kk : 0] : vop(kk);
-#pragma unroll
-                for (int b0 = 0; b0 < NB; b0 += CB) {
-                    bf16x8 ah[CB], al[CB];
-#pragma unroll
-                    for (int j = 0; j < CB; ++j) {
-                        const int off = (32 * kq + 8 * g + (ln >> 2)) * P + 16 * (b0 + j) + 4 * (ln & 3);
-                        ah[j] = cat(lds_read_tr(sm.dh + off), lds_read_tr(sm.dh + off + 4 * P));
-                        al[j] = cat(lds_read_tr(sm.dl + off), lds_read_tr(sm.dl + off + 4 * P));
-                    }
-#pragma unroll
-                    for (int j = 0; j < CB; ++j) dka[b0 + j] = mfma(ah[j], vbk, dka[b0 + j]);
-#pragma unroll
-                    for (int j = 0; j < CB; ++j) dka[b0 + j] = mfma(al[j], vbk, dka[b0 + j]);
-                }
+            for (int tb = 0; tb < TB; ++tb) {
+                const int off = (16 * tb + ln) * P + 32 * kk + 8 * g;
+                dva[TB * sl + tb] = mfma(*reinterpret_cast<const bf16x8*>(th + off), kbk, dva[TB * sl + tb]);
+                dva[TB * sl + tb] = mfma(*reinterpret_cast<const bf16x8*>(tl_ + off), kbk, dva[TB * sl + tb]);
             }
         }
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
+        for (int kq = 0; kq < QB / 32; ++kq) {
+            const int kk = QB / 32 * sl + kq;
+            const bf16x8 vbk = KV_REG ? vb[KV_REG ? kk : 0] : vop(kk);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int jj = 16 * b + 4 * g + i;
-                dka[b][i] = omega * (dka[b][i] + (jj < dqk ? dnt[jj] : 0.0f));
-                dva[b][i] *= omega;
+            for (int b0 = 0; b0 < NB; b0 += CB) {
+                bf16x8 ah[CB], al[CB];
+#pragma unroll
+                for (int j = 0; j < CB; ++j) {
+                    const int off = (32 * kq + 8 * g + (ln >> 2)) * P + 16 * (b0 + j) + 4 * (ln & 3);
+                    ah[j] = cat(lds_read_tr(th + off), lds_read_tr(th + off + 4 * P));
+                    al[j] = cat(lds_read_tr(tl_ + off), lds_read_tr(tl_ + off + 4 * P));
+                }
+#pragma unroll
+                for (int j = 0; j < CB; ++j) dka[b0 + j] = mfma(ah[j], vbk, dka[b0 + j]);
+#pragma unroll
+                for (int j = 0; j < CB; ++j) dka[b0 + j] = mfma(al[j], vbk, dka[b0 + j]);
             }
+        }
+    });
+    if (nsl > 0) {
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            dka[b] *= omega;
+            dva[b] *= omega;
         }
     }
 
-    for (int r0 = c0; r0 < r_hi; r0 += QB) {
-        __syncthreads();
-        if constexpr (QB * D <= 32 * 384) {
-            stage_qd<QB, D, P>(sm.q, sm.dh, sm.dl, in.q, dnh_g, dnl_g, tokh, r0, S, dqk, dv, tid);
-        } else {
-            stage_rows<QB, D, P, 4>(sm.q, in.q, tokh, r0, S, dqk, tid);
-            stage_rows<QB, D, P, 4>(sm.dh, dnh_g, tokh, r0, S, dv, tid);
-            stage_rows<QB, D, P, 4>(sm.dl, dnl_g, tokh, r0, S, dv, tid);
-        }
-        if (tid < QB) {
-            const int tt = min(r0 + tid, S - 1);
-            sm.rt[tid] = ws.F[tokh + tt] - ws.m[tokh + tt];
-            sm.dd[tid] = r0 + tid < S ? ws.dden[tokh + tt] : 0.0f;
-        }
-        __syncthreads();
+    for (int p = nsl; p < np; ++p) {
+        const int r0 = c0 + QB * (p - nsl);
+        begin(p);
+        const int b = NBUF == 2 ? (p & 1) : 0;
+        const bf16* tq = sq[b];
+        const bf16* th = sdh[b];
+        const bf16* tl_ = sdl[b];
+        const double* rt = srt[b];
+        const float* ddp = sdd[b];
         // S[t][s] and dA[t][s] - dden'_t for the TB query blocks
         f32x4 sc[TB], da[TB];
 #pragma unroll
@@ -1428,9 +1581,9 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
                 const int off = (16 * tb + ln) * P + 32 * kk + 8 * g;
-                sc[tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.q + off), kbk, sc[tb]);
-                da[tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.dh + off), vbk, da[tb]);
-                da[tb] = mfma(*reinterpret_cast<const bf16x8*>(sm.dl + off), vbk, da[tb]);
+                sc[tb] = mfma(*reinterpret_cast<const bf16x8*>(tq + off), kbk, sc[tb]);
+                da[tb] = mfma(*reinterpret_cast<const bf16x8*>(th + off), vbk, da[tb]);
+                da[tb] = mfma(*reinterpret_cast<const bf16x8*>(tl_ + off), vbk, da[tb]);
             }
         }
         // P = S (.) D', G = (dA + dden') (.) D', as hi/lo B operands over query slots
@@ -1440,12 +1593,12 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tl = 16 * tb + 4 * g + i;
-                const float d = (sval && s <= r0 + tl && r0 + tl < S) ? exp_arg(sm.rt[tl] - Qs) : 0.0f;
+                const float d = (sval && s <= r0 + tl && r0 + tl < S) ? exp_arg(rt[tl] - Qs) : 0.0f;
                 bf16 hi, lo;
                 hilo(sc[tb][i] * d, hi, lo);
                 ph[tb >> 1][4 * (tb & 1) + i] = hi;
                 pl[tb >> 1][4 * (tb & 1) + i] = lo;
-                hilo((da[tb][i] + sm.dd[tl]) * d, hi, lo);
+                hilo((da[tb][i] + ddp[tl]) * d, hi, lo);
                 gh[tb >> 1][4 * (tb & 1) + i] = hi;
                 gl[tb >> 1][4 * (tb & 1) + i] = lo;
             }
@@ -1459,9 +1612,9 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
 #pragma unroll
                 for (int j = 0; j < CB; ++j) {
                     const int off = (32 * pr + 4 * g + (ln >> 2)) * P + 16 * (b0 + j) + 4 * (ln & 3);
-                    aq[j] = cat(lds_read_tr(sm.q + off), lds_read_tr(sm.q + off + 16 * P));
-                    ah[j] = cat(lds_read_tr(sm.dh + off), lds_read_tr(sm.dh + off + 16 * P));
-                    al[j] = cat(lds_read_tr(sm.dl + off), lds_read_tr(sm.dl + off + 16 * P));
+                    aq[j] = cat(lds_read_tr(tq + off), lds_read_tr(tq + off + 16 * P));
+                    ah[j] = cat(lds_read_tr(th + off), lds_read_tr(th + off + 16 * P));
+                    al[j] = cat(lds_read_tr(tl_ + off), lds_read_tr(tl_ + off + 16 * P));
                 }
 #pragma unroll
                 for (int j = 0; j < CB; ++j) dka[b0 + j] = mfma(aq[j], gh[pr], dka[b0 + j]);
@@ -1475,11 +1628,14 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
                 for (int j = 0; j < CB; ++j) dva[b0 + j] = mfma(al[j], ph[pr], dva[b0 + j]);
             }
     }
+    // the state gradient's share omega_s dn~, loaded now that no tile loads are in flight
+    const float* dnt = ss.dn + ((size_t)bh * (in.G - 1) + (nsl > 0 ? sg : 0)) * dqk;
     float kdk = 0.0f;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
         const int j0 = 16 * b + 4 * g;
         if (sval && j0 < dqk) {
+            if (nsl > 0) dka[b] += omega * load4(dnt + j0);
             *reinterpret_cast<f32x4*>(dk + (tokh + s) * dqk + j0) = dka[b];
             const f32x4 k4 = load4(in.k + (tokh + s) * dqk + j0);
 #pragma unroll
@@ -1954,7 +2110,7 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
     hipLaunchKernelGGL(bwd_gate_local, sgrid, dim3(BW_THREADS), 0, a.stream, a.i_pre, a.f_pre, a.S, w);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(bwd_gate_fix, sgrid, dim3(BW_THREADS), 0, a.stream, a.S, w);
+    hipLaunchKernelGGL(bwd_gate_fix, sgrid, dim3(BW_THREADS), 0, a.stream, a.i_pre, a.S, w);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if constexpr (sizeof(T) == 2) {
         if (bwd_gemm_path(a)) {
@@ -1964,7 +2120,7 @@ hipError_t launch_bwd_t(const BwdArgs& a) {
         switch (mfma_bwd_width(a)) {
             case 64: return launch_bwd_mfma<64, 64>(a, in, w, ss);
             case 128: return launch_bwd_mfma<128, 64>(a, in, w, ss);
-            case 256: return launch_bwd_mfma<256, 64>(a, in, w, ss);
+            case 256: return launch_bwd_mfma<256, 32>(a, in, w, ss);
             case 384: return launch_bwd_mfma<384, 32>(a, in, w, ss);
             case 512: return launch_bwd_mfma<512, 32>(a, in, w, ss);
             default: break;
