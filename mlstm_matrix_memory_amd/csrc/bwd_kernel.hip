@@ -934,11 +934,13 @@ __device__ __forceinline__ u32x4 span_rsrc(const void* base, unsigned bytes) {
 }
 
 // this lane's 16 bytes at byte offset voff of the descriptor's range into LDS at
-// dst + 16 * lane (dst is the wave's, so uniform).  M0 is saved and restored around
+// byte address la + 16 * lane (la is the wave's, so uniform).  M0 is saved and restored around
 // the load (the compiler keeps it as its own); one wait state between the M0 write
 // and the load that reads it.
-__device__ __forceinline__ void dma16(void* dst, unsigned voff, u32x4 rs) {
-    const unsigned la = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_ptr)dst);
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_ptr)p);
+}
+__device__ __forceinline__ void dma16(unsigned la, unsigned voff, u32x4 rs) {
     unsigned keep;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %1\n\ts_nop 0\n\t"
                  "buffer_load_dwordx4 %2, %3, 0 offen lds\n\ts_mov_b32 m0, %0"
@@ -963,33 +965,50 @@ struct DmaTile {
     static constexpr int MIN_PER_WAVE = NCH / 4;      // loads every wave issues for one tile, at least
 };
 
-// Rows [0, R) of a row-major bf16 block (row stride d elements, `rows` of them present)
-// into LDS at dst, columns [0, D).  Granules past the present rows or past column d,
-// and the padding granules, are read beyond the descriptor's range and land as zeros.
+// The byte offsets of this wave's granules of a tile whose rows are d elements apart,
+// one per 1 KB run (c = wave, wave + 4, ...), computed once per kernel: granule u =
+// 64 c + lane is row u / GR, column granule u % GR.  Granules past column d and the
+// padding granules get an offset beyond any descriptor's range (they land as zeros);
+// lanes past the end of the tile get NONE and issue nothing.
 template <int R, int D>
-__device__ __forceinline__ void dma_tile(bf16* dst, const bf16* src, int rows, int d, int wave, int lane) {
+struct DmaOffs {
+    using T = DmaTile<R, D>;
+    static constexpr int NI = (T::NCH + 3) / 4;
+    static constexpr unsigned NONE = 0xffffffffu;
+    unsigned o[NI];
+    __device__ __forceinline__ DmaOffs(int d, int wave, int lane) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int u = 64 * (wave + 4 * i) + lane;
+            const int r = u / T::GR, gc = u - r * T::GR;
+            o[i] = u >= T::TOT ? NONE
+                   : (gc < D / 8 && 8 * gc < d) ? (unsigned)(r * d + 8 * gc) * 2u : 0x80000000u;
+        }
+    }
+};
+
+// Rows [0, R) of a row-major bf16 block (`rows` rows present, at the stride the
+// offsets were made for) into LDS at byte address dst, columns [0, D); rows past `rows` read
+// beyond the descriptor's range and land as zeros.
+template <int R, int D>
+__device__ __forceinline__ void dma_tile(unsigned dst, const bf16* src, int rows, int d, const DmaOffs<R, D>& of,
+                                         int wave) {
     using T = DmaTile<R, D>;
     const unsigned bytes = rows > 0 ? (unsigned)(rows < R ? rows : R) * (unsigned)d * 2u : 0u;
     const u32x4 rs = span_rsrc(src, bytes);
-    // the lane's offsets are recomputed at every call rather than held in registers
-    // across the kernel (they are a few integer operations per load)
-    int l = lane;
-    asm volatile("" : "+v"(l));
 #pragma unroll
-    for (int c0 = 0; c0 < T::NCH; c0 += 4) {
-        const int c = c0 + wave;
+    for (int i = 0; i < DmaOffs<R, D>::NI; ++i) {
+        const int c = wave + 4 * i;
         if (c < T::NCH) {
-            const int u = 64 * c + l;
-            const int r = u / T::GR, gc = u - r * T::GR;
-            const unsigned off = (gc < D / 8 && 8 * gc < d) ? (unsigned)(r * d + 8 * gc) * 2u : 0x80000000u;
-            if (T::TOT % 64 == 0 || u < T::TOT) dma16(dst + 512 * c, off, rs);
+            if (T::TOT % 64 == 0 || i + 1 < DmaOffs<R, D>::NI) dma16(dst + 1024u * c, of.o[i], rs);
+            else if (of.o[i] != DmaOffs<R, D>::NONE) dma16(dst + 1024u * c, of.o[i], rs);
         }
     }
 }
 
-// n16 granules (n16 <= 64) of 16 bytes from src into LDS at dst by one wave; bytes past
-// `bytes` land as zeros
-__device__ __forceinline__ void dma_span(void* dst, const void* src, unsigned bytes, int n16, int lane) {
+// n16 granules (n16 <= 64) of 16 bytes from src into LDS at byte address dst by one
+// wave; bytes past `bytes` land as zeros
+__device__ __forceinline__ void dma_span(unsigned dst, const void* src, unsigned bytes, int n16, int lane) {
     const u32x4 rs = span_rsrc(src, bytes);
     if (lane < n16) dma16(dst, 16u * lane, rs);
 }
@@ -1046,33 +1065,36 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
 
     // loads of the tiles of pair p: state rows (hi, lo) or key block rows (K, V); the
     // key block's F_s - i~_s goes with the tile whose products come first
-    auto dma_state = [&](bf16* dst, const bf16* base, int p) __attribute__((always_inline)) {
-        dma_tile<64, D>(dst, base + (size_t)64 * p * dqk, dv - 64 * p, dqk, wave, lane);
+    const DmaOffs<64, D> ofk(dqk, wave, lane), ofv(dv, wave, lane);
+    const unsigned ak = lds_addr(sk), av = lds_addr(sv), ag = lds_addr(sgs);
+    auto dma_state = [&](unsigned dst, const bf16* base, int p) __attribute__((always_inline)) {
+        dma_tile<64, D>(dst, base + (size_t)64 * p * dqk, dv - 64 * p, dqk, ofk, wave);
     };
-    auto dma_keys = [&](bf16* dst, const bf16* x, int d, int cb, bool with_gs) __attribute__((always_inline)) {
-        dma_tile<64, D>(dst, x + (tokh + 64 * cb) * d, S - 64 * cb, d, wave, lane);
+    auto dma_keys = [&](unsigned dst, const bf16* x, int d, const DmaOffs<64, D>& of, int cb, bool with_gs)
+                        __attribute__((always_inline)) {
+        dma_tile<64, D>(dst, x + (tokh + 64 * cb) * d, S - 64 * cb, d, of, wave);
         if (with_gs && wave == 1)
-            dma_span(sgs[cb & 1], ws.gk + tokh + 64 * cb, 8u * (unsigned)min(64, S - 64 * cb), 32, lane);
+            dma_span(ag + 512u * (cb & 1), ws.gk + tokh + 64 * cb, 8u * (unsigned)min(64, S - 64 * cb), 32, lane);
     };
     auto issue1_first = [&](int p) __attribute__((always_inline)) {
         if (p >= np) return;
-        if (p < nsl) dma_state(sk, Chi, p);
-        else dma_keys(sk, in.k, dqk, cb_lo + p - nsl, true);
+        if (p < nsl) dma_state(ak, Chi, p);
+        else dma_keys(ak, in.k, dqk, ofk, cb_lo + p - nsl, true);
     };
     auto issue1_second = [&](int p) __attribute__((always_inline)) {
         if (p >= np) return;
-        if (p < nsl) dma_state(sv, Clo, p);
-        else dma_keys(sv, in.v, dv, cb_lo + p - nsl, false);
+        if (p < nsl) dma_state(av, Clo, p);
+        else dma_keys(av, in.v, dv, ofv, cb_lo + p - nsl, false);
     };
     auto issue2_first = [&](int p) __attribute__((always_inline)) {
         if (p >= np) return;
-        if (p < nsl) dma_state(sv, Clo, p);
-        else dma_keys(sv, in.v, dv, cb_lo + p - nsl, true);
+        if (p < nsl) dma_state(av, Clo, p);
+        else dma_keys(av, in.v, dv, ofv, cb_lo + p - nsl, true);
     };
     auto issue2_second = [&](int p) __attribute__((always_inline)) {
         if (p >= np) return;
-        if (p < nsl) dma_state(sk, Chi, p);
-        else dma_keys(sk, in.k, dqk, cb_lo + p - nsl, false);
+        if (p < nsl) dma_state(ak, Chi, p);
+        else dma_keys(ak, in.k, dqk, ofk, cb_lo + p - nsl, false);
     };
     // the first tile of pair p has landed once no more than the second one's loads are
     // outstanding; the second once no more than the next pair's first
@@ -1461,20 +1483,23 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
     }
     const int np = nsl + (r_hi - c0 + QB - 1) / QB;
 
+    const DmaOffs<QB, D> ofq(dqk, wave, lane), ofn(dv, wave, lane);
+    const unsigned aq = lds_addr(sq), ah = lds_addr(sdh), al = lds_addr(sdl), art = lds_addr(srt), add = lds_addr(sdd);
+    constexpr unsigned TILE_B = QB * P * 2;
     auto issue = [&](int p) __attribute__((always_inline)) {
         if (p >= np) return;
         const int b = NBUF == 2 ? (p & 1) : 0;
         if (p < nsl) {
-            dma_tile<QB, D>(sdh[b], Nhi + (size_t)QB * p * dqk, dv - QB * p, dqk, wave, lane);
-            dma_tile<QB, D>(sdl[b], Nlo + (size_t)QB * p * dqk, dv - QB * p, dqk, wave, lane);
+            dma_tile<QB, D>(ah + TILE_B * b, Nhi + (size_t)QB * p * dqk, dv - QB * p, dqk, ofq, wave);
+            dma_tile<QB, D>(al + TILE_B * b, Nlo + (size_t)QB * p * dqk, dv - QB * p, dqk, ofq, wave);
         } else {
             const int r0 = c0 + QB * (p - nsl);
-            dma_tile<QB, D>(sq[b], in.q + (tokh + r0) * dqk, S - r0, dqk, wave, lane);
-            dma_tile<QB, D>(sdh[b], dnh_g + (tokh + r0) * dv, S - r0, dv, wave, lane);
-            dma_tile<QB, D>(sdl[b], dnl_g + (tokh + r0) * dv, S - r0, dv, wave, lane);
+            dma_tile<QB, D>(aq + TILE_B * b, in.q + (tokh + r0) * dqk, S - r0, dqk, ofq, wave);
+            dma_tile<QB, D>(ah + TILE_B * b, dnh_g + (tokh + r0) * dv, S - r0, dv, ofn, wave);
+            dma_tile<QB, D>(al + TILE_B * b, dnl_g + (tokh + r0) * dv, S - r0, dv, ofn, wave);
             const unsigned nq = (unsigned)min(QB, S - r0);
-            if (wave == 1) dma_span(srt[b], ws.rt + tokh + r0, 8u * nq, QB / 2, lane);
-            if (wave == 2) dma_span(sdd[b], ws.dden + tokh + r0, 4u * nq, QB / 4, lane);
+            if (wave == 1) dma_span(art + 8u * QB * b, ws.rt + tokh + r0, 8u * nq, QB / 2, lane);
+            if (wave == 2) dma_span(add + 4u * QB * b, ws.dden + tokh + r0, 4u * nq, QB / 4, lane);
         }
     };
     // at item p: wait for its loads (the next item's may stay outstanding)
