@@ -130,8 +130,8 @@ def test_bf16_mfma_widths(orc, name, over):
 
 # the two-level form (sequences of 1024 tokens or more: superchunks of 256 tokens,
 # the earlier ones reached through the states at their ends) at every tile width,
-# with ragged last superchunks and tiles, unequal d_qk / d_v and the long-context
-# gates with input-gate spikes
+# with ragged last superchunks and tiles, unequal d_qk / d_v, widths below the tile
+# width and the long-context gates with input-gate spikes
 TWO_LEVEL_CASES = [
     ("lm_125m", dict(B=1, NH=1, S=1090, dqk=64, dv=48)),
     ("lm_125m", dict(B=2, NH=1, S=1030, dqk=128, dv=80)),
@@ -140,6 +140,9 @@ TWO_LEVEL_CASES = [
     ("lm_125m", dict(B=1, NH=1, S=1024, dqk=512, dv=512)),
     ("long_ctx", dict(B=1, NH=1, S=1200, dqk=112, dv=448)),
     ("long_ctx", dict(B=1, NH=1, S=2200, dqk=256, dv=256)),
+    # feature widths below the tile's (the tiles' columns past d_qk / d_v load as zeros)
+    ("long_ctx", dict(B=1, NH=2, S=1100, dqk=192, dv=240)),
+    ("lm_125m", dict(B=1, NH=1, S=1300, dqk=320, dv=384)),
 ]
 
 
