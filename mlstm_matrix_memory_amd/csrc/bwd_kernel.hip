@@ -1029,7 +1029,6 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
     // Up to width 256 two workgroups share a CU (two waves per SIMD, 256 registers
     // each): fewer operands are read ahead there.
     constexpr int GB = D <= 256 ? 2 : 4;        // value / key blocks whose operands are read together
-    constexpr int NW = DmaTile<64, D>::MIN_PER_WAVE;
     static_assert(NB % GB == 0, "width must be a multiple of 64");
     __shared__ __attribute__((aligned(16))) bf16 sk[64 * P];
     __shared__ __attribute__((aligned(16))) bf16 sv[64 * P];
@@ -1096,19 +1095,15 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
         if (p < nsl) dma_state(ak, Chi, p);
         else dma_keys(ak, in.k, dqk, ofk, cb_lo + p - nsl, false);
     };
-    // the first tile of pair p has landed once no more than the second one's loads are
-    // outstanding; the second once no more than the next pair's first
-    auto wait_first = [&]() __attribute__((always_inline)) {
-        wait_vm<NW>();
-        __syncthreads();
-    };
-    auto wait_second = [&](int p) __attribute__((always_inline)) {
-        if (p + 1 < np) wait_vm<NW>();
-        else wait_vm<0>();
+    // One tile is in flight at a time: before the products on a tile, wait for its
+    // loads and pass a barrier (after which every wave is done with the other
+    // buffer), then issue the other buffer's next tile, which loads during these
+    // products.
+    auto wait_all = [&]() __attribute__((always_inline)) {
+        wait_vm<0>();
         __syncthreads();
     };
     issue1_first(0);
-    issue1_second(0);
 
     // q_t as B operands: k-slot 8g + j <-> key dimension 32 kk + 8g + j
     bf16x8 qb[KS];
@@ -1150,7 +1145,8 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
     static_for<D / 64>([&](auto slc) __attribute__((always_inline)) {
         constexpr int sl = decltype(slc)::value;
         if (sl >= nsl) return;
-        wait_first();
+        wait_all();
+        issue1_second(sl);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             bf16x8 a[4];
@@ -1159,9 +1155,8 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) num[4 * sl + sb] = mfma(a[sb], qb[kk], num[4 * sl + sb]);
         }
-        __syncthreads();
+        wait_all();
         issue1_first(sl + 1);
-        wait_second(sl);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) {
             bf16x8 a[4];
@@ -1170,8 +1165,6 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
 #pragma unroll
             for (int sb = 0; sb < 4; ++sb) num[4 * sl + sb] = mfma(a[sb], qb[kk], num[4 * sl + sb]);
         }
-        __syncthreads();
-        issue1_second(sl + 1);
     });
     if (sg > 0) {
 #pragma unroll
@@ -1180,7 +1173,8 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
     for (int cb = cb_lo; cb <= rb; ++cb) {
         const int p = nsl + cb - cb_lo;
         const int c0 = 64 * cb;
-        wait_first();
+        wait_all();
+        issue1_second(p);
         f32x4 st[4];
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) st[sb] = f32x4{0, 0, 0, 0};
@@ -1202,8 +1196,6 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
         }
         float d[4][4];
         decay4(d, c0, sgs[cb & 1]);
-        __syncthreads();
-        issue1_first(p + 1);
         bf16x8 ph[2], pl[2];
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb)
@@ -1216,7 +1208,8 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
                 ph[sb >> 1][4 * (sb & 1) + i] = hi;
                 pl[sb >> 1][4 * (sb & 1) + i] = lo;
             }
-        wait_second(p);
+        wait_all();
+        issue1_first(p + 1);
         // operands of GB value blocks read together, then their products with
         // consecutive MFMAs on independent accumulators (LDS latency overlaps)
 #pragma unroll
@@ -1237,12 +1230,11 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
                 for (int j = 0; j < GB; ++j) num[nb0 + j] = mfma(a[j][pr], pl[pr], num[nb0 + j]);
             }
         }
-        __syncthreads();
-        issue1_second(p + 1);
     }
-    // both buffers are free: pass 2's first pair loads during the per-query phase
+    // pass 2's first tile loads during the per-query phase, once every wave is done
+    // with the last pass-1 tile in its buffer
+    __syncthreads();
     issue2_first(0);
-    issue2_second(0);
 
     // ---- per query: u, do~, dnum', dden' ------------------------------------
     den += __shfl_xor(den, 16, 64);
@@ -1302,9 +1294,6 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
     f32x4 dqa[NB];
 #pragma unroll
     for (int jb = 0; jb < NB; ++jb) dqa[jb] = f32x4{0, 0, 0, 0};
-    // the stores above are outstanding too: wait for everything once
-    wait_vm<0>();
-    __syncthreads();
     // dq^T[j][t] = beta_t (C~^T dnum'_t + n~ dden'_t)[j]: transposing reads of the
     // state slices, whose n order follows dnum''s k-slots (as V's in pass 1); the lo
     // slice (in sv) first, then the hi one (in sk)
@@ -1312,7 +1301,8 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
     static_for<D / 64>([&](auto slc) __attribute__((always_inline)) {
         constexpr int sl = decltype(slc)::value;
         if (sl >= nsl) return;
-        if (sl > 0) wait_first();
+        wait_all();
+        issue2_second(sl);
 #pragma unroll
         for (int jb0 = 0; jb0 < NB; jb0 += GI) {
             bf16x8 a[GI][2];
@@ -1328,9 +1318,8 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
 #pragma unroll
                 for (int j = 0; j < GI; ++j) dqa[jb0 + j] = mfma(a[j][pr], dnh[2 * sl + pr], dqa[jb0 + j]);
         }
-        __syncthreads();
+        wait_all();
         issue2_first(sl + 1);
-        wait_second(sl);
 #pragma unroll
         for (int jb0 = 0; jb0 < NB; jb0 += GI) {
             bf16x8 a[GI][2];
@@ -1349,8 +1338,6 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
                 for (int j = 0; j < GI; ++j) dqa[jb0 + j] = mfma(a[j][pr], dnl[2 * sl + pr], dqa[jb0 + j]);
             }
         }
-        __syncthreads();
-        issue2_second(sl + 1);
     });
     if (sg > 0) {
 #pragma unroll
@@ -1359,7 +1346,8 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
     for (int cb = cb_lo; cb <= rb; ++cb) {
         const int p = nsl + cb - cb_lo;
         const int c0 = 64 * cb;
-        if (p > 0) wait_first();
+        wait_all();
+        issue2_second(p);
         f32x4 da[4];
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb) da[sb] = f32x4{0, 0, 0, 0};
@@ -1378,8 +1366,6 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
         }
         float d[4][4];
         decay4(d, c0, sgs[cb & 1]);
-        __syncthreads();
-        issue2_first(p + 1);
         bf16x8 gh[2], gl[2];
 #pragma unroll
         for (int sb = 0; sb < 4; ++sb)
@@ -1390,7 +1376,8 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
                 gh[sb >> 1][4 * (sb & 1) + i] = hi;
                 gl[sb >> 1][4 * (sb & 1) + i] = lo;
             }
-        wait_second(p);
+        wait_all();
+        issue2_first(p + 1);
 #pragma unroll
         for (int jb0 = 0; jb0 < NB; jb0 += GB) {
             bf16x8 a[GB][2];
@@ -1409,8 +1396,6 @@ __global__ __launch_bounds__(MB_THREADS, D <= 256 ? 2 : 1) void bwd_rows_mfma(Bw
                 for (int j = 0; j < GB; ++j) dqa[jb0 + j] = mfma(a[j][pr], gl[pr], dqa[jb0 + j]);
             }
         }
-        __syncthreads();
-        issue2_second(p + 1);
     }
     // the state's share beta_t n~ dden'_t, loaded now that no tile loads are in flight
     const float bdd = beta * dd;
@@ -1446,7 +1431,6 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
     constexpr int NB = D / 16, KS = D / 32, TB = QB / 16;
     constexpr int CB = 2;                       // key / value blocks whose operands are read together
     constexpr int NBUF = 2 * 3 * QB * P * 2 <= 152 * 1024 ? 2 : 1;
-    constexpr int NW = DmaTile<QB, D>::MIN_PER_WAVE;
     static_assert(TB % 2 == 0, "query slabs are whole MFMA k-steps");
     __shared__ __attribute__((aligned(16))) bf16 sq[NBUF][QB * P];
     __shared__ __attribute__((aligned(16))) bf16 sdh[NBUF][QB * P];    // dnum' hi, or state gradient hi
@@ -1502,22 +1486,22 @@ __global__ __launch_bounds__(MB_THREADS) void bwd_cols_mfma(BwdIn<bf16> in, BwdW
             if (wave == 2) dma_span(add + 4u * QB * b, ws.dden + tokh + r0, 4u * nq, QB / 4, lane);
         }
     };
-    // at item p: wait for its loads (the next item's may stay outstanding)
+    // at item p: wait for its loads and pass a barrier (after which item p - 1, the
+    // other set's user, is done everywhere), then issue item p + 1 into that set; with
+    // one set, the next item is issued only after this one's products
     auto begin = [&](int p) __attribute__((always_inline)) {
         if constexpr (NBUF == 2) {
-            __syncthreads();                    // item p - 1, the other set's user, is done
+            wait_vm<0>();
+            __syncthreads();
             issue(p + 1);
-            if (p + 1 < nsl) wait_vm<2 * NW>();
-            else if (p + 1 < np) wait_vm<3 * NW>();
-            else wait_vm<0>();
         } else {
             if (p > 0) {
                 __syncthreads();
                 issue(p);
             }
             wait_vm<0>();
+            __syncthreads();
         }
-        __syncthreads();
     };
     issue(0);
 
