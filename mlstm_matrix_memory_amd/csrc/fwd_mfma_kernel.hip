@@ -63,6 +63,35 @@ __device__ __forceinline__ bf16x8 cvt8(f32x4 a, f32x4 b) {
                   (bf16)b[0], (bf16)b[1], (bf16)b[2], (bf16)b[3]};
 }
 
+// Two floats to a pair of bf16 (round to nearest even), first in the low half.
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(4))) unsigned u32x4;
+__device__ __forceinline__ unsigned pk2(float a, float b) {
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+
+// x = hi + lo for eight floats.  Each pair is rounded once into its packed hi word
+// and the two hi values are read back from that word's halves (a shift and a mask),
+// so a float costs one subtraction and two half-conversions besides.
+__device__ __forceinline__ void split8(f32x4 x0, f32x4 x1, bf16x8& hi, bf16x8& lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = i < 2 ? x0[2 * i] : x1[2 * i - 4], b = i < 2 ? x0[2 * i + 1] : x1[2 * i - 3];
+        h[i] = pk2(a, b);
+        l[i] = pk2(a - __builtin_bit_cast(float, h[i] << 16), b - __builtin_bit_cast(float, h[i] & 0xffff0000u));
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
+// x = hi + lo for the products w * v of one weight and eight bf16 values
+__device__ __forceinline__ void split8w(float w, bf16x8 v, bf16x8& hi, bf16x8& lo) {
+    split8(f32x4{w * (float)v[0], w * (float)v[1], w * (float)v[2], w * (float)v[3]},
+           f32x4{w * (float)v[4], w * (float)v[5], w * (float)v[6], w * (float)v[7]}, hi, lo);
+}
+
 // Sum over the 16 lanes of each row of a wave with DPP lane permutes (VALU only,
 // no LDS round trips): swap neighbours, swap pairs, mirror within 8, mirror within 16.
 __device__ __forceinline__ float row16_sum(float x) {
@@ -705,14 +734,8 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
             if (idx < UNITS) {
                 const int row = idx / (SS_TILE / 8), c8 = 8 * (idx % (SS_TILE / 8));
                 *reinterpret_cast<bf16x8*>(sk + row * SS_P + c8) = rk[u];
-                const float om = rw[u] * A;
                 bf16x8 xh, xl;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float x = om * (float)rv[u][e];
-                    xh[e] = (bf16)x;
-                    xl[e] = (bf16)(x - (float)xh[e]);
-                }
+                split8w(rw[u] * A, rv[u], xh, xl);
                 *reinterpret_cast<bf16x8*>(svh + row * SS_P + c8) = xh;
                 *reinterpret_cast<bf16x8*>(svl + row * SS_P + c8) = xl;
             }
@@ -791,12 +814,6 @@ __global__ __launch_bounds__(SC_THREADS) void seg_combine_kernel(Ws ws, int nC, 
 }
 
 // bf16 hi + lo split of two f32x4 state blocks into one B operand (8 key rows)
-__device__ __forceinline__ void split8(f32x4 x0, f32x4 x1, bf16x8& hi, bf16x8& lo) {
-    hi = cvt8(x0, x1);
-    f32x4 r0 = x0 - f32x4{(float)hi[0], (float)hi[1], (float)hi[2], (float)hi[3]};
-    f32x4 r1 = x1 - f32x4{(float)hi[4], (float)hi[5], (float)hi[6], (float)hi[7]};
-    lo = cvt8(r0, r1);
-}
 
 // ---------------------------------------------------------------------------
 // kernel 2, pipelined form (chunks of 32 or 64 tokens)
@@ -949,14 +966,8 @@ __device__ __forceinline__ void chunk_store(const f32x4 (&reg)[Pref<C>::NCH], co
         const int row = idx / (C::TV / 8), col = 8 * (idx % (C::TV / 8));
         *reinterpret_cast<f32x4*>(sm.v + row * C::VP + col) = reg[u];
         const bf16x8 vb = __builtin_bit_cast(bf16x8, reg[u]);
-        const float wi = wrow[u] * inv_sig;
         bf16x8 h, l;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float xv = wi * (float)vb[e];
-            h[e] = (bf16)xv;
-            l[e] = (bf16)(xv - (float)h[e]);
-        }
+        split8w(wrow[u] * inv_sig, vb, h, l);
         *reinterpret_cast<bf16x8*>(sm.vwh + row * C::VP + col) = h;
         *reinterpret_cast<bf16x8*>(sm.vwl + row * C::VP + col) = l;
     });
@@ -1420,14 +1431,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan4_kernel(
                 const f32x4 val = col < vcols ? rv[u] : f32x4{0, 0, 0, 0};
                 *reinterpret_cast<f32x4*>(vr + row * VP + col) = val;
                 const bf16x8 vb8 = __builtin_bit_cast(bf16x8, val);
-                const float wi = rw[u] * inv_sig;
                 bf16x8 hh, ll;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float xv = wi * (float)vb8[e];
-                    hh[e] = (bf16)xv;
-                    ll[e] = (bf16)(xv - (float)hh[e]);
-                }
+                split8w(rw[u] * inv_sig, vb8, hh, ll);
                 *reinterpret_cast<bf16x8*>(vh + row * VP + col) = hh;
                 *reinterpret_cast<bf16x8*>(vl2 + row * VP + col) = ll;
             }
