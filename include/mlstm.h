@@ -103,16 +103,22 @@ size_t mlstm_fwd_workspace_bytes(int B, int NH, int S, int d_qk, int d_v, int ch
  * from chunk to chunk.  Results agree with the token-by-token recurrence up to
  * rounding for every chunk size.
  *
- * Where it runs: bf16 inputs with d_qk a multiple of 64 up to 1024 run on the
- * matrix cores (MFMA), in chunks of 64 tokens (also for chunk = 128, and for
- * chunk = 16 or 32 except d_qk 128 and 384 at chunk 32, which have tilings of
- * their own); when S is not a multiple of that, the last S mod 64 tokens run on
- * the vector-ALU kernel.  fp32 inputs and every other d_qk run entirely on the
- * vector ALUs, which is correct at every size but two to three orders of
- * magnitude slower on wide heads (d_qk = 2048: about 0.7 TFLOP/s).  Only the
- * matrix-core path uses the workspace; at d_qk 512 and 1024 it also holds copies
- * of q and k in the order the matrix-core operands are read (2 * B*NH*S*d_qk
- * bf16 elements).
+ * Where it runs: bf16 inputs with d_qk up to 1024 run on the matrix cores
+ * (MFMA), in chunks of 64 tokens (also for chunk = 128, and for chunk = 16 or 32
+ * except d_qk 128 and 384 at chunk 32, which have tilings of their own); when S
+ * is not a multiple of that, the last S mod 64 tokens run on the vector-ALU
+ * kernel.  The matrix-core tilings cover d_qk multiples of 64; any other d_qk
+ * runs at the next multiple of 64 on copies of q and k (and of C_init, n_init)
+ * padded with zero key columns, which change no product of the cell (section
+ * 2.3: q and k enter only through contractions over the key dimension); the
+ * final C' and n' are narrowed back to d_qk.  fp32 inputs and bf16 d_qk above
+ * 1024 run entirely on the vector ALUs, which is correct at every size but two
+ * to three orders of magnitude slower on wide heads (d_qk = 2048: about 0.7
+ * TFLOP/s).  Only the matrix-core path uses the workspace; at (padded) d_qk 512
+ * and 1024 it also holds copies of q and k in the order the matrix-core operands
+ * are read (2 * B*NH*S*d_qk bf16 elements), and at a padded d_qk the padded
+ * copies of q and k (2 * B*NH*S*d_pad bf16) and of the initial and final C'
+ * and n' (2 * B*NH*(d_v + 1)*d_pad fp32).
  *
  * Arguments
  *   q, k, v         inputs, dtype, layouts above (read only)

@@ -37,13 +37,20 @@ class MlstmError(RuntimeError):
 
 
 def load_library(path: str = LIBRARY) -> ctypes.CDLL:
-    """Load libmlstm.so; raises if it has not been built (no fallback exists)."""
+    """Load libmlstm.so; raises if it has not been built (no fallback exists).
+
+    torch is imported first.  The library's HIP runtime dependency
+    (libamdhip64.so.7) then binds to the runtime torch has already loaded, so the
+    device pointers and streams torch hands over belong to the runtime that
+    launches the kernels.  Loaded before torch, the library would bring up a
+    second HIP runtime beside torch's, which does not see the device."""
     global _lib
     if _lib is not None and path == LIBRARY:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
                            "or `python mlstm_matrix_memory_amd/build.py`")
+    import torch  # noqa: F401  (loads torch's HIP runtime before the library's dependency is resolved)
     lib = ctypes.CDLL(path)
     vp, fp, i, sz = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.mlstm_fwd_workspace_bytes.restype = sz

@@ -77,27 +77,50 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // MFMA path executes (see mfma_fwd_chunk) on that path when it covers the shape,
 // the rest (a ragged tail, or everything on the fp32 path and on shapes the MFMA
 // path does not cover) on the VALU kernel.  Between the two, the state passes
-// through the workspace.
+// through the workspace.  A bf16 key width below 1024 that is not a multiple of
+// 64 runs on the MFMA path at the next multiple of 64, from zero-padded copies of
+// q and k (and of a given C'_0 and n'_0) in the workspace; zero key columns add
+// nothing to any product of the cell, and the final C' and n' are narrowed back.
+constexpr int KEY_PAD = 64;
+constexpr int KEY_PAD_MAX = 1024;
+
 struct FwdPlan {
     int S_main;             // tokens on the MFMA path (0 = none)
     bool tail;              // the VALU kernel runs over [S_main, S)
+    int dq_run;             // key width the MFMA path runs at (d_qk, or d_qk padded)
+    bool pad;               // dq_run > d_qk: the MFMA path runs on padded copies
     size_t main_bytes;      // workspace of the MFMA path
+    size_t qk_bytes;        // one padded copy of q or k (whole sequences)
+    size_t cpad_bytes;      // one padded C' (initial or final)
+    size_t npad_bytes;      // one padded n' (initial or final)
+    size_t pad_bytes;       // all padded copies
     size_t mid_bytes;       // state handed from the MFMA path to the tail
-    size_t total() const { return align256(main_bytes) + mid_bytes; }
+    size_t total() const { return align256(main_bytes) + pad_bytes + mid_bytes; }
 };
 
 FwdPlan plan_fwd(int B, int NH, int S, int dqk, int dv, int chunk, mlstm_dtype dt) {
     FwdPlan pl = {};
-    const int L = mlstm::mfma_fwd_chunk(make_fwd_args(B, NH, S, dqk, dv, chunk, dt));
+    pl.dq_run = dqk;
+    const int dq_run = (dt == MLSTM_BF16 && dqk % KEY_PAD != 0 && dqk < KEY_PAD_MAX)
+                           ? (dqk + KEY_PAD - 1) / KEY_PAD * KEY_PAD : dqk;
+    const int L = mlstm::mfma_fwd_chunk(make_fwd_args(B, NH, S, dq_run, dv, chunk, dt));
     const int S_main = L > 0 ? S - S % L : 0;
-    mlstm::FwdArgs a = make_fwd_args(B, NH, S_main, dqk, dv, chunk, dt);
+    mlstm::FwdArgs a = make_fwd_args(B, NH, S_main, dq_run, dv, chunk, dt);
+    const size_t heads = (size_t)B * NH;
     if (S_main > 0 && dt == MLSTM_BF16 && mlstm::mfma_fwd_supported(a)) {
         pl.S_main = S_main;
         pl.main_bytes = mlstm::mfma_fwd_workspace_bytes(a);
+        pl.dq_run = dq_run;
+        pl.pad = dq_run != dqk;
+    }
+    if (pl.pad) {
+        pl.qk_bytes = align256(heads * (size_t)S * pl.dq_run * 2);
+        pl.cpad_bytes = align256(heads * (size_t)dv * pl.dq_run * 4);
+        pl.npad_bytes = align256(heads * (size_t)pl.dq_run * 4);
+        pl.pad_bytes = 2 * pl.qk_bytes + 2 * (pl.cpad_bytes + pl.npad_bytes);
     }
     pl.tail = pl.S_main < S;
     if (pl.tail && pl.S_main > 0) {
-        const size_t heads = (size_t)B * NH;
         pl.mid_bytes = align256(heads * dv * dqk * 4) + align256(heads * dqk * 4) + align256(heads * 4);
     }
     return pl;
@@ -242,23 +265,58 @@ static mlstm_status fwd_common(const void* q, const void* k, const void* v,
     }
     hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     hipError_t e = hipSuccess;
-    // state handed from the MFMA part to the tail, in the workspace after the MFMA part's own
+    // the workspace: the MFMA part's own, then the padded copies, then the state
+    // handed from the MFMA part to the tail
+    char* pad_base = (char*)workspace + align256(pl.main_bytes);
     float* C_mid = nullptr; float* n_mid = nullptr; float* m_mid = nullptr;
     if (pl.mid_bytes > 0) {
-        char* base = (char*)workspace + align256(pl.main_bytes);
+        char* base = pad_base + pl.pad_bytes;
         C_mid = (float*)base;
         n_mid = (float*)(base + align256(heads * d_v * d_qk * 4));
         m_mid = (float*)(base + align256(heads * d_v * d_qk * 4) + align256(heads * d_qk * 4));
     }
     if (pl.S_main > 0) {
-        mlstm::FwdArgs a = make_fwd_args(B, NH, pl.S_main, d_qk, d_v, chunk, dtype);
+        mlstm::FwdArgs a = make_fwd_args(B, NH, pl.S_main, pl.dq_run, d_v, chunk, dtype);
         a.Sx = S;
         a.q = q; a.k = k; a.v = v; a.i_pre = i_pre; a.f_pre = f_pre; a.o_pre = o_pre; a.h = h_out;
-        a.C = pl.tail ? C_mid : C_final; a.n = pl.tail ? n_mid : n_final; a.m = pl.tail ? m_mid : m_final;
+        float* C_dst = pl.tail ? C_mid : C_final;
+        float* n_dst = pl.tail ? n_mid : n_final;
+        a.C = C_dst; a.n = n_dst; a.m = pl.tail ? m_mid : m_final;
         a.C0 = C_init; a.n0 = n_init; a.m0 = m_init;
         a.ws = workspace; a.ws_bytes = pl.main_bytes; a.stream = st;
-        if (stages & 1) e = mlstm::launch_fwd_mfma_prepare(a);
-        if (e == hipSuccess && (stages & 2)) e = mlstm::launch_fwd_mfma_scan(a);
+        if (pl.pad) {
+            // zero-padded copies (whole sequences, so the token stride stays S); the
+            // staged entry points take no initial state, so C'_0 and n'_0 only come
+            // with both stages
+            char* p = pad_base;
+            void* q_p = p; p += pl.qk_bytes;
+            void* k_p = p; p += pl.qk_bytes;
+            float* C0_p = (float*)p; p += pl.cpad_bytes;
+            float* n0_p = (float*)p; p += pl.npad_bytes;
+            float* C_p = (float*)p; p += pl.cpad_bytes;
+            float* n_p = (float*)p;
+            const size_t el = 2, rows = heads * (size_t)S;
+            if (stages & 1) {
+                e = mlstm::launch_copy_cols(q, q_p, rows, (size_t)d_qk * el, (size_t)pl.dq_run * el, st);
+                if (e == hipSuccess) e = mlstm::launch_copy_cols(k, k_p, rows, (size_t)d_qk * el, (size_t)pl.dq_run * el, st);
+                if (e == hipSuccess && given == 3)
+                    e = mlstm::launch_copy_cols(C_init, C0_p, heads * d_v, (size_t)d_qk * 4, (size_t)pl.dq_run * 4, st);
+                if (e == hipSuccess && given == 3)
+                    e = mlstm::launch_copy_cols(n_init, n0_p, heads, (size_t)d_qk * 4, (size_t)pl.dq_run * 4, st);
+            }
+            a.q = q_p; a.k = k_p;
+            if (given == 3) { a.C0 = C0_p; a.n0 = n0_p; }
+            a.C = C_p; a.n = n_p;
+            if (e == hipSuccess && (stages & 1)) e = mlstm::launch_fwd_mfma_prepare(a);
+            if (e == hipSuccess && (stages & 2)) e = mlstm::launch_fwd_mfma_scan(a);
+            if (e == hipSuccess && (stages & 2))
+                e = mlstm::launch_copy_cols(C_p, C_dst, heads * d_v, (size_t)pl.dq_run * 4, (size_t)d_qk * 4, st);
+            if (e == hipSuccess && (stages & 2))
+                e = mlstm::launch_copy_cols(n_p, n_dst, heads, (size_t)pl.dq_run * 4, (size_t)d_qk * 4, st);
+        } else {
+            if (stages & 1) e = mlstm::launch_fwd_mfma_prepare(a);
+            if (e == hipSuccess && (stages & 2)) e = mlstm::launch_fwd_mfma_scan(a);
+        }
     }
     if (e == hipSuccess && pl.tail && (stages & 2)) {
         mlstm::FwdArgs a = make_fwd_args(B, NH, S, d_qk, d_v, chunk, dtype);

@@ -173,6 +173,12 @@ size_t mfma_fwd_workspace_bytes(const FwdArgs& a);
 hipError_t launch_fwd_mfma_prepare(const FwdArgs& a);
 hipError_t launch_fwd_mfma_scan(const FwdArgs& a);
 
+// Row-major rows of src_row_bytes copied to rows of dst_row_bytes: zero-filled
+// past the source width when widening, cut when narrowing (16-byte units where
+// both widths and both pointers allow, else 4-byte units)
+hipError_t launch_copy_cols(const void* src, void* dst, size_t rows, size_t src_row_bytes, size_t dst_row_bytes,
+                            hipStream_t stream);
+
 // backward of the zero-state forward (tiled quadratic form on the vector ALUs)
 size_t bwd_workspace_bytes(const BwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);

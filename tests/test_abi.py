@@ -373,6 +373,18 @@ def test_bf16_widths_with_a_tiling_take_the_matrix_core_path(S, dqk, chunk):
     assert b.mlstm_fwd_workspace_bytes(1, 2, S, dqk, 64, chunk, b.MLSTM_BF16) > 0
 
 
-@pytest.mark.parametrize("dqk,chunk,dt", [(2048, 64, b.MLSTM_BF16), (96, 64, b.MLSTM_BF16), (256, 64, b.MLSTM_F32)])
+@pytest.mark.parametrize("dqk,chunk,dt", [(2048, 64, b.MLSTM_BF16), (1088, 64, b.MLSTM_BF16), (256, 64, b.MLSTM_F32)])
 def test_shapes_without_a_tiling_run_on_the_vector_alus(dqk, chunk, dt):
     assert b.mlstm_fwd_workspace_bytes(1, 2, 256, dqk, 64, chunk, dt) == 0
+
+
+@pytest.mark.parametrize("dqk,chunk", [(96, 64), (16, 16), (48, 32), (1008, 64), (464, 128)])
+def test_bf16_widths_off_the_tiling_grid_take_the_matrix_core_path_padded(dqk, chunk):
+    # below 1024, a bf16 key width that is not a multiple of 64 runs at the next multiple
+    # of 64 from zero-padded copies of q and k, which the workspace holds besides the
+    # padded width's own workspace
+    pad = (dqk + 63) // 64 * 64
+    S, heads, dv = 256, 2, 64
+    own = b.mlstm_fwd_workspace_bytes(1, 2, S, pad, dv, chunk, b.MLSTM_BF16)
+    got = b.mlstm_fwd_workspace_bytes(1, 2, S, dqk, dv, chunk, b.MLSTM_BF16)
+    assert own > 0 and got >= own + 2 * heads * S * pad * 2

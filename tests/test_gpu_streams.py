@@ -64,3 +64,30 @@ def test_step_on_a_side_stream():
     errs = {}
     for name, g, r in (("h", h, rh), ("C", C, rC), ("n", n, rn), ("m", m, rm)):
         check(name, to_np(g), r, TOL["bf16"], errs)
+
+
+def test_library_loaded_before_torch_touches_the_gpu():
+    # A fresh process that loads the library (a workspace query) before torch has
+    # used the GPU must still launch on torch's HIP runtime: the binding imports
+    # torch before loading the library, so one runtime serves both.
+    import os
+    import subprocess
+    import sys
+    announce("fwd in a fresh process that loads the library before torch uses the GPU")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from mlstm_matrix_memory_amd import MLSTM_BF16, mlstm_fwd_workspace_bytes, mlstm_fwd_parallel\n"
+        "assert mlstm_fwd_workspace_bytes(1, 2, 128, 96, 64, 64, MLSTM_BF16) > 0\n"
+        "import torch\n"
+        "g = torch.Generator().manual_seed(1)\n"
+        "q, k = (torch.randn(1, 2, 128, 96, generator=g).to('cuda', torch.bfloat16) for _ in range(2))\n"
+        "v = torch.randn(1, 2, 128, 64, generator=g).to('cuda', torch.bfloat16)\n"
+        "i, f = (torch.randn(1, 2, 128, generator=g).cuda() for _ in range(2))\n"
+        "o = torch.randn(1, 2, 128, 64, generator=g).cuda()\n"
+        "h, C, n, m = mlstm_fwd_parallel(q, k, v, i, f + 3.0, o, 64)\n"
+        "torch.cuda.synchronize()\n"
+        "assert bool(torch.isfinite(h.float()).all()) and bool(torch.isfinite(C).all())\n"
+        "print('ok')\n" % root)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0 and r.stdout.strip().endswith("ok"), r.stdout + r.stderr

@@ -56,6 +56,14 @@ def test_noalloc_streaming_scan_two_calls_second_smaller():
     _run_both(dict(B=1, NH=2, S=256, dqk=512, dv=512), 64, 823)
 
 
+def test_noalloc_padded_key_width_two_calls_second_smaller():
+    # a key width that is not a multiple of 64 runs on zero-padded copies of q and k,
+    # which the scratch also holds
+    announce("fwd noalloc: B=1 NH=2 S=512 dqk=96 dv=80 chunk=64, then B=1 NH=1 S=256 dqk=48 dv=64 chunk=64")
+    _run_both(dict(B=1, NH=2, S=512, dqk=96, dv=80), 64, 824)
+    _run_both(dict(B=1, NH=1, S=256, dqk=48, dv=64), 64, 825)
+
+
 def test_noalloc_rejects_a_forward_larger_than_its_scratch():
     from mlstm_matrix_memory_amd import MLSTM_BF16, binding
     lib = binding.load_library()
