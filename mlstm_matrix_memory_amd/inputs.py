@@ -67,6 +67,8 @@ WORKLOADS = {
     "long_ctx": Workload("long_ctx", "fwd", 1, 8, 32768, 256, 256, 128, "bf16",
                          i_mu=0.0, i_sd=8.0, f_mu=1.0, f_sd=2.0, spike_frac=0.01, seed=4),
     "decode": Workload("decode", "step", 256, 4, 128, 512, 512, 0, "bf16", scale_k=False, seed=5),
+    # a key width off the matrix cores' 64-column grid (runs zero-padded to 128)
+    "lm_125m_d96": Workload("lm_125m_d96", "fwd", 8, 4, 2048, 96, 96, 64, "bf16", seed=7),
     # sLSTM: d_qk = d_v = d_h, the cells per head (embedding 768 over 4 heads)
     "slstm_125m": Workload("slstm_125m", "slstm", 8, 4, 2048, 192, 192, 0, "bf16", seed=6),
 }
