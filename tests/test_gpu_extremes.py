@@ -96,6 +96,8 @@ SHAPES = [
     ("segmented", "long_ctx", dict(B=1, NH=1, S=4096, dqk=256, dv=256), 128, "bf16", 512),
     # width 512 (the streaming form of the scan) over 2048 tokens: 8 segments of 256
     ("streaming_segmented", "lm_1_3b", dict(B=1, NH=1, S=2048, dqk=512, dv=512), 64, "bf16", 256),
+    # a key width off the 64-column grid: zero-padded to the width-128 tiling
+    ("padded_d96", "lm_125m", dict(B=1, NH=2, S=512, dqk=96, dv=80), 64, "bf16", None),
     # the fp32 path
     ("fp32_c64", "tiny", dict(B=1, NH=2, S=256, dqk=48, dv=80), 64, "f32", None),
     ("fp32_c16", "tiny", dict(B=1, NH=2, S=256, dqk=48, dv=80), 16, "f32", None),
@@ -146,6 +148,7 @@ STATE_CASES = [
     ("one_token_between", "lm_125m", dict(B=1, NH=2, S=300, dqk=384, dv=384), (128, 129), 64, "bf16"),
     ("S1_only", "lm_125m", dict(B=2, NH=2, S=1, dqk=128, dv=96), (), 64, "bf16"),
     ("S17_only", "lm_1_3b", dict(B=1, NH=1, S=17), (), 64, "bf16"),
+    ("padded_pieces", "lm_125m", dict(B=1, NH=2, S=200, dqk=96, dv=64), (1, 65), 64, "bf16"),
     ("fp32_short_pieces", "tiny", dict(B=2, NH=2, S=90, dqk=48, dv=80), (1, 18, 19), 16, "f32"),
 ]
 
