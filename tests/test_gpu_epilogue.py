@@ -32,10 +32,11 @@ def _run(e, dtype, eps, act, inplace=None):
 def _compare(orc, e, dtype, eps=1e-5, act=0, inplace=None):
     y = _run(e, dtype, eps, act, inplace)
     r = orc.epilogue(e["h"], e["x"], e["z"], e["gn_w"], e["gn_b"], e["skip_w"], eps, act)
-    if dtype == "bf16":
-        r = inputs.bf16_round(r.astype(np.float32)).astype(np.float64)  # y is stored in bf16
     errs = {}
+    # against the oracle itself, and (bf16) against its output rounded as y is stored
     check("y", y, r, TOL[dtype], errs)
+    if dtype == "bf16":
+        check("y_rounded", y, inputs.bf16_round(r.astype(np.float32)).astype(np.float64), TOL[dtype], errs)
     return errs
 
 

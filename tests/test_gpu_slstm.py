@@ -33,9 +33,11 @@ def _compare(orc, x, dtype, forget=0, state=None):
     got = _run(x, dtype, forget, state)
     ref = orc.slstm(x["x_pre"], x["R"], forget, *(state if state is not None else []))
     ref = list(ref)
-    if dtype == "bf16":
-        ref[0] = inputs.bf16_round(ref[0].astype(np.float32)).astype(np.float64)   # h is stored in bf16
     errs = {}
+    if dtype == "bf16":
+        # h against the oracle itself here, and below against its output rounded as h is stored
+        check("h_unrounded", got[0], ref[0], TOL[dtype], errs)
+        ref[0] = inputs.bf16_round(ref[0].astype(np.float32)).astype(np.float64)
     # c and n are the stabilized states (c e^{-m}, n e^{-m}); once m matches, each is
     # fixed on its own, so each is compared, and so is their ratio (what h is made of)
     check("h", got[0], ref[0], TOL[dtype], errs)
