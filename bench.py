@@ -223,6 +223,8 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-epilogue", action="store_true")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the forward + block epilogue leg (fused against two calls)")
     ap.add_argument("--no-slstm", action="store_true")
     ap.add_argument("--bwd-steps", type=int, default=5)
     ap.add_argument("--bwd-warmup", type=int, default=10,
@@ -243,7 +245,9 @@ def main() -> int:
 
     from mlstm_matrix_memory_amd import (MLSTM_BF16, MLSTM_GATE_SWISH, inputs, mlstm_block_epilogue, slstm_fwd,
                                          mlstm_bwd_parallel, mlstm_bwd_workspace_bytes,
-                                         mlstm_fwd_prepare, mlstm_fwd_scan, mlstm_fwd_workspace_bytes, mlstm_step)
+                                         mlstm_fwd_prepare, mlstm_fwd_scan, mlstm_fwd_workspace_bytes, mlstm_step,
+                                         mlstm_fwd_block_workspace_bytes, mlstm_fwd_parallel,
+                                         mlstm_fwd_parallel_block)
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -416,6 +420,65 @@ def main() -> int:
                          "alg_bytes_per_launch": ep_bytes},
         }
         del de, y, ea
+        torch.cuda.empty_cache()
+
+    # ---------------- forward + block epilogue --------------------------------
+    # mlstm_fwd_parallel_block on a shape with one value tile per head, where the
+    # scan applies the epilogue itself, against mlstm_fwd_parallel followed by
+    # mlstm_block_epilogue on the same inputs (events over 10 calls each)
+    if not args.no_block:
+        wb = inputs.WORKLOADS["heads64"]
+        xb = inputs.fwd_inputs(wb)
+        eb = inputs.epilogue_inputs(wb)
+        db = [gpu(xb[k], "bf16" if k in ("q", "k", "v") else "f32") for k in ("q", "k", "v", "i_pre", "f_pre", "o_pre")]
+        xe, ze = gpu(eb["x"], "bf16"), gpu(eb["z"], "bf16")
+        gw, gb, sw = (gpu(eb[k], "f32") for k in ("gn_w", "gn_b", "skip_w"))
+        del xb, eb
+        yb = torch.empty_like(xe)
+        hb = torch.empty_like(xe)
+        Cb = torch.empty((wb.B, wb.NH, wb.dv, wb.dqk), dtype=torch.float32, device=dev)
+        nb = torch.empty((wb.B, wb.NH, wb.dqk), dtype=torch.float32, device=dev)
+        mb = torch.empty((wb.B, wb.NH), dtype=torch.float32, device=dev)
+        wsb = torch.empty(max(1, mlstm_fwd_block_workspace_bytes(wb.B, wb.NH, wb.S, wb.dqk, wb.dv, wb.chunk,
+                                                                 MLSTM_BF16, 1)), dtype=torch.uint8, device=dev)
+        wsb0 = torch.empty(max(1, mlstm_fwd_block_workspace_bytes(wb.B, wb.NH, wb.S, wb.dqk, wb.dv, wb.chunk,
+                                                                  MLSTM_BF16, 0)), dtype=torch.uint8, device=dev)
+        wsf = torch.empty(max(1, mlstm_fwd_workspace_bytes(wb.B, wb.NH, wb.S, wb.dqk, wb.dv, wb.chunk, MLSTM_BF16)),
+                          dtype=torch.uint8, device=dev)
+
+        def fused():
+            mlstm_fwd_parallel_block(*db, xe, ze, gw, gb, sw, wb.chunk, eps=1e-5, act=MLSTM_GATE_SWISH, fuse=1,
+                                     y_out=yb, C_final=Cb, n_final=nb, m_final=mb, workspace=wsb)
+
+        def unfused():
+            mlstm_fwd_parallel_block(*db, xe, ze, gw, gb, sw, wb.chunk, eps=1e-5, act=MLSTM_GATE_SWISH, fuse=0,
+                                     y_out=yb, C_final=Cb, n_final=nb, m_final=mb, workspace=wsb0)
+
+        def two_calls():
+            mlstm_fwd_parallel(*db, wb.chunk, h_out=hb, C_final=Cb, n_final=nb, m_final=mb, workspace=wsf)
+            mlstm_block_epilogue(hb, xe, ze, gw, gb, sw, eps=1e-5, act=MLSTM_GATE_SWISH, y_out=yb)
+
+        def time_calls(fn, n=10):
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(n):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / n
+
+        t_two = time_calls(two_calls)
+        t_fused = time_calls(fused)
+        t_unfused = time_calls(unfused)
+        out["block"] = {
+            "workload": f"{describe(wb)}; block epilogue (swish gate) on h",
+            "fuse1_ms": t_fused, "fuse0_ms": t_unfused, "two_calls_ms": t_two,
+            "tokens_per_s_fuse0": wb.B * wb.S / (t_unfused / 1e3),
+        }
+        del db, xe, ze, gw, gb, sw, yb, hb, Cb, nb, mb, wsb, wsb0, wsf
         torch.cuda.empty_cache()
 
     # ---------------- sLSTM recurrence -----------------------------------------

@@ -13,6 +13,9 @@ Entry points (same names as include/mlstm.h):
   mlstm_bwd_workspace_bytes
   mlstm_block_epilogue
                       the mLSTM block's per-head GroupNorm, learnable skip and external output gate
+  mlstm_fwd_parallel_block, mlstm_fwd_block_workspace_bytes
+                      the forward and the block epilogue in one call (fused where a
+                      workgroup holds a head's whole rows)
   slstm_fwd           the sLSTM recurrence with block-diagonal (per-head) memory mixing
   mlstm_fwd_workspace_bytes, mlstm_status_string, mlstm_error_detail
 """
@@ -29,8 +32,10 @@ from .binding import (  # noqa: F401
     mlstm_bwd_workspace_bytes,
     mlstm_block_epilogue,
     mlstm_error_detail,
+    mlstm_fwd_block_workspace_bytes,
     mlstm_fwd_noalloc_scratch_bytes,
     mlstm_fwd_parallel,
+    mlstm_fwd_parallel_block,
     mlstm_fwd_parallel_noalloc,
     mlstm_fwd_parallel_state,
     mlstm_fwd_prepare,

@@ -76,6 +76,11 @@ def load_library(path: str = LIBRARY) -> ctypes.CDLL:
     lib.mlstm_bwd_parallel.restype = i
     lib.mlstm_bwd_parallel.argtypes = [vp, vp, vp, fp, fp, fp, vp, i, i, i, i, i, i,
                                        fp, fp, fp, fp, fp, fp, vp, sz, vp]
+    lib.mlstm_fwd_block_workspace_bytes.restype = sz
+    lib.mlstm_fwd_block_workspace_bytes.argtypes = [i, i, i, i, i, i, i, i]
+    lib.mlstm_fwd_parallel_block.restype = i
+    lib.mlstm_fwd_parallel_block.argtypes = [vp, vp, vp, fp, fp, fp, vp, vp, fp, fp, fp, i, i, i, i, i, i,
+                                             ctypes.c_float, i, i, i, vp, fp, fp, fp, vp, sz, vp]
     lib.mlstm_block_epilogue.restype = i
     lib.mlstm_block_epilogue.argtypes = [vp, vp, vp, fp, fp, fp, i, i, i, i, ctypes.c_float, i, i, vp, vp]
     lib.slstm_fwd.restype = i
@@ -216,6 +221,74 @@ def mlstm_fwd_parallel(q, k, v, i_pre, f_pre, o_pre, chunk: int,
     if st != MLSTM_OK:
         raise MlstmError("mlstm_fwd_parallel", st, mlstm_error_detail())
     return h_out, C_final, n_final, m_final
+
+
+def mlstm_fwd_block_workspace_bytes(B: int, NH: int, S: int, d_qk: int, d_v: int, chunk: int, dtype: int,
+                                    fuse: int = 0) -> int:
+    return int(load_library().mlstm_fwd_block_workspace_bytes(B, NH, S, d_qk, d_v, chunk, dtype, int(fuse)))
+
+
+def mlstm_fwd_parallel_block(q, k, v, i_pre, f_pre, o_pre, x, z, gn_weight, gn_bias, skip_weight, chunk: int,
+                             eps: float = 1e-5, act: int = 0, fuse: int = 0, y_out=None, C_final=None,
+                             n_final=None, m_final=None, workspace=None, stream=None):
+    """Zero-state forward followed by the block epilogue; returns (y, C, n, m).
+
+    The inputs of mlstm_fwd_parallel, plus x, z like v and gn_weight, gn_bias,
+    skip_weight [NH,d_v] float32 (see mlstm_block_epilogue); h is not returned.
+    fuse=1 applies the epilogue inside the scan where the tiling allows it.
+    """
+    import torch
+    lib = load_library()
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, NH, S, d]")
+    B, NH, S, dqk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must live on a GPU")
+    dt = _dtype_code(q)
+    for t, name, shape, dtype in ((q, "q", (B, NH, S, dqk), q.dtype), (k, "k", (B, NH, S, dqk), q.dtype),
+                                  (v, "v", (B, NH, S, dv), q.dtype), (i_pre, "i_pre", (B, NH, S), torch.float32),
+                                  (f_pre, "f_pre", (B, NH, S), torch.float32),
+                                  (o_pre, "o_pre", (B, NH, S, dv), torch.float32),
+                                  (x, "x", (B, NH, S, dv), q.dtype), (z, "z", (B, NH, S, dv), q.dtype),
+                                  (gn_weight, "gn_weight", (NH, dv), torch.float32),
+                                  (gn_bias, "gn_bias", (NH, dv), torch.float32),
+                                  (skip_weight, "skip_weight", (NH, dv), torch.float32)):
+        _check(t, name, shape, dtype, dev)
+    owned = []
+    if y_out is None:
+        y_out = torch.empty((B, NH, S, dv), dtype=q.dtype, device=dev)
+        owned.append(y_out)
+    if C_final is None:
+        C_final = torch.empty((B, NH, dv, dqk), dtype=torch.float32, device=dev)
+        owned.append(C_final)
+    if n_final is None:
+        n_final = torch.empty((B, NH, dqk), dtype=torch.float32, device=dev)
+        owned.append(n_final)
+    if m_final is None:
+        m_final = torch.empty((B, NH), dtype=torch.float32, device=dev)
+        owned.append(m_final)
+    _check(y_out, "y_out", (B, NH, S, dv), q.dtype, dev)
+    _check(C_final, "C_final", (B, NH, dv, dqk), torch.float32, dev)
+    _check(n_final, "n_final", (B, NH, dqk), torch.float32, dev)
+    _check(m_final, "m_final", (B, NH), torch.float32, dev)
+    need = int(lib.mlstm_fwd_block_workspace_bytes(B, NH, S, dqk, dv, int(chunk), dt, int(fuse)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        owned.append(workspace)
+    _keep_for_stream(stream, dev, owned)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lib.mlstm_fwd_parallel_block(q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                      i_pre.data_ptr(), f_pre.data_ptr(), o_pre.data_ptr(),
+                                      x.data_ptr(), z.data_ptr(), gn_weight.data_ptr(), gn_bias.data_ptr(),
+                                      skip_weight.data_ptr(), B, NH, S, dqk, dv, int(chunk), float(eps), int(act),
+                                      dt, int(fuse), y_out.data_ptr(), C_final.data_ptr(), n_final.data_ptr(),
+                                      m_final.data_ptr(), ws_ptr, ws_bytes, _stream_handle(stream, dev))
+    if st != MLSTM_OK:
+        raise MlstmError("mlstm_fwd_parallel_block", st, mlstm_error_detail())
+    return y_out, C_final, n_final, m_final
 
 
 def mlstm_fwd_noalloc_scratch_bytes() -> int:

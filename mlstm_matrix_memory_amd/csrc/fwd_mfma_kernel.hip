@@ -986,12 +986,23 @@ __device__ __forceinline__ void chunk_store(const f32x4 (&reg)[Pref<C>::NCH], co
     });
 }
 
-template <class C>
+// The mLSTM block's epilogue ("xLSTM: Extended Long Short-Term Memory", Figure 10
+// and its caption) applied to whole rows of h in the scan's output phase:
+// y = (gn_w (.) (h - mean) / sqrt(var + eps) + gn_b + skip_w (.) x) (.) act(z), the
+// mean and population variance over the head's d_v channels of the row.
+struct EpiArgs {
+    const bf16* x; const bf16* z;
+    const float* gw; const float* gb; const float* sw;   // [NH][d_v]
+    float eps; int act; int NH;
+};
+
+template <class C, bool EPI = false>
 __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
     const bf16* __restrict__ q, const bf16* __restrict__ k, const bf16* __restrict__ v,
     const float* __restrict__ o_pre, Ws ws, int S, int Sx, int G, int dv, int n_vt, int remap,
     const float* __restrict__ C0,
-    bf16* __restrict__ h, float* __restrict__ Cout, float* __restrict__ nout, float* __restrict__ mout)
+    bf16* __restrict__ h, float* __restrict__ Cout, float* __restrict__ nout, float* __restrict__ mout,
+    EpiArgs ep)
 {
     constexpr int L = C::L, DQ = C::DQ, NC = C::NC, NK = C::NK, SB = C::SB, CW = C::CW;
     constexpr int THREADS = C::THREADS, TV = C::TV, NS = C::NS;
@@ -1064,6 +1075,97 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
     slab_load<C>(rs, tid, qh, kh, 0, 0);
     float sigma = 1.0f;
 
+    // the block epilogue's per-channel parameters of this lane's columns, and the skip
+    // inputs and gate pre-activations of the rows this wave finishes, loaded a chunk
+    // ahead of the output phase that uses them
+    constexpr int NOB = LB / NK;
+    bf16 xr[NOB][CW][4], zr[NOB][CW][4];
+    // element offset of this lane's (row 4 lg + 16 (kq + NK j) + i, column 16 x + ln)
+    // within a chunk's rows, 32-bit: the chunk base is the only 64-bit address
+    auto rc_off = [&](int j, int x, int i) {
+        return (16 * (kq + NK * j) + 4 * lg + i) * dv + min(vcol + 16 * x, dv - 16) + ln;
+    };
+    auto load_xz = [&](int cc) {
+        const bf16* xb = ep.x + (tinh + (size_t)cc * L) * dv;
+        const bf16* zb = ep.z + (tinh + (size_t)cc * L) * dv;
+#pragma unroll
+        for (int j = 0; j < NOB; ++j)
+#pragma unroll
+            for (int x = 0; x < CW; ++x)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    xr[j][x][i] = xb[rc_off(j, x, i)];
+                    zr[j][x][i] = zb[rc_off(j, x, i)];
+                }
+    };
+    float egw[CW] = {}, egb[CW] = {}, esw[CW] = {};
+    // Rows of chunk c are finished during chunk c + 1: the row sums written in chunk
+    // c's output phase are complete after its last barrier, so epi_mean runs at the
+    // top of chunk c + 1 and writes the centered sums, which are complete after the
+    // next slab barrier, where epi_out normalizes, gates and stores the rows (beside
+    // that slab's products).  No barrier is added to the chunk.
+    __shared__ float epi[EPI ? 2 : 1][2][EPI ? L : 1][EPI ? NC : 1];  // [chunk parity][sums, centered][row][wave]
+    f32x4 yyp[NOB][CW];
+    float mup[NOB][4];
+    const float inv_dv = 1.0f / (float)dv;
+    auto epi_mean = [&](int cc) {
+#pragma unroll
+        for (int j = 0; j < NOB; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int row = 16 * (kq + NK * j) + 4 * lg + i;
+                float t = 0.0f;
+#pragma unroll
+                for (int c2 = 0; c2 < NC; ++c2) t += epi[cc & 1][0][row][c2];
+                mup[j][i] = t * inv_dv;
+                float s2 = 0.0f;
+#pragma unroll
+                for (int x = 0; x < CW; ++x)
+                    if (act[x]) {
+                        const float d = yyp[j][x][i] - mup[j][i];
+                        s2 += d * d;
+                    }
+                s2 = row16_sum(s2);
+                if (ln == 0) epi[cc & 1][1][row][cb] = s2;
+            }
+    };
+    auto epi_out = [&](int cc) {
+        if (active) {
+            bf16* yb = hh + (size_t)cc * L * dv;
+#pragma unroll
+            for (int j = 0; j < NOB; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int row = 16 * (kq + NK * j) + 4 * lg + i;
+                    float t = 0.0f;
+#pragma unroll
+                    for (int c2 = 0; c2 < NC; ++c2) t += epi[cc & 1][1][row][c2];
+                    const float rs = __builtin_amdgcn_rsqf(t * inv_dv + ep.eps);
+#pragma unroll
+                    for (int x = 0; x < CW; ++x) {
+                        if (!act[x]) continue;
+                        const float xv = (float)xr[j][x][i], zv = (float)zr[j][x][i];
+                        const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-zv));
+                        const float g = ep.act ? zv * sg : sg;
+                        const float yo = (egw[x] * (yyp[j][x][i] - mup[j][i]) * rs + egb[x] + esw[x] * xv) * g;
+                        yb[rc_off(j, x, i)] = (bf16)yo;
+                    }
+                }
+        }
+        load_xz(min(cc + 1, nC - 1));   // the rows finished during the next chunk
+    };
+    if constexpr (EPI) {
+        load_xz(0);
+        const int hd = bh % ep.NH;
+#pragma unroll
+        for (int x = 0; x < CW; ++x) {
+            const size_t pc = (size_t)hd * dv + min(vcol + 16 * x, dv - 16) + ln;
+            egw[x] = ep.gw[pc];
+            egb[x] = ep.gb[pc];
+            esw[x] = ep.sw[pc];
+        }
+    }
+
     for (int c = 0; c < nC; ++c) {
         const size_t t0 = (size_t)c * L;
         // sigma' after this chunk's decay; the registers are rescaled instead when
@@ -1083,11 +1185,17 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
             const int buf = (c * NS + s) & 1;
+            if constexpr (EPI) {
+                if (s == 0 && c > 0) epi_mean(c - 1);
+            }
             slab_store<C>(rs, sm, buf, tid);
             lds_barrier();
             // next loads in flight while this slab is multiplied
             if (s + 1 < NS) slab_load<C>(rs, tid, qh, kh, t0, s + 1);
             else if (c + 1 < nC) slab_load<C>(rs, tid, qh, kh, t0 + L, 0);
+            if constexpr (EPI) {
+                if (s == 0 && c > 0) epi_out(c - 1);
+            }
             if (active) {
                 if (s == 0) {
                     // this wave's columns of (w / sigma') (.) V, hi and lo, as B operands
@@ -1186,7 +1294,67 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
             }
         }
         lds_barrier();
-        if (active) {
+        if constexpr (EPI) {
+            // Whole rows of the head are in this workgroup (one value tile): each wave
+            // keeps h of its row blocks in registers and puts the row sums over its
+            // columns in LDS; the next chunk finishes these rows (epi_mean, epi_out).
+            f32x4 (&yy)[NOB][CW] = yyp;
+#pragma unroll
+            for (int j = 0; j < NOB; ++j)
+#pragma unroll
+                for (int x = 0; x < CW; ++x) yy[j][x] = f32x4{0, 0, 0, 0};
+            // row blocks walked with compile-time indices (this wave's are tb = kq + NK j)
+#pragma unroll
+            for (int tb = 0; tb < LB; ++tb) {
+                if (tb % NK != kq || !active) continue;
+                const int j = tb / NK;
+                f32x4 inter[CW], intra[CW];
+#pragma unroll
+                for (int x = 0; x < CW; ++x) {
+                    inter[x] = acc_inter[tb][x];
+#pragma unroll
+                    for (int sl = 0; sl < NK - 1; ++sl)
+                        inter[x] += *reinterpret_cast<const f32x4*>(
+                            red + ((((tb * (NK - 1) + sl) * NC + cb) * CW + x) * 256 + lane * 4));
+                    intra[x] = f32x4{0, 0, 0, 0};
+                }
+#pragma unroll
+                for (int kk = 0; kk <= (16 * tb + 15) / 32; ++kk) {
+                    const bf16x8 ahi = *reinterpret_cast<const bf16x8*>(sm.p[0] + (16 * tb + ln) * PP + 32 * kk + 8 * lg);
+                    const bf16x8 alo = *reinterpret_cast<const bf16x8*>(sm.p[1] + (16 * tb + ln) * PP + 32 * kk + 8 * lg);
+#pragma unroll
+                    for (int x = 0; x < CW; ++x) {
+                        const bf16* vb = sm.v + (32 * kk + 8 * lg + (ln >> 2)) * VP + tcol + 16 * x + 4 * (ln & 3);
+                        const bf16x8 bop = cat(lds_read_tr(vb), lds_read_tr(vb + 4 * VP));
+                        intra[x] = mfma(ahi, bop, intra[x]);
+                        intra[x] = mfma(alo, bop, intra[x]);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int tau = 16 * tb + 4 * lg + i;
+                    const float aa = sm.sc[0][tau] * sigma, ra = sm.sc[1][tau], rden = sm.sc[2][tau];
+#pragma unroll
+                    for (int x = 0; x < CW; ++x) {
+                        if (!act[x]) continue;
+                        const float num = ra * intra[x][i] + aa * inter[x][i];
+                        const float og = __builtin_amdgcn_rcpf(1.0f + __expf(-sm.o[tau * OP + tcol + 16 * x + ln]));
+                        yy[j][x][i] = og * num * rden;
+                    }
+                }
+            }
+            // row sums over this wave's columns (the 16 lanes of a lane group hold one row)
+#pragma unroll
+            for (int j = 0; j < NOB; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float s1 = 0.0f;
+#pragma unroll
+                    for (int x = 0; x < CW; ++x) s1 += yy[j][x][i];
+                    s1 = row16_sum(s1);
+                    if (ln == 0) epi[c & 1][0][16 * (kq + NK * j) + 4 * lg + i][cb] = s1;
+                }
+        } else if (active) {
 #pragma unroll
             for (int tb = 0; tb < LB; ++tb) {
                 if (tb % NK != kq) continue;
@@ -1242,6 +1410,11 @@ __global__ __launch_bounds__(C::THREADS, C::MINB) void chunk_scan2_kernel(
         }
         sigma = sig_new;
         lds_barrier();
+    }
+    if constexpr (EPI) {
+        epi_mean(nC - 1);
+        lds_barrier();
+        epi_out(nC - 1);
     }
 
     if (seg != G - 1) return;
@@ -1675,7 +1848,7 @@ int segments(const FwdArgs& a) {
     return G;
 }
 
-template <class C>
+template <class C, bool EPI>
 hipError_t launch_scan2(const FwdArgs& a, const Ws& w, int G) {
     constexpr int L = C::L;
     const int heads = a.B * a.NH;
@@ -1694,9 +1867,10 @@ hipError_t launch_scan2(const FwdArgs& a, const Ws& w, int G) {
     const int n_vt = (a.dv + C::TV - 1) / C::TV;
     const int nwg = heads * G * n_vt;
     const int remap = (nwg % 8 == 0) ? 1 : 0;
-    hipLaunchKernelGGL((chunk_scan2_kernel<C>), dim3(nwg), dim3(C::THREADS), 0, a.stream,
+    const EpiArgs ep = {(const bf16*)a.ep_x, (const bf16*)a.ep_z, a.ep_gw, a.ep_gb, a.ep_sw, a.ep_eps, a.ep_act, a.NH};
+    hipLaunchKernelGGL((chunk_scan2_kernel<C, EPI>), dim3(nwg), dim3(C::THREADS), 0, a.stream,
                        (const bf16*)a.q, (const bf16*)a.k, (const bf16*)a.v, a.o_pre, w, a.S, a.Sx, G, a.dv, n_vt, remap,
-                       a.C0, (bf16*)a.h, a.C, a.n, a.m);
+                       a.C0, (bf16*)a.h, a.C, a.n, a.m, ep);
     return hipGetLastError();
 }
 
@@ -1733,6 +1907,11 @@ hipError_t run4(const FwdArgs& a, int stage, size_t* bytes) {
     using C = Scan4Cfg<DQ, NK, CW, MINB, PD, OP>;
     // the operand copies of one head are addressed with 32-bit buffer offsets
     if ((size_t)a.S * DQ * sizeof(bf16) > (size_t)INT_MAX) return pick_pipelined(C::L, DQ)(a, stage, bytes);
+    if (stage == 3) {                     // the streaming form writes h as is
+        *bytes = 0;
+        return hipSuccess;
+    }
+    if (stage == 1 && a.ep_x != nullptr) return hipErrorNotSupported;
     const int G = segments<C>(a);
     if (stage == 2) {
         *bytes = ws_bytes((size_t)a.B * a.NH, a.S, C::L, a.dqk, a.dv, G, true);
@@ -1745,9 +1924,18 @@ hipError_t run4(const FwdArgs& a, int stage, size_t* bytes) {
 
 // stage 0 = prepare (chunk_prep, gate_scan, den), stage 1 = scan (segments, chunk_scan2),
 // stage 2 = workspace size only
+// stage 3 = whether this tiling can apply the block epilogue itself (*bytes = 1)
 template <int L, int DQ, int NC, int NK, int SB, int MINB, int CW, bool RS>
 hipError_t run2(const FwdArgs& a, int stage, size_t* bytes) {
     using C = Scan2Cfg<L, DQ, NC, NK, SB, MINB, CW, RS>;
+    // the fused epilogue is built for the 64-column tiles of one wave per SIMD (one key
+    // part), with one tile per head: the two-key-part tilings run two waves per SIMD
+    // and have no registers left for the epilogue's operands
+    constexpr bool EPI_OK = C::TV == 64 && C::NK == 1;
+    if (stage == 3) {
+        *bytes = (EPI_OK && a.dv <= C::TV) ? 1 : 0;
+        return hipSuccess;
+    }
     const int G = segments<C>(a);
     if (stage == 2) {
         *bytes = ws_bytes((size_t)a.B * a.NH, a.S, L, a.dqk, a.dv, G, false);
@@ -1755,7 +1943,13 @@ hipError_t run2(const FwdArgs& a, int stage, size_t* bytes) {
     }
     Ws w = ws_layout(a.ws, (size_t)a.B * a.NH, a.S, L, a.dqk, a.dv, G, false);
     if (stage == 0) return launch_prep<L>(a, w);
-    return launch_scan2<C>(a, w, G);
+    if (a.ep_x != nullptr) {
+        if constexpr (EPI_OK) {
+            if (a.dv <= C::TV) return launch_scan2<C, true>(a, w, G);
+        }
+        return hipErrorNotSupported;
+    }
+    return launch_scan2<C, false>(a, w, G);
 }
 
 // supported (chunk, d_qk) pairs and the tiling used for each:
@@ -1841,6 +2035,14 @@ size_t mfma_fwd_workspace_bytes(const FwdArgs& a) {
     size_t bytes = 0;
     if (f) (void)f(a, 2, &bytes);
     return bytes;
+}
+
+bool mfma_fwd_block_fusable(const FwdArgs& a) {
+    if (!mfma_fwd_supported(a)) return false;
+    RunFn f = pick(mfma_chunk(a), a.dqk);
+    size_t ok = 0;
+    if (!f || f(a, 3, &ok) != hipSuccess) return false;
+    return ok != 0;
 }
 
 hipError_t launch_fwd_mfma_prepare(const FwdArgs& a) {

@@ -197,6 +197,13 @@ size_t mlstm_fwd_workspace_bytes(int B, int NH, int S, int d_qk, int d_v, int ch
     return plan_fwd(B, NH, S, d_qk, d_v, chunk, dtype).total();
 }
 
+// The block epilogue's inputs when the scan applies it itself (h_out then receives y).
+struct EpiIn {
+    const void* x; const void* z;
+    const float* gw; const float* gb; const float* sw;
+    float eps; int act;
+};
+
 // Validates the forward's arguments and launches it; stage bits: 1 = prepare, 2 = scan
 // (the staged entry points require S to be a multiple of chunk and the zero initial state).
 static mlstm_status fwd_common(const void* q, const void* k, const void* v,
@@ -205,7 +212,7 @@ static mlstm_status fwd_common(const void* q, const void* k, const void* v,
                                const float* C_init, const float* n_init, const float* m_init,
                                void* h_out, float* C_final, float* n_final, float* m_final,
                                void* workspace, size_t workspace_bytes, void* stream, int stages,
-                               bool ragged_ok) {
+                               bool ragged_ok, const EpiIn* ep = nullptr) {
     mlstm_status s = check_fwd_sizes(B, NH, S, d_qk, d_v, chunk, dtype, ragged_ok);
     if (s != MLSTM_OK) return s;
     // tensors read or written with vector accesses need 16-byte alignment, the others their element size
@@ -284,6 +291,10 @@ static mlstm_status fwd_common(const void* q, const void* k, const void* v,
         a.C = C_dst; a.n = n_dst; a.m = pl.tail ? m_mid : m_final;
         a.C0 = C_init; a.n0 = n_init; a.m0 = m_init;
         a.ws = workspace; a.ws_bytes = pl.main_bytes; a.stream = st;
+        if (ep) {
+            a.ep_x = ep->x; a.ep_z = ep->z; a.ep_gw = ep->gw; a.ep_gb = ep->gb; a.ep_sw = ep->sw;
+            a.ep_eps = ep->eps; a.ep_act = ep->act;
+        }
         if (pl.pad) {
             // zero-padded copies (whole sequences, so the token stride stays S); the
             // staged entry points take no initial state, so C'_0 and n'_0 only come
@@ -351,6 +362,88 @@ mlstm_status mlstm_fwd_parallel_state(const void* q, const void* k, const void* 
                                       void* workspace, size_t workspace_bytes, void* stream) {
     return fwd_common(q, k, v, i_pre, f_pre, o_pre, B, NH, S, d_qk, d_v, chunk, dtype, C_init, n_init, m_init,
                       h_out, C_final, n_final, m_final, workspace, workspace_bytes, stream, 3, true);
+}
+
+// How a forward with the block epilogue runs: fused into the scan's output rows when
+// the caller asks for it and the shape runs whole on the matrix cores with one value
+// tile per head; otherwise the forward writes h into the workspace (after its own
+// part) and the epilogue kernel reads it from there.
+struct BlockPlan {
+    bool fused;
+    size_t fwd_bytes;       // the forward's own workspace
+    size_t total;           // plus h when not fused
+};
+
+static BlockPlan plan_block(int B, int NH, int S, int d_qk, int d_v, int chunk, mlstm_dtype dtype, int fuse) {
+    BlockPlan bp = {};
+    const FwdPlan pl = plan_fwd(B, NH, S, d_qk, d_v, chunk, dtype);
+    if (fuse && dtype == MLSTM_BF16 && pl.S_main == S && !pl.tail)
+        bp.fused = mlstm::mfma_fwd_block_fusable(make_fwd_args(B, NH, S, pl.dq_run, d_v, chunk, dtype));
+    bp.fwd_bytes = pl.total();
+    const size_t el = dtype == MLSTM_BF16 ? 2 : 4;
+    bp.total = bp.fused ? bp.fwd_bytes : align256(bp.fwd_bytes) + align256((size_t)B * NH * S * d_v * el);
+    return bp;
+}
+
+size_t mlstm_fwd_block_workspace_bytes(int B, int NH, int S, int d_qk, int d_v, int chunk, mlstm_dtype dtype,
+                                       int fuse) {
+    if (check_fwd_sizes(B, NH, S, d_qk, d_v, chunk, dtype, false) != MLSTM_OK) return 0;
+    return plan_block(B, NH, S, d_qk, d_v, chunk, dtype, fuse).total;
+}
+
+mlstm_status mlstm_fwd_parallel_block(const void* q, const void* k, const void* v,
+                                      const float* i_pre, const float* f_pre, const float* o_pre,
+                                      const void* x, const void* z,
+                                      const float* gn_weight, const float* gn_bias, const float* skip_weight,
+                                      int B, int NH, int S, int d_qk, int d_v, int chunk,
+                                      float eps, mlstm_gate_act act, mlstm_dtype dtype, int fuse,
+                                      void* y_out, float* C_final, float* n_final, float* m_final,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+    mlstm_status s = check_fwd_sizes(B, NH, S, d_qk, d_v, chunk, dtype, false);
+    if (fuse != 0 && fuse != 1) return fail(MLSTM_ERR_INVALID_ARG, "fuse=%d is neither 0 nor 1", fuse);
+    if (s != MLSTM_OK) return s;
+    if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(MLSTM_ERR_INVALID_ARG, "eps=%g must be finite and >= 0", eps);
+    if (act != MLSTM_GATE_SIGMOID && act != MLSTM_GATE_SWISH)
+        return fail(MLSTM_ERR_INVALID_ARG, "act=%d is neither MLSTM_GATE_SIGMOID nor MLSTM_GATE_SWISH", (int)act);
+    const void* eptrs[] = {x, z, gn_weight, gn_bias, skip_weight, y_out};
+    const char* enames[] = {"x", "z", "gn_weight", "gn_bias", "skip_weight", "y_out"};
+    for (int p = 0; p < 6; ++p) {
+        if (!eptrs[p]) return fail(MLSTM_ERR_INVALID_ARG, "%s is NULL", enames[p]);
+        if (!aligned16(eptrs[p])) return fail(MLSTM_ERR_INVALID_ARG, "%s is not 16-byte aligned", enames[p]);
+    }
+    const BlockPlan bp = plan_block(B, NH, S, d_qk, d_v, chunk, dtype, fuse);
+    if (bp.total > 0) {
+        if (!workspace || workspace_bytes < bp.total)
+            return fail(MLSTM_ERR_WORKSPACE, "workspace of %zu bytes given, %zu needed", workspace_bytes, bp.total);
+        if (!aligned16(workspace)) return fail(MLSTM_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    }
+    {
+        // y is written while x and z are still read, and the parameters are read throughout
+        const size_t el = dtype == MLSTM_BF16 ? 2 : 4;
+        const size_t yb = (size_t)B * NH * S * d_v * el, pb = (size_t)NH * d_v * 4;
+        const Buf bufs[] = {
+            {y_out, yb, "y_out"},
+            {x, yb, "x"}, {z, yb, "z"}, {gn_weight, pb, "gn_weight"}, {gn_bias, pb, "gn_bias"},
+            {skip_weight, pb, "skip_weight"}, {bp.total > 0 ? workspace : nullptr, bp.total, "workspace"},
+        };
+        if ((s = check_disjoint(bufs, (int)(sizeof(bufs) / sizeof(bufs[0])), 1)) != MLSTM_OK) return s;
+    }
+    if (bp.fused) {
+        const EpiIn e = {x, z, gn_weight, gn_bias, skip_weight, eps, (int)act};
+        return fwd_common(q, k, v, i_pre, f_pre, o_pre, B, NH, S, d_qk, d_v, chunk, dtype, nullptr, nullptr,
+                          nullptr, y_out, C_final, n_final, m_final, workspace, bp.fwd_bytes, stream, 3, false, &e);
+    }
+    void* h_tmp = (char*)workspace + align256(bp.fwd_bytes);
+    s = fwd_common(q, k, v, i_pre, f_pre, o_pre, B, NH, S, d_qk, d_v, chunk, dtype, nullptr, nullptr, nullptr,
+                   h_tmp, C_final, n_final, m_final, workspace, bp.fwd_bytes, stream, 3, false);
+    if (s != MLSTM_OK) return s;
+    mlstm::EpilogueArgs a = {};
+    a.h = h_tmp; a.x = x; a.z = z; a.gn_w = gn_weight; a.gn_b = gn_bias; a.skip_w = skip_weight;
+    a.B = B; a.NH = NH; a.S = S; a.dv = d_v; a.eps = eps; a.act = (int)act; a.dtype = dtype; a.y = y_out;
+    a.stream = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = mlstm::launch_epilogue(a);
+    if (e != hipSuccess) return fail(MLSTM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
 }
 
 size_t mlstm_fwd_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }

@@ -114,6 +114,11 @@ struct FwdArgs {
     const float* C0; const float* n0; const float* m0;   // initial state, all null = zero
     void* ws; size_t ws_bytes;
     hipStream_t stream;
+    // block epilogue applied to h in the scan's output rows (mlstm_fwd_parallel_block
+    // on a fusable shape; ep_x null = h is written as is): h then receives y
+    const void* ep_x; const void* ep_z;
+    const float* ep_gw; const float* ep_gb; const float* ep_sw;
+    float ep_eps; int ep_act;
 };
 
 struct StepArgs {
@@ -170,6 +175,9 @@ hipError_t launch_fwd_valu(const FwdArgs& a);
 int mfma_fwd_chunk(const FwdArgs& a);          // chunk the MFMA path executes for these widths, 0 = none
 bool mfma_fwd_supported(const FwdArgs& a);
 size_t mfma_fwd_workspace_bytes(const FwdArgs& a);
+// whether the scan can apply the block epilogue to whole rows itself: the pipelined
+// form with one value tile per head (d_v <= its 64-column tile)
+bool mfma_fwd_block_fusable(const FwdArgs& a);
 hipError_t launch_fwd_mfma_prepare(const FwdArgs& a);
 hipError_t launch_fwd_mfma_scan(const FwdArgs& a);
 

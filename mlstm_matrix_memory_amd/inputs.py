@@ -69,6 +69,9 @@ WORKLOADS = {
     "decode": Workload("decode", "step", 256, 4, 128, 512, 512, 0, "bf16", scale_k=False, seed=5),
     # a key width off the matrix cores' 64-column grid (runs zero-padded to 128)
     "lm_125m_d96": Workload("lm_125m_d96", "fwd", 8, 4, 2048, 96, 96, 64, "bf16", seed=7),
+    # many narrow heads: one 64-column value tile per head, where the block epilogue
+    # runs inside the scan (embedding 1024 over 16 heads)
+    "heads64": Workload("heads64", "fwd", 8, 16, 2048, 64, 64, 64, "bf16", seed=8),
     # sLSTM: d_qk = d_v = d_h, the cells per head (embedding 768 over 4 heads)
     "slstm_125m": Workload("slstm_125m", "slstm", 8, 4, 2048, 192, 192, 0, "bf16", seed=6),
 }

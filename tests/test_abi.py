@@ -388,3 +388,42 @@ def test_bf16_widths_off_the_tiling_grid_take_the_matrix_core_path_padded(dqk, c
     own = b.mlstm_fwd_workspace_bytes(1, 2, S, pad, dv, chunk, b.MLSTM_BF16)
     got = b.mlstm_fwd_workspace_bytes(1, 2, S, dqk, dv, chunk, b.MLSTM_BF16)
     assert own > 0 and got >= own + 2 * heads * S * pad * 2
+
+
+def _blk(lib, eps=1e-5, act=0, ptrs=None, ws=None, ws_bytes=0, dt=b.MLSTM_BF16, S=256, dqk=64, dv=64, fuse=1):
+    p = [FAKE * (j + 1) for j in range(15)] if ptrs is None else ptrs
+    return lib.mlstm_fwd_parallel_block(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], p[8], p[9], p[10],
+                                        1, 2, S, dqk, dv, 64, eps, act, dt, fuse, p[11], p[12], p[13], p[14],
+                                        ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,detail", [(dict(eps=-1.0), "eps"), (dict(act=5), "act=5"), (dict(S=100), "multiple"),
+                                       (dict(fuse=2), "fuse=2")])
+def test_block_forward_rejects_bad_arguments(lib, kw, detail):
+    assert _blk(lib, **kw) == b.MLSTM_ERR_INVALID_ARG
+    assert detail in b.mlstm_error_detail()
+
+
+@pytest.mark.parametrize("which,name", [(6, "x"), (7, "z"), (8, "gn_weight"), (11, "y_out")])
+def test_block_forward_rejects_null_epilogue_pointers(lib, which, name):
+    p = [FAKE * (j + 1) for j in range(15)]
+    p[which] = None
+    assert _blk(lib, ptrs=p) == b.MLSTM_ERR_INVALID_ARG
+    assert f"{name} is NULL" in b.mlstm_error_detail()
+
+
+def test_block_forward_workspace():
+    # a shape with one 64-column value tile per head fuses the epilogue into the scan
+    # and needs only the forward's workspace; one with several tiles also holds h
+    own = b.mlstm_fwd_workspace_bytes(1, 2, 256, 64, 64, 64, b.MLSTM_BF16)
+    assert b.mlstm_fwd_block_workspace_bytes(1, 2, 256, 64, 64, 64, b.MLSTM_BF16, 1) == own > 0
+    # unfused (asked for, or a shape without a fusable tiling): the forward's own plus h
+    assert b.mlstm_fwd_block_workspace_bytes(1, 2, 256, 64, 64, 64, b.MLSTM_BF16, 0) >= own + 2 * 256 * 64 * 2
+    tiles = b.mlstm_fwd_block_workspace_bytes(1, 2, 256, 384, 384, 64, b.MLSTM_BF16, 1)
+    assert tiles >= b.mlstm_fwd_workspace_bytes(1, 2, 256, 384, 384, 64, b.MLSTM_BF16) + 2 * 256 * 384 * 2
+    assert b.mlstm_fwd_block_workspace_bytes(1, 2, 256, 64, 64, 48, b.MLSTM_BF16, 1) == 0
+
+
+def test_block_forward_rejects_small_workspace(lib):
+    need = b.mlstm_fwd_block_workspace_bytes(1, 2, 256, 64, 64, 64, b.MLSTM_BF16, 1)
+    assert _blk(lib, ws=0x40000000, ws_bytes=need - 1) == b.MLSTM_ERR_WORKSPACE
