@@ -9,6 +9,7 @@ normalizes each row of h in registers); every other call runs the forward into
 the workspace and the epilogue kernel after it.  Which path a call takes shows
 in the workspace: the fused path needs exactly the forward's own.
 """
+import numpy as np
 import pytest
 
 import oracle
@@ -114,3 +115,41 @@ def test_fused_equals_forward_then_epilogue_up_to_rounding():
     assert torch.equal(C, C2) and torch.equal(n, n2) and torch.equal(m, m2)
     errs = {}
     check("y", to_np(y), to_np(y2), 2e-2, errs)
+
+
+# (batch index, head index) of the sampled heads
+SAMPLED = [(0, 0), (3, 7), (7, 15)]
+
+
+@pytest.mark.parametrize("fuse", [1, 0])
+def test_full_size_heads64_sampled_heads(orc, fuse):
+    """The whole 16-head workload (B=8, NH=16, S=2048, d=64, chunk 64) in the launch
+    configuration the benchmark times, compared with the oracle on sampled heads
+    (each head is an independent recurrence and its own GroupNorm group)."""
+    import torch
+    from mlstm_matrix_memory_amd import (MLSTM_BF16, mlstm_fwd_block_workspace_bytes, mlstm_fwd_parallel_block,
+                                         mlstm_fwd_workspace_bytes)
+    w = inputs.WORKLOADS["heads64"]
+    announce(f"fwd+epilogue full size heads64 B={w.B} NH={w.NH} S={w.S} d={w.dqk} fuse={fuse}")
+    own = mlstm_fwd_workspace_bytes(w.B, w.NH, w.S, w.dqk, w.dv, w.chunk, MLSTM_BF16)
+    assert (mlstm_fwd_block_workspace_bytes(w.B, w.NH, w.S, w.dqk, w.dv, w.chunk, MLSTM_BF16, fuse) == own) == bool(fuse)
+    x = inputs.fwd_inputs(w)
+    e = inputs.epilogue_inputs(w)
+    dev = [to_gpu(x[key], "bf16" if key in ("q", "k", "v") else "f32") for key in KEYS]
+    xe, ze = to_gpu(e["x"], "bf16"), to_gpu(e["z"], "bf16")
+    gw, gb, sw = (to_gpu(e[n], "f32") for n in ("gn_w", "gn_b", "skip_w"))
+    y, C, n, m = mlstm_fwd_parallel_block(*dev, xe, ze, gw, gb, sw, w.chunk, eps=1e-5, act=1, fuse=fuse)
+    torch.cuda.synchronize()
+    y, C, n, m = to_np(y), to_np(C), to_np(n), to_np(m)
+    errs = {}
+    for b, h in SAMPLED:
+        one = {key: x[key][b:b + 1, h:h + 1] for key in KEYS}
+        rh, rC, rn, rm = orc.fwd(*(one[key] for key in KEYS))
+        ry = orc.epilogue(rh, e["x"][b:b + 1, h:h + 1], e["z"][b:b + 1, h:h + 1], e["gn_w"][h:h + 1],
+                          e["gn_b"][h:h + 1], e["skip_w"][h:h + 1], 1e-5, 1)
+        check(f"y{b},{h}", y[b:b + 1, h:h + 1], ry, TOL["bf16"], errs)
+        check(f"C{b},{h}", C[b:b + 1, h:h + 1], rC, TOL["bf16"], errs)
+        check(f"n{b},{h}", n[b:b + 1, h:h + 1], rn, TOL["bf16"], errs)
+        check(f"m{b},{h}", m[b:b + 1, h:h + 1], rm, TOL["bf16"], errs)
+    assert np.all(np.isfinite(y))
+    print(errs)
