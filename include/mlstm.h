@@ -347,7 +347,7 @@ mlstm_status mlstm_block_epilogue(const void *h, const void *x, const void *z,
  *             reads it back.
  * The fused rows add their normalization to the scan's sequential chunk loop, while
  * the epilogue kernel runs over the whole chip at the memory rate: on one MI355X,
- * B=8, NH=16, S=2048, d_qk=d_v=64 took 0.27 ms fused against 0.21 ms unfused, so
+ * B=8, NH=16, S=2048, d_qk=d_v=64 took 0.198 ms fused against 0.188 ms unfused, so
  * fuse = 1 is for callers that must save the 2 * |h| bytes of HBM traffic.  The
  * result is the same up to rounding either way (the fused path normalizes h
  * before its rounding to the output dtype).

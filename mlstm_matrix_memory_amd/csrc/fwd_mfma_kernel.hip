@@ -184,7 +184,7 @@ constexpr int SS_TILE = 128;           // key rows and value columns of a segmen
 constexpr int SS_MAXP = 8;
 inline int seg_parts(size_t heads, size_t nC, int DQ, int DV, int G) {
     if (G <= 1) return 1;
-    const size_t tiles = (size_t)(DQ / SS_TILE) * ((DV + SS_TILE - 1) / SS_TILE);
+    const size_t tiles = (size_t)((DQ + SS_TILE - 1) / SS_TILE) * ((DV + SS_TILE - 1) / SS_TILE);
     const size_t nCs = nC / G;
     int P = 1;
     while (2 * P <= SS_MAXP && tiles * (G - 1) * heads * P < 512 && nCs % (2 * P) == 0 && nCs / (2 * P) >= 4) P *= 2;
@@ -686,7 +686,9 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
     constexpr int UNITS = L * SS_TILE / 8;                  // 16-byte units of one tile
     constexpr int UPT = (UNITS + SS_THREADS - 1) / SS_THREADS;
 
-    const int n_kt = dqk / SS_TILE;
+    // a key width that is an odd multiple of 64 leaves the last tile's upper 64 keys
+    // empty: they load as zeros and their waves skip the products and the store
+    const int n_kt = (dqk + SS_TILE - 1) / SS_TILE;
     const int kt = blockIdx.x % n_kt, vt = blockIdx.x / n_kt;
     const int g = blockIdx.y / ws.sp, part = blockIdx.y % ws.sp, bh = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -709,7 +711,8 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
             const int idx = tid + u * SS_THREADS;
             if (idx < UNITS) {
                 const int row = idx / (SS_TILE / 8), c8 = 8 * (idx % (SS_TILE / 8));
-                rk[u] = *reinterpret_cast<const bf16x8*>(k + (ti0 + row) * dqk + key0 + c8);
+                rk[u] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
+                if (key0 + c8 < dqk) rk[u] = *reinterpret_cast<const bf16x8*>(k + (ti0 + row) * dqk + key0 + c8);
                 rv[u] = bf16x8{0, 0, 0, 0, 0, 0, 0, 0};
                 if (val0 + c8 < dv) rv[u] = *reinterpret_cast<const bf16x8*>(v + (ti0 + row) * dv + val0 + c8);
                 rw[u] = ws.w[t0 + row];
@@ -725,6 +728,7 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
         for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0, 0, 0, 0};
 
     float A = 1.0f;          // product of alpha over the part's chunks after the current one
+    const bool keys_in = key0 + 64 * wr < dqk;              // wave-uniform
     load(nCp - 1);
     for (int ci = nCp - 1; ci >= 0; --ci) {
         __syncthreads();     // previous tiles consumed
@@ -743,6 +747,7 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
         A *= ralpha;
         __syncthreads();
         if (ci > 0) load(ci - 1);
+        if (!keys_in) continue;
 #pragma unroll
         for (int kk = 0; kk < L / 32; ++kk) {
             const int trow = 32 * kk + 8 * lg + (ln >> 2);
@@ -770,6 +775,7 @@ __global__ __launch_bounds__(SS_THREADS) void seg_state_kernel(
     for (int c = c_first + nCp; c < (g + 1) * nCs; ++c) later *= ws.alpha[(size_t)bh * nC + c];
     // this part's share of dC_g: rows of the D layout are keys, columns are values
     float* dst = ws.cpart + (((size_t)bh * (G - 1) + g) * ws.sp + part) * (size_t)dv * dqk;
+    if (!keys_in) return;
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
@@ -1843,7 +1849,7 @@ int segments(const FwdArgs& a) {
     const int units = a.B * a.NH * ((a.dv + C::TV - 1) / C::TV);
     const int nC = a.S / C::L;
     int G = 1;
-    if (a.dqk % SS_TILE != 0) return G;       // the segment-state tiles cover whole key blocks
+    if (a.dqk % 64 != 0) return G;            // the segment-state waves cover whole 64-key blocks
     while (2 * G <= SC_MAXG && units * 2 * G <= 256 && nC % (2 * G) == 0 && nC / (2 * G) >= 4) G *= 2;
     return G;
 }
@@ -1853,7 +1859,7 @@ hipError_t launch_scan2(const FwdArgs& a, const Ws& w, int G) {
     constexpr int L = C::L;
     const int heads = a.B * a.NH;
     if (G > 1) {
-        dim3 sgrid((a.dqk / SS_TILE) * ((a.dv + SS_TILE - 1) / SS_TILE), (G - 1) * w.sp, heads);
+        dim3 sgrid(((a.dqk + SS_TILE - 1) / SS_TILE) * ((a.dv + SS_TILE - 1) / SS_TILE), (G - 1) * w.sp, heads);
         hipLaunchKernelGGL((seg_state_kernel<L>), sgrid, dim3(SS_THREADS), 0, a.stream,
                            (const bf16*)a.k, (const bf16*)a.v, w, a.S, a.Sx, a.dqk, a.dv, G);
         hipError_t e = hipGetLastError();
@@ -1879,7 +1885,7 @@ hipError_t launch_scan4(const FwdArgs& a, const Ws& w, int G) {
     constexpr int L = C::L;
     const int heads = a.B * a.NH;
     if (G > 1) {
-        dim3 sgrid((a.dqk / SS_TILE) * ((a.dv + SS_TILE - 1) / SS_TILE), (G - 1) * w.sp, heads);
+        dim3 sgrid(((a.dqk + SS_TILE - 1) / SS_TILE) * ((a.dv + SS_TILE - 1) / SS_TILE), (G - 1) * w.sp, heads);
         hipLaunchKernelGGL((seg_state_kernel<L>), sgrid, dim3(SS_THREADS), 0, a.stream,
                            (const bf16*)a.k, (const bf16*)a.v, w, a.S, a.Sx, a.dqk, a.dv, G);
         hipError_t e = hipGetLastError();

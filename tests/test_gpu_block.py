@@ -63,6 +63,7 @@ FUSED = [
     (dict(B=1, NH=2, S=256, dqk=64, dv=64), 16),         # 16-token chunks run as 64-token ones
     (dict(B=1, NH=2, S=256, dqk=128, dv=64), 32),        # the 32-token tiling of width 128
     (dict(B=1, NH=1, S=4096, dqk=128, dv=64), 64),       # several sequence segments
+    (dict(B=1, NH=2, S=2048, dqk=64, dv=64), 64),        # segments at width 64
 ]
 
 

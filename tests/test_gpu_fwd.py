@@ -117,7 +117,12 @@ def test_maximum_widths(orc, dtype, dqk, dv):
 SEGMENTED = [(dict(B=1, NH=1, S=2048, dqk=128, dv=96), 64), (dict(B=1, NH=2, S=1024, dqk=384, dv=384), 32),
              (dict(B=1, NH=1, S=4096, dqk=256, dv=256), 128),
              # the streaming form of the scan (widths 512 and 1024), one with a ragged value tile
-             (dict(B=1, NH=1, S=2048, dqk=512, dv=512), 64), (dict(B=1, NH=2, S=1024, dqk=1024, dv=112), 64)]
+             (dict(B=1, NH=1, S=2048, dqk=512, dv=512), 64), (dict(B=1, NH=2, S=1024, dqk=1024, dv=112), 64),
+             # key widths that are odd multiples of 64 (the segment sums' last key tile half
+             # empty), one of them reached by padding 160 to 192
+             (dict(B=1, NH=2, S=2048, dqk=64, dv=64), 64), (dict(B=1, NH=1, S=2048, dqk=192, dv=96), 64),
+             (dict(B=1, NH=2, S=1024, dqk=320, dv=64), 64), (dict(B=1, NH=1, S=2048, dqk=448, dv=160), 64),
+             (dict(B=1, NH=1, S=2048, dqk=160, dv=64), 64)]
 
 
 @pytest.mark.parametrize("over,chunk", SEGMENTED, ids=lambda v: str(v))
@@ -135,10 +140,11 @@ def test_bf16_segmented_sequence(orc, over, chunk):
 # first shape runs as 8 segments of 2 token parts each, the second (8 heads, two of
 # them compared) as 4 segments of 4 parts.
 SEGMENTED_SLOW_DECAY = [(dict(B=1, NH=1, S=4096, dqk=256, dv=256), None),
-                        (dict(B=1, NH=8, S=4096, dqk=256, dv=256), (np.array([[0, 0]]), np.array([[1, 6]])))]
+                        (dict(B=1, NH=8, S=4096, dqk=256, dv=256), (np.array([[0, 0]]), np.array([[1, 6]]))),
+                        (dict(B=1, NH=2, S=4096, dqk=64, dv=64), None)]
 
 
-@pytest.mark.parametrize("over,sel", SEGMENTED_SLOW_DECAY, ids=["1head", "8heads"])
+@pytest.mark.parametrize("over,sel", SEGMENTED_SLOW_DECAY, ids=["1head", "8heads", "2heads_d64"])
 def test_bf16_segmented_slow_decay(orc, over, sel):
     w = inputs.WORKLOADS["lm_125m"]
     announce(f"fwd bf16 segmented slow decay {over}")

@@ -55,6 +55,7 @@ CASES = [
     ("lm_1_3b", dict(B=1, NH=1, S=300), (64,), 64, "bf16"),
     ("lm_1_3b", dict(B=1, NH=2, S=1100, dqk=512, dv=512), (320,), 64, "bf16"),   # streaming scan from a state
     ("long_ctx", dict(B=1, NH=1, S=3000, dqk=256, dv=256), (1024,), 64, "bf16"),  # segments from a state
+    ("lm_125m", dict(B=1, NH=2, S=3000, dqk=64, dv=64), (1024,), 64, "bf16"),      # segments from a state, d 64
     ("long_ctx", dict(B=1, NH=2, S=1100), (129,), 128, "bf16"),
     ("tiny", dict(B=2, NH=2, S=150, dqk=48, dv=80), (37, 100), 16, "f32"),
 ]
